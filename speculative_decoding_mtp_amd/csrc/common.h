@@ -1,0 +1,120 @@
+// Shared device helpers for the MTP kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mtp {
+
+constexpr int kWG = 256;   // threads per workgroup in every kernel here (4 waves)
+constexpr int kWave = 64;
+
+// Workspace status word bits (the first int32 of every workspace).
+constexpr int kFlagCapacity = 1;
+constexpr int kFlagToken = 2;
+
+// ----------------------------------------------------------------------------------------------
+// element types: a 16-byte vector of weights holds VE elements
+// ----------------------------------------------------------------------------------------------
+struct BF16 {
+  using T = uint16_t;
+  static constexpr int VE = 8;
+  __device__ __forceinline__ static void cvt(const uint4 v, float (&f)[8]) {
+    f[0] = __uint_as_float(v.x << 16);
+    f[1] = __uint_as_float(v.x & 0xffff0000u);
+    f[2] = __uint_as_float(v.y << 16);
+    f[3] = __uint_as_float(v.y & 0xffff0000u);
+    f[4] = __uint_as_float(v.z << 16);
+    f[5] = __uint_as_float(v.z & 0xffff0000u);
+    f[6] = __uint_as_float(v.w << 16);
+    f[7] = __uint_as_float(v.w & 0xffff0000u);
+  }
+  __device__ __forceinline__ static float get(const T* p, long i) { return __uint_as_float(uint32_t(p[i]) << 16); }
+  // round-to-nearest-even float -> bf16 (finite inputs; NaN stays NaN)
+  __device__ __forceinline__ static T put(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7f800000u) == 0x7f800000u) return T((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return T(u >> 16);
+  }
+};
+
+struct F32 {
+  using T = float;
+  static constexpr int VE = 4;
+  __device__ __forceinline__ static void cvt(const uint4 v, float (&f)[4]) {
+    f[0] = __uint_as_float(v.x);
+    f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z);
+    f[3] = __uint_as_float(v.w);
+  }
+  __device__ __forceinline__ static float get(const T* p, long i) { return p[i]; }
+  __device__ __forceinline__ static T put(float f) { return f; }
+};
+
+// streaming 16-byte load (weights are read once per step: do not keep them in cache)
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_stream(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// (value, index) order used by every argmax: larger value first, lower index on ties.
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    float ov = __shfl_xor(v, o, kWave);
+    int oi = __shfl_xor(i, o, kWave);
+    if (better(ov, oi, v, i)) { v = ov; i = oi; }
+  }
+}
+
+// Sum of `n` per-thread values across the 256-thread workgroup; every thread gets the totals.
+// red: __shared__ float[4 * n] scratch.  Contains two barriers.
+template <int N>
+__device__ __forceinline__ void wg_sum(float (&v)[N], float* red) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    float s = wave_sum(v[k]);
+    if (lane == 0) red[wid * N + k] = s;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < N; ++k) v[k] = red[k] + red[N + k] + red[2 * N + k] + red[3 * N + k];
+  __syncthreads();
+}
+
+// Number of valid rows of a sequence: the prefix of non-negative tokens that are inside the
+// vocabulary and still fit in the cache.  Also returns the flags that stopped the prefix.
+__device__ __forceinline__ int count_rows(const int32_t* tok, int rps, int V, int len, int max_len, int* flags) {
+  int n = 0;
+  int f = 0;
+  for (; n < rps; ++n) {
+    int t = tok[n];
+    if (t < 0) break;
+    if (t >= V) { f |= kFlagToken; break; }
+    if (len + n >= max_len) { f |= kFlagCapacity; break; }
+  }
+  if (flags) *flags = f;
+  return n;
+}
+
+}  // namespace mtp

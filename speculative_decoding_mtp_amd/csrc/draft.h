@@ -1,0 +1,70 @@
+// Host/device interface of the draft-head kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/mtp.h"
+
+namespace mtp {
+
+constexpr int kLmRows = 16;  // weight rows per lm_head workgroup iteration
+
+// Positions per attention split for a sequence of T cached positions (a multiple of 16).
+__host__ __device__ inline int attn_chunk(int T, int nsplit) {
+  int c = (T + nsplit - 1) / nsplit;
+  c = (c + 15) & ~15;
+  return c < 16 ? 16 : c;
+}
+
+struct AttnArgs {
+  const float* q;  // [R][nq][hd]
+  const void *kc, *vc;
+  const int32_t* tok;
+  int tok_sb;
+  const int32_t* len;
+  int B, rps, nq, nkv, max_len, V, nsplit, qstride;
+  float* part;  // [B][nkv][nsplit][qstride][hd + 2]
+};
+
+// Carved out of the caller's workspace.
+struct DraftWs {
+  int* status;
+  unsigned* ticket_lm;
+  float* x;
+  float* q;
+  float* attn_part;
+  float* attn_out;
+  float* act;
+  float* lm_part_v;
+  int* lm_part_i;
+  float* hid_fb;  // [B][D][H] step hiddens when the caller does not want them
+};
+
+struct StepArgs {
+  mtp_config cfg;
+  const mtp_weights* w;
+  void *kc, *vc;
+  int32_t* kv_len;
+  int B, max_len, rps, nsplit;
+  const int32_t* tok;  // token of (b, i) at tok[b * tok_sb + i]
+  int tok_sb;
+  const float* hin;  // hidden of (b, i) at hin + (b * hin_sb + i) * H
+  int hin_sb;
+  float* hout;  // output hidden of (b, i) at hout + (b * hout_sb + (hout_last ? 0 : i)) * H
+  int hout_sb, hout_last;
+  int32_t* draft;  // draft of b at draft[b * dr_sb]
+  int dr_sb;
+  float* logits;  // NULL or logits of b at logits + b * lg_sb
+  long lg_sb;
+  DraftWs ws;
+  hipStream_t stream;
+  hipEvent_t ev_begin, ev_end;  // optional, around the lm_head launch
+};
+
+int lm_head_grid(const mtp_config& cfg);
+int attn_nsplit(int B, int nkv, int max_len);
+hipError_t run_step(const StepArgs& s);
+
+}  // namespace mtp

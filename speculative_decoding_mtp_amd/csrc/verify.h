@@ -1,0 +1,41 @@
+// Host/device interface of the verification kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mtp {
+
+constexpr int kChunk = 4096;    // logits per workgroup in the sampling top-k pass
+constexpr int kTopCap = 8192;   // candidates one workgroup can merge (chunks * top_k)
+constexpr int kMaxTopK = 128;   // largest top_k on the device path
+
+struct VerifyArgs {
+  int B, D, V;
+  int greedy, q_mode, top_k;
+  float temperature, top_p;
+  const float* tl;  // target logits [B][D+1][V]
+  const float* dl;  // draft logits [B][D][V] (q_mode 1)
+  const int32_t* drafts;
+  const float *u_accept, *u_sample;
+  const int32_t* ctx_len;
+  int32_t *n_accept, *out, *crop;
+  int nchunk, chunk;
+  // greedy scratch
+  float* part_v;
+  int* part_i;
+  int* row_tok;
+  // sampling scratch
+  float* cand_v;  // [rows][nchunk][top_k]
+  int* cand_i;
+  float* top_v;  // [rows][top_k]
+  int* top_i;
+  int* top_n;      // [rows]
+  float* scratch;  // [B][4 * kMaxTopK]
+  unsigned* tick_row;  // [rows]
+  unsigned* tick_seq;  // [B]
+};
+
+hipError_t run_verify(const VerifyArgs& a, hipStream_t st);
+
+}  // namespace mtp

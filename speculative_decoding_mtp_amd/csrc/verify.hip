@@ -1,0 +1,400 @@
+// Verification of D drafts against D+1 target rows: greedy prefix match and speculative
+// sampling after temperature, top-k and top-p.
+//
+// Sources: [HB14] "14. MTP: speculative decoding with the built-in draft head", the speculative
+// loop of section "The draft head" (verify two positions, accept the guess and the next token on
+// a hit); [DLM] "The decoding loop and MTP", items 2-3 (7 distributions checked in order, the
+// first refused guess replaced by the model's pick, one more token when all hold, a guess kept
+// with its post-warp probability, otherwise a draw from the other candidates; temperature, top-k
+// and top-p applied in turn); [YL] "MTP 原理详解" 三 stages 3-4 (accept when P/Q >= U, resample
+// on rejection, 1..D+1 tokens per round).
+//
+// Both kernels run in one launch each: workgroups scan chunks of a row, the last workgroup of a
+// row (an atomic ticket) merges that row, and the last row of a sequence runs the sequence's
+// decision.  Every ticket is reset by the workgroup that consumed it.
+#include <float.h>
+
+#include "common.h"
+#include "verify.h"
+
+namespace mtp {
+
+__device__ __forceinline__ bool last_arrival(unsigned* ticket, unsigned total, int* s_flag) {
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned t = atomicAdd(ticket, 1u);
+    *s_flag = (t == total - 1);
+    if (t == total - 1) *ticket = 0u;
+  }
+  __syncthreads();
+  const bool last = *s_flag;
+  if (last) __threadfence();
+  return last;
+}
+
+// workgroup argmax (value desc, index asc) of one value per thread
+__device__ __forceinline__ void wg_argmax(float& v, int& i, float* sv, int* si) {
+  wave_argmax(v, i);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  if (lane == 0) {
+    sv[wid] = v;
+    si[wid] = i;
+  }
+  __syncthreads();
+  v = sv[0];
+  i = si[0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w)
+    if (better(sv[w], si[w], v, i)) {
+      v = sv[w];
+      i = si[w];
+    }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------------------------
+// greedy
+// ---------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(kWG) void k_verify_greedy(VerifyArgs a) {
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  __shared__ int s_flag;
+  const int c = blockIdx.x, row = blockIdx.y;
+  const int rows_per_seq = a.D + 1;
+  const float* x = a.tl + (long)row * a.V;
+  const int beg = c * a.chunk, end = min(a.V, beg + a.chunk);
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  if ((a.V & 3) == 0) {
+    for (int k = beg + 4 * threadIdx.x; k < end; k += 4 * kWG) {
+      const uint4 u = ld_stream(x + k);
+      const float f[4] = {__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w)};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (better(f[e], k + e, bv, bi)) {
+          bv = f[e];
+          bi = k + e;
+        }
+    }
+  } else {
+    for (int k = beg + threadIdx.x; k < end; k += kWG)
+      if (better(x[k], k, bv, bi)) {
+        bv = x[k];
+        bi = k;
+      }
+  }
+  wg_argmax(bv, bi, sv, si);
+  if (threadIdx.x == 0) {
+    a.part_v[(long)row * a.nchunk + c] = bv;
+    a.part_i[(long)row * a.nchunk + c] = bi;
+  }
+  if (!last_arrival(a.tick_row + row, a.nchunk, &s_flag)) return;
+  // this row is complete
+  bv = -INFINITY;
+  bi = 0x7fffffff;
+  for (int k = threadIdx.x; k < a.nchunk; k += kWG) {
+    const float v = a.part_v[(long)row * a.nchunk + k];
+    const int i = a.part_i[(long)row * a.nchunk + k];
+    if (better(v, i, bv, bi)) {
+      bv = v;
+      bi = i;
+    }
+  }
+  wg_argmax(bv, bi, sv, si);
+  if (threadIdx.x == 0) a.row_tok[row] = bi;
+  const int b = row / rows_per_seq;
+  if (!last_arrival(a.tick_seq + b, rows_per_seq, &s_flag)) return;
+  // every target row of sequence b has its argmax: prefix match
+  if (threadIdx.x == 0) {
+    const int* t = a.row_tok + (long)b * rows_per_seq;
+    const int* d = a.drafts + (long)b * a.D;
+    int n = 0;
+    while (n < a.D && t[n] == d[n]) ++n;
+    int32_t* out = a.out + (long)b * rows_per_seq;
+    for (int j = 0; j < n; ++j) out[j] = d[j];
+    out[n] = t[n];
+    for (int j = n + 1; j < rows_per_seq; ++j) out[j] = -1;
+    a.n_accept[b] = n;
+    a.crop[b] = a.ctx_len[b] + 1 + n;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// sampling: top-k selection
+// ---------------------------------------------------------------------------------------------
+// LDS sized for the largest selection (kTopCap candidates) plus a 256-entry bitonic buffer.
+struct TopkSmem {
+  float v[kTopCap];
+  int i[kTopCap];
+  float tm[kWG];
+  int cnt;
+  int flag;
+};
+
+// bitonic sort of n (power of two <= kTopCap) (v, i) pairs in LDS, best first
+__device__ void bitonic_sort_pairs(float* v, int* id, int n) {
+  for (int k = 2; k <= n; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int t = threadIdx.x; t < n; t += kWG) {
+        const int p = t ^ j;
+        if (p > t) {
+          const bool first_best = (t & k) == 0;  // this half ends best-first
+          const bool p_better = better(v[p], id[p], v[t], id[t]);
+          if (p_better == first_best) {
+            const float tv = v[t];
+            v[t] = v[p];
+            v[p] = tv;
+            const int ti = id[t];
+            id[t] = id[p];
+            id[p] = ti;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// bitonic sort of kWG floats (one per thread), descending
+__device__ void bitonic_sort_desc(float* v) {
+  const int t = threadIdx.x;
+  for (int k = 2; k <= kWG; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const int p = t ^ j;
+      if (p > t) {
+        const bool desc = (t & k) == 0;
+        if ((v[p] > v[t]) == desc) {
+          const float tv = v[t];
+          v[t] = v[p];
+          v[p] = tv;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// Top K (value desc, id asc) of the items held by the workgroup (IPT per thread; id < 0 marks
+// an empty slot).  A lower bound on the K-th best value is the K-th best of the per-thread
+// maxima (K threads each hold an item at least that large); only items at or above it are
+// sorted.  Writes min(K, items) entries to out_v/out_i and returns that count (all threads).
+template <int IPT>
+__device__ int wg_topk(const float (&v)[IPT], const int (&id)[IPT], int K, TopkSmem& sm, float* out_v, int* out_i) {
+  float tmax = -INFINITY;
+  bool have = false;
+#pragma unroll
+  for (int e = 0; e < IPT; ++e)
+    if (id[e] >= 0) {
+      tmax = have ? fmaxf(tmax, v[e]) : v[e];
+      have = true;
+    }
+  sm.tm[threadIdx.x] = have ? tmax : -INFINITY;
+  if (threadIdx.x == 0) sm.cnt = 0;
+  __syncthreads();
+  bitonic_sort_desc(sm.tm);
+  const float lb = sm.tm[K - 1];
+#pragma unroll
+  for (int e = 0; e < IPT; ++e)
+    if (id[e] >= 0 && v[e] >= lb) {
+      const int pos = atomicAdd(&sm.cnt, 1);
+      sm.v[pos] = v[e];
+      sm.i[pos] = id[e];
+    }
+  __syncthreads();
+  const int S = sm.cnt;
+  int n2 = 1;
+  while (n2 < S) n2 <<= 1;
+  for (int t = S + threadIdx.x; t < n2; t += kWG) {
+    sm.v[t] = -INFINITY;
+    sm.i[t] = 0x7fffffff;
+  }
+  __syncthreads();
+  bitonic_sort_pairs(sm.v, sm.i, n2);
+  const int n = min(K, S);
+  for (int t = threadIdx.x; t < n; t += kWG) {
+    out_v[t] = sm.v[t];
+    out_i[t] = sm.i[t];
+  }
+  __syncthreads();
+  return n;
+}
+
+// Warped distribution of one row from its sorted top-k candidates: probabilities of the kept
+// prefix (temperature softmax over the k candidates, then top-p: a candidate stays while the
+// mass ranked before it is below p; the first always stays), renormalised.  Runs on one thread.
+__device__ int warp_row(const float* tv, int n, float T, float top_p, float* prob) {
+  float S = 0.f;
+  for (int k = 0; k < n; ++k) {
+    prob[k] = expf((tv[k] - tv[0]) / T);
+    S += prob[k];
+  }
+  int m = n;
+  if (top_p < 1.f) {
+    float before = 0.f;
+    m = 0;
+    for (int k = 0; k < n; ++k) {
+      const float pk = prob[k] / S;
+      if (k > 0 && !(before < top_p)) break;
+      before += pk;
+      ++m;
+    }
+  }
+  float Z = 0.f;
+  for (int k = 0; k < m; ++k) Z += prob[k];
+  for (int k = 0; k < m; ++k) prob[k] = prob[k] / Z;
+  return m;
+}
+
+__device__ float lookup(const int* ids, const float* prob, int m, int tok) {
+  for (int k = 0; k < m; ++k)
+    if (ids[k] == tok) return prob[k];
+  return 0.f;
+}
+
+// Inverse-CDF draw over (id, weight) pairs in ascending id order: the smallest id whose
+// cumulative weight exceeds u * total.  Sorts the pairs by id in place.
+__device__ int draw_ascending(int* ids, float* w, int m, float u) {
+  for (int a = 1; a < m; ++a) {  // insertion sort by id (m <= 128)
+    const int ki = ids[a];
+    const float kw = w[a];
+    int b = a - 1;
+    while (b >= 0 && ids[b] > ki) {
+      ids[b + 1] = ids[b];
+      w[b + 1] = w[b];
+      --b;
+    }
+    ids[b + 1] = ki;
+    w[b + 1] = kw;
+  }
+  float S = 0.f;
+  for (int k = 0; k < m; ++k) S += w[k];
+  const float t = u * S;
+  float c = 0.f;
+  int last = -1;
+  for (int k = 0; k < m; ++k) {
+    if (w[k] <= 0.f) continue;
+    c += w[k];
+    last = ids[k];
+    if (c > t) return ids[k];
+  }
+  return last;  // u * S rounded onto S
+}
+
+__global__ __launch_bounds__(kWG) void k_verify_sample(VerifyArgs a) {
+  __shared__ TopkSmem sm;
+  __shared__ int s_flag;
+  const int c = blockIdx.x, row = blockIdx.y;
+  const int K = a.top_k;
+  const int tgt_rows = a.B * (a.D + 1);
+  const float* x = row < tgt_rows ? a.tl + (long)row * a.V : a.dl + (long)(row - tgt_rows) * a.V;
+  {  // chunk candidates
+    constexpr int IPT = kChunk / kWG;
+    float v[IPT];
+    int id[IPT];
+    const int beg = c * kChunk;
+#pragma unroll
+    for (int e = 0; e < IPT; ++e) {
+      const int k = beg + threadIdx.x + e * kWG;
+      id[e] = k < a.V ? k : -1;
+      v[e] = k < a.V ? x[k] : -INFINITY;
+    }
+    float* ov = a.cand_v + ((long)row * a.nchunk + c) * K;
+    int* oi = a.cand_i + ((long)row * a.nchunk + c) * K;
+    const int n = wg_topk<IPT>(v, id, K, sm, ov, oi);
+    for (int t = n + threadIdx.x; t < K; t += kWG) {
+      ov[t] = -INFINITY;
+      oi[t] = -1;
+    }
+  }
+  if (!last_arrival(a.tick_row + row, a.nchunk, &s_flag)) return;
+  {  // merge the row's candidates
+    constexpr int IPT = kTopCap / kWG;
+    float v[IPT];
+    int id[IPT];
+    const int total = a.nchunk * K;
+#pragma unroll
+    for (int e = 0; e < IPT; ++e) {
+      const int k = threadIdx.x + e * kWG;
+      v[e] = k < total ? a.cand_v[(long)row * a.nchunk * K + k] : -INFINITY;
+      id[e] = k < total ? a.cand_i[(long)row * a.nchunk * K + k] : -1;
+    }
+    const int n = wg_topk<IPT>(v, id, K, sm, a.top_v + (long)row * K, a.top_i + (long)row * K);
+    if (threadIdx.x == 0) a.top_n[row] = n;
+  }
+  // sequence of this row: target row j of sequence b, or draft row j of sequence b
+  const int b = row < tgt_rows ? row / (a.D + 1) : (row - tgt_rows) / a.D;
+  const int need = (a.D + 1) + (a.q_mode == 1 ? a.D : 0);
+  if (!last_arrival(a.tick_seq + b, need, &s_flag)) return;
+  if (threadIdx.x != 0) return;
+  // ---- the sequence's decision, one thread ----
+  float* P = a.scratch + (long)b * 4 * kMaxTopK;  // [kMaxTopK] probs of the target row
+  float* Q = P + kMaxTopK;
+  float* w = Q + kMaxTopK;
+  int* ids = reinterpret_cast<int*>(w + kMaxTopK);
+  const float T = a.temperature;
+  int32_t* out = a.out + (long)b * (a.D + 1);
+  int n_acc = 0;
+  int tok = -1;
+  for (int j = 0; j < a.D; ++j) {
+    const int tr = b * (a.D + 1) + j;
+    const float* tv = a.top_v + (long)tr * K;
+    const int* ti = a.top_i + (long)tr * K;
+    const int mP = warp_row(tv, a.top_n[tr], T, a.top_p, P);
+    const int d = a.drafts[(long)b * a.D + j];
+    const float Pd = lookup(ti, P, mP, d);
+    float Qd = 1.f;
+    int mQ = 0;
+    const int* qi = nullptr;
+    if (a.q_mode == 1) {
+      const int dr = tgt_rows + b * a.D + j;
+      qi = a.top_i + (long)dr * K;
+      mQ = warp_row(a.top_v + (long)dr * K, a.top_n[dr], T, a.top_p, Q);
+      Qd = lookup(qi, Q, mQ, d);
+    }
+    const float u = a.u_accept[(long)b * a.D + j];
+    const bool accept = Pd > 0.f && (Qd == 0.f || u <= Pd / Qd);
+    if (accept) {
+      out[j] = d;
+      ++n_acc;
+      continue;
+    }
+    // residual max(0, P - Q); its support lies inside P's kept set
+    float rs = 0.f;
+    for (int k = 0; k < mP; ++k) {
+      ids[k] = ti[k];
+      const float q = a.q_mode == 1 ? lookup(qi, Q, mQ, ti[k]) : (ti[k] == d ? 1.f : 0.f);
+      w[k] = fmaxf(P[k] - q, 0.f);
+      rs += w[k];
+    }
+    if (!(rs > 0.f))
+      for (int k = 0; k < mP; ++k) w[k] = P[k];
+    tok = draw_ascending(ids, w, mP, a.u_sample[b]);
+    break;
+  }
+  if (tok < 0) {  // every draft held: one more token from row D
+    const int tr = b * (a.D + 1) + a.D;
+    const int mP = warp_row(a.top_v + (long)tr * K, a.top_n[tr], T, a.top_p, P);
+    for (int k = 0; k < mP; ++k) {
+      ids[k] = a.top_i[(long)tr * K + k];
+      w[k] = P[k];
+    }
+    tok = draw_ascending(ids, w, mP, a.u_sample[b]);
+  }
+  out[n_acc] = tok;
+  for (int j = n_acc + 1; j <= a.D; ++j) out[j] = -1;
+  a.n_accept[b] = n_acc;
+  a.crop[b] = a.ctx_len[b] + 1 + n_acc;
+}
+
+hipError_t run_verify(const VerifyArgs& a, hipStream_t st) {
+  if (a.greedy) {
+    hipLaunchKernelGGL(k_verify_greedy, dim3(a.nchunk, a.B * (a.D + 1)), dim3(kWG), 0, st, a);
+  } else {
+    const int rows = a.B * (a.D + 1) + (a.q_mode == 1 ? a.B * a.D : 0);
+    hipLaunchKernelGGL(k_verify_sample, dim3(a.nchunk, rows), dim3(kWG), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mtp
