@@ -1,0 +1,195 @@
+"""Benchmark of one MTP speculative-decoding step on one MI355X.
+
+A step is one round of the whole path on synthetic inputs resident in HBM:
+  mtp_draft_loop (catch-up rows + D-1 serial draft steps: dual RMSNorm + eh_proj, decoder
+  block with RoPE over the head's KV cache, final norm, lm_head + argmax)
+  -> synthetic target logits (draft logits + seeded noise, standing in for the main model)
+  -> mtp_state_snapshot (recurrent state of the target, p1's 19 MB per sequence)
+  -> spec_verify -> mtp_state_restore (where a draft was rejected) -> kv_crop.
+The workload is the single-layer bf16 head with H=2048, 16/4 heads of 128, FFN 6144, vocab
+151936, a 4096-position KV context, B=1, D=1, greedy verification over 2 positions with target
+logits = draft logits + N(0, 0.5).
+
+Prints one JSON line: accepted tokens/s (sum over rounds and sequences of accepted drafts + 1,
+divided by the timed wall time), the lm_head kernel's HBM roofline and the CPU oracle timed on
+a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "accepted tokens/s per MTP draft+verify step; kernel HBM GB/s vs MI355X peak"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="qwen")
+    ap.add_argument("--state-bytes", type=int, default=None, help="recurrent state bytes per sequence")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle baseline sample budget (0: skip)")
+    ap.add_argument("--traffic", default=None, help="JSON file with counter-measured lm_head bytes per launch")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import speculative_decoding_mtp_amd as M
+    from synth import CONFIGS, make_first_round, make_kv_prefix, make_round_hiddens, make_round_noise, make_state, \
+        make_weights
+    from tests.gpu_util import config, f32, i32, kv_from_numpy, upload_weights
+
+    cfg = CONFIGS[args.config]
+    B, D, H, V = cfg.batch, cfg.D, cfg.hidden, cfg.vocab
+    state_bytes = cfg.state_bytes_per_seq if args.state_bytes is None else args.state_bytes
+    rounds_total = args.warmup + args.steps
+    max_len = cfg.ctx + 1 + rounds_total * (D + 1) + 64
+    t0 = time.time()
+    w = make_weights(cfg)
+    c = config(cfg)
+    gw = upload_weights(cfg, w)
+    K, Vv = make_kv_prefix(cfg)
+    kv = kv_from_numpy(cfg, K, Vv, cfg.ctx, max_len)
+    print(f"[bench] inputs ready in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+
+    rps = D + 1
+    toks0, hid0 = make_first_round(cfg)
+    tok_pad = np.full((B, rps), -1, np.int32)
+    tok_pad[:, :1] = toks0
+    hid_pad = np.zeros((B, rps, H), np.float32)
+    hid_pad[:, :1] = hid0
+    NBUF = 16
+    hid_bufs = [f32(make_round_hiddens(cfg, r)) for r in range(NBUF)]
+    noise_bufs = [f32(make_round_noise(cfg, r)) for r in range(NBUF)]
+    tokens = i32(tok_pad)
+    hidden0 = f32(hid_pad)
+    ws = M.new_workspace(M.mtp_draft_workspace_size(c, B, rps, D, max_len))
+    vws = M.new_workspace(M.spec_verify_workspace_size(B, D, V, None))
+    drafts = torch.zeros(B, D, dtype=torch.int32, device="cuda")
+    hiddens = torch.zeros(B, D, H, device="cuda")
+    dlog = torch.zeros(B, D, V, device="cuda")
+    tl = torch.zeros(B, D + 1, V, device="cuda")
+    n_acc = torch.zeros(B, dtype=torch.int32, device="cuda")
+    out_tok = [torch.zeros(B, D + 1, dtype=torch.int32, device="cuda") for _ in range(2)]
+    ctx = [torch.full((B,), cfg.ctx + 1, dtype=torch.int32, device="cuda"),
+           torch.zeros(B, dtype=torch.int32, device="cuda")]
+    hist = torch.zeros(rounds_total, B, dtype=torch.int32, device="cuda")
+    state = snap = None
+    if state_bytes:
+        state = torch.from_numpy(make_state(B, state_bytes)).cuda()
+        snap = torch.empty_like(state)
+
+    def step(r):
+        cur, nxt = r % 2, (r + 1) % 2
+        tk = tokens if r == 0 else out_tok[cur]
+        hin = hidden0 if r == 0 else hid_bufs[r % NBUF]
+        M.mtp_draft_loop(c, gw, kv, D, rps, tk, hin, drafts, hiddens, dlog, ws)
+        # stand-in target forward: target row j = draft logits of step j+1 (row D reuses step D)
+        tl[:, :D].copy_(dlog)
+        tl[:, D].copy_(dlog[:, D - 1])
+        tl.add_(noise_bufs[r % NBUF])
+        if state is not None:
+            M.mtp_state_snapshot(state, snap, state_bytes, B)
+        M.spec_verify(B, D, V, tl, drafts, None, None, None, None, ctx[cur], n_acc, out_tok[nxt], ctx[nxt], vws)
+        if state is not None:
+            M.mtp_state_restore(state, snap, state_bytes, B, n_acc, D)
+        M.kv_crop(kv, ctx[cur])
+        hist[r].copy_(n_acc)
+
+    for r in range(args.warmup):
+        step(r)
+    torch.cuda.synchronize()
+    M.mtp_check(ws)
+    M.mtp_timer_start(M.MTP_KERNEL_LM_HEAD, args.steps * D)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    ev0.record()
+    for r in range(args.warmup, rounds_total):
+        step(r)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    gpu_ms = ev0.elapsed_time(ev1)
+    lm_ms, lm_n = M.mtp_timer_read(M.MTP_KERNEL_LM_HEAD)
+    M.mtp_check(ws)
+    acc = hist[args.warmup:].cpu().numpy()
+    tokens_out = int((acc + 1).sum())
+    value = tokens_out / wall
+    ms_per_step = wall * 1e3 / args.steps
+
+    lm_bytes = V * H * cfg.wbytes + B * H * 4 + B * V * 4      # weights + activations in + logits out
+    lm_avg_s = lm_ms / 1e3 / max(lm_n, 1)
+    achieved = lm_bytes / lm_avg_s / 1e9
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        traffic = json.load(open(args.traffic)).get("bytes_per_launch")
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(cfg, w, K, Vv, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "accepted tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded random-init weights, KV prefix, hiddens and target-logit noise)",
+        "config": {"workload": cfg.name, "batch": B, "draft_tokens": D, "kv_context": cfg.ctx,
+                   "target_noise_std": cfg.noise_std, "verify": "greedy",
+                   "recurrent_state_bytes_per_seq": state_bytes},
+        "steps_per_s": round(args.steps / wall, 2),
+        "acceptance": round(float(acc.mean()) / D, 4),
+        "gpu_event_ms_per_step": round(gpu_ms / args.steps, 4),
+        "roofline": {"bound": "hbm", "kernel": "lm_head GEMV + argmax", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "bytes_per_launch": lm_bytes,
+                     "avg_launch_us": round(lm_avg_s * 1e6, 2), "launches": lm_n},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(cfg, w, K, Vv, budget_s):
+    """The float64 oracle on the same workload, rounds until the time budget is spent."""
+    import oracle as O
+    from synth import make_first_round, make_round_hiddens, make_round_noise
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    model = O.OracleModel(cfg, w)
+    B, D = cfg.batch, cfg.D
+    cache = O.KVCache(cfg, B, cfg.ctx + 256)
+    cache.load_prefix(K, Vv, cfg.ctx)
+    toks, hid = make_first_round(cfg)
+    tokens_out = rounds = 0
+    t0 = time.perf_counter()
+    while rounds < 2 or time.perf_counter() - t0 < budget_s:
+        drafts, _, logits, _ = O.draft_loop(model, cache, toks, hid, D)
+        ctx = cache.len.copy() - (D - 1)
+        tl = np.concatenate([logits, logits[:, D - 1:D]], axis=1).astype(np.float32) + make_round_noise(cfg, rounds)
+        res = O.greedy_verify(tl, drafts, ctx)
+        O.kv_crop(cache, ctx)
+        tokens_out += int((res.n_accept + 1).sum())
+        toks, hid = res.out_tokens, make_round_hiddens(cfg, rounds)
+        rounds += 1
+        if cache.len.max() + D + 2 >= cache.max_len:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(tokens_out / dt, 4), "unit": "accepted tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rounds} rounds of the same workload (float64 NumPy, row by row), {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmtp_hip.so")
 BUILD = os.path.join(os.path.dirname(HERE), "_build")
-SOURCES = ["draft.hip", "verify.hip", "state.hip", "capi.hip"]
+SOURCES = ["draft_bf16.hip", "draft_f32.hip", "draft.hip", "attn.hip", "verify.hip", "state.hip", "capi.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "--offload-arch=gfx950", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",

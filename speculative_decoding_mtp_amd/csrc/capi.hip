@@ -108,14 +108,14 @@ DraftLayout draft_layout(const mtp_config& c, int B, int rps, int D, int max_len
   const int nsplit = attn_nsplit(B, c.n_kv_heads, max_len);
   const size_t G = c.n_heads / c.n_kv_heads;
   const size_t sizes[10] = {
-      256,                                                                            // status + ticket
+      256,                                                                            // status word
       R * c.hidden * 4,                                                               // x
       R * c.n_heads * c.head_dim * 4,                                                 // q
       (size_t)B * c.n_kv_heads * nsplit * (rps * G) * (c.head_dim + 2) * 4,          // attention partials
       R * c.n_heads * c.head_dim * 4,                                                 // attention output
       R * c.ffn * 4,                                                                  // act
-      (size_t)B * lm_head_grid(c) * 4,                                                // lm partial values
-      (size_t)B * lm_head_grid(c) * 4,                                                // lm partial ids
+      (size_t)B * lm_head_grid(c, B) * 4,                                             // lm partial values
+      (size_t)B * lm_head_grid(c, B) * 4,                                             // lm partial ids
       (size_t)B * (D < 1 ? 1 : D) * c.hidden * 4,                                     // step hiddens
       0};
   DraftLayout L;
@@ -132,7 +132,6 @@ DraftWs carve(void* ws, const DraftLayout& L) {
   char* base = static_cast<char*>(ws);
   DraftWs w;
   w.status = reinterpret_cast<int*>(base);
-  w.ticket_lm = reinterpret_cast<unsigned*>(base + 4);
   w.x = reinterpret_cast<float*>(base + L.off[1]);
   w.q = reinterpret_cast<float*>(base + L.off[2]);
   w.attn_part = reinterpret_cast<float*>(base + L.off[3]);
@@ -276,10 +275,11 @@ int spec_verify_workspace_size(int32_t B, int32_t D, int32_t V, const mtp_sampli
   if (B < 1 || D < 1 || V < 1) return fail(MTP_ERR_ARG, "B, D, V must be positive");
   const bool greedy = !sp || !(sp->temperature > 0.f);
   const size_t rows = (size_t)B * (D + 1) + (size_t)(!greedy && sp->q_mode == 1 ? B * D : 0);
-  size_t t = 256 + up256(rows * 4) + up256((size_t)B * 4);
+  if (D > kMaxDraft) return fail(MTP_ERR_ARG, "D must be <= %d", kMaxDraft);
+  size_t t = 256;
   if (greedy) {
     const size_t nchunk = 1024;  // upper bound of the chunk count chosen at launch
-    t += 2 * up256(rows * nchunk * 4) + up256(rows * 4);
+    t += 2 * up256(rows * nchunk * 4);
   } else {
     const int K = sp->top_k;
     if (K < 1 || K > kMaxTopK) return fail(MTP_ERR_ARG, "top_k must be in [1, %d]", kMaxTopK);
@@ -316,10 +316,6 @@ int spec_verify(int32_t B, int32_t D, int32_t V, const float* target_logits, con
   char* base = static_cast<char*>(ws);
   size_t o = 256;
   const int rows = B * (D + 1) + (!a.greedy && sp->q_mode == 1 ? B * D : 0);
-  a.tick_row = reinterpret_cast<unsigned*>(base + o);
-  o += up256((size_t)rows * 4);
-  a.tick_seq = reinterpret_cast<unsigned*>(base + o);
-  o += up256((size_t)B * 4);
   if (a.greedy) {
     int target = (1024 + rows - 1) / rows;
     int chunk = (V + target - 1) / target;
@@ -330,7 +326,6 @@ int spec_verify(int32_t B, int32_t D, int32_t V, const float* target_logits, con
     o += up256((size_t)rows * 1024 * 4);
     a.part_i = reinterpret_cast<int*>(base + o);
     o += up256((size_t)rows * 1024 * 4);
-    a.row_tok = reinterpret_cast<int*>(base + o);
   } else {
     if (sp->q_mode != 0 && sp->q_mode != 1) return fail(MTP_ERR_ARG, "q_mode must be 0 or 1");
     if (sp->q_mode == 1 && (!draft_logits || !aligned16(draft_logits)))

@@ -28,10 +28,29 @@ struct AttnArgs {
   float* part;  // [B][nkv][nsplit][qstride][hd + 2]
 };
 
+// Arguments of the lm_head finalisation kernel.
+struct LmFinal {
+  const int32_t* tok;
+  int tok_sb, rps, V;
+  int32_t* len;
+  int max_len;
+  const float* part_v;  // [B][nparts]
+  const int* part_i;
+  int nparts;
+  const float* x;  // pre-norm residual stream [B * rps][H]
+  const void* gain;
+  int H;
+  float eps;
+  float* hout;
+  int hout_sb, hout_last;
+  int32_t* draft;
+  int dr_sb;
+  int* status;
+};
+
 // Carved out of the caller's workspace.
 struct DraftWs {
   int* status;
-  unsigned* ticket_lm;
   float* x;
   float* q;
   float* attn_part;
@@ -63,8 +82,22 @@ struct StepArgs {
   hipEvent_t ev_begin, ev_end;  // optional, around the lm_head launch
 };
 
-int lm_head_grid(const mtp_config& cfg);
+// Which GEMV layout, variant and grid serve nact activation rows of width K (VE elements per
+// 16-byte vector) over N output rows.  kind 0: k_gemv_w with nj = NJ; kind 1: k_gemv_s with
+// nj = NXM.  The same plan sizes the lm_head partial buffer and launches the kernel.
+struct GemvPlan {
+  int kind, nj, rb, grid;
+};
+GemvPlan plan_gemv(int nact, int K, int VE, int N);
+
+int lm_head_grid(const mtp_config& cfg, int B);
 int attn_nsplit(int B, int nkv, int max_len);
+hipError_t run_attention(const AttnArgs& a, int hd, int wdtype, float* out, hipStream_t st);
 hipError_t run_step(const StepArgs& s);
+
+struct BF16;
+struct F32;
+template <class W>
+hipError_t run_step_t(const StepArgs& s);
 
 }  // namespace mtp

@@ -1,0 +1,451 @@
+// Draft-head step: GEMV policies and the kernel sequence, templated on the weight type.
+// Instantiated once per weight type in draft_bf16.hip and draft_f32.hip.
+//
+// One draft step over R = B * rows_per_seq padded rows (a row is valid when its token is
+// non-negative, inside the vocabulary and its position fits the cache):
+//   eh_proj   : x = W_eh [rms(E[tok]) * g_e ; rms(h) * g_h]           (embedding half first)
+//   per layer : q,k,v = W_qkv rms(x) * g_in, RoPE(q,k) at pos, k,v -> cache[pos]
+//               o = softmax(q K^T / sqrt(hd)) V over positions 0..pos   (split over T, combined)
+//               x += W_o o
+//               x += W_d (silu(W_g m) * W_u m),  m = rms(x) * g_post
+//   lm_head   : g = rms(x) * g_f; logits = W_lm g for each sequence's last row; argmax with the
+//               lowest id on ties; the last workgroup writes the draft and grows len[b].
+// Sources: [HB14] "14. MTP: speculative decoding with the built-in draft head", section "The
+// draft head"; [YL] "MTP 原理详解" sections 二.1-二.3 and 三 stages 1-2.
+#pragma once
+
+#include "draft.h"
+#include "gemv.h"
+
+namespace mtp {
+
+// ---------------------------------------------------------------------------------------------
+// common part of every drafter GEMV policy: row addressing and validity
+// ---------------------------------------------------------------------------------------------
+template <class W>
+struct PBase {
+  using T = typename W::T;
+  static constexpr bool kPair = false;
+  static constexpr bool kArgmax = false;
+  const int32_t* tok;
+  int tok_sb;
+  int B, rps;
+  const int32_t* len;
+  int max_len, V;
+  int K, N, nact, split;
+  float eps;
+
+  __device__ void setup(int* s_n) const {
+    for (int b = threadIdx.x; b < B; b += kWG)
+      s_n[b] = count_rows(tok + (long)b * tok_sb, rps, V, len[b], max_len, nullptr);
+  }
+  __device__ void act(int a, const int* s_n, int& row, bool& valid) const {
+    row = a;
+    valid = false;
+    if (a < B * rps) {
+      const int b = a / rps, i = a - b * rps;
+      valid = i < s_n[b];
+    }
+  }
+  __device__ void store(int, int, int, float) {}
+  __device__ void store_pair(int, int, int, float, float) {}
+  __device__ void partial(int, float, int) {}
+  __device__ void finish(const int*) {}
+};
+
+// eh_proj over [embedding ; hidden], each half RMS-normalised with its own gain
+template <class W>
+struct PEhProj : PBase<W> {
+  using T = typename W::T;
+  static constexpr int kNorm = 2;
+  const T *embed, *enorm, *hnorm, *w;
+  const float* hin;
+  int hin_sb, H;
+  float* xout;
+
+  __device__ void load_x(int row, int k, float (&f)[W::VE]) const {
+    const int b = row / this->rps, i = row - b * this->rps;
+    if (k < H) {
+      const int t = this->tok[(long)b * this->tok_sb + i];
+      W::cvt(ld16(embed + (long)t * H + k), f);
+    } else {
+      load_f32_vec<W::VE>(hin + ((long)b * hin_sb + i) * H + (k - H), f);
+    }
+  }
+  __device__ void gain_vec(int k, float (&f)[W::VE]) const { W::cvt(ld16(k < H ? enorm + k : hnorm + (k - H)), f); }
+  __device__ const T* wrow(int m) const { return w + (long)m * (2 * H); }
+  __device__ void store(int m, int, int row, float v) { xout[(long)row * H + m] = v; }
+};
+
+// Q/K/V projection of rms(x) with RoPE on q and k and the K/V append.  Logical rows are
+// ordered per head as (0, hd/2, 1, hd/2+1, ...) so a rotation pair is one (even, odd) pair.
+template <class W>
+struct PQKV : PBase<W> {
+  using T = typename W::T;
+  static constexpr int kNorm = 1;
+  static constexpr bool kPair = true;
+  const T *g, *wq, *wk, *wv;
+  const float* xin;
+  int H, nq, nkv, hd;
+  double log_theta;
+  float* qout;
+  T *kc, *vc;  // this layer's cache [B][nkv][max_len][hd]
+
+  __device__ void load_x(int row, int k, float (&f)[W::VE]) const { load_f32_vec<W::VE>(xin + (long)row * H + k, f); }
+  __device__ void gain_vec(int k, float (&f)[W::VE]) const { W::cvt(ld16(g + k), f); }
+  __device__ const T* wrow(int m) const {
+    const int head = m / hd, mm = m - head * hd;
+    const int dim = (mm >> 1) + (mm & 1) * (hd >> 1);
+    if (head < nq) return wq + ((long)head * hd + dim) * H;
+    if (head < nq + nkv) return wk + ((long)(head - nq) * hd + dim) * H;
+    return wv + ((long)(head - nq - nkv) * hd + dim) * H;
+  }
+  __device__ void store_pair(int m, int, int row, float v0, float v1) {
+    const int head = m / hd, u = (m - head * hd) >> 1, half = hd >> 1;
+    const int b = row / this->rps, i = row - b * this->rps;
+    const int pos = this->len[b] + i;
+    if (head < nq + nkv) {  // rotate q and k: angle pos * theta^(-2u/hd), computed in double
+      const double ang = double(pos) * exp(-2.0 * double(u) / double(hd) * log_theta);
+      double s, c;
+      sincos(ang, &s, &c);
+      const float cf = float(c), sf = float(s);
+      const float a0 = v0 * cf - v1 * sf, a1 = v1 * cf + v0 * sf;
+      v0 = a0;
+      v1 = a1;
+    }
+    if (head < nq) {
+      float* qp = qout + (long)row * nq * hd + (long)head * hd;
+      qp[u] = v0;
+      qp[u + half] = v1;
+    } else {
+      const int kvh = head < nq + nkv ? head - nq : head - nq - nkv;
+      T* dst = (head < nq + nkv ? kc : vc) + (((long)b * nkv + kvh) * this->max_len + pos) * hd;
+      dst[u] = W::put(v0);
+      dst[u + half] = W::put(v1);
+    }
+  }
+};
+
+// y = W a added into the residual stream (o_proj and down_proj)
+template <class W>
+struct PResidual : PBase<W> {
+  using T = typename W::T;
+  static constexpr int kNorm = 0;
+  const T* w;
+  const float* ain;  // [R][K]
+  float* xres;       // [R][N]
+
+  __device__ void load_x(int row, int k, float (&f)[W::VE]) const {
+    load_f32_vec<W::VE>(ain + (long)row * this->K + k, f);
+  }
+  __device__ void gain_vec(int, float (&f)[W::VE]) const {
+#pragma unroll
+    for (int e = 0; e < W::VE; ++e) f[e] = 1.f;
+  }
+  __device__ const T* wrow(int m) const { return w + (long)m * this->K; }
+  __device__ void store(int m, int, int row, float v) { xres[(long)row * this->N + m] += v; }
+};
+
+// gate/up of rms(x), interleaved as (gate f, up f); stores silu(gate) * up
+template <class W>
+struct PGateUp : PBase<W> {
+  using T = typename W::T;
+  static constexpr int kNorm = 1;
+  static constexpr bool kPair = true;
+  const T *g, *wg, *wu;
+  const float* xin;
+  int H, F;
+  float* aout;  // [R][F]
+
+  __device__ void load_x(int row, int k, float (&f)[W::VE]) const { load_f32_vec<W::VE>(xin + (long)row * H + k, f); }
+  __device__ void gain_vec(int k, float (&f)[W::VE]) const { W::cvt(ld16(g + k), f); }
+  __device__ const T* wrow(int m) const { return ((m & 1) ? wu : wg) + (long)(m >> 1) * H; }
+  __device__ void store_pair(int m, int, int row, float gt, float up) {
+    aout[(long)row * F + (m >> 1)] = gt / (1.0f + expf(-gt)) * up;
+  }
+};
+
+// final RMSNorm + lm_head + argmax for each sequence's last row; output hiddens; finalisation
+template <class W>
+struct PLmHead : PBase<W> {
+  using T = typename W::T;
+  static constexpr int kNorm = 1;
+  static constexpr bool kArgmax = true;
+  const T *g, *w;
+  const float* xin;
+  int H;
+  float* logits;  // NULL or row b at logits + b * lg_sb
+  long lg_sb;
+  float* part_v;  // [B][gridDim]
+  int* part_i;
+
+  __device__ void act(int a, const int* s_n, int& row, bool& valid) const {
+    valid = a < this->B && s_n[a] > 0;
+    row = valid ? a * this->rps + s_n[a] - 1 : 0;
+  }
+  __device__ void load_x(int row, int k, float (&f)[W::VE]) const { load_f32_vec<W::VE>(xin + (long)row * H + k, f); }
+  __device__ void gain_vec(int k, float (&f)[W::VE]) const { W::cvt(ld16(g + k), f); }
+  __device__ const T* wrow(int m) const { return w + (long)m * H; }
+  __device__ void store(int m, int a, int, float v) {
+    if (logits) logits[(long)a * lg_sb + m] = v;
+  }
+  __device__ void partial(int a, float v, int i) {
+    if (a < this->B) {
+      part_v[(long)a * gridDim.x + blockIdx.x] = v;
+      part_i[(long)a * gridDim.x + blockIdx.x] = i;
+    }
+  }
+  __device__ void finish(const int* s_n) {
+    // activation blocks with no valid row were skipped: their partials must still be written
+    for (int a = threadIdx.x; a < this->B; a += kWG)
+      if (s_n[a] == 0) {
+        part_v[(long)a * gridDim.x + blockIdx.x] = -INFINITY;
+        part_i[(long)a * gridDim.x + blockIdx.x] = 0x7fffffff;
+      }
+  }
+};
+
+// After the lm_head: one workgroup per sequence reduces the per-workgroup argmax partials
+// (the lowest id among equal maxima), writes the draft, grows len[b], records device errors,
+// and writes the post-norm hidden of the rows the caller wants.
+template <class W>
+__global__ __launch_bounds__(kWG) void k_lm_finalize(LmFinal f) {
+  using T = typename W::T;
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  __shared__ float red[8];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  int flags = 0;
+  const int n = count_rows(f.tok + (long)b * f.tok_sb, f.rps, f.V, f.len[b], f.max_len, &flags);
+  float v = -INFINITY;
+  int id = 0x7fffffff;
+  for (int k = tid; k < f.nparts; k += kWG) {
+    const float pv = f.part_v[(long)b * f.nparts + k];
+    const int pi = f.part_i[(long)b * f.nparts + k];
+    if (better(pv, pi, v, id)) {
+      v = pv;
+      id = pi;
+    }
+  }
+  wave_argmax(v, id);
+  if ((tid & 63) == 0) {
+    sv[tid >> 6] = v;
+    si[tid >> 6] = id;
+  }
+  __syncthreads();
+  const T* g = reinterpret_cast<const T*>(f.gain);
+  for (int i = (f.hout_last ? n - 1 : 0); i < n; ++i) {
+    const float* xr = f.x + ((long)b * f.rps + i) * f.H;
+    float ss[1] = {0.f};
+    for (int k = tid; k < f.H; k += kWG) ss[0] += xr[k] * xr[k];
+    wg_sum<1>(ss, red);
+    const float sc = 1.0f / sqrtf(ss[0] / float(f.H) + f.eps);
+    float* dst = f.hout + ((long)b * f.hout_sb + (f.hout_last ? 0 : i)) * f.H;
+    for (int k = tid; k < f.H; k += kWG) dst[k] = xr[k] * sc * W::get(g, k);
+  }
+  if (tid == 0) {
+    v = sv[0];
+    id = si[0];
+    for (int w = 1; w < 4; ++w)
+      if (better(sv[w], si[w], v, id)) {
+        v = sv[w];
+        id = si[w];
+      }
+    f.draft[(long)b * f.dr_sb] = n > 0 ? id : -1;
+    f.len[b] = f.len[b] + n;
+    if (flags) atomicOr(f.status, flags);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// launch selection
+// ---------------------------------------------------------------------------------------------
+template <class W, class P>
+hipError_t launch_gemv(P& p, hipStream_t st) {
+  const GemvPlan pl = plan_gemv(p.nact, p.K, W::VE, p.N);
+  if (pl.kind == 0) {
+#define MTP_W(NJ_, RB_)                                                                        \
+  if (pl.nj == NJ_ && pl.rb == RB_) {                                                          \
+    hipLaunchKernelGGL((k_gemv_w<W, RB_, NJ_, 16 / NJ_, P>), dim3(pl.grid), dim3(kWG), 0, st, p); \
+    return hipGetLastError();                                                                  \
+  }
+    MTP_W(1, 1) MTP_W(1, 2) MTP_W(1, 4) MTP_W(2, 1) MTP_W(2, 2) MTP_W(2, 4) MTP_W(4, 1) MTP_W(4, 2) MTP_W(8, 1)
+    MTP_W(8, 2)
+#undef MTP_W
+  } else {
+#define MTP_S(NX_, RB_)                                                                    \
+  if (pl.nj == NX_ && pl.rb == RB_) {                                                      \
+    hipLaunchKernelGGL((k_gemv_s<W, RB_, NX_, 8, P>), dim3(pl.grid), dim3(kWG), 0, st, p); \
+    return hipGetLastError();                                                              \
+  }
+    MTP_S(4, 1) MTP_S(4, 2) MTP_S(4, 4) MTP_S(8, 1) MTP_S(8, 2) MTP_S(16, 1)
+#undef MTP_S
+  }
+  return hipErrorInvalidValue;
+}
+
+template <class W, class P>
+void fill_base(P& p, const StepArgs& s) {
+  p.tok = s.tok;
+  p.tok_sb = s.tok_sb;
+  p.B = s.B;
+  p.rps = s.rps;
+  p.len = s.kv_len;
+  p.max_len = s.max_len;
+  p.V = s.cfg.vocab;
+  p.eps = s.cfg.rms_eps;
+  p.split = 0;
+}
+
+template <class W>
+hipError_t run_step_t(const StepArgs& s) {
+  using T = typename W::T;
+  const mtp_config& c = s.cfg;
+  const int H = c.hidden, F = c.ffn, nq = c.n_heads, nkv = c.n_kv_heads, hd = c.head_dim;
+  const int R = s.B * s.rps;
+  hipError_t e;
+
+  {  // eh_proj
+    PEhProj<W> p;
+    fill_base<W>(p, s);
+    p.K = 2 * H;
+    p.N = H;
+    p.nact = R;
+    p.split = H;
+    p.embed = (const T*)s.w->embed;
+    p.enorm = (const T*)s.w->enorm;
+    p.hnorm = (const T*)s.w->hnorm;
+    p.w = (const T*)s.w->eh_proj;
+    p.hin = s.hin;
+    p.hin_sb = s.hin_sb;
+    p.H = H;
+    p.xout = s.ws.x;
+    if ((e = launch_gemv<W>(p, s.stream)) != hipSuccess) return e;
+  }
+  for (int l = 0; l < c.n_layers; ++l) {
+    const mtp_layer_weights& lw = s.w->layers[l];
+    const long layer_off = (long)l * s.B * nkv * s.max_len * hd;
+    {  // q/k/v + RoPE + append
+      PQKV<W> p;
+      fill_base<W>(p, s);
+      p.K = H;
+      p.N = (nq + 2 * nkv) * hd;
+      p.nact = R;
+      p.g = (const T*)lw.in_norm;
+      p.wq = (const T*)lw.wq;
+      p.wk = (const T*)lw.wk;
+      p.wv = (const T*)lw.wv;
+      p.xin = s.ws.x;
+      p.H = H;
+      p.nq = nq;
+      p.nkv = nkv;
+      p.hd = hd;
+      p.log_theta = log((double)c.rope_theta);
+      p.qout = s.ws.q;
+      p.kc = (T*)s.kc + layer_off;
+      p.vc = (T*)s.vc + layer_off;
+      if ((e = launch_gemv<W>(p, s.stream)) != hipSuccess) return e;
+    }
+    {  // attention
+      AttnArgs a;
+      a.q = s.ws.q;
+      a.kc = (const T*)s.kc + layer_off;
+      a.vc = (const T*)s.vc + layer_off;
+      a.tok = s.tok;
+      a.tok_sb = s.tok_sb;
+      a.len = s.kv_len;
+      a.B = s.B;
+      a.rps = s.rps;
+      a.nq = nq;
+      a.nkv = nkv;
+      a.max_len = s.max_len;
+      a.V = c.vocab;
+      a.nsplit = s.nsplit;
+      a.qstride = s.rps * (nq / nkv);
+      a.part = s.ws.attn_part;
+      if ((e = run_attention(a, hd, c.wdtype, s.ws.attn_out, s.stream)) != hipSuccess) return e;
+    }
+    {  // o_proj + residual
+      PResidual<W> p;
+      fill_base<W>(p, s);
+      p.K = nq * hd;
+      p.N = H;
+      p.nact = R;
+      p.w = (const T*)lw.wo;
+      p.ain = s.ws.attn_out;
+      p.xres = s.ws.x;
+      if ((e = launch_gemv<W>(p, s.stream)) != hipSuccess) return e;
+    }
+    {  // gate/up + SwiGLU
+      PGateUp<W> p;
+      fill_base<W>(p, s);
+      p.K = H;
+      p.N = 2 * F;
+      p.nact = R;
+      p.g = (const T*)lw.post_norm;
+      p.wg = (const T*)lw.wgate;
+      p.wu = (const T*)lw.wup;
+      p.xin = s.ws.x;
+      p.H = H;
+      p.F = F;
+      p.aout = s.ws.act;
+      if ((e = launch_gemv<W>(p, s.stream)) != hipSuccess) return e;
+    }
+    {  // down + residual
+      PResidual<W> p;
+      fill_base<W>(p, s);
+      p.K = F;
+      p.N = H;
+      p.nact = R;
+      p.w = (const T*)lw.wdown;
+      p.ain = s.ws.act;
+      p.xres = s.ws.x;
+      if ((e = launch_gemv<W>(p, s.stream)) != hipSuccess) return e;
+    }
+  }
+  {  // final norm + lm_head + argmax + finalisation
+    PLmHead<W> p;
+    fill_base<W>(p, s);
+    p.K = H;
+    p.N = c.vocab;
+    p.nact = s.B;
+    p.g = (const T*)s.w->final_norm;
+    p.w = (const T*)s.w->lm_head;
+    p.xin = s.ws.x;
+    p.H = H;
+    p.logits = s.logits;
+    p.lg_sb = s.lg_sb;
+    p.part_v = s.ws.lm_part_v;
+    p.part_i = s.ws.lm_part_i;
+    if (s.ev_begin) (void)hipEventRecord(s.ev_begin, s.stream);
+    e = launch_gemv<W>(p, s.stream);
+    if (s.ev_end) (void)hipEventRecord(s.ev_end, s.stream);
+    if (e != hipSuccess) return e;
+    LmFinal f;
+    f.tok = s.tok;
+    f.tok_sb = s.tok_sb;
+    f.rps = s.rps;
+    f.V = c.vocab;
+    f.len = s.kv_len;
+    f.max_len = s.max_len;
+    f.part_v = s.ws.lm_part_v;
+    f.part_i = s.ws.lm_part_i;
+    f.nparts = plan_gemv(s.B, H, W::VE, c.vocab).grid;
+    f.x = s.ws.x;
+    f.gain = s.w->final_norm;
+    f.H = H;
+    f.eps = c.rms_eps;
+    f.hout = s.hout;
+    f.hout_sb = s.hout_sb;
+    f.hout_last = s.hout_last;
+    f.draft = s.draft;
+    f.dr_sb = s.dr_sb;
+    f.status = s.ws.status;
+    hipLaunchKernelGGL((k_lm_finalize<W>), dim3(s.B), dim3(kWG), 0, s.stream, f);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace mtp

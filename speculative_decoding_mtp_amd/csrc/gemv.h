@@ -1,16 +1,22 @@
 // Weight-streaming GEMV for the draft head (few activation rows, bf16 or fp32 weights,
-// fp32 activations and accumulation).
+// fp32 activations and fp32 accumulation).
 //
-// y[a][m] = sum_k W[row(m)][k] * x[a][k] for every logical output row m and activation row a.
+//   y[a][m] = sum_k W[row(m)][k] * x[a][k]   for every logical output row m, activation row a.
 //
-// Layout of the work: the 256 threads of a workgroup split K into 16-byte weight chunks
-// (chunk c = tid + 256*j, j < nx), so one wave-wide load reads 1 KB of a weight row and the
-// whole workgroup reads 4 KB contiguous.  Each thread keeps its slice of RB activation rows in
-// registers for the whole kernel and streams ROWS weight rows at a time through it; the ROWS*RB
-// partial dot products are reduced across the workgroup once per ROWS rows.  Workgroups take
-// row groups in a grid-stride loop.  Activation rows beyond RB are handled in further passes
-// over the weights.  A policy class supplies the activation prologue (raw loads, RMSNorm), the
-// logical-row -> weight-row map and the epilogue.
+// Two layouts of the same computation:
+//
+// * k_gemv_w ("wave rows", rows of up to 64*8 16-byte chunks): every wave owns whole weight
+//   rows.  Lane l reads chunks c = l + 64 j of a row, so one load instruction covers 1 KB of a
+//   row and a wave keeps RW*NJ loads (about 16) in flight.  The lane's slice of RB activation
+//   rows stays in registers for the whole kernel.  Row sums are wave reductions through DPP
+//   moves and lane reads: no LDS traffic and no barrier in the streaming loop; the waves of a
+//   workgroup are independent.
+// * k_gemv_s ("split K", wider rows): the 256 threads of a workgroup share each row (chunk
+//   c = tid + 256 j); partial sums meet in LDS once per ROWS rows.
+//
+// Activation rows beyond RB are handled in further passes over the weights.  A policy class
+// supplies the activation prologue (raw loads, RMSNorm), the logical-row -> weight-row map and
+// the stores; the argmax over logical rows (the lm_head) is tracked by the kernel.
 #pragma once
 
 #include "common.h"
@@ -32,40 +38,159 @@ __device__ __forceinline__ void load_f32_vec(const float* p, float (&f)[VE]) {
   }
 }
 
-template <class W>
-__device__ __forceinline__ void load_w_vec(const typename W::T* p, float (&f)[W::VE]) {
-  W::cvt(ld16(p), f);
+// DPP lane move (gfx9 encodings: quad_perm 0x00-0xff, row_mirror 0x140, row_half_mirror 0x141)
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+
+// Sum over the 64 lanes of a wave; the result is wave-uniform.  Pairs lanes i^1 and i^2 inside
+// each quad, then mirrors inside each 8-lane half row and each 16-lane row (every lane of a row
+// then holds the row sum), and adds the four row sums read from lanes 0, 16, 32, 48.  Must be
+// called with all lanes active.
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_mov<0xb1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_mov<0x4e>(v);   // quad_perm [2,3,0,1]
+  v += dpp_mov<0x141>(v);  // row_half_mirror
+  v += dpp_mov<0x140>(v);  // row_mirror
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
 }
 
 // Policy hooks (all __device__):
-//   static constexpr int kNorm;             0: none, 1: RMSNorm of the whole row, 2: separate
-//                                           RMSNorms of [0, split) and [split, K)
-//   void setup(int* s_n)                    fill per-sequence row counts (then the kernel syncs)
+//   static constexpr int kNorm;     0: none, 1: RMSNorm of the row, 2: RMSNorms of [0, split) and
+//                                   [split, K) separately
+//   static constexpr bool kPair;    outputs come as logical-row pairs (m even, m + 1)
+//   static constexpr bool kArgmax;  track the argmax over logical rows of every activation row
+//   void setup(int* s_n)            per-sequence row counts into LDS (the kernel then syncs)
 //   void act(int a, const int* s_n, int& row, bool& valid)
-//   void load_x(int row, int k, float (&f)[VE])   raw activations k..k+VE-1 of a row
-//   void gain_vec(int k, float (&g)[VE])    norm gains k..k+VE-1 (kNorm > 0)
-//   const T* wrow(int m)                    weight row of logical row m (m < N)
-//   void epilogue(int m0, const float* tile, const int* rows, const bool* valid, int nval)
-//                                           tile[q*RB + r] = y[a0+r][m0+q]; called by all threads
-//   void act_block_done(int a0, ...)        after the last row group of an activation block
-//   void finish()                           once per workgroup at the end
-template <class W, int RB, int NXM, int ROWS, class P>
-__global__ __launch_bounds__(kWG, 2) void k_gemv(P p) {
+//   void load_x(int row, int k, float (&f)[VE])     raw activations k..k+VE-1 of a row
+//   void gain_vec(int k, float (&g)[VE])            norm gains (kNorm > 0)
+//   const T* wrow(int m)                            weight row of logical row m < N
+//   void store(int m, int a, int row, float v)      (!kPair)
+//   void store_pair(int m, int a, int row, float v0, float v1)   (kPair)
+//   void partial(int a, float v, int i)             (kArgmax) this workgroup's best of row a
+//   void finish(const int* s_n)                     once per workgroup at the end
+
+// Register slice of RB activation rows: x[r][j] holds the VE activations of chunk
+// c = cbase + j * cstride (zero outside the row and for invalid rows), RMS-normalised when the
+// policy asks.  `reduce(s0, s1)` turns per-thread sums of squares into row totals.
+template <class W, int RB, int NJ, class P, class Reduce>
+__device__ __forceinline__ void load_slice(const P& p, const int (&rows)[RB], const bool (&valid)[RB], int cbase,
+                                           int cstride, int Kc, float (&x)[RB][NJ][W::VE], Reduce reduce) {
+  constexpr int VE = W::VE;
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int c = cbase + j * cstride;
+      if (valid[r] && c < Kc) {
+        p.load_x(rows[r], c * VE, x[r][j]);
+        if constexpr (P::kNorm > 0) {
+          float s = 0.f;
+#pragma unroll
+          for (int e = 0; e < VE; ++e) s = fmaf(x[r][j][e], x[r][j][e], s);
+          if (P::kNorm == 2 && c * VE >= p.split)
+            s1 += s;
+          else
+            s0 += s;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < VE; ++e) x[r][j][e] = 0.f;
+      }
+    }
+    if constexpr (P::kNorm > 0) {
+      reduce(s0, s1);
+      float sc0, sc1;
+      if constexpr (P::kNorm == 2) {
+        sc0 = 1.0f / sqrtf(s0 / float(p.split) + p.eps);
+        sc1 = 1.0f / sqrtf(s1 / float(p.K - p.split) + p.eps);
+      } else {
+        sc0 = sc1 = 1.0f / sqrtf(s0 / float(p.K) + p.eps);
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int c = cbase + j * cstride;
+        if (c < Kc) {
+          const int k0 = c * VE;
+          const float sc = (P::kNorm == 2 && k0 >= p.split) ? sc1 : sc0;
+          float gv[VE];
+          p.gain_vec(k0, gv);
+#pragma unroll
+          for (int e = 0; e < VE; ++e) x[r][j][e] = x[r][j][e] * sc * gv[e];
+        }
+      }
+    }
+  }
+}
+
+// Hand the reduced, wave-uniform tile v[q][r] to the policy: item (q, r) -- or pair (q, q+1) --
+// is stored by one lane.
+template <int RW, int RB, class P>
+__device__ __forceinline__ void store_tile(P& p, int m0, int a0, const int (&rows)[RB], const bool (&valid)[RB],
+                                           const float (&v)[RW][RB], int lane) {
+  if constexpr (P::kPair) {
+#pragma unroll
+    for (int q = 0; q < RW; q += 2)
+#pragma unroll
+      for (int r = 0; r < RB; ++r)
+        if (lane == ((q / 2) * RB + r) % kWave && valid[r] && m0 + q < p.N)
+          p.store_pair(m0 + q, a0 + r, rows[r], v[q][r], v[q + 1][r]);
+  } else {
+#pragma unroll
+    for (int q = 0; q < RW; ++q)
+#pragma unroll
+      for (int r = 0; r < RB; ++r)
+        if (lane == (q * RB + r) % kWave && valid[r] && m0 + q < p.N) p.store(m0 + q, a0 + r, rows[r], v[q][r]);
+  }
+}
+
+// Combine the per-wave argmax of RB activation rows across the workgroup and hand it to the
+// policy (thread r).  Contains barriers: call with the whole workgroup.
+template <int RB, class P>
+__device__ __forceinline__ void argmax_partials(P& p, int a0, const float (&bv)[RB], const int (&bi)[RB], float* sv,
+                                                int* si) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  if (lane == 0)
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      sv[wid * RB + r] = bv[r];
+      si[wid * RB + r] = bi[r];
+    }
+  __syncthreads();
+  if (threadIdx.x < RB) {
+    const int r = threadIdx.x;
+    float v = sv[r];
+    int i = si[r];
+    for (int w = 1; w < 4; ++w)
+      if (better(sv[w * RB + r], si[w * RB + r], v, i)) {
+        v = sv[w * RB + r];
+        i = si[w * RB + r];
+      }
+    p.partial(a0 + r, v, i);
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------------------------
+template <class W, int RB, int NJ, int RW, class P>
+__global__ __launch_bounds__(kWG) void k_gemv_w(P p) {
   using T = typename W::T;
   constexpr int VE = W::VE;
-  __shared__ float s_red[4 * ROWS * RB];
-  __shared__ float s_tile[ROWS * RB];
-  __shared__ float s_norm[8 * RB];
   __shared__ int s_n[kMaxBatch];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wid = tid >> 6;
-
+  __shared__ float s_bv[4 * RB];
+  __shared__ int s_bi[4 * RB];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   p.setup(s_n);
   __syncthreads();
-
   const int Kc = p.K / VE;
-  const int nx = (Kc + kWG - 1) / kWG;
-  const int ngroups = (p.N + ROWS - 1) / ROWS;
+  const int ngroups = (p.N + RW - 1) / RW;
+  const int wave = blockIdx.x * 4 + wid, nwaves = gridDim.x * 4;
 
   for (int a0 = 0; a0 < p.nact; a0 += RB) {
     int rows[RB];
@@ -77,76 +202,123 @@ __global__ __launch_bounds__(kWG, 2) void k_gemv(P p) {
       any |= valid[r];
     }
     if (!any) continue;  // uniform across the workgroup
-
-    float x[RB][NXM][VE];
-    float ss[2 * RB];
-#pragma unroll
-    for (int r = 0; r < 2 * RB; ++r) ss[r] = 0.f;
+    float x[RB][NJ][VE];
+    load_slice<W, RB, NJ>(p, rows, valid, lane, kWave, Kc, x, [](float& s0, float& s1) {
+      s0 = wave_sum_dpp(s0);
+      s1 = wave_sum_dpp(s1);
+    });
+    float bv[RB];
+    int bi[RB];
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
+      bv[r] = -INFINITY;
+      bi[r] = 0x7fffffff;
+    }
+    for (int g = wave; g < ngroups; g += nwaves) {
+      const int m0 = g * RW;
+      uint4 wv[RW][NJ];
 #pragma unroll
-      for (int j = 0; j < NXM; ++j) {
-        const int c = tid + j * kWG;
-        if (valid[r] && j < nx && c < Kc) {
-          p.load_x(rows[r], c * VE, x[r][j]);
-          if constexpr (P::kNorm > 0) {
-            float s = 0.f;
+      for (int q = 0; q < RW; ++q) {
+        const T* wp = p.wrow(min(m0 + q, p.N - 1));
 #pragma unroll
-            for (int e = 0; e < VE; ++e) s += x[r][j][e] * x[r][j][e];
-            const int half = (P::kNorm == 2 && c * VE >= p.split) ? 1 : 0;
-            ss[2 * r + half] += s;
-          }
-        } else {
+        for (int j = 0; j < NJ; ++j) wv[q][j] = ld_stream(wp + (long)min(lane + j * kWave, Kc - 1) * VE);
+      }
+      float acc[RW][RB];
 #pragma unroll
-          for (int e = 0; e < VE; ++e) x[r][j][e] = 0.f;
+      for (int q = 0; q < RW; ++q) {
+#pragma unroll
+        for (int r = 0; r < RB; ++r) acc[q][r] = 0.f;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          float wf[VE];
+          W::cvt(wv[q][j], wf);
+#pragma unroll
+          for (int r = 0; r < RB; ++r)
+#pragma unroll
+            for (int e = 0; e < VE; ++e) acc[q][r] = fmaf(wf[e], x[r][j][e], acc[q][r]);
         }
       }
-    }
-    if constexpr (P::kNorm > 0) {
-      wg_sum<2 * RB>(ss, s_norm);
 #pragma unroll
-      for (int r = 0; r < RB; ++r) {
-        float sc0, sc1;
-        if constexpr (P::kNorm == 2) {
-          sc0 = 1.0f / sqrtf(ss[2 * r] / float(p.split) + p.eps);
-          sc1 = 1.0f / sqrtf(ss[2 * r + 1] / float(p.K - p.split) + p.eps);
-        } else {
-          sc0 = sc1 = 1.0f / sqrtf((ss[2 * r] + ss[2 * r + 1]) / float(p.K) + p.eps);
-        }
+      for (int q = 0; q < RW; ++q)
 #pragma unroll
-        for (int j = 0; j < NXM; ++j) {
-          const int c = tid + j * kWG;
-          if (j < nx && c < Kc) {
-            const int k0 = c * VE;
-            const float sc = (P::kNorm == 2 && k0 >= p.split) ? sc1 : sc0;
-            float gv[VE];
-            p.gain_vec(k0, gv);
+        for (int r = 0; r < RB; ++r) acc[q][r] = wave_sum_dpp(acc[q][r]);
+      store_tile<RW, RB>(p, m0, a0, rows, valid, acc, lane);
+      if constexpr (P::kArgmax) {
 #pragma unroll
-            for (int e = 0; e < VE; ++e) x[r][j][e] = x[r][j][e] * sc * gv[e];
-          }
-        }
+        for (int r = 0; r < RB; ++r)
+#pragma unroll
+          for (int q = 0; q < RW; ++q)
+            if (m0 + q < p.N && better(acc[q][r], m0 + q, bv[r], bi[r])) {
+              bv[r] = acc[q][r];
+              bi[r] = m0 + q;
+            }
       }
     }
+    if constexpr (P::kArgmax) argmax_partials<RB>(p, a0, bv, bi, s_bv, s_bi);
+  }
+  p.finish(s_n);
+}
 
+// ---------------------------------------------------------------------------------------------
+template <class W, int RB, int NXM, int ROWS, class P>
+__global__ __launch_bounds__(kWG) void k_gemv_s(P p) {
+  constexpr int VE = W::VE;
+  __shared__ float s_red[4 * ROWS * RB];
+  __shared__ float s_norm[8];
+  __shared__ int s_n[kMaxBatch];
+  __shared__ float s_bv[4 * RB];
+  __shared__ int s_bi[4 * RB];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  p.setup(s_n);
+  __syncthreads();
+  const int Kc = p.K / VE;
+  const int ngroups = (p.N + ROWS - 1) / ROWS;
+
+  for (int a0 = 0; a0 < p.nact; a0 += RB) {
+    int rows[RB];
+    bool valid[RB];
+    bool any = false;
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      p.act(a0 + r, s_n, rows[r], valid[r]);
+      any |= valid[r];
+    }
+    if (!any) continue;
+    float x[RB][NXM][VE];
+    load_slice<W, RB, NXM>(p, rows, valid, tid, kWG, Kc, x, [&](float& s0, float& s1) {
+      s0 = wave_sum_dpp(s0);
+      s1 = wave_sum_dpp(s1);
+      if (lane == 0) {
+        s_norm[wid] = s0;
+        s_norm[4 + wid] = s1;
+      }
+      __syncthreads();
+      s0 = (s_norm[0] + s_norm[1]) + (s_norm[2] + s_norm[3]);
+      s1 = (s_norm[4] + s_norm[5]) + (s_norm[6] + s_norm[7]);
+      __syncthreads();
+    });
+    float bv[RB];
+    int bi[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      bv[r] = -INFINITY;
+      bi[r] = 0x7fffffff;
+    }
     for (int g = blockIdx.x; g < ngroups; g += gridDim.x) {
       const int m0 = g * ROWS;
-      const T* wp[ROWS];
-#pragma unroll
-      for (int q = 0; q < ROWS; ++q) wp[q] = (m0 + q < p.N) ? p.wrow(m0 + q) : nullptr;
       float acc[ROWS][RB];
 #pragma unroll
       for (int q = 0; q < ROWS; ++q)
 #pragma unroll
         for (int r = 0; r < RB; ++r) acc[q][r] = 0.f;
-
 #pragma unroll
       for (int j = 0; j < NXM; ++j) {
         const int c = tid + j * kWG;
-        if (j < nx && c < Kc) {
+        if (j * kWG < Kc) {  // uniform; lanes past the row end read a clamped chunk against x = 0
           uint4 wv[ROWS];
 #pragma unroll
           for (int q = 0; q < ROWS; ++q)
-            wv[q] = wp[q] ? ld_stream(wp[q] + (long)c * VE) : make_uint4(0, 0, 0, 0);
+            wv[q] = ld_stream(p.wrow(min(m0 + q, p.N - 1)) + (long)min(c, Kc - 1) * VE);
 #pragma unroll
           for (int q = 0; q < ROWS; ++q) {
             float wf[VE];
@@ -158,21 +330,35 @@ __global__ __launch_bounds__(kWG, 2) void k_gemv(P p) {
           }
         }
       }
-      // reduce ROWS*RB partial sums over the workgroup
 #pragma unroll
       for (int q = 0; q < ROWS; ++q)
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
-          const float s = wave_sum(acc[q][r]);
+          const float s = wave_sum_dpp(acc[q][r]);
           if (lane == 0) s_red[wid * ROWS * RB + q * RB + r] = s;
         }
       __syncthreads();
-      if (tid < ROWS * RB)
-        s_tile[tid] = s_red[tid] + s_red[ROWS * RB + tid] + s_red[2 * ROWS * RB + tid] + s_red[3 * ROWS * RB + tid];
+#pragma unroll
+      for (int q = 0; q < ROWS; ++q)
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+          const int k = q * RB + r;
+          acc[q][r] = (s_red[k] + s_red[ROWS * RB + k]) + (s_red[2 * ROWS * RB + k] + s_red[3 * ROWS * RB + k]);
+        }
       __syncthreads();
-      p.template epilogue<ROWS, RB>(m0, s_tile, rows, valid, a0);
+      if (wid == 0) store_tile<ROWS, RB>(p, m0, a0, rows, valid, acc, lane);
+      if constexpr (P::kArgmax) {
+#pragma unroll
+        for (int r = 0; r < RB; ++r)
+#pragma unroll
+          for (int q = 0; q < ROWS; ++q)
+            if (m0 + q < p.N && better(acc[q][r], m0 + q, bv[r], bi[r])) {
+              bv[r] = acc[q][r];
+              bi[r] = m0 + q;
+            }
+      }
     }
-    p.template act_block_done<RB>(a0, rows, valid);
+    if constexpr (P::kArgmax) argmax_partials<RB>(p, a0, bv, bi, s_bv, s_bi);
   }
   p.finish(s_n);
 }

@@ -9,6 +9,7 @@ namespace mtp {
 constexpr int kChunk = 4096;    // logits per workgroup in the sampling top-k pass
 constexpr int kTopCap = 8192;   // candidates one workgroup can merge (chunks * top_k)
 constexpr int kMaxTopK = 128;   // largest top_k on the device path
+constexpr int kMaxDraft = 63;   // largest D on the device path
 
 struct VerifyArgs {
   int B, D, V;
@@ -24,7 +25,6 @@ struct VerifyArgs {
   // greedy scratch
   float* part_v;
   int* part_i;
-  int* row_tok;
   // sampling scratch
   float* cand_v;  // [rows][nchunk][top_k]
   int* cand_i;
@@ -32,8 +32,6 @@ struct VerifyArgs {
   int* top_i;
   int* top_n;      // [rows]
   float* scratch;  // [B][4 * kMaxTopK]
-  unsigned* tick_row;  // [rows]
-  unsigned* tick_seq;  // [B]
 };
 
 hipError_t run_verify(const VerifyArgs& a, hipStream_t st);

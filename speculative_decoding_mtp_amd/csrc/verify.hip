@@ -9,29 +9,14 @@
 // and top-p applied in turn); [YL] "MTP 原理详解" 三 stages 3-4 (accept when P/Q >= U, resample
 // on rejection, 1..D+1 tokens per round).
 //
-// Both kernels run in one launch each: workgroups scan chunks of a row, the last workgroup of a
-// row (an atomic ticket) merges that row, and the last row of a sequence runs the sequence's
-// decision.  Every ticket is reset by the workgroup that consumed it.
+// Each verifier is a short chain of kernels: workgroups scan chunks of every row, then rows are
+// merged, then one workgroup per sequence takes the sequence's decisions.
 #include <float.h>
 
 #include "common.h"
 #include "verify.h"
 
 namespace mtp {
-
-__device__ __forceinline__ bool last_arrival(unsigned* ticket, unsigned total, int* s_flag) {
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned t = atomicAdd(ticket, 1u);
-    *s_flag = (t == total - 1);
-    if (t == total - 1) *ticket = 0u;
-  }
-  __syncthreads();
-  const bool last = *s_flag;
-  if (last) __threadfence();
-  return last;
-}
 
 // workgroup argmax (value desc, index asc) of one value per thread
 __device__ __forceinline__ void wg_argmax(float& v, int& i, float* sv, int* si) {
@@ -59,9 +44,7 @@ __device__ __forceinline__ void wg_argmax(float& v, int& i, float* sv, int* si) 
 __global__ __launch_bounds__(kWG) void k_verify_greedy(VerifyArgs a) {
   __shared__ float sv[4];
   __shared__ int si[4];
-  __shared__ int s_flag;
   const int c = blockIdx.x, row = blockIdx.y;
-  const int rows_per_seq = a.D + 1;
   const float* x = a.tl + (long)row * a.V;
   const int beg = c * a.chunk, end = min(a.V, beg + a.chunk);
   float bv = -INFINITY;
@@ -89,31 +72,36 @@ __global__ __launch_bounds__(kWG) void k_verify_greedy(VerifyArgs a) {
     a.part_v[(long)row * a.nchunk + c] = bv;
     a.part_i[(long)row * a.nchunk + c] = bi;
   }
-  if (!last_arrival(a.tick_row + row, a.nchunk, &s_flag)) return;
-  // this row is complete
-  bv = -INFINITY;
-  bi = 0x7fffffff;
-  for (int k = threadIdx.x; k < a.nchunk; k += kWG) {
-    const float v = a.part_v[(long)row * a.nchunk + k];
-    const int i = a.part_i[(long)row * a.nchunk + k];
-    if (better(v, i, bv, bi)) {
-      bv = v;
-      bi = i;
+}
+
+// one workgroup per sequence: argmax of each of its D+1 rows, then the prefix match
+__global__ __launch_bounds__(kWG) void k_verify_greedy_final(VerifyArgs a) {
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  __shared__ int st[kMaxDraft + 1];
+  const int b = blockIdx.x, rows_per_seq = a.D + 1;
+  for (int j = 0; j < rows_per_seq; ++j) {
+    const long row = (long)b * rows_per_seq + j;
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int k = threadIdx.x; k < a.nchunk; k += kWG) {
+      const float v = a.part_v[row * a.nchunk + k];
+      const int i = a.part_i[row * a.nchunk + k];
+      if (better(v, i, bv, bi)) {
+        bv = v;
+        bi = i;
+      }
     }
+    wg_argmax(bv, bi, sv, si);
+    if (threadIdx.x == 0) st[j] = bi;
   }
-  wg_argmax(bv, bi, sv, si);
-  if (threadIdx.x == 0) a.row_tok[row] = bi;
-  const int b = row / rows_per_seq;
-  if (!last_arrival(a.tick_seq + b, rows_per_seq, &s_flag)) return;
-  // every target row of sequence b has its argmax: prefix match
   if (threadIdx.x == 0) {
-    const int* t = a.row_tok + (long)b * rows_per_seq;
     const int* d = a.drafts + (long)b * a.D;
     int n = 0;
-    while (n < a.D && t[n] == d[n]) ++n;
+    while (n < a.D && st[n] == d[n]) ++n;
     int32_t* out = a.out + (long)b * rows_per_seq;
     for (int j = 0; j < n; ++j) out[j] = d[j];
-    out[n] = t[n];
+    out[n] = st[n];
     for (int j = n + 1; j < rows_per_seq; ++j) out[j] = -1;
     a.n_accept[b] = n;
     a.crop[b] = a.ctx_len[b] + 1 + n;
@@ -281,9 +269,8 @@ __device__ int draw_ascending(int* ids, float* w, int m, float u) {
   return last;  // u * S rounded onto S
 }
 
-__global__ __launch_bounds__(kWG) void k_verify_sample(VerifyArgs a) {
+__global__ __launch_bounds__(kWG) void k_topk_chunks(VerifyArgs a) {
   __shared__ TopkSmem sm;
-  __shared__ int s_flag;
   const int c = blockIdx.x, row = blockIdx.y;
   const int K = a.top_k;
   const int tgt_rows = a.B * (a.D + 1);
@@ -307,7 +294,13 @@ __global__ __launch_bounds__(kWG) void k_verify_sample(VerifyArgs a) {
       oi[t] = -1;
     }
   }
-  if (!last_arrival(a.tick_row + row, a.nchunk, &s_flag)) return;
+}
+
+// one workgroup per row: the top-k of the row from its chunks' candidates
+__global__ __launch_bounds__(kWG) void k_topk_rows(VerifyArgs a) {
+  __shared__ TopkSmem sm;
+  const int row = blockIdx.x;
+  const int K = a.top_k;
   {  // merge the row's candidates
     constexpr int IPT = kTopCap / kWG;
     float v[IPT];
@@ -322,10 +315,13 @@ __global__ __launch_bounds__(kWG) void k_verify_sample(VerifyArgs a) {
     const int n = wg_topk<IPT>(v, id, K, sm, a.top_v + (long)row * K, a.top_i + (long)row * K);
     if (threadIdx.x == 0) a.top_n[row] = n;
   }
-  // sequence of this row: target row j of sequence b, or draft row j of sequence b
-  const int b = row < tgt_rows ? row / (a.D + 1) : (row - tgt_rows) / a.D;
-  const int need = (a.D + 1) + (a.q_mode == 1 ? a.D : 0);
-  if (!last_arrival(a.tick_seq + b, need, &s_flag)) return;
+}
+
+// one workgroup per sequence (one thread does the work): accept / reject / draw
+__global__ __launch_bounds__(64) void k_sample_decide(VerifyArgs a) {
+  const int b = blockIdx.x;
+  const int K = a.top_k;
+  const int tgt_rows = a.B * (a.D + 1);
   if (threadIdx.x != 0) return;
   // ---- the sequence's decision, one thread ----
   float* P = a.scratch + (long)b * 4 * kMaxTopK;  // [kMaxTopK] probs of the target row
@@ -390,9 +386,12 @@ __global__ __launch_bounds__(kWG) void k_verify_sample(VerifyArgs a) {
 hipError_t run_verify(const VerifyArgs& a, hipStream_t st) {
   if (a.greedy) {
     hipLaunchKernelGGL(k_verify_greedy, dim3(a.nchunk, a.B * (a.D + 1)), dim3(kWG), 0, st, a);
+    hipLaunchKernelGGL(k_verify_greedy_final, dim3(a.B), dim3(kWG), 0, st, a);
   } else {
     const int rows = a.B * (a.D + 1) + (a.q_mode == 1 ? a.B * a.D : 0);
-    hipLaunchKernelGGL(k_verify_sample, dim3(a.nchunk, rows), dim3(kWG), 0, st, a);
+    hipLaunchKernelGGL(k_topk_chunks, dim3(a.nchunk, rows), dim3(kWG), 0, st, a);
+    hipLaunchKernelGGL(k_topk_rows, dim3(rows), dim3(kWG), 0, st, a);
+    hipLaunchKernelGGL(k_sample_decide, dim3(a.B), dim3(64), 0, st, a);
   }
   return hipGetLastError();
 }

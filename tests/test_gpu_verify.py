@@ -1,0 +1,141 @@
+"""GPU parity of spec_verify (greedy and speculative sampling) against the oracle.
+
+Bar: n_accept, out_tokens and crop_len bit-exact; a sequence whose oracle decisions include a
+margin below 1e-4 (top-p crossing, |p/q - U|, inverse-CDF boundary) is excluded and counted."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from synth import Sampling, VERIFY_CONFIGS, gen, make_verify_inputs
+
+pytestmark = pytest.mark.gpu
+
+M = pytest.importorskip("speculative_decoding_mtp_amd")
+from tests.gpu_util import MARGIN, f32, i32  # noqa: E402
+
+
+def _gpu_verify(tl, drafts, dl, sp, ua, us, ctx):
+    B, D1, V = tl.shape
+    D = D1 - 1
+    csp = None if sp is None else M.sampling(sp.temperature, sp.top_k, sp.top_p, sp.q_mode)
+    ws = M.new_workspace(M.spec_verify_workspace_size(B, D, V, csp))
+    n = torch.zeros(B, dtype=torch.int32, device="cuda")
+    out = torch.zeros(B, D + 1, dtype=torch.int32, device="cuda")
+    crop = torch.zeros(B, dtype=torch.int32, device="cuda")
+    M.spec_verify(B, D, V, f32(tl), i32(drafts), None if dl is None else f32(dl), csp,
+                  None if ua is None else f32(ua), None if us is None else f32(us), i32(ctx), n, out, crop, ws)
+    torch.cuda.synchronize()
+    return n.cpu().numpy(), out.cpu().numpy(), crop.cpu().numpy()
+
+
+def _sample_drafts(dl, sp, seed):
+    """q_mode 1 drafts: drawn from the warped draft logits (input preparation via the oracle)."""
+    B, D, V = dl.shape
+    u = gen(77, 6, seed).random((B, D))
+    return np.array([[O.sample(O.warp(dl[b, j], sp.temperature, sp.top_k, sp.top_p)[0], u[b, j])[0]
+                      for j in range(D)] for b in range(B)], np.int32)
+
+
+def _compare(tl, drafts, dl, sp, ua, us, ctx, seqs=None):
+    n, out, crop = _gpu_verify(tl, drafts, dl, sp, ua, us, ctx)
+    seqs = range(tl.shape[0]) if seqs is None else seqs
+    excluded = 0
+    for b in seqs:
+        r = O.spec_verify(tl[b:b + 1], drafts[b:b + 1], ctx[b:b + 1], sp, None if dl is None else dl[b:b + 1],
+                          None if ua is None else ua[b:b + 1], None if us is None else us[b:b + 1])
+        if sp is not None and min(r.margins[0], default=1.0) < MARGIN:
+            excluded += 1
+            continue
+        assert n[b] == r.n_accept[0], b
+        assert np.array_equal(out[b], r.out_tokens[0]), (b, out[b], r.out_tokens[0])
+        assert crop[b] == r.crop_len[0], b
+    return excluded, n
+
+
+def _inputs(B, D, V, sigma, seed):
+    g = gen(60, 7, seed)
+    dl = (g.standard_normal((B, D, V), dtype=np.float32) * 3).astype(np.float32)
+    tl = np.empty((B, D + 1, V), np.float32)
+    tl[:, :D] = dl + g.standard_normal((B, D, V), dtype=np.float32) * sigma
+    tl[:, D] = g.standard_normal((B, V), dtype=np.float32) * 3
+    ua = g.random((B, D), dtype=np.float32)
+    us = g.random(B, dtype=np.float32)
+    ctx = g.integers(1, 8192, size=B).astype(np.int32)
+    return tl, dl, ua, us, ctx
+
+
+SETTINGS = [
+    None,
+    Sampling(1.0, 64, 0.95, 0),
+    Sampling(0.7, 50, 0.9, 0),
+    Sampling(0.7, 50, 0.9, 1),
+    Sampling(1.3, 1, 1.0, 0),
+    Sampling(0.9, 128, 1.0, 1),
+    Sampling(0.5, 7, 0.3, 1),
+    Sampling(2.0, 20, 0.5, 0),
+]
+
+
+@pytest.mark.parametrize("V", [1000, 4093, 20000])
+@pytest.mark.parametrize("si", range(len(SETTINGS)))
+def test_verify_small_matches_oracle(V, si):
+    sp = SETTINGS[si]
+    B, D = 24, 4
+    tl, dl, ua, us, ctx = _inputs(B, D, V, 1.0, seed=V + si)
+    if sp is not None and sp.q_mode == 1:
+        drafts = _sample_drafts(dl, sp, V + si)
+    else:
+        drafts = np.argmax(dl, axis=-1).astype(np.int32)
+        drafts[::3, 0] = np.argmax(tl[::3, 0], -1)          # some sequences accept at least one draft
+    excl, n = _compare(tl, drafts, dl if sp is not None and sp.q_mode == 1 else None, sp, ua, us, ctx)
+    assert excl <= B // 4
+
+
+def test_verify_all_accept_gives_the_bonus_row():
+    B, D, V = 8, 3, 3000
+    tl, dl, ua, us, ctx = _inputs(B, D, V, 0.0, seed=5)
+    drafts = np.argmax(tl[:, :D], axis=-1).astype(np.int32)
+    n, out, _ = _gpu_verify(tl, drafts, None, None, None, None, ctx)
+    assert np.all(n == D)
+    assert np.array_equal(out[:, D], np.argmax(tl[:, D], -1))
+    # sampling with Q = P (q_mode 1, draft logits = target logits) accepts every draft
+    sp = Sampling(0.8, 40, 0.9, 1)
+    d1 = _sample_drafts(tl[:, :D], sp, 9)
+    n, out, _ = _gpu_verify(tl, d1, tl[:, :D].copy(), sp, ua * np.float32(0.999), us, ctx)
+    assert np.all(n == D)
+
+
+def test_verify_uniform_zero_and_near_one():
+    B, D, V = 16, 2, 2048
+    tl, dl, ua, us, ctx = _inputs(B, D, V, 1.0, seed=6)
+    sp = Sampling(1.0, 30, 1.0, 0)
+    drafts = np.argmax(tl[:, :D], axis=-1).astype(np.int32)        # drafts with mass
+    n, _, _ = _gpu_verify(tl, drafts, None, sp, np.zeros((B, D), np.float32), us, ctx)
+    assert np.all(n == D)                                          # U = 0 keeps a draft with P > 0
+    n, _, _ = _gpu_verify(tl, drafts, None, sp, np.full((B, D), 1 - 2 ** -24, np.float32), us, ctx)
+    r = O.spec_verify(tl, drafts, ctx, sp, None, np.full((B, D), 1 - 2 ** -24), us)
+    assert np.array_equal(n, r.n_accept)
+
+
+@pytest.mark.parametrize("sigma", [0.3, 1.0, 3.0])
+def test_verify_stress_full_size_sampled(sigma):
+    """B=256, D=4, V=151936 (the verifier-only workload): every sequence runs on the GPU, a
+    fixed sample of 32 is recomputed by the oracle; greedy is compared on all 256."""
+    vc = VERIFY_CONFIGS["stress"]
+    dl, tl, ctx = make_verify_inputs(vc, sigma)
+    B, D = vc.batch, vc.D
+    g = gen(vc.index, 6, int(sigma * 10))
+    ua, us = g.random((B, D), dtype=np.float32), g.random(B, dtype=np.float32)
+    drafts = np.argmax(dl, axis=-1).astype(np.int32)
+    sample = list(range(0, B, 8))
+    excl, n = _compare(tl, drafts, None, vc.sampling, ua, us, ctx, seqs=sample)
+    assert excl <= 4
+    _compare(tl, drafts, None, None, None, None, ctx)
+    if sigma == 1.0:
+        sp1 = Sampling(vc.sampling.temperature, vc.sampling.top_k, vc.sampling.top_p, 1)
+        d1 = _sample_drafts(dl[sample], sp1, 3)
+        dr = drafts.copy()
+        dr[sample] = d1
+        excl, _ = _compare(tl, dr, dl, sp1, ua, us, ctx, seqs=sample)
+        assert excl <= 4
