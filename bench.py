@@ -35,6 +35,7 @@ def parse():
     ap.add_argument("--state-bytes", type=int, default=None, help="recurrent state bytes per sequence")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle baseline sample budget (0: skip)")
     ap.add_argument("--traffic", default=None, help="JSON file with counter-measured lm_head bytes per launch")
+    ap.add_argument("--graph", type=int, default=0, help="capture this many rounds per HIP graph (0: eager)")
     return ap.parse_args()
 
 
@@ -53,7 +54,7 @@ def main():
     B, D, H, V = cfg.batch, cfg.D, cfg.hidden, cfg.vocab
     state_bytes = cfg.state_bytes_per_seq if args.state_bytes is None else args.state_bytes
     rounds_total = args.warmup + args.steps
-    max_len = cfg.ctx + 1 + rounds_total * (D + 1) + 64
+    max_len = cfg.ctx + 1 + (rounds_total + args.graph) * (D + 1) + 64
     t0 = time.time()
     w = make_weights(cfg)
     c = config(cfg)
@@ -79,11 +80,10 @@ def main():
     hiddens = torch.zeros(B, D, H, device="cuda")
     dlog = torch.zeros(B, D, V, device="cuda")
     tl = torch.zeros(B, D + 1, V, device="cuda")
-    n_acc = torch.zeros(B, dtype=torch.int32, device="cuda")
     out_tok = [torch.zeros(B, D + 1, dtype=torch.int32, device="cuda") for _ in range(2)]
     ctx = [torch.full((B,), cfg.ctx + 1, dtype=torch.int32, device="cuda"),
            torch.zeros(B, dtype=torch.int32, device="cuda")]
-    hist = torch.zeros(rounds_total, B, dtype=torch.int32, device="cuda")
+    hist = torch.zeros(rounds_total + max(args.graph, 0), B, dtype=torch.int32, device="cuda")
     state = snap = None
     if state_bytes:
         state = torch.from_numpy(make_state(B, state_bytes)).cuda()
@@ -94,37 +94,64 @@ def main():
         tk = tokens if r == 0 else out_tok[cur]
         hin = hidden0 if r == 0 else hid_bufs[r % NBUF]
         M.mtp_draft_loop(c, gw, kv, D, rps, tk, hin, drafts, hiddens, dlog, ws)
-        # stand-in target forward: target row j = draft logits of step j+1 (row D reuses step D)
-        tl[:, :D].copy_(dlog)
-        tl[:, D].copy_(dlog[:, D - 1])
-        tl.add_(noise_bufs[r % NBUF])
+        # stand-in target forward: target row j = draft logits of step j+1 + noise (row D
+        # reuses step D's logits), one elementwise kernel for D = 1
+        noise = noise_bufs[r % NBUF]
+        if D == 1:
+            torch.add(noise, dlog.expand(B, 2, V), out=tl)
+        else:
+            torch.add(noise[:, :D], dlog, out=tl[:, :D])
+            torch.add(noise[:, D], dlog[:, D - 1], out=tl[:, D])
         if state is not None:
             M.mtp_state_snapshot(state, snap, state_bytes, B)
+        n_acc = hist[r]
         M.spec_verify(B, D, V, tl, drafts, None, None, None, None, ctx[cur], n_acc, out_tok[nxt], ctx[nxt], vws)
         if state is not None:
             M.mtp_state_restore(state, snap, state_bytes, B, n_acc, D)
         M.kv_crop(kv, ctx[cur])
-        hist[r].copy_(n_acc)
 
     for r in range(args.warmup):
         step(r)
     torch.cuda.synchronize()
     M.mtp_check(ws)
-    M.mtp_timer_start(M.MTP_KERNEL_LM_HEAD, args.steps * D)
+    graph = None
+    G = args.graph
+    if G:
+        # rounds warmup .. warmup+G-1 captured once (their buffers cycle with r), replayed
+        assert G % 2 == 0 and args.steps % G == 0 and args.warmup % 2 == 0
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for r in range(args.warmup, args.warmup + G):
+                step(r)
+        torch.cuda.synchronize()   # capture ran nothing: the state after warmup is still current
+    else:
+        M.mtp_timer_start(M.MTP_KERNEL_LM_HEAD, args.steps * D)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ctx0 = int(ctx[args.warmup % 2].sum())
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     ev0.record()
-    for r in range(args.warmup, rounds_total):
-        step(r)
+    if graph is not None:
+        for _ in range(args.steps // G):
+            graph.replay()
+    else:
+        for r in range(args.warmup, rounds_total):
+            step(r)
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     gpu_ms = ev0.elapsed_time(ev1)
+    if graph is not None:
+        # kernel events cannot be timed inside a graph: time the same rounds eagerly right after
+        M.mtp_timer_start(M.MTP_KERNEL_LM_HEAD, G * D)
+        for r in range(rounds_total, rounds_total + G):
+            step(r)
+        torch.cuda.synchronize()
     lm_ms, lm_n = M.mtp_timer_read(M.MTP_KERNEL_LM_HEAD)
     M.mtp_check(ws)
-    acc = hist[args.warmup:].cpu().numpy()
-    tokens_out = int((acc + 1).sum())
+    # every round grows the target length by the accepted drafts + 1
+    tokens_out = int(ctx[rounds_total % 2].sum()) - ctx0
+    acc = hist[args.warmup:].cpu().numpy() if graph is None else hist[args.warmup:args.warmup + G].cpu().numpy()
     value = tokens_out / wall
     ms_per_step = wall * 1e3 / args.steps
 

@@ -16,18 +16,29 @@ namespace mtp {
 // T = len[b] + rows, for all queries (row i, query head kvh*G + g) of the sequence.  K/V tiles of
 // 64 positions are staged through LDS; an online softmax keeps (m, l, o) per query.  Output per
 // query: the unnormalised o, the running max m and the sum l.
-constexpr int kTile = 64;
-constexpr int kQB = 32;
+constexpr int kTile = 64;  // cached positions per LDS tile
+constexpr int kQB = 32;    // queries per pass
 
+// Workgroup (s, kvh, b) handles positions [s*chunk, min(T, (s+1)*chunk)) of sequence b, where
+// T = len[b] + rows, for every query (row i, query head kvh*G + g) of the sequence.  K/V tiles
+// of 64 positions go through registers (the next tile is fetched while the current one is
+// used) into LDS; an online softmax keeps (m, l, o) per query.  Output per query: the
+// unnormalised o, the running max m and the sum l.
 template <class W, int HD>
 __global__ __launch_bounds__(kWG) void k_attn(AttnArgs a) {
   using T = typename W::T;
-  constexpr int VE = W::VE;
-  constexpr int LDR = HD + VE;  // padded tile row (elements)
+  constexpr int VE = W::VE;               // elements per 16-byte vector
+  constexpr int VPR = HD / VE;            // vectors per cached row
+  constexpr int NV = kTile * VPR / kWG;   // vectors per thread per tile and matrix
+  constexpr int LDR = HD + VE;            // padded LDS row (elements)
+  constexpr int SPT = kQB / 4;            // score accumulators per thread
+  constexpr int QG = kWG / HD;            // query groups in the PV phase
+  constexpr int QPT = kQB / QG;           // PV accumulators per thread
   __shared__ __align__(16) T sK[kTile * LDR];
   __shared__ __align__(16) T sV[kTile * LDR];
   __shared__ __align__(16) float sQ[kQB * HD];
-  __shared__ float sS[kQB * kTile];
+  __shared__ float sS[kQB * (kTile + 1)];           // scores [q][p], padded rows
+  __shared__ __align__(16) float sP[kTile * kQB];   // probabilities [p][q]
   __shared__ float sAlpha[kQB];
   __shared__ int s_n;
 
@@ -48,43 +59,48 @@ __global__ __launch_bounds__(kWG) void k_attn(AttnArgs a) {
   const T* Kb = reinterpret_cast<const T*>(a.kc) + ((long)b * a.nkv + kvh) * a.max_len * HD;
   const T* Vb = reinterpret_cast<const T*>(a.vc) + ((long)b * a.nkv + kvh) * a.max_len * HD;
   const float scale = 1.0f / sqrtf(float(HD));
+  const int dpv = tid % HD, qg = tid / HD;
 
   for (int q0 = 0; q0 < NQ; q0 += kQB) {
     const int nqb = min(kQB, NQ - q0);
-    // queries of this block -> LDS
-    for (int idx = tid; idx < nqb * HD; idx += kWG) {
+    for (int idx = tid; idx < kQB * HD; idx += kWG) {
       const int ql = idx / HD, d = idx - ql * HD;
-      const int qi = q0 + ql, i = qi / G, gg = qi - i * G;
-      const long row = (long)b * a.rps + i;
-      sQ[idx] = a.q[(row * a.nq + (kvh * G + gg)) * HD + d];
+      float v = 0.f;
+      if (ql < nqb) {
+        const int qi = q0 + ql, i = qi / G, gg = qi - i * G;
+        const long row = (long)b * a.rps + i;
+        v = a.q[(row * a.nq + (kvh * G + gg)) * HD + d];
+      }
+      sQ[idx] = v;
     }
     float m_run = -INFINITY, l_run = 0.f;  // owned by thread tid < nqb
-    constexpr int QPT = kQB / (kWG / HD);  // PV accumulators per thread
     float o[QPT];
 #pragma unroll
     for (int k = 0; k < QPT; ++k) o[k] = 0.f;
-    const int dpv = tid % HD, qsub = tid / HD;
 
-    for (int t0 = p_beg; t0 < p_end; t0 += kTile) {
-      __syncthreads();
-      // stage K and V tiles (16-byte vectors)
-      constexpr int VPR = HD / VE;  // vectors per row
-      for (int idx = tid; idx < kTile * VPR; idx += kWG) {
-        const int pr = idx / VPR, c = idx - pr * VPR;
+    uint4 kr[NV], vr[NV];
+    auto fetch = [&](int t0) {
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const int idx = tid + v * kWG, pr = idx / VPR, c = idx - pr * VPR;
         const int p = t0 + pr;
-        uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-        if (p < p_end) {
-          kv = ld16(Kb + (long)p * HD + c * VE);
-          vv = ld16(Vb + (long)p * HD + c * VE);
-        }
-        *reinterpret_cast<uint4*>(sK + pr * LDR + c * VE) = kv;
-        *reinterpret_cast<uint4*>(sV + pr * LDR + c * VE) = vv;
+        kr[v] = p < p_end ? ld16(Kb + (long)p * HD + c * VE) : make_uint4(0, 0, 0, 0);
+        vr[v] = p < p_end ? ld16(Vb + (long)p * HD + c * VE) : make_uint4(0, 0, 0, 0);
+      }
+    };
+    fetch(p_beg);
+    for (int t0 = p_beg; t0 < p_end; t0 += kTile) {
+      __syncthreads();  // the previous tile is no longer read
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const int idx = tid + v * kWG, pr = idx / VPR, c = idx - pr * VPR;
+        *reinterpret_cast<uint4*>(sK + pr * LDR + c * VE) = kr[v];
+        *reinterpret_cast<uint4*>(sV + pr * LDR + c * VE) = vr[v];
       }
       __syncthreads();
-      // scores: thread -> position pl, queries qs, qs+4, ...
-      {
+      if (t0 + kTile < p_end) fetch(t0 + kTile);  // in flight while this tile is used
+      {  // scores: thread -> position pl, queries qs + 4k
         const int pl = tid & (kTile - 1), qs = tid >> 6;
-        constexpr int SPT = kQB / 4;
         float acc[SPT];
 #pragma unroll
         for (int k = 0; k < SPT; ++k) acc[k] = 0.f;
@@ -103,54 +119,55 @@ __global__ __launch_bounds__(kWG) void k_attn(AttnArgs a) {
 #pragma unroll
         for (int k = 0; k < SPT; ++k) {
           const int ql = qs + 4 * k;
-          if (ql < nqb) {
-            const int qi = q0 + ql, i = qi / G;
-            const bool ok = p < p_end && p <= L0 + i;
-            sS[ql * kTile + pl] = ok ? acc[k] * scale : -INFINITY;
-          }
+          const int i = (q0 + ql) / G;
+          const bool ok = ql < nqb && p < p_end && p <= L0 + i;
+          sS[ql * (kTile + 1) + pl] = ok ? acc[k] * scale : -INFINITY;
         }
       }
       __syncthreads();
-      // online softmax update, one thread per query
-      if (tid < nqb) {
-        float* srow = sS + tid * kTile;
+      if (tid < kQB) {  // online softmax, one thread per query; probabilities written transposed
+        const float* srow = sS + tid * (kTile + 1);
         float tmax = -INFINITY;
         for (int k = 0; k < kTile; ++k) tmax = fmaxf(tmax, srow[k]);
         const float m_new = fmaxf(m_run, tmax);
-        float alpha, lsum = 0.f;
-        if (m_new == -INFINITY) {
-          alpha = 1.f;
-          for (int k = 0; k < kTile; ++k) srow[k] = 0.f;
-        } else {
+        float alpha = 1.f, lsum = 0.f;
+        if (m_new != -INFINITY) {
           alpha = (m_run == -INFINITY) ? 0.f : expf(m_run - m_new);
           for (int k = 0; k < kTile; ++k) {
             const float e = (srow[k] == -INFINITY) ? 0.f : expf(srow[k] - m_new);
-            srow[k] = e;
+            sP[k * kQB + tid] = e;
             lsum += e;
           }
+        } else {
+          for (int k = 0; k < kTile; ++k) sP[k * kQB + tid] = 0.f;
         }
         l_run = l_run * alpha + lsum;
         m_run = m_new;
         sAlpha[tid] = alpha;
       }
       __syncthreads();
-      // o = o * alpha + P V
+      {  // o = o * alpha + P V: thread -> dim dpv, queries qg*QPT .. qg*QPT+QPT-1
 #pragma unroll
-      for (int k = 0; k < QPT; ++k) {
-        const int ql = qsub + (kWG / HD) * k;
-        if (ql < nqb) {
-          float acc = o[k] * sAlpha[ql];
-          const float* prow = sS + ql * kTile;
-          for (int pl = 0; pl < kTile; ++pl) acc = fmaf(prow[pl], W::get(sV, pl * LDR + dpv), acc);
-          o[k] = acc;
+        for (int k = 0; k < QPT; ++k) o[k] *= sAlpha[qg * QPT + k];
+#pragma unroll 4
+        for (int pl = 0; pl < kTile; ++pl) {
+          const float v = W::get(sV, pl * LDR + dpv);
+          const float4* pp = reinterpret_cast<const float4*>(sP + pl * kQB + qg * QPT);
+#pragma unroll
+          for (int k4 = 0; k4 < QPT / 4; ++k4) {
+            const float4 pv = pp[k4];
+            o[4 * k4 + 0] = fmaf(pv.x, v, o[4 * k4 + 0]);
+            o[4 * k4 + 1] = fmaf(pv.y, v, o[4 * k4 + 1]);
+            o[4 * k4 + 2] = fmaf(pv.z, v, o[4 * k4 + 2]);
+            o[4 * k4 + 3] = fmaf(pv.w, v, o[4 * k4 + 3]);
+          }
         }
       }
     }
-    // write partials
     float* P = a.part + (((long)b * a.nkv + kvh) * a.nsplit + s) * (long)a.qstride * (HD + 2);
 #pragma unroll
     for (int k = 0; k < QPT; ++k) {
-      const int ql = qsub + (kWG / HD) * k;
+      const int ql = qg * QPT + k;
       if (ql < nqb) P[(long)(q0 + ql) * (HD + 2) + dpv] = o[k];
     }
     if (tid < nqb) {
@@ -161,40 +178,41 @@ __global__ __launch_bounds__(kWG) void k_attn(AttnArgs a) {
   }
 }
 
-// Merge the split partials: o = sum_s o_s e^{m_s - M} / sum_s l_s e^{m_s - M}.
+// Merge the split partials of one (row, query head): o = sum_s o_s e^{m_s - M} / sum_s l_s e^{m_s - M}.
 template <int HD>
-__global__ __launch_bounds__(kWG) void k_attn_combine(AttnArgs a, float* out) {
-  const int per = kWG / HD;
-  const int item = blockIdx.x * per + threadIdx.x / HD;  // (row, head)
-  const int d = threadIdx.x % HD;
-  const int R = a.B * a.rps;
-  if (item >= R * a.nq) return;
+__global__ __launch_bounds__(HD) void k_attn_combine(AttnArgs a, float* out) {
+  __shared__ float sw[kMaxSplit];
+  __shared__ float sl[kMaxSplit];
+  const int item = blockIdx.x, d = threadIdx.x;
   const int row = item / a.nq, h = item - row * a.nq;
   const int b = row / a.rps, i = row - b * a.rps;
   const int n = count_rows(a.tok + (long)b * a.tok_sb, a.rps, a.V, a.len[b], a.max_len, nullptr);
   if (i >= n) return;
   const int G = a.nq / a.nkv, kvh = h / G, qi = i * G + (h - kvh * G);
-  const int T = a.len[b] + n;
-  const int chunk = attn_chunk(T, a.nsplit);
-  const float* P = a.part + ((long)b * a.nkv + kvh) * a.nsplit * (long)a.qstride * (HD + 2) + (long)qi * (HD + 2);
+  const int Tn = a.len[b] + n;
+  const int chunk = attn_chunk(Tn, a.nsplit);
+  const int ns = min(a.nsplit, (Tn + chunk - 1) / chunk);
   const long sstride = (long)a.qstride * (HD + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < a.nsplit && s * chunk < T; ++s) {
+  const float* P = a.part + ((long)b * a.nkv + kvh) * a.nsplit * sstride + (long)qi * (HD + 2);
+  for (int s = d; s < ns; s += HD) {
     const float l = P[s * sstride + HD + 1];
-    if (l > 0.f) M = fmaxf(M, P[s * sstride + HD]);
+    sw[s] = l > 0.f ? P[s * sstride + HD] : -INFINITY;
+    sl[s] = l;
   }
+  __syncthreads();
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, sw[s]);
+  __syncthreads();
+  for (int s = d; s < ns; s += HD) sw[s] = sl[s] > 0.f ? expf(sw[s] - M) : 0.f;
+  __syncthreads();
   float L = 0.f, O = 0.f;
-  for (int s = 0; s < a.nsplit && s * chunk < T; ++s) {
-    const float l = P[s * sstride + HD + 1];
-    if (l > 0.f) {
-      const float e = expf(P[s * sstride + HD] - M);
-      L = fmaf(l, e, L);
-      O = fmaf(P[s * sstride + d], e, O);
-    }
+#pragma unroll 8
+  for (int s = 0; s < ns; ++s) {
+    L = fmaf(sl[s], sw[s], L);
+    O = fmaf(P[s * sstride + d], sw[s], O);
   }
   out[((long)row * a.nq + h) * HD + d] = O / L;
 }
-
 
 hipError_t run_attention(const AttnArgs& a, int hd, int wdtype, float* out, hipStream_t st) {
   dim3 grid(a.nsplit, a.nkv, a.B);
@@ -204,13 +222,13 @@ hipError_t run_attention(const AttnArgs& a, int hd, int wdtype, float* out, hipS
       hipLaunchKernelGGL((k_attn<BF16, 128>), grid, dim3(kWG), 0, st, a);
     else
       hipLaunchKernelGGL((k_attn<F32, 128>), grid, dim3(kWG), 0, st, a);
-    hipLaunchKernelGGL((k_attn_combine<128>), dim3((items + 1) / 2), dim3(kWG), 0, st, a, out);
+    hipLaunchKernelGGL((k_attn_combine<128>), dim3(items), dim3(128), 0, st, a, out);
   } else {
     if (wdtype == MTP_BF16)
       hipLaunchKernelGGL((k_attn<BF16, 64>), grid, dim3(kWG), 0, st, a);
     else
       hipLaunchKernelGGL((k_attn<F32, 64>), grid, dim3(kWG), 0, st, a);
-    hipLaunchKernelGGL((k_attn_combine<64>), dim3((items + 3) / 4), dim3(kWG), 0, st, a, out);
+    hipLaunchKernelGGL((k_attn_combine<64>), dim3(items), dim3(64), 0, st, a, out);
   }
   return hipGetLastError();
 }

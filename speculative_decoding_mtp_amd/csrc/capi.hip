@@ -179,8 +179,8 @@ StepArgs base_step(const mtp_config* cfg, const mtp_weights* w, const mtp_kv* kv
 
 namespace mtp {
 int attn_nsplit(int B, int nkv, int max_len) {
-  int n = (1024 + B * nkv - 1) / (B * nkv);
-  if (n > 64) n = 64;
+  int n = (512 + B * nkv - 1) / (B * nkv);
+  if (n > kMaxSplit) n = kMaxSplit;
   const int cap = (max_len + 63) / 64;
   if (n > cap) n = cap;
   return n < 1 ? 1 : n;

@@ -11,11 +11,13 @@ namespace mtp {
 
 constexpr int kLmRows = 16;  // weight rows per lm_head workgroup iteration
 
-// Positions per attention split for a sequence of T cached positions (a multiple of 16).
+constexpr int kMaxSplit = 128;  // attention splits per (sequence, kv head)
+
+// Positions per attention split for a sequence of T cached positions (a multiple of 64).
 __host__ __device__ inline int attn_chunk(int T, int nsplit) {
   int c = (T + nsplit - 1) / nsplit;
-  c = (c + 15) & ~15;
-  return c < 16 ? 16 : c;
+  c = (c + 63) & ~63;
+  return c < 64 ? 64 : c;
 }
 
 struct AttnArgs {
