@@ -15,6 +15,7 @@ divided by the timed wall time), the lm_head kernel's HBM roofline and the CPU o
 a bounded sample of the same workload.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -34,8 +35,12 @@ def parse():
     ap.add_argument("--config", default="qwen")
     ap.add_argument("--state-bytes", type=int, default=None, help="recurrent state bytes per sequence")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle baseline sample budget (0: skip)")
-    ap.add_argument("--traffic", default=None, help="JSON file with counter-measured lm_head bytes per launch")
+    ap.add_argument("--traffic", default=os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                                                      "lm_head_counters.json"),
+                    help="counter-measured lm_head bytes per launch (ignored when the kernel sources changed)")
     ap.add_argument("--graph", type=int, default=0, help="capture this many rounds per HIP graph (0: eager)")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (counter calibration)")
     return ap.parse_args()
 
 
@@ -62,6 +67,14 @@ def main():
     K, Vv = make_kv_prefix(cfg)
     kv = kv_from_numpy(cfg, K, Vv, cfg.ctx, max_len)
     print(f"[bench] inputs ready in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+
+    if args.calib_copy_mb:
+        src = torch.ones(args.calib_copy_mb * 1024 * 1024 // 4, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     rps = D + 1
     toks0, hid0 = make_first_round(cfg)
@@ -160,7 +173,13 @@ def main():
     achieved = lm_bytes / lm_avg_s / 1e9
     traffic = None
     if args.traffic and os.path.exists(args.traffic):
-        traffic = json.load(open(args.traffic)).get("bytes_per_launch")
+        rec = json.load(open(args.traffic))
+        root = os.path.dirname(os.path.abspath(__file__))
+        h = hashlib.sha256()
+        for p in rec.get("source_files", []):
+            h.update(open(os.path.join(root, p), "rb").read())
+        if h.hexdigest() == rec.get("source_sha256"):
+            traffic = rec.get("bytes_per_launch")
 
     cpu = None
     if args.cpu_seconds > 0:
