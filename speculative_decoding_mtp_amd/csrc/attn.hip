@@ -45,11 +45,11 @@ __global__ __launch_bounds__(kWG) void k_attn(AttnArgs a) {
   const int tid = threadIdx.x;
   const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int G = a.nq / a.nkv;
-  if (tid == 0) s_n = count_rows(a.tok + (long)b * a.tok_sb, a.rps, a.V, a.len[b], a.max_len, nullptr);
+  const int L0 = a.len[b];
+  if (tid == 0) s_n = count_rows(a.tok + (long)b * a.tok_sb, a.rps, a.V, L0, a.max_len, nullptr);
   __syncthreads();
   const int n = s_n;
   if (n == 0) return;
-  const int L0 = a.len[b];
   const int Tn = L0 + n;
   const int chunk = attn_chunk(Tn, a.nsplit);
   const int p_beg = s * chunk;
@@ -63,6 +63,17 @@ __global__ __launch_bounds__(kWG) void k_attn(AttnArgs a) {
 
   for (int q0 = 0; q0 < NQ; q0 += kQB) {
     const int nqb = min(kQB, NQ - q0);
+    uint4 kr[NV], vr[NV];
+    auto fetch = [&](int t0) {
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const int idx = tid + v * kWG, pr = idx / VPR, c = idx - pr * VPR;
+        const int p = t0 + pr;
+        kr[v] = p < p_end ? ld16(Kb + (long)p * HD + c * VE) : make_uint4(0, 0, 0, 0);
+        vr[v] = p < p_end ? ld16(Vb + (long)p * HD + c * VE) : make_uint4(0, 0, 0, 0);
+      }
+    };
+    fetch(p_beg);
     for (int idx = tid; idx < kQB * HD; idx += kWG) {
       const int ql = idx / HD, d = idx - ql * HD;
       float v = 0.f;
@@ -78,17 +89,6 @@ __global__ __launch_bounds__(kWG) void k_attn(AttnArgs a) {
 #pragma unroll
     for (int k = 0; k < QPT; ++k) o[k] = 0.f;
 
-    uint4 kr[NV], vr[NV];
-    auto fetch = [&](int t0) {
-#pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        const int idx = tid + v * kWG, pr = idx / VPR, c = idx - pr * VPR;
-        const int p = t0 + pr;
-        kr[v] = p < p_end ? ld16(Kb + (long)p * HD + c * VE) : make_uint4(0, 0, 0, 0);
-        vr[v] = p < p_end ? ld16(Vb + (long)p * HD + c * VE) : make_uint4(0, 0, 0, 0);
-      }
-    };
-    fetch(p_beg);
     for (int t0 = p_beg; t0 < p_end; t0 += kTile) {
       __syncthreads();  // the previous tile is no longer read
 #pragma unroll

@@ -99,7 +99,7 @@ int check_kv(const mtp_kv* kv) {
 
 // ------------------------------------------------------------------ drafter workspace
 struct DraftLayout {
-  size_t off[10];
+  size_t off[14];
   size_t total;
 };
 
@@ -107,20 +107,28 @@ DraftLayout draft_layout(const mtp_config& c, int B, int rps, int D, int max_len
   const size_t R = (size_t)B * (rps < 1 ? 1 : rps);
   const int nsplit = attn_nsplit(B, c.n_kv_heads, max_len);
   const size_t G = c.n_heads / c.n_kv_heads;
-  const size_t sizes[10] = {
-      256,                                                                            // status word
-      R * c.hidden * 4,                                                               // x
-      R * c.n_heads * c.head_dim * 4,                                                 // q
-      (size_t)B * c.n_kv_heads * nsplit * (rps * G) * (c.head_dim + 2) * 4,          // attention partials
-      R * c.n_heads * c.head_dim * 4,                                                 // attention output
-      R * c.ffn * 4,                                                                  // act
-      (size_t)B * lm_head_grid(c, B) * 4,                                             // lm partial values
-      (size_t)B * lm_head_grid(c, B) * 4,                                             // lm partial ids
-      (size_t)B * (D < 1 ? 1 : D) * c.hidden * 4,                                     // step hiddens
-      0};
+  size_t kmax = 2 * (size_t)c.hidden;
+  if ((size_t)c.ffn > kmax) kmax = c.ffn;
+  if ((size_t)c.n_heads * c.head_dim > kmax) kmax = (size_t)c.n_heads * c.head_dim;
+  const bool mfma = c.wdtype == MTP_BF16 && R >= 16;
+  const size_t sizes[14] = {
+      256,                                                                   // status word
+      R * c.hidden * 4,                                                      // x
+      R * c.n_heads * c.head_dim * 4,                                        // q
+      (size_t)B * c.n_kv_heads * nsplit * (rps * G) * (c.head_dim + 2) * 4, // attention partials
+      R * c.n_heads * c.head_dim * 4,                                        // attention output
+      R * c.ffn * 4,                                                         // act
+      (size_t)B * kMaxGemvGrid * 4,                                          // lm partial values
+      (size_t)B * kMaxGemvGrid * 4,                                          // lm partial ids
+      (size_t)B * (D < 1 ? 1 : D) * c.hidden * 4,                            // step hiddens
+      mfma ? R * kmax * 2 : 0,                                               // split activations, hi
+      mfma ? R * kmax * 2 : 0,                                               // split activations, lo
+      mfma ? R * 4 : 0,                                                      // compact row map
+      mfma ? R * 4 : 0,                                                      // compact activation map
+      mfma ? (size_t)4 : (size_t)0};                                         // compact count
   DraftLayout L;
   size_t o = 0;
-  for (int i = 0; i < 10; ++i) {
+  for (int i = 0; i < 14; ++i) {
     L.off[i] = o;
     o += up256(sizes[i]);
   }
@@ -140,6 +148,12 @@ DraftWs carve(void* ws, const DraftLayout& L) {
   w.lm_part_v = reinterpret_cast<float*>(base + L.off[6]);
   w.lm_part_i = reinterpret_cast<int*>(base + L.off[7]);
   w.hid_fb = reinterpret_cast<float*>(base + L.off[8]);
+  const bool mfma = L.off[10] > L.off[9];
+  w.xhi = mfma ? reinterpret_cast<uint16_t*>(base + L.off[9]) : nullptr;
+  w.xlo = mfma ? reinterpret_cast<uint16_t*>(base + L.off[10]) : nullptr;
+  w.rowmap = mfma ? reinterpret_cast<int*>(base + L.off[11]) : nullptr;
+  w.amap = mfma ? reinterpret_cast<int*>(base + L.off[12]) : nullptr;
+  w.mcount = mfma ? reinterpret_cast<int*>(base + L.off[13]) : nullptr;
   return w;
 }
 

@@ -11,7 +11,8 @@ namespace mtp {
 
 constexpr int kLmRows = 16;  // weight rows per lm_head workgroup iteration
 
-constexpr int kMaxSplit = 128;  // attention splits per (sequence, kv head)
+constexpr int kMaxSplit = 128;     // attention splits per (sequence, kv head)
+constexpr int kMaxGemvGrid = 2048; // workgroups of one GEMV launch (also sizes the lm_head partials)
 
 // Positions per attention split for a sequence of T cached positions (a multiple of 64).
 __host__ __device__ inline int attn_chunk(int T, int nsplit) {
@@ -61,6 +62,10 @@ struct DraftWs {
   float* lm_part_v;
   int* lm_part_i;
   float* hid_fb;  // [B][D][H] step hiddens when the caller does not want them
+  // MFMA path (bf16 heads, 16+ activation rows): compact split-bf16 activations
+  uint16_t *xhi, *xlo;  // [R][Kmax]
+  int *rowmap, *amap;   // [R]
+  int* mcount;
 };
 
 struct StepArgs {
@@ -92,7 +97,6 @@ struct GemvPlan {
 };
 GemvPlan plan_gemv(int nact, int K, int VE, int N);
 
-int lm_head_grid(const mtp_config& cfg, int B);
 int attn_nsplit(int B, int nkv, int max_len);
 hipError_t run_attention(const AttnArgs& a, int hd, int wdtype, float* out, hipStream_t st);
 hipError_t run_step(const StepArgs& s);

@@ -29,21 +29,18 @@ GemvPlan plan_gemv(int nact, int K, int VE, int N) {
     const int rw = 16 / pl.nj;
     const int groups = (N + rw - 1) / rw;
     const int wgs = (groups + 3) / 4;
-    pl.grid = wgs < 1024 ? wgs : 1024;
+    pl.grid = wgs < kMaxGemvGrid ? wgs : kMaxGemvGrid;
   } else {  // rows split over the workgroup
     pl.kind = 1;
     pl.nj = pow2_at_least((Kc + kWG - 1) / kWG);
     const int rbmax = 16 / pl.nj;
     pl.rb = pow2_at_most(nact < rbmax ? (nact < 1 ? 1 : nact) : rbmax);
     const int groups = (N + 7) / 8;
-    pl.grid = groups < 1024 ? groups : 1024;
+    pl.grid = groups < kMaxGemvGrid ? groups : kMaxGemvGrid;
   }
   return pl;
 }
 
-int lm_head_grid(const mtp_config& cfg, int B) {
-  return plan_gemv(B, cfg.hidden, cfg.wdtype == MTP_BF16 ? 8 : 4, cfg.vocab).grid;
-}
 
 hipError_t run_step(const StepArgs& s) {
   return s.cfg.wdtype == MTP_BF16 ? run_step_t<BF16>(s) : run_step_t<F32>(s);

@@ -14,8 +14,11 @@
 // draft head"; [YL] "MTP 原理详解" sections 二.1-二.3 and 三 stages 1-2.
 #pragma once
 
+#include <type_traits>
+
 #include "draft.h"
 #include "gemv.h"
+#include "mfma_gemm.h"
 
 namespace mtp {
 
@@ -34,10 +37,15 @@ struct PBase {
   int max_len, V;
   int K, N, nact, split;
   float eps;
+  const int* lds_len;  // cache lengths in LDS, set by setup()
 
-  __device__ void setup(int* s_n) const {
-    for (int b = threadIdx.x; b < B; b += kWG)
-      s_n[b] = count_rows(tok + (long)b * tok_sb, rps, V, len[b], max_len, nullptr);
+  __device__ void setup(int* s_n, int* s_len) {
+    for (int b = threadIdx.x; b < B; b += kWG) {
+      const int l = len[b];
+      s_len[b] = l;
+      s_n[b] = count_rows(tok + (long)b * tok_sb, rps, V, l, max_len, nullptr);
+    }
+    lds_len = s_len;
   }
   __device__ void act(int a, const int* s_n, int& row, bool& valid) const {
     row = a;
@@ -103,7 +111,7 @@ struct PQKV : PBase<W> {
   __device__ void store_pair(int m, int, int row, float v0, float v1) {
     const int head = m / hd, u = (m - head * hd) >> 1, half = hd >> 1;
     const int b = row / this->rps, i = row - b * this->rps;
-    const int pos = this->len[b] + i;
+    const int pos = this->lds_len[b] + i;
     if (head < nq + nkv) {  // rotate q and k: angle pos * theta^(-2u/hd), computed in double
       const double ang = double(pos) * exp(-2.0 * double(u) / double(hd) * log_theta);
       double s, c;
@@ -260,13 +268,51 @@ __global__ __launch_bounds__(kWG) void k_lm_finalize(LmFinal f) {
 // ---------------------------------------------------------------------------------------------
 // launch selection
 // ---------------------------------------------------------------------------------------------
+// Workgroups that can be resident at once for a kernel (occupancy x compute units), cached.
+template <class K>
+int resident_cap(K kernel, int* cache) {
+  if (*cache == 0) {
+    int dev = 0, cus = 0, nb = 0;
+    (void)hipGetDevice(&dev);
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(kernel), kWG, 0);
+    *cache = (nb < 1 ? 1 : nb) * (cus < 1 ? 1 : cus);
+  }
+  return *cache;
+}
+
+// Launch the planned variant with a grid of at most one resident wave of workgroups (the
+// kernels loop over row groups), so no partial second wave of workgroups trails the first.
+// The bf16 MFMA path serves activation counts of 16 and more (a batch of sequences) when K
+// is a multiple of the 128-wide chunk; fewer rows stream through the VALU GEMVs.
 template <class W, class P>
-hipError_t launch_gemv(P& p, hipStream_t st) {
+bool use_mfma(const P& p, const MfmaBufs* mb) {
+  return mb && std::is_same<W, BF16>::value && p.nact >= 16 && p.K % kMfmaKC == 0;
+}
+
+template <class W, class P>
+hipError_t launch_gemv(P& p, hipStream_t st, int* grid_used = nullptr, const MfmaBufs* mb = nullptr) {
+  if constexpr (std::is_same<W, BF16>::value) {
+    if (use_mfma<W>(p, mb)) {
+      constexpr int NT = 2, MG = P::kArgmax ? 4 : 8;
+      hipLaunchKernelGGL((k_prep<W, P>), dim3(p.nact), dim3(kWG), 0, st, p, *mb);
+      static int cap = 0;
+      const int groups = (p.N + 4 * NT * 16 - 1) / (4 * NT * 16);
+      int grid = min(groups, resident_cap(k_gemm_mfma<P, NT, MG>, &cap));
+      grid = min(grid, kMaxGemvGrid);
+      if (grid_used) *grid_used = grid;
+      hipLaunchKernelGGL((k_gemm_mfma<P, NT, MG>), dim3(grid), dim3(kWG), 0, st, p, *mb);
+      return hipGetLastError();
+    }
+  }
   const GemvPlan pl = plan_gemv(p.nact, p.K, W::VE, p.N);
   if (pl.kind == 0) {
 #define MTP_W(NJ_, RB_)                                                                        \
   if (pl.nj == NJ_ && pl.rb == RB_) {                                                          \
-    hipLaunchKernelGGL((k_gemv_w<W, RB_, NJ_, 16 / NJ_, P>), dim3(pl.grid), dim3(kWG), 0, st, p); \
+    static int cap = 0;                                                                        \
+    const int grid = min(pl.grid, resident_cap(k_gemv_w<W, RB_, NJ_, 16 / NJ_, P>, &cap));    \
+    if (grid_used) *grid_used = grid;                                                          \
+    hipLaunchKernelGGL((k_gemv_w<W, RB_, NJ_, 16 / NJ_, P>), dim3(grid), dim3(kWG), 0, st, p); \
     return hipGetLastError();                                                                  \
   }
     MTP_W(1, 1) MTP_W(1, 2) MTP_W(1, 4) MTP_W(2, 1) MTP_W(2, 2) MTP_W(2, 4) MTP_W(4, 1) MTP_W(4, 2) MTP_W(8, 1)
@@ -275,7 +321,10 @@ hipError_t launch_gemv(P& p, hipStream_t st) {
   } else {
 #define MTP_S(NX_, RB_)                                                                    \
   if (pl.nj == NX_ && pl.rb == RB_) {                                                      \
-    hipLaunchKernelGGL((k_gemv_s<W, RB_, NX_, 8, P>), dim3(pl.grid), dim3(kWG), 0, st, p); \
+    static int cap = 0;                                                                    \
+    const int grid = min(pl.grid, resident_cap(k_gemv_s<W, RB_, NX_, 8, P>, &cap));        \
+    if (grid_used) *grid_used = grid;                                                      \
+    hipLaunchKernelGGL((k_gemv_s<W, RB_, NX_, 8, P>), dim3(grid), dim3(kWG), 0, st, p);    \
     return hipGetLastError();                                                              \
   }
     MTP_S(4, 1) MTP_S(4, 2) MTP_S(4, 4) MTP_S(8, 1) MTP_S(8, 2) MTP_S(16, 1)
@@ -304,6 +353,8 @@ hipError_t run_step_t(const StepArgs& s) {
   const int H = c.hidden, F = c.ffn, nq = c.n_heads, nkv = c.n_kv_heads, hd = c.head_dim;
   const int R = s.B * s.rps;
   hipError_t e;
+  const MfmaBufs mbuf = {s.ws.xhi, s.ws.xlo, s.ws.rowmap, s.ws.amap, s.ws.mcount};
+  const MfmaBufs* mb = s.ws.xhi ? &mbuf : nullptr;
 
   {  // eh_proj
     PEhProj<W> p;
@@ -320,7 +371,7 @@ hipError_t run_step_t(const StepArgs& s) {
     p.hin_sb = s.hin_sb;
     p.H = H;
     p.xout = s.ws.x;
-    if ((e = launch_gemv<W>(p, s.stream)) != hipSuccess) return e;
+    if ((e = launch_gemv<W>(p, s.stream, nullptr, mb)) != hipSuccess) return e;
   }
   for (int l = 0; l < c.n_layers; ++l) {
     const mtp_layer_weights& lw = s.w->layers[l];
@@ -344,7 +395,7 @@ hipError_t run_step_t(const StepArgs& s) {
       p.qout = s.ws.q;
       p.kc = (T*)s.kc + layer_off;
       p.vc = (T*)s.vc + layer_off;
-      if ((e = launch_gemv<W>(p, s.stream)) != hipSuccess) return e;
+      if ((e = launch_gemv<W>(p, s.stream, nullptr, mb)) != hipSuccess) return e;
     }
     {  // attention
       AttnArgs a;
@@ -374,7 +425,7 @@ hipError_t run_step_t(const StepArgs& s) {
       p.w = (const T*)lw.wo;
       p.ain = s.ws.attn_out;
       p.xres = s.ws.x;
-      if ((e = launch_gemv<W>(p, s.stream)) != hipSuccess) return e;
+      if ((e = launch_gemv<W>(p, s.stream, nullptr, mb)) != hipSuccess) return e;
     }
     {  // gate/up + SwiGLU
       PGateUp<W> p;
@@ -389,7 +440,7 @@ hipError_t run_step_t(const StepArgs& s) {
       p.H = H;
       p.F = F;
       p.aout = s.ws.act;
-      if ((e = launch_gemv<W>(p, s.stream)) != hipSuccess) return e;
+      if ((e = launch_gemv<W>(p, s.stream, nullptr, mb)) != hipSuccess) return e;
     }
     {  // down + residual
       PResidual<W> p;
@@ -400,7 +451,7 @@ hipError_t run_step_t(const StepArgs& s) {
       p.w = (const T*)lw.wdown;
       p.ain = s.ws.act;
       p.xres = s.ws.x;
-      if ((e = launch_gemv<W>(p, s.stream)) != hipSuccess) return e;
+      if ((e = launch_gemv<W>(p, s.stream, nullptr, mb)) != hipSuccess) return e;
     }
   }
   {  // final norm + lm_head + argmax + finalisation
@@ -418,7 +469,8 @@ hipError_t run_step_t(const StepArgs& s) {
     p.part_v = s.ws.lm_part_v;
     p.part_i = s.ws.lm_part_i;
     if (s.ev_begin) (void)hipEventRecord(s.ev_begin, s.stream);
-    e = launch_gemv<W>(p, s.stream);
+    int grid = 0;
+    e = launch_gemv<W>(p, s.stream, &grid, mb);
     if (s.ev_end) (void)hipEventRecord(s.ev_end, s.stream);
     if (e != hipSuccess) return e;
     LmFinal f;
@@ -430,7 +482,7 @@ hipError_t run_step_t(const StepArgs& s) {
     f.max_len = s.max_len;
     f.part_v = s.ws.lm_part_v;
     f.part_i = s.ws.lm_part_i;
-    f.nparts = plan_gemv(s.B, H, W::VE, c.vocab).grid;
+    f.nparts = grid;
     f.x = s.ws.x;
     f.gain = s.w->final_norm;
     f.H = H;

@@ -65,7 +65,8 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
 //                                   [split, K) separately
 //   static constexpr bool kPair;    outputs come as logical-row pairs (m even, m + 1)
 //   static constexpr bool kArgmax;  track the argmax over logical rows of every activation row
-//   void setup(int* s_n)            per-sequence row counts into LDS (the kernel then syncs)
+//   void setup(int* s_n, int* s_len) per-sequence row counts and cache lengths into LDS (the
+//                                   kernel then syncs)
 //   void act(int a, const int* s_n, int& row, bool& valid)
 //   void load_x(int row, int k, float (&f)[VE])     raw activations k..k+VE-1 of a row
 //   void gain_vec(int k, float (&g)[VE])            norm gains (kNorm > 0)
@@ -183,14 +184,26 @@ __global__ __launch_bounds__(kWG) void k_gemv_w(P p) {
   using T = typename W::T;
   constexpr int VE = W::VE;
   __shared__ int s_n[kMaxBatch];
+  __shared__ int s_len[kMaxBatch];
   __shared__ float s_bv[4 * RB];
   __shared__ int s_bi[4 * RB];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  p.setup(s_n);
-  __syncthreads();
   const int Kc = p.K / VE;
   const int ngroups = (p.N + RW - 1) / RW;
   const int wave = blockIdx.x * 4 + wid, nwaves = gridDim.x * 4;
+  uint4 wv[RW][NJ];
+  auto load_group = [&](int g) {
+    const int m0 = g * RW;
+#pragma unroll
+    for (int q = 0; q < RW; ++q) {
+      const T* wp = p.wrow(min(m0 + q, p.N - 1));
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) wv[q][j] = ld_stream(wp + (long)min(lane + j * kWave, Kc - 1) * VE);
+    }
+  };
+  p.setup(s_n, s_len);                   // issues the token / length loads first
+  if (wave < ngroups) load_group(wave);  // the first weights are in flight during the prologue
+  __syncthreads();
 
   for (int a0 = 0; a0 < p.nact; a0 += RB) {
     int rows[RB];
@@ -201,7 +214,7 @@ __global__ __launch_bounds__(kWG) void k_gemv_w(P p) {
       p.act(a0 + r, s_n, rows[r], valid[r]);
       any |= valid[r];
     }
-    if (!any) continue;  // uniform across the workgroup
+    if (!any) continue;  // uniform across the workgroup; the prefetched group is the next block's first
     float x[RB][NJ][VE];
     load_slice<W, RB, NJ>(p, rows, valid, lane, kWave, Kc, x, [](float& s0, float& s1) {
       s0 = wave_sum_dpp(s0);
@@ -216,13 +229,6 @@ __global__ __launch_bounds__(kWG) void k_gemv_w(P p) {
     }
     for (int g = wave; g < ngroups; g += nwaves) {
       const int m0 = g * RW;
-      uint4 wv[RW][NJ];
-#pragma unroll
-      for (int q = 0; q < RW; ++q) {
-        const T* wp = p.wrow(min(m0 + q, p.N - 1));
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) wv[q][j] = ld_stream(wp + (long)min(lane + j * kWave, Kc - 1) * VE);
-      }
       float acc[RW][RB];
 #pragma unroll
       for (int q = 0; q < RW; ++q) {
@@ -238,6 +244,10 @@ __global__ __launch_bounds__(kWG) void k_gemv_w(P p) {
             for (int e = 0; e < VE; ++e) acc[q][r] = fmaf(wf[e], x[r][j][e], acc[q][r]);
         }
       }
+      // next group's weights (this block's next group, or the next block's first) are loaded
+      // while this group is reduced and stored
+      const int gn = g + nwaves < ngroups ? g + nwaves : (a0 + RB < p.nact ? wave : -1);
+      if (gn >= 0) load_group(gn);
 #pragma unroll
       for (int q = 0; q < RW; ++q)
 #pragma unroll
@@ -266,10 +276,11 @@ __global__ __launch_bounds__(kWG) void k_gemv_s(P p) {
   __shared__ float s_red[4 * ROWS * RB];
   __shared__ float s_norm[8];
   __shared__ int s_n[kMaxBatch];
+  __shared__ int s_len[kMaxBatch];
   __shared__ float s_bv[4 * RB];
   __shared__ int s_bi[4 * RB];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  p.setup(s_n);
+  p.setup(s_n, s_len);
   __syncthreads();
   const int Kc = p.K / VE;
   const int ngroups = (p.N + ROWS - 1) / ROWS;

@@ -1,0 +1,280 @@
+// Skinny GEMM on bf16 MFMA for draft steps with many activation rows (a batch of sequences).
+//
+//   y[row][m] = sum_k W[m][k] * x[row][k],   W bf16 [N][K], x fp32 (after the policy's norm)
+//
+// Two kernels:
+// * k_prep: one workgroup per activation row; the policy's prologue (raw loads, RMSNorm, gains)
+//   gives the fp32 row, which is written as two bf16 rows hi = bf16(x), lo = bf16(x - hi)
+//   (x = hi + lo to about 2^-17 relative), compacted over the valid rows.  rowmap / amap record
+//   each compact row's padded row and activation index; `count` the number of compact rows.
+// * k_gemm_mfma: each workgroup owns 4 waves x NT tiles of 16 weight rows and walks K in chunks
+//   of 128.  Per chunk the workgroup stages the compact activations (hi and lo, up to MG tiles of
+//   16 rows) in LDS, and every wave streams its weight rows once from HBM: lane l reads 64
+//   contiguous bytes of row l % 16 at column 32 (l / 16) of the chunk, so four lanes cover 256
+//   contiguous bytes of a row.  v_mfma_f32_16x16x32_bf16 consumes the chunk in four steps; the K
+//   order inside a step is the same permutation for both operands, so the dot products are
+//   unchanged.  Two MFMAs (hi, lo) per step keep fp32-like accuracy.  Rows beyond MG tiles are
+//   handled in further passes.
+// Operand layout of v_mfma_f32_16x16x32_bf16 (checked on the device): lane l supplies
+// A[l % 16][8 (l / 16) + e] and B[8 (l / 16) + e][l % 16], e < 8; result r of lane l is
+// D[4 (l / 16) + r][l % 16].
+#pragma once
+
+#include "gemv.h"
+
+namespace mtp {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kMfmaKC = 128;          // K per LDS chunk
+constexpr int kMfmaLdr = kMfmaKC + 8; // padded LDS row (bf16 elements)
+
+struct MfmaBufs {
+  uint16_t *xhi, *xlo;  // [cap][K] compact split activations
+  int* rowmap;          // [cap] padded row of a compact row
+  int* amap;            // [cap] activation index of a compact row
+  int* count;           // number of compact rows
+};
+
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+// One workgroup per activation index a (grid = nact).
+template <class W, class P>
+__global__ __launch_bounds__(kWG) void k_prep(P p, MfmaBufs mb) {
+  constexpr int VE = W::VE;
+  __shared__ int s_n[kMaxBatch];
+  __shared__ int s_len[kMaxBatch];
+  __shared__ float red[8];
+  const int a = blockIdx.x, tid = threadIdx.x;
+  p.setup(s_n, s_len);
+  __syncthreads();
+  int row;
+  bool valid;
+  p.act(a, s_n, row, valid);
+  // compact index: activations before this one that are valid
+  int c = 0, total = 0;
+  if (P::kArgmax) {  // one activation per sequence with rows
+    for (int b = 0; b < p.B; ++b) {
+      const int v = s_n[b] > 0 ? 1 : 0;
+      if (b < a) c += v;
+      total += v;
+    }
+  } else {
+    const int b = a / p.rps, i = a - b * p.rps;
+    for (int bb = 0; bb < p.B; ++bb) {
+      if (bb < b) c += s_n[bb];
+      total += s_n[bb];
+    }
+    c += i;
+  }
+  if (a == 0 && tid == 0) *mb.count = total;
+  if (!valid) return;
+  const int Kc = p.K / VE;
+  float ss[2] = {0.f, 0.f};
+  if constexpr (P::kNorm > 0) {
+    for (int ch = tid; ch < Kc; ch += kWG) {
+      float f[VE];
+      p.load_x(row, ch * VE, f);
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < VE; ++e) s = fmaf(f[e], f[e], s);
+      if (P::kNorm == 2 && ch * VE >= p.split)
+        ss[1] += s;
+      else
+        ss[0] += s;
+    }
+    wg_sum<2>(ss, red);
+  }
+  float sc0 = 1.f, sc1 = 1.f;
+  if constexpr (P::kNorm == 2) {
+    sc0 = 1.0f / sqrtf(ss[0] / float(p.split) + p.eps);
+    sc1 = 1.0f / sqrtf(ss[1] / float(p.K - p.split) + p.eps);
+  } else if constexpr (P::kNorm == 1) {
+    sc0 = sc1 = 1.0f / sqrtf(ss[0] / float(p.K) + p.eps);
+  }
+  uint16_t* hi = mb.xhi + (long)c * p.K;
+  uint16_t* lo = mb.xlo + (long)c * p.K;
+  for (int ch = tid; ch < Kc; ch += kWG) {
+    float f[VE], g[VE];
+    p.load_x(row, ch * VE, f);
+    if constexpr (P::kNorm > 0) {
+      p.gain_vec(ch * VE, g);
+    } else {
+#pragma unroll
+      for (int e = 0; e < VE; ++e) g[e] = 1.f;
+    }
+    const float sc = (P::kNorm == 2 && ch * VE >= p.split) ? sc1 : sc0;
+    uint16_t h16[VE], l16[VE];
+#pragma unroll
+    for (int e = 0; e < VE; ++e) {
+      const float x = P::kNorm > 0 ? f[e] * sc * g[e] : f[e];
+      h16[e] = bf16_rne(x);
+      l16[e] = bf16_rne(x - __uint_as_float(uint32_t(h16[e]) << 16));
+    }
+#pragma unroll
+    for (int e = 0; e < VE; ++e) {
+      hi[ch * VE + e] = h16[e];
+      lo[ch * VE + e] = l16[e];
+    }
+  }
+  if (tid == 0) {
+    mb.rowmap[c] = row;
+    mb.amap[c] = a;
+  }
+}
+
+// NT weight-row tiles (16 rows each) per wave, MG activation tiles (16 compact rows) per pass.
+template <class P, int NT, int MG>
+__global__ __launch_bounds__(kWG) void k_gemm_mfma(P p, MfmaBufs mb) {
+  using T = uint16_t;
+  __shared__ __align__(16) uint16_t sA[2][MG * 16 * kMfmaLdr];  // [hi/lo][row][k]
+  __shared__ int s_n[kMaxBatch];
+  __shared__ int s_len[kMaxBatch];
+  __shared__ float s_bv[4 * MG * 16];
+  __shared__ int s_bi[4 * MG * 16];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int jl = lane & 15, hq = lane >> 4;  // column of the tile, quarter of the wave
+  p.setup(s_n, s_len);
+  const int count = *mb.count;
+  __syncthreads();
+  const int Kc = p.K / kMfmaKC;  // K is a multiple of 128 on this path
+  const int rows_per_wg = 4 * NT * 16;
+  const int ngroups = (p.N + rows_per_wg - 1) / rows_per_wg;
+
+  for (int mg0 = 0; mg0 < count; mg0 += MG * 16) {
+    const int mrows = min(MG * 16, count - mg0);
+    const int mt = (mrows + 15) / 16;
+    for (int g = blockIdx.x; g < ngroups; g += gridDim.x) {
+      const int n0 = g * rows_per_wg + wid * NT * 16;
+      f32x4_t acc[MG][NT];
+#pragma unroll
+      for (int m = 0; m < MG; ++m)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[m][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const T* wrow[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) wrow[t] = p.wrow(min(n0 + t * 16 + jl, p.N - 1));
+      for (int kc = 0; kc < Kc; ++kc) {
+        const int k0 = kc * kMfmaKC;
+        // this chunk's weights: 64 bytes of each of the NT rows of this lane
+        uint4 wv[NT][4];
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int s = 0; s < 4; ++s) wv[t][s] = ld_stream(wrow[t] + k0 + 32 * hq + 8 * s);
+        // stage the chunk's activations (hi, lo) of this pass in LDS
+        __syncthreads();
+        for (int idx = tid; idx < 2 * MG * 16 * (kMfmaKC / 8); idx += kWG) {
+          const int half = idx / (MG * 16 * (kMfmaKC / 8));
+          const int rem = idx - half * (MG * 16 * (kMfmaKC / 8));
+          const int r = rem / (kMfmaKC / 8), cv = rem - r * (kMfmaKC / 8);
+          uint4 v = make_uint4(0, 0, 0, 0);
+          if (r < mrows) v = ld16((half ? mb.xlo : mb.xhi) + (long)(mg0 + r) * p.K + k0 + cv * 8);
+          *reinterpret_cast<uint4*>(&sA[half][r * kMfmaLdr + cv * 8]) = v;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < MG; ++m) {
+          if (m < mt) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+              const int kk = 32 * hq + 8 * s;
+              const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(&sA[0][(m * 16 + jl) * kMfmaLdr + kk]);
+              const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(&sA[1][(m * 16 + jl) * kMfmaLdr + kk]);
+#pragma unroll
+              for (int t = 0; t < NT; ++t) {
+                const bf16x8_t bw = __builtin_bit_cast(bf16x8_t, wv[t][s]);
+                acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bw, acc[m][t], 0, 0, 0);
+                acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bw, acc[m][t], 0, 0, 0);
+              }
+            }
+          }
+        }
+      }
+      // epilogue: lane holds rows 4 hq + r of each activation tile, column jl of each weight tile
+#pragma unroll
+      for (int m = 0; m < MG; ++m) {
+        if (m >= mt) continue;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const int col = n0 + t * 16 + jl;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int cr = mg0 + m * 16 + 4 * hq + r;
+            const float v = acc[m][t][r];
+            const float partner = __shfl_xor(v, 1, kWave);
+            if (cr < count && col < p.N) {
+              const int row = mb.rowmap[cr], a = mb.amap[cr];
+              if constexpr (P::kPair) {
+                if ((jl & 1) == 0) p.store_pair(col, a, row, v, partner);
+              } else {
+                p.store(col, a, row, v);
+              }
+            }
+          }
+        }
+      }
+      if constexpr (P::kArgmax) {
+        // running best per compact row over this group's columns, lowest id on ties
+#pragma unroll
+        for (int m = 0; m < MG; ++m) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float bv = -INFINITY;
+            int bi = 0x7fffffff;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+              const int col = n0 + t * 16 + jl;
+              if (m < mt && col < p.N && better(acc[m][t][r], col, bv, bi)) {
+                bv = acc[m][t][r];
+                bi = col;
+              }
+            }
+#pragma unroll
+            for (int o = 8; o > 0; o >>= 1) {  // over the 16 lanes of this quarter
+              const float ov = __shfl_xor(bv, o, kWave);
+              const int oi = __shfl_xor(bi, o, kWave);
+              if (better(ov, oi, bv, bi)) {
+                bv = ov;
+                bi = oi;
+              }
+            }
+            const int k = m * 16 + 4 * hq + r;
+            if (jl == 0) {
+              if (g == (int)blockIdx.x) {
+                s_bv[wid * MG * 16 + k] = bv;
+                s_bi[wid * MG * 16 + k] = bi;
+              } else if (better(bv, bi, s_bv[wid * MG * 16 + k], s_bi[wid * MG * 16 + k])) {
+                s_bv[wid * MG * 16 + k] = bv;
+                s_bi[wid * MG * 16 + k] = bi;
+              }
+            }
+          }
+        }
+      }
+    }
+    if constexpr (P::kArgmax) {
+      __syncthreads();
+      for (int k = tid; k < mrows; k += kWG) {
+        float v = -INFINITY;
+        int i = 0x7fffffff;
+        if ((int)blockIdx.x < ngroups)
+          for (int w = 0; w < 4; ++w)
+            if (better(s_bv[w * MG * 16 + k], s_bi[w * MG * 16 + k], v, i)) {
+              v = s_bv[w * MG * 16 + k];
+              i = s_bi[w * MG * 16 + k];
+            }
+        p.partial(mb.amap[mg0 + k], v, i);
+      }
+      __syncthreads();
+    }
+  }
+  p.finish(s_n);
+}
+
+}  // namespace mtp

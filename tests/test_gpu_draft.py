@@ -134,3 +134,13 @@ def test_two_layer_bf16_small_head():
                                   hidden=512, ffn=1024, vocab=5000, batch=2, D=2, prefill_rows=0, ctx=300,
                                   noise_std=0.01, rounds=6, embed_std=1.0)
     _run_rounds(cfg, cfg.rounds)
+
+
+def test_batched_bf16_head_mfma_path():
+    # 20 sequences and two drafts: 60 padded catch-up rows and 20 rows per serial step take the
+    # bf16 MFMA path (split-bf16 activations); the oracle stays the plain float64 definition
+    cfg = CONFIGS["tiny"].replace(index=13, wdtype="bf16", n_heads=2, n_kv_heads=1, head_dim=128, hidden=256,
+                                  ffn=512, vocab=3000, batch=20, D=2, prefill_rows=0, ctx=200, noise_std=0.01,
+                                  rounds=5, embed_std=1.0)
+    s = _run_rounds(cfg, cfg.rounds)
+    assert s["accepted"] > 0
