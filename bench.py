@@ -51,8 +51,8 @@ def main():
         sys.exit(2)
     import torch
     import speculative_decoding_mtp_amd as M
-    from synth import CONFIGS, make_first_round, make_kv_prefix, make_round_hiddens, make_round_noise, make_state, \
-        make_weights
+    from synth import CONFIGS, make_first_round, make_kv_prefix, make_round_hiddens, make_round_noise, \
+        make_round_uniforms, make_state, make_weights
     from tests.gpu_util import config, f32, i32, kv_from_numpy, upload_weights
 
     cfg = CONFIGS[args.config]
@@ -88,7 +88,10 @@ def main():
     tokens = i32(tok_pad)
     hidden0 = f32(hid_pad)
     ws = M.new_workspace(M.mtp_draft_workspace_size(c, B, rps, D, max_len))
-    vws = M.new_workspace(M.spec_verify_workspace_size(B, D, V, None))
+    sp = cfg.sampling
+    csp = None if sp is None else M.sampling(sp.temperature, sp.top_k, sp.top_p, sp.q_mode)
+    vws = M.new_workspace(M.spec_verify_workspace_size(B, D, V, csp))
+    unif = [tuple(f32(u) for u in make_round_uniforms(cfg.index, B, D, r)) for r in range(NBUF)] if sp else None
     drafts = torch.zeros(B, D, dtype=torch.int32, device="cuda")
     hiddens = torch.zeros(B, D, H, device="cuda")
     dlog = torch.zeros(B, D, V, device="cuda")
@@ -118,7 +121,8 @@ def main():
         if state is not None:
             M.mtp_state_snapshot(state, snap, state_bytes, B)
         n_acc = hist[r]
-        M.spec_verify(B, D, V, tl, drafts, None, None, None, None, ctx[cur], n_acc, out_tok[nxt], ctx[nxt], vws)
+        ua, us = unif[r % NBUF] if unif else (None, None)
+        M.spec_verify(B, D, V, tl, drafts, None, csp, ua, us, ctx[cur], n_acc, out_tok[nxt], ctx[nxt], vws)
         if state is not None:
             M.mtp_state_restore(state, snap, state_bytes, B, n_acc, D)
         M.kv_crop(kv, ctx[cur])
@@ -191,7 +195,9 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded random-init weights, KV prefix, hiddens and target-logit noise)",
         "config": {"workload": cfg.name, "batch": B, "draft_tokens": D, "kv_context": cfg.ctx,
-                   "target_noise_std": cfg.noise_std, "verify": "greedy",
+                   "target_noise_std": cfg.noise_std,
+                   "verify": "greedy" if sp is None else
+                   f"sampling T={sp.temperature} top_k={sp.top_k} top_p={sp.top_p} q_mode={sp.q_mode}",
                    "recurrent_state_bytes_per_seq": state_bytes},
         "steps_per_s": round(args.steps / wall, 2),
         "acceptance": round(float(acc.mean()) / D, 4),
@@ -208,7 +214,7 @@ def main():
 def cpu_baseline(cfg, w, K, Vv, budget_s):
     """The float64 oracle on the same workload, rounds until the time budget is spent."""
     import oracle as O
-    from synth import make_first_round, make_round_hiddens, make_round_noise
+    from synth import make_first_round, make_round_hiddens, make_round_noise, make_round_uniforms
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -225,7 +231,8 @@ def cpu_baseline(cfg, w, K, Vv, budget_s):
         drafts, _, logits, _ = O.draft_loop(model, cache, toks, hid, D)
         ctx = cache.len.copy() - (D - 1)
         tl = np.concatenate([logits, logits[:, D - 1:D]], axis=1).astype(np.float32) + make_round_noise(cfg, rounds)
-        res = O.greedy_verify(tl, drafts, ctx)
+        ua, us = make_round_uniforms(cfg.index, B, D, rounds)
+        res = O.spec_verify(tl, drafts, ctx, cfg.sampling, None, ua, us)
         O.kv_crop(cache, ctx)
         tokens_out += int((res.n_accept + 1).sum())
         toks, hid = res.out_tokens, make_round_hiddens(cfg, rounds)

@@ -6,6 +6,7 @@
 // every cached position up to their own.  Scores q.k / sqrt(hd), softmax, weighted sum of V.
 #include "common.h"
 #include "draft.h"
+#include "gemv.h"
 
 namespace mtp {
 
@@ -34,6 +35,7 @@ __global__ __launch_bounds__(kWG) void k_attn(AttnArgs a) {
   constexpr int SPT = kQB / 4;            // score accumulators per thread
   constexpr int QG = kWG / HD;            // query groups in the PV phase
   constexpr int QPT = kQB / QG;           // PV accumulators per thread
+  constexpr int QW = kQB / 4;             // softmax queries per wave
   __shared__ __align__(16) T sK[kTile * LDR];
   __shared__ __align__(16) T sV[kTile * LDR];
   __shared__ __align__(16) float sQ[kQB * HD];
@@ -84,7 +86,12 @@ __global__ __launch_bounds__(kWG) void k_attn(AttnArgs a) {
       }
       sQ[idx] = v;
     }
-    float m_run = -INFINITY, l_run = 0.f;  // owned by thread tid < nqb
+    float m_run[QW], l_run[QW];  // wave-uniform running max and sum of the wave's queries
+#pragma unroll
+    for (int k = 0; k < QW; ++k) {
+      m_run[k] = -INFINITY;
+      l_run[k] = 0.f;
+    }
     float o[QPT];
 #pragma unroll
     for (int k = 0; k < QPT; ++k) o[k] = 0.f;
@@ -110,9 +117,11 @@ __global__ __launch_bounds__(kWG) void k_attn(AttnArgs a) {
           W::cvt(*reinterpret_cast<const uint4*>(sK + pl * LDR + d0), kf);
 #pragma unroll
           for (int k = 0; k < SPT; ++k) {
-            const float* qp = sQ + (qs + 4 * k) * HD + d0;
+            if (qs + 4 * k < nqb) {  // wave-uniform: only the live queries read Q from LDS
+              const float* qp = sQ + (qs + 4 * k) * HD + d0;
 #pragma unroll
-            for (int e = 0; e < VE; ++e) acc[k] = fmaf(qp[e], kf[e], acc[k]);
+              for (int e = 0; e < VE; ++e) acc[k] = fmaf(qp[e], kf[e], acc[k]);
+            }
           }
         }
         const int p = t0 + pl;
@@ -125,36 +134,37 @@ __global__ __launch_bounds__(kWG) void k_attn(AttnArgs a) {
         }
       }
       __syncthreads();
-      if (tid < kQB) {  // online softmax, one thread per query; probabilities written transposed
-        const float* srow = sS + tid * (kTile + 1);
-        float tmax = -INFINITY;
-        for (int k = 0; k < kTile; ++k) tmax = fmaxf(tmax, srow[k]);
-        const float m_new = fmaxf(m_run, tmax);
-        float alpha = 1.f, lsum = 0.f;
-        if (m_new != -INFINITY) {
-          alpha = (m_run == -INFINITY) ? 0.f : expf(m_run - m_new);
-          for (int k = 0; k < kTile; ++k) {
-            const float e = (srow[k] == -INFINITY) ? 0.f : expf(srow[k] - m_new);
-            sP[k * kQB + tid] = e;
-            lsum += e;
+      {  // online softmax: wave w owns queries w, w+4, ...; lane = position in the tile
+        const int lane = tid & 63, wid = tid >> 6;
+#pragma unroll
+        for (int k = 0; k < QW; ++k) {
+          const int ql = wid + 4 * k;
+          if (ql >= nqb) continue;  // wave-uniform
+          const float sc = sS[ql * (kTile + 1) + lane];
+          const float m_new = fmaxf(m_run[k], wave_max_dpp(sc));
+          float alpha = 1.f, e = 0.f;
+          if (m_new != -INFINITY) {
+            alpha = (m_run[k] == -INFINITY) ? 0.f : expf(m_run[k] - m_new);
+            e = (sc == -INFINITY) ? 0.f : expf(sc - m_new);
           }
-        } else {
-          for (int k = 0; k < kTile; ++k) sP[k * kQB + tid] = 0.f;
+          sP[lane * kQB + ql] = e;
+          l_run[k] = l_run[k] * alpha + wave_sum_dpp(e);
+          m_run[k] = m_new;
+          if (lane == 0) sAlpha[ql] = alpha;
         }
-        l_run = l_run * alpha + lsum;
-        m_run = m_new;
-        sAlpha[tid] = alpha;
       }
       __syncthreads();
       {  // o = o * alpha + P V: thread -> dim dpv, queries qg*QPT .. qg*QPT+QPT-1
 #pragma unroll
         for (int k = 0; k < QPT; ++k) o[k] *= sAlpha[qg * QPT + k];
+        const int live4 = (min(QPT, max(0, nqb - qg * QPT)) + 3) / 4;  // float4 groups with live queries
 #pragma unroll 4
         for (int pl = 0; pl < kTile; ++pl) {
           const float v = W::get(sV, pl * LDR + dpv);
           const float4* pp = reinterpret_cast<const float4*>(sP + pl * kQB + qg * QPT);
 #pragma unroll
           for (int k4 = 0; k4 < QPT / 4; ++k4) {
+            if (k4 >= live4) continue;  // wave-uniform
             const float4 pv = pp[k4];
             o[4 * k4 + 0] = fmaf(pv.x, v, o[4 * k4 + 0]);
             o[4 * k4 + 1] = fmaf(pv.y, v, o[4 * k4 + 1]);
@@ -170,9 +180,15 @@ __global__ __launch_bounds__(kWG) void k_attn(AttnArgs a) {
       const int ql = qg * QPT + k;
       if (ql < nqb) P[(long)(q0 + ql) * (HD + 2) + dpv] = o[k];
     }
-    if (tid < nqb) {
-      P[(long)(q0 + tid) * (HD + 2) + HD] = m_run;
-      P[(long)(q0 + tid) * (HD + 2) + HD + 1] = l_run;
+    if ((tid & 63) == 0) {
+#pragma unroll
+      for (int k = 0; k < QW; ++k) {
+        const int ql = (tid >> 6) + 4 * k;
+        if (ql < nqb) {
+          P[(long)(q0 + ql) * (HD + 2) + HD] = m_run[k];
+          P[(long)(q0 + ql) * (HD + 2) + HD + 1] = l_run[k];
+        }
+      }
     }
     __syncthreads();
   }

@@ -99,7 +99,7 @@ int check_kv(const mtp_kv* kv) {
 
 // ------------------------------------------------------------------ drafter workspace
 struct DraftLayout {
-  size_t off[14];
+  size_t off[15];
   size_t total;
 };
 
@@ -111,7 +111,7 @@ DraftLayout draft_layout(const mtp_config& c, int B, int rps, int D, int max_len
   if ((size_t)c.ffn > kmax) kmax = c.ffn;
   if ((size_t)c.n_heads * c.head_dim > kmax) kmax = (size_t)c.n_heads * c.head_dim;
   const bool mfma = c.wdtype == MTP_BF16 && R >= 16;
-  const size_t sizes[14] = {
+  const size_t sizes[15] = {
       256,                                                                   // status word
       R * c.hidden * 4,                                                      // x
       R * c.n_heads * c.head_dim * 4,                                        // q
@@ -125,10 +125,11 @@ DraftLayout draft_layout(const mtp_config& c, int B, int rps, int D, int max_len
       mfma ? R * kmax * 2 : 0,                                               // split activations, lo
       mfma ? R * 4 : 0,                                                      // compact row map
       mfma ? R * 4 : 0,                                                      // compact activation map
-      mfma ? (size_t)4 : (size_t)0};                                         // compact count
+      mfma ? (size_t)4 : (size_t)0,                                          // compact count
+      mfma ? R * kPartCols * 4 : 0};                                         // split-K partials
   DraftLayout L;
   size_t o = 0;
-  for (int i = 0; i < 14; ++i) {
+  for (int i = 0; i < 15; ++i) {
     L.off[i] = o;
     o += up256(sizes[i]);
   }
@@ -154,6 +155,8 @@ DraftWs carve(void* ws, const DraftLayout& L) {
   w.rowmap = mfma ? reinterpret_cast<int*>(base + L.off[11]) : nullptr;
   w.amap = mfma ? reinterpret_cast<int*>(base + L.off[12]) : nullptr;
   w.mcount = mfma ? reinterpret_cast<int*>(base + L.off[13]) : nullptr;
+  w.kpart = mfma ? reinterpret_cast<float*>(base + L.off[14]) : nullptr;
+  w.kpart_cap = mfma ? (long)((L.total - L.off[14]) / 4) : 0;
   return w;
 }
 
@@ -193,7 +196,7 @@ StepArgs base_step(const mtp_config* cfg, const mtp_weights* w, const mtp_kv* kv
 
 namespace mtp {
 int attn_nsplit(int B, int nkv, int max_len) {
-  int n = (512 + B * nkv - 1) / (B * nkv);
+  int n = (2048 + B * nkv - 1) / (B * nkv);
   if (n > kMaxSplit) n = kMaxSplit;
   const int cap = (max_len + 63) / 64;
   if (n > cap) n = cap;
@@ -298,8 +301,7 @@ int spec_verify_workspace_size(int32_t B, int32_t D, int32_t V, const mtp_sampli
     const int K = sp->top_k;
     if (K < 1 || K > kMaxTopK) return fail(MTP_ERR_ARG, "top_k must be in [1, %d]", kMaxTopK);
     const size_t nchunk = (V + kChunk - 1) / kChunk;
-    t += 2 * up256(rows * nchunk * K * 4) + 2 * up256(rows * K * 4) + up256(rows * 4) +
-         up256((size_t)B * 4 * kMaxTopK * 4);
+    t += 2 * up256(rows * nchunk * K * 4) + 2 * up256(rows * K * 4) + up256(rows * 4);
   }
   *bytes = t;
   return MTP_OK;
@@ -368,7 +370,6 @@ int spec_verify(int32_t B, int32_t D, int32_t V, const float* target_logits, con
     o += up256((size_t)rows * K * 4);
     a.top_n = reinterpret_cast<int*>(base + o);
     o += up256((size_t)rows * 4);
-    a.scratch = reinterpret_cast<float*>(base + o);
   }
   hipEvent_t eb, ee;
   timer_events(MTP_KERNEL_VERIFY, &eb, &ee);

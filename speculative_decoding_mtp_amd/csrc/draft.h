@@ -13,6 +13,8 @@ constexpr int kLmRows = 16;  // weight rows per lm_head workgroup iteration
 
 constexpr int kMaxSplit = 128;     // attention splits per (sequence, kv head)
 constexpr int kMaxGemvGrid = 2048; // workgroups of one GEMV launch (also sizes the lm_head partials)
+constexpr int kMaxKSplit = 16;     // K ranges of a split-K MFMA GEMM
+constexpr long kPartCols = 98304;  // split-K partial columns per activation row (ksplit x N)
 
 // Positions per attention split for a sequence of T cached positions (a multiple of 64).
 __host__ __device__ inline int attn_chunk(int T, int nsplit) {
@@ -66,6 +68,8 @@ struct DraftWs {
   uint16_t *xhi, *xlo;  // [R][Kmax]
   int *rowmap, *amap;   // [R]
   int* mcount;
+  float* kpart;    // [kPartCols][R] split-K partial sums
+  long kpart_cap;  // floats in kpart
 };
 
 struct StepArgs {

@@ -290,19 +290,49 @@ bool use_mfma(const P& p, const MfmaBufs* mb) {
   return mb && std::is_same<W, BF16>::value && p.nact >= 16 && p.K % kMfmaKC == 0;
 }
 
+// MFMA GEMM with MG activation tiles per pass.  Few weight-row groups (N < 256 x 128): K is
+// split over workgroups so every compute unit streams weights, and a second kernel sums the
+// partials in split order and applies the policy's store.
+constexpr int kMfmaItems = 1024;  // (row group, K range) items a launch aims for: 4 per CU
+
+template <class P, int MG>
+hipError_t launch_mfma(P& p, hipStream_t st, int* grid_used, const MfmaBufs& mb) {
+  constexpr int NT = 2;
+  MfmaBufs m = mb;
+  const int groups = (p.N + 4 * NT * 16 - 1) / (4 * NT * 16);
+  int ks = 1;
+  if (!P::kArgmax && groups < kMfmaItems && m.part) {
+    ks = (kMfmaItems + groups - 1) / groups;
+    const int kc = p.K / kMfmaKC;
+    if (ks > kc) ks = kc;
+    if (ks > kMaxKSplit) ks = kMaxKSplit;
+    const long fit = m.part_cap / ((long)m.cap * p.N);
+    if (ks > fit) ks = (int)fit;
+  }
+  if (ks <= 1) m.part = nullptr;
+  m.ksplit = ks;
+  static int cap = 0;
+  int grid = min(groups * ks, resident_cap(k_gemm_mfma<P, NT, MG>, &cap));
+  grid = min(grid, kMaxGemvGrid);
+  if (grid_used) *grid_used = grid;
+  hipLaunchKernelGGL((k_gemm_mfma<P, NT, MG>), dim3(grid), dim3(kWG), 0, st, p, m);
+  if (m.part) {
+    const long items = (long)m.cap * (p.N / (P::kPair ? 2 : 1));
+    const int rgrid = (int)std::min<long>((items + kWG - 1) / kWG, 4096);
+    hipLaunchKernelGGL((k_splitk_reduce<P>), dim3(rgrid), dim3(kWG), 0, st, p, m);
+  }
+  return hipGetLastError();
+}
+
 template <class W, class P>
 hipError_t launch_gemv(P& p, hipStream_t st, int* grid_used = nullptr, const MfmaBufs* mb = nullptr) {
   if constexpr (std::is_same<W, BF16>::value) {
     if (use_mfma<W>(p, mb)) {
-      constexpr int NT = 2, MG = P::kArgmax ? 4 : 8;
       hipLaunchKernelGGL((k_prep<W, P>), dim3(p.nact), dim3(kWG), 0, st, p, *mb);
-      static int cap = 0;
-      const int groups = (p.N + 4 * NT * 16 - 1) / (4 * NT * 16);
-      int grid = min(groups, resident_cap(k_gemm_mfma<P, NT, MG>, &cap));
-      grid = min(grid, kMaxGemvGrid);
-      if (grid_used) *grid_used = grid;
-      hipLaunchKernelGGL((k_gemm_mfma<P, NT, MG>), dim3(grid), dim3(kWG), 0, st, p, *mb);
-      return hipGetLastError();
+      // activation tiles per pass from the activation count (an upper bound of the valid rows)
+      if (p.nact <= 32) return launch_mfma<P, 2>(p, st, grid_used, *mb);
+      if (p.nact <= 64) return launch_mfma<P, 4>(p, st, grid_used, *mb);
+      return launch_mfma<P, 8>(p, st, grid_used, *mb);
     }
   }
   const GemvPlan pl = plan_gemv(p.nact, p.K, W::VE, p.N);
@@ -353,7 +383,8 @@ hipError_t run_step_t(const StepArgs& s) {
   const int H = c.hidden, F = c.ffn, nq = c.n_heads, nkv = c.n_kv_heads, hd = c.head_dim;
   const int R = s.B * s.rps;
   hipError_t e;
-  const MfmaBufs mbuf = {s.ws.xhi, s.ws.xlo, s.ws.rowmap, s.ws.amap, s.ws.mcount};
+  const MfmaBufs mbuf = {s.ws.xhi, s.ws.xlo, s.ws.rowmap, s.ws.amap, s.ws.mcount, s.ws.kpart, 1, s.B * s.rps,
+                         s.ws.kpart_cap};
   const MfmaBufs* mb = s.ws.xhi ? &mbuf : nullptr;
 
   {  // eh_proj

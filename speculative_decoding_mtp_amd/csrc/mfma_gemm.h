@@ -7,14 +7,17 @@
 //   gives the fp32 row, which is written as two bf16 rows hi = bf16(x), lo = bf16(x - hi)
 //   (x = hi + lo to about 2^-17 relative), compacted over the valid rows.  rowmap / amap record
 //   each compact row's padded row and activation index; `count` the number of compact rows.
-// * k_gemm_mfma: each workgroup owns 4 waves x NT tiles of 16 weight rows and walks K in chunks
-//   of 128.  Per chunk the workgroup stages the compact activations (hi and lo, up to MG tiles of
-//   16 rows) in LDS, and every wave streams its weight rows once from HBM: lane l reads 64
-//   contiguous bytes of row l % 16 at column 32 (l / 16) of the chunk, so four lanes cover 256
-//   contiguous bytes of a row.  v_mfma_f32_16x16x32_bf16 consumes the chunk in four steps; the K
-//   order inside a step is the same permutation for both operands, so the dot products are
-//   unchanged.  Two MFMAs (hi, lo) per step keep fp32-like accuracy.  Rows beyond MG tiles are
-//   handled in further passes.
+// * k_gemm_mfma: each workgroup owns 4 waves x NT tiles of 16 weight rows and a range of K
+//   (the whole of K, or one of `ksplit` ranges when there are few row groups), walked in
+//   chunks of 128.  Per chunk the workgroup stages the compact activations (hi and lo, up to MG
+//   tiles of 16 rows) in LDS, and every wave streams its weight rows once from HBM, the next
+//   chunk's weights in flight while this one is multiplied.  In step s of a chunk, lane l holds
+//   columns 32 s + 8 (l / 16) .. +7 of row l % 16, so the four lanes of a row read 64
+//   contiguous bytes per load.  v_mfma_f32_16x16x32_bf16 consumes the chunk in four steps; the
+//   activations are read with the same column order, so the dot products are unchanged.  Two
+//   MFMAs (hi, lo) per step keep fp32-like accuracy.  Rows beyond MG tiles are handled in
+//   further passes.  With K split, raw partial sums go to a buffer and k_splitk_reduce adds
+//   them in range order and applies the policy's store.
 // Operand layout of v_mfma_f32_16x16x32_bf16 (checked on the device): lane l supplies
 // A[l % 16][8 (l / 16) + e] and B[8 (l / 16) + e][l % 16], e < 8; result r of lane l is
 // D[4 (l / 16) + r][l % 16].
@@ -35,6 +38,9 @@ struct MfmaBufs {
   int* rowmap;          // [cap] padded row of a compact row
   int* amap;            // [cap] activation index of a compact row
   int* count;           // number of compact rows
+  float* part;          // split-K partial sums [ksplit][cap][N] (NULL: no split)
+  int ksplit, cap;      // K ranges; activation rows the partial buffer is laid out for
+  long part_cap;        // floats available at part
 };
 
 __device__ __forceinline__ uint16_t bf16_rne(float f) {
@@ -145,11 +151,15 @@ __global__ __launch_bounds__(kWG) void k_gemm_mfma(P p, MfmaBufs mb) {
   const int Kc = p.K / kMfmaKC;  // K is a multiple of 128 on this path
   const int rows_per_wg = 4 * NT * 16;
   const int ngroups = (p.N + rows_per_wg - 1) / rows_per_wg;
+  const int ks = mb.part ? mb.ksplit : 1;           // K ranges per row group
+  const int kper = (Kc + ks - 1) / ks;
 
   for (int mg0 = 0; mg0 < count; mg0 += MG * 16) {
     const int mrows = min(MG * 16, count - mg0);
     const int mt = (mrows + 15) / 16;
-    for (int g = blockIdx.x; g < ngroups; g += gridDim.x) {
+    for (int gk = blockIdx.x; gk < ngroups * ks; gk += gridDim.x) {
+      const int g = gk / ks, kpart = gk - g * ks;
+      const int kc_beg = kpart * kper, kc_end = min(Kc, kc_beg + kper);
       const int n0 = g * rows_per_wg + wid * NT * 16;
       f32x4_t acc[MG][NT];
 #pragma unroll
@@ -159,19 +169,34 @@ __global__ __launch_bounds__(kWG) void k_gemm_mfma(P p, MfmaBufs mb) {
       const T* wrow[NT];
 #pragma unroll
       for (int t = 0; t < NT; ++t) wrow[t] = p.wrow(min(n0 + t * 16 + jl, p.N - 1));
-      for (int kc = 0; kc < Kc; ++kc) {
-        const int k0 = kc * kMfmaKC;
-        // this chunk's weights: 64 bytes of each of the NT rows of this lane
-        uint4 wv[NT][4];
+      // weights of a chunk: 64 bytes of each of the NT rows of this lane; the next chunk's are
+      // requested before this chunk's activations are staged and multiplied
+      uint4 wv[NT][4], wn[NT][4];
+      if (kc_beg < kc_end) {
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
-          for (int s = 0; s < 4; ++s) wv[t][s] = ld_stream(wrow[t] + k0 + 32 * hq + 8 * s);
-        // stage the chunk's activations (hi, lo) of this pass in LDS
+          for (int s = 0; s < 4; ++s) wn[t][s] = ld_stream(wrow[t] + kc_beg * kMfmaKC + 32 * s + 8 * hq);
+      }
+      for (int kc = kc_beg; kc < kc_end; ++kc) {
+        const int k0 = kc * kMfmaKC;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int s = 0; s < 4; ++s) wv[t][s] = wn[t][s];
+        if (kc + 1 < kc_end) {
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) wn[t][s] = ld_stream(wrow[t] + k0 + kMfmaKC + 32 * s + 8 * hq);
+        }
+        // stage the chunk's activations (hi, lo) of this pass in LDS; rows past the pass's
+        // count within its last tile are zero
         __syncthreads();
-        for (int idx = tid; idx < 2 * MG * 16 * (kMfmaKC / 8); idx += kWG) {
-          const int half = idx / (MG * 16 * (kMfmaKC / 8));
-          const int rem = idx - half * (MG * 16 * (kMfmaKC / 8));
+        const int srows = mt * 16;
+        for (int idx = tid; idx < 2 * srows * (kMfmaKC / 8); idx += kWG) {
+          const int half = idx / (srows * (kMfmaKC / 8));
+          const int rem = idx - half * (srows * (kMfmaKC / 8));
           const int r = rem / (kMfmaKC / 8), cv = rem - r * (kMfmaKC / 8);
           uint4 v = make_uint4(0, 0, 0, 0);
           if (r < mrows) v = ld16((half ? mb.xlo : mb.xhi) + (long)(mg0 + r) * p.K + k0 + cv * 8);
@@ -183,7 +208,7 @@ __global__ __launch_bounds__(kWG) void k_gemm_mfma(P p, MfmaBufs mb) {
           if (m < mt) {
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-              const int kk = 32 * hq + 8 * s;
+              const int kk = 32 * s + 8 * hq;
               const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(&sA[0][(m * 16 + jl) * kMfmaLdr + kk]);
               const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(&sA[1][(m * 16 + jl) * kMfmaLdr + kk]);
 #pragma unroll
@@ -195,6 +220,22 @@ __global__ __launch_bounds__(kWG) void k_gemm_mfma(P p, MfmaBufs mb) {
             }
           }
         }
+      }
+      if (mb.part) {  // split-K: raw partial sums, reduced and stored by k_splitk_reduce
+#pragma unroll
+        for (int m = 0; m < MG; ++m) {
+          if (m >= mt) continue;
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            const int col = n0 + t * 16 + jl;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int cr = mg0 + m * 16 + 4 * hq + r;
+              if (cr < count && col < p.N) mb.part[((long)kpart * mb.cap + cr) * p.N + col] = acc[m][t][r];
+            }
+          }
+        }
+        continue;
       }
       // epilogue: lane holds rows 4 hq + r of each activation tile, column jl of each weight tile
 #pragma unroll
@@ -246,7 +287,7 @@ __global__ __launch_bounds__(kWG) void k_gemm_mfma(P p, MfmaBufs mb) {
             }
             const int k = m * 16 + 4 * hq + r;
             if (jl == 0) {
-              if (g == (int)blockIdx.x) {
+              if (gk == (int)blockIdx.x) {
                 s_bv[wid * MG * 16 + k] = bv;
                 s_bi[wid * MG * 16 + k] = bi;
               } else if (better(bv, bi, s_bv[wid * MG * 16 + k], s_bi[wid * MG * 16 + k])) {
@@ -263,7 +304,7 @@ __global__ __launch_bounds__(kWG) void k_gemm_mfma(P p, MfmaBufs mb) {
       for (int k = tid; k < mrows; k += kWG) {
         float v = -INFINITY;
         int i = 0x7fffffff;
-        if ((int)blockIdx.x < ngroups)
+        if ((int)blockIdx.x < ngroups * ks)
           for (int w = 0; w < 4; ++w)
             if (better(s_bv[w * MG * 16 + k], s_bi[w * MG * 16 + k], v, i)) {
               v = s_bv[w * MG * 16 + k];
@@ -275,6 +316,34 @@ __global__ __launch_bounds__(kWG) void k_gemm_mfma(P p, MfmaBufs mb) {
     }
   }
   p.finish(s_n);
+}
+
+// Sum the split-K partials of each (compact row, column) in split order and store them through
+// the policy (pairs for pair policies).  One thread per output (or output pair).
+template <class P>
+__global__ __launch_bounds__(kWG) void k_splitk_reduce(P p, MfmaBufs mb) {
+  __shared__ int s_n[kMaxBatch];
+  __shared__ int s_len[kMaxBatch];
+  p.setup(s_n, s_len);
+  __syncthreads();
+  const int count = *mb.count;
+  const int step = P::kPair ? 2 : 1;
+  const long items = (long)count * (p.N / step);
+  for (long it = (long)blockIdx.x * kWG + threadIdx.x; it < items; it += (long)gridDim.x * kWG) {
+    const int cr = (int)(it / (p.N / step));
+    const int col = (int)(it - (long)cr * (p.N / step)) * step;
+    float v0 = 0.f, v1 = 0.f;
+    for (int k = 0; k < mb.ksplit; ++k) {
+      const float* pp = mb.part + ((long)k * mb.cap + cr) * p.N + col;
+      v0 += pp[0];
+      if (P::kPair) v1 += pp[1];
+    }
+    const int row = mb.rowmap[cr], a = mb.amap[cr];
+    if constexpr (P::kPair)
+      p.store_pair(col, a, row, v0, v1);
+    else
+      p.store(col, a, row, v0);
+  }
 }
 
 }  // namespace mtp

@@ -30,8 +30,7 @@ struct VerifyArgs {
   int* cand_i;
   float* top_v;  // [rows][top_k]
   int* top_i;
-  int* top_n;      // [rows]
-  float* scratch;  // [B][4 * kMaxTopK]
+  int* top_n;  // [rows]
 };
 
 hipError_t run_verify(const VerifyArgs& a, hipStream_t st);

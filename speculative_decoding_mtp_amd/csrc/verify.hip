@@ -322,12 +322,10 @@ __global__ __launch_bounds__(64) void k_sample_decide(VerifyArgs a) {
   const int b = blockIdx.x;
   const int K = a.top_k;
   const int tgt_rows = a.B * (a.D + 1);
+  __shared__ float P[kMaxTopK], Q[kMaxTopK], w[kMaxTopK];  // probabilities, draft probs, residual
+  __shared__ int ids[kMaxTopK];
   if (threadIdx.x != 0) return;
-  // ---- the sequence's decision, one thread ----
-  float* P = a.scratch + (long)b * 4 * kMaxTopK;  // [kMaxTopK] probs of the target row
-  float* Q = P + kMaxTopK;
-  float* w = Q + kMaxTopK;
-  int* ids = reinterpret_cast<int*>(w + kMaxTopK);
+  // ---- the sequence's decision, one thread, working in LDS ----
   const float T = a.temperature;
   int32_t* out = a.out + (long)b * (a.D + 1);
   int n_acc = 0;
