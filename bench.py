@@ -59,7 +59,7 @@ def main():
     B, D, H, V = cfg.batch, cfg.D, cfg.hidden, cfg.vocab
     state_bytes = cfg.state_bytes_per_seq if args.state_bytes is None else args.state_bytes
     rounds_total = args.warmup + args.steps
-    max_len = cfg.ctx + 1 + (rounds_total + args.graph) * (D + 1) + 64
+    max_len = M.round_max_len(cfg.ctx + 1 + (rounds_total + args.graph) * (D + 1) + 64)
     t0 = time.time()
     w = make_weights(cfg)
     c = config(cfg)

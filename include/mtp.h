@@ -82,9 +82,12 @@ typedef struct {
 } mtp_weights;
 
 /* The head's own KV cache ([HB14]: an attention state truncated along T on rollback).
- * k, v: [n_layers][batch][n_kv_heads][max_len][head_dim] in cfg->wdtype, keys stored after
- * RoPE.  len: device int32[batch], the number of valid positions per sequence; position p
- * lives in slot p. */
+ * k: [n_layers][batch][n_kv_heads][max_len][head_dim] in cfg->wdtype, keys stored after RoPE;
+ * v: [n_layers][batch][n_kv_heads][head_dim][max_len] in cfg->wdtype: values are stored
+ * transposed (each channel's positions contiguous), the layout the attention's value
+ * contraction over positions reads.  max_len: a positive multiple of 8 (MTP_ERR_ARG
+ * otherwise).  len: device int32[batch], the number of valid positions per sequence;
+ * position p lives in slot p.  Slots at or past len may hold anything. */
 typedef struct {
   void *k, *v;
   int32_t* len;

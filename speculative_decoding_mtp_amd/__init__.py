@@ -162,13 +162,22 @@ class Weights:
                             tensors["lm_head"].data_ptr(), self._layers)
 
 
+def round_max_len(n: int) -> int:
+    """The smallest cache capacity >= n that the library accepts (a multiple of 8)."""
+    return -(-int(n) // 8) * 8
+
+
 class KVCache:
-    """The head's K/V cache [n_layers][batch][n_kv_heads][max_len][head_dim] and lengths [batch]."""
+    """The head's cache: keys [n_layers][batch][n_kv_heads][max_len][head_dim], values transposed
+    [n_layers][batch][n_kv_heads][head_dim][max_len], lengths [batch].  max_len: multiple of 8."""
 
     def __init__(self, cfg: Config, batch: int, max_len: int, device="cuda"):
-        shape = (cfg.n_layers, batch, cfg.n_kv_heads, max_len, cfg.head_dim)
-        self.k = torch.zeros(shape, dtype=cfg.torch_dtype, device=device)
-        self.v = torch.zeros(shape, dtype=cfg.torch_dtype, device=device)
+        if max_len < 8 or max_len % 8:
+            raise MTPError(-1, f"max_len must be a positive multiple of 8, got {max_len}")
+        self.k = torch.zeros((cfg.n_layers, batch, cfg.n_kv_heads, max_len, cfg.head_dim),
+                             dtype=cfg.torch_dtype, device=device)
+        self.v = torch.zeros((cfg.n_layers, batch, cfg.n_kv_heads, cfg.head_dim, max_len),
+                             dtype=cfg.torch_dtype, device=device)
         self.len = torch.zeros(batch, dtype=torch.int32, device=device)
         self.batch, self.max_len = batch, max_len
 

@@ -11,20 +11,16 @@
 namespace mtp {
 
 // ---------------------------------------------------------------------------------------------
-// decode attention, split over the cached positions
+// decode attention, split over the cached positions (fp32 caches: VALU kernel)
 // ---------------------------------------------------------------------------------------------
-// Workgroup (s, kvh, b) handles positions [s*chunk, min(T, (s+1)*chunk)) of sequence b, where
-// T = len[b] + rows, for all queries (row i, query head kvh*G + g) of the sequence.  K/V tiles of
-// 64 positions are staged through LDS; an online softmax keeps (m, l, o) per query.  Output per
-// query: the unnormalised o, the running max m and the sum l.
 constexpr int kTile = 64;  // cached positions per LDS tile
 constexpr int kQB = 32;    // queries per pass
 
 // Workgroup (s, kvh, b) handles positions [s*chunk, min(T, (s+1)*chunk)) of sequence b, where
 // T = len[b] + rows, for every query (row i, query head kvh*G + g) of the sequence.  K/V tiles
 // of 64 positions go through registers (the next tile is fetched while the current one is
-// used) into LDS; an online softmax keeps (m, l, o) per query.  Output per query: the
-// unnormalised o, the running max m and the sum l.
+// used) into LDS, values transposed back to [position][channel]; an online softmax keeps
+// (m, l, o) per query.  Output per query: the unnormalised o, the running max m and the sum l.
 template <class W, int HD>
 __global__ __launch_bounds__(kWG) void k_attn(AttnArgs a) {
   using T = typename W::T;
@@ -59,7 +55,7 @@ __global__ __launch_bounds__(kWG) void k_attn(AttnArgs a) {
   const int p_end = min(Tn, p_beg + chunk);
   const int NQ = n * G;
   const T* Kb = reinterpret_cast<const T*>(a.kc) + ((long)b * a.nkv + kvh) * a.max_len * HD;
-  const T* Vb = reinterpret_cast<const T*>(a.vc) + ((long)b * a.nkv + kvh) * a.max_len * HD;
+  const T* Vt = reinterpret_cast<const T*>(a.vc) + ((long)b * a.nkv + kvh) * a.max_len * HD;  // [HD][max_len]
   const float scale = 1.0f / sqrtf(float(HD));
   const int dpv = tid % HD, qg = tid / HD;
 
@@ -72,7 +68,10 @@ __global__ __launch_bounds__(kWG) void k_attn(AttnArgs a) {
         const int idx = tid + v * kWG, pr = idx / VPR, c = idx - pr * VPR;
         const int p = t0 + pr;
         kr[v] = p < p_end ? ld16(Kb + (long)p * HD + c * VE) : make_uint4(0, 0, 0, 0);
-        vr[v] = p < p_end ? ld16(Vb + (long)p * HD + c * VE) : make_uint4(0, 0, 0, 0);
+        // values: VE positions of one channel; positions past the range are zero
+        const int d = idx / (kTile / VE), pv = t0 + (idx - d * (kTile / VE)) * VE;
+        vr[v] = pv < p_end ? ld16(Vt + (long)d * a.max_len + pv) : make_uint4(0, 0, 0, 0);
+        if (pv < p_end && pv + VE > p_end) vr[v] = W::keep_first(vr[v], p_end - pv);
       }
     };
     fetch(p_beg);
@@ -102,7 +101,11 @@ __global__ __launch_bounds__(kWG) void k_attn(AttnArgs a) {
       for (int v = 0; v < NV; ++v) {
         const int idx = tid + v * kWG, pr = idx / VPR, c = idx - pr * VPR;
         *reinterpret_cast<uint4*>(sK + pr * LDR + c * VE) = kr[v];
-        *reinterpret_cast<uint4*>(sV + pr * LDR + c * VE) = vr[v];
+        const int d = idx / (kTile / VE), pl = (idx - d * (kTile / VE)) * VE;
+        T ve[VE];
+        __builtin_memcpy(ve, &vr[v], 16);
+#pragma unroll
+        for (int e = 0; e < VE; ++e) sV[(pl + e) * LDR + d] = ve[e];  // transposed into [p][d]
       }
       __syncthreads();
       if (t0 + kTile < p_end) fetch(t0 + kTile);  // in flight while this tile is used
@@ -194,6 +197,226 @@ __global__ __launch_bounds__(kWG) void k_attn(AttnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// bf16 heads: decode attention on MFMA (v_mfma_f32_16x16x32_bf16), same split and partials
+// ---------------------------------------------------------------------------------------------
+// Workgroup (s, kvh, b) as above.  Each wave walks its own 32-position slices of the range
+// (wave w takes slices w, w + 4, ...) with its own online softmax, and the four waves are merged
+// in LDS at the end.  Per slice, with queries in tiles of 16 (NQT tiles per pass):
+// * scores, transposed: S^T[p][q] = sum_d K[p][d] Q[q][d] with K as the A operand straight from
+//   the cache and Q (fp32, split into bf16 hi + lo) as B.  The A row m of sub-tile t is position
+//   8 (m / 4) + 4 t + m % 4 of the slice, so that result element r of lane (h = l / 16, j = l % 16)
+//   in sub-tile t is position 8 h + 4 t + r: each lane ends up with 8 consecutive positions of
+//   query column j;
+// * softmax over those 8 scores, reduced over the four lanes of the column;
+// * O^T[d][q] += sum_p V^T[d][p] P[q][p] with V^T (the cache holds values transposed) as A and
+//   the lane's 8 probabilities (split hi + lo) as B: the K index 8 h + e of a lane is exactly its
+//   position 8 h + e.
+// Masked positions get probability 0; values past the range are zeroed before the product.
+template <int HD, int NQT>
+__global__ __launch_bounds__(kWG) void k_attn_mfma(AttnArgs a) {
+  constexpr int NS = HD / 32;   // q.k steps
+  constexpr int ND = HD / 16;   // 16-channel tiles of the output
+  constexpr int QB = 16 * NQT;  // queries per pass
+  constexpr int OP = HD + 4;    // padded LDS row of the merged output
+  constexpr int QP = HD + 8;    // padded LDS row of the split queries (bf16)
+  __shared__ float sm[4][QB], sl[4][QB];
+  __shared__ __align__(16) float sO[QB * OP];
+  __shared__ __align__(16) __bf16 sQ[2 * QB * QP];  // [hi/lo][query][channel]
+  __shared__ int s_n;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, j = lane & 15, hq = lane >> 4;
+  const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int G = a.nq / a.nkv;
+  const int L0 = a.len[b];
+  if (tid == 0) s_n = count_rows(a.tok + (long)b * a.tok_sb, a.rps, a.V, L0, a.max_len, nullptr);
+  __syncthreads();
+  const int n = s_n;
+  if (n == 0) return;
+  const int Tn = L0 + n;
+  const int chunk = attn_chunk(Tn, a.nsplit);
+  const int p_beg = s * chunk;
+  if (p_beg >= Tn) return;
+  const int p_end = min(Tn, p_beg + chunk);
+  const int NQ = n * G;
+  const uint16_t* Kb = reinterpret_cast<const uint16_t*>(a.kc) + ((long)b * a.nkv + kvh) * a.max_len * HD;
+  const uint16_t* Vt = reinterpret_cast<const uint16_t*>(a.vc) + ((long)b * a.nkv + kvh) * a.max_len * HD;
+  const float scale = 1.0f / sqrtf(float(HD));
+  const int krow = 8 * (j >> 2) + (j & 3);  // this lane's K row in sub-tile 0 (+4 in sub-tile 1)
+
+  for (int q0 = 0; q0 < NQ; q0 += QB) {
+    // queries of this pass as bf16 hi + lo in LDS (B operand of the scores); absent ones zero
+    for (int idx = tid; idx < QB * (HD / 8); idx += kWG) {
+      const int q = idx / (HD / 8), c = idx - q * (HD / 8), qi = q0 + q;
+      float f[8];
+      if (qi < NQ) {
+        const int i = qi / G, g = qi - i * G;
+        const float* qp = a.q + (((long)b * a.rps + i) * a.nq + kvh * G + g) * HD + 8 * c;
+        const float4 x0 = *reinterpret_cast<const float4*>(qp);
+        const float4 x1 = *reinterpret_cast<const float4*>(qp + 4);
+        f[0] = x0.x; f[1] = x0.y; f[2] = x0.z; f[3] = x0.w;
+        f[4] = x1.x; f[5] = x1.y; f[6] = x1.z; f[7] = x1.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = 0.f;
+      }
+      bf16x8_t h, l;
+      split_bf16x8(f, h, l);
+      *reinterpret_cast<bf16x8_t*>(sQ + q * QP + 8 * c) = h;
+      *reinterpret_cast<bf16x8_t*>(sQ + (QB + q) * QP + 8 * c) = l;
+    }
+    int lim[NQT];  // last position query column j may attend (-1: no query)
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) {
+      const int qi = q0 + 16 * qt + j;
+      lim[qt] = qi < NQ ? L0 + qi / G : -1;
+    }
+    __syncthreads();
+    float m_run[NQT], l_run[NQT];
+    f32x4_t acc[ND][NQT];
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) {
+      m_run[qt] = -INFINITY;
+      l_run[qt] = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) acc[dt][qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    // operands of one slice: K rows (A of the scores) and V^T rows (A of the output)
+    uint4 ck[2][NS], cv[ND];
+    // Loads are unconditional from clamped, in-range addresses (rows past the range are
+    // masked as scores; value positions past the range are zeroed).
+    auto load = [&](int pw, uint4 (&kk)[2][NS], uint4 (&vv)[ND]) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int p = min(pw + krow + 4 * t, p_end - 1);
+        const uint16_t* kp = Kb + (long)p * HD + 8 * hq;
+#pragma unroll
+        for (int st = 0; st < NS; ++st) kk[t][st] = ld16(kp + 32 * st);
+      }
+      const int pv = pw + 8 * hq;
+      const uint16_t* vp = Vt + min(pv, (p_end - 1) & ~7) + (long)j * a.max_len;
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) vv[dt] = ld16(vp + (long)(16 * dt) * a.max_len);
+    };
+    // Two waves per SIMD hide the load latency of each other's slices (a register prefetch of
+    // the next slice would cost that occupancy).
+    for (int pw = p_beg + 32 * wid; pw < p_end; pw += 128) {
+      load(pw, ck, cv);
+      __builtin_amdgcn_sched_barrier(0);  // all of the slice's loads are issued before any use
+#pragma unroll
+      for (int qt = 0; qt < NQT; ++qt) {
+        f32x4_t sc[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          sc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int st = 0; st < NS; ++st) {
+            const bf16x8_t kop = __builtin_bit_cast(bf16x8_t, ck[t][st]);
+            const bf16x8_t qh = *reinterpret_cast<const bf16x8_t*>(sQ + (16 * qt + j) * QP + 32 * st + 8 * hq);
+            const bf16x8_t ql = *reinterpret_cast<const bf16x8_t*>(sQ + (QB + 16 * qt + j) * QP + 32 * st + 8 * hq);
+            sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qh, sc[t], 0, 0, 0);
+            sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, ql, sc[t], 0, 0, 0);
+          }
+        }
+        float pe[8];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int p = pw + 8 * hq + e;
+          const float v = (p < p_end && p <= lim[qt]) ? sc[e >> 2][e & 3] * scale : -INFINITY;
+          pe[e] = v;
+          mx = fmaxf(mx, v);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+        const float m_new = fmaxf(m_run[qt], mx);
+        float alpha = 1.f, rs = 0.f;
+        if (m_new != -INFINITY) {
+          alpha = m_run[qt] == -INFINITY ? 0.f : expf(m_run[qt] - m_new);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            pe[e] = pe[e] == -INFINITY ? 0.f : expf(pe[e] - m_new);
+            rs += pe[e];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pe[e] = 0.f;
+        }
+        rs += __shfl_xor(rs, 16, kWave);
+        rs += __shfl_xor(rs, 32, kWave);
+        l_run[qt] = l_run[qt] * alpha + rs;
+        m_run[qt] = m_new;
+        bf16x8_t ph, pl;
+        split_bf16x8(pe, ph, pl);
+        // value positions of this lane past the range are zeroed (they may hold anything)
+        const int keep = p_end - (pw + 8 * hq);
+        uint32_t vm[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          vm[w] = (2 * w < keep ? 0x0000ffffu : 0u) | (2 * w + 1 < keep ? 0xffff0000u : 0u);
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) {
+          acc[dt][qt] *= alpha;
+          const uint4 vr = cv[dt];
+          const bf16x8_t vop =
+              __builtin_bit_cast(bf16x8_t, make_uint4(vr.x & vm[0], vr.y & vm[1], vr.z & vm[2], vr.w & vm[3]));
+          acc[dt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, ph, acc[dt][qt], 0, 0, 0);
+          acc[dt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pl, acc[dt][qt], 0, 0, 0);
+        }
+      }
+    }
+    // merge the four waves: o = sum_w o_w e^{m_w - M}, l = sum_w l_w e^{m_w - M}
+    if (hq == 0) {
+#pragma unroll
+      for (int qt = 0; qt < NQT; ++qt) {
+        sm[wid][16 * qt + j] = m_run[qt];
+        sl[wid][16 * qt + j] = l_run[qt];
+      }
+    }
+    __syncthreads();
+    float cw[NQT];
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) {
+      const int q = 16 * qt + j;
+      const float M = fmaxf(fmaxf(sm[0][q], sm[1][q]), fmaxf(sm[2][q], sm[3][q]));
+      cw[qt] = m_run[qt] == -INFINITY ? 0.f : expf(m_run[qt] - M);
+    }
+    for (int w = 0; w < 4; ++w) {
+      if (wid == w) {
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+          for (int dt = 0; dt < ND; ++dt) {
+            float4* op = reinterpret_cast<float4*>(sO + (16 * qt + j) * OP + 16 * dt + 4 * hq);
+            const f32x4_t v = acc[dt][qt] * cw[qt];
+            if (w == 0) {
+              *op = make_float4(v[0], v[1], v[2], v[3]);
+            } else {
+              const float4 o = *op;
+              *op = make_float4(o.x + v[0], o.y + v[1], o.z + v[2], o.w + v[3]);
+            }
+          }
+      }
+      __syncthreads();
+    }
+    float* P = a.part + (((long)b * a.nkv + kvh) * a.nsplit + s) * (long)a.qstride * (HD + 2);
+    for (int idx = tid; idx < QB * HD; idx += kWG) {
+      const int q = idx / HD, d = idx - q * HD;
+      if (q0 + q < NQ) P[(long)(q0 + q) * (HD + 2) + d] = sO[q * OP + d];
+    }
+    for (int q = tid; q < QB; q += kWG) {
+      if (q0 + q < NQ) {
+        const float M = fmaxf(fmaxf(sm[0][q], sm[1][q]), fmaxf(sm[2][q], sm[3][q]));
+        float L = 0.f;
+        for (int w = 0; w < 4; ++w)
+          if (sm[w][q] != -INFINITY) L += sl[w][q] * expf(sm[w][q] - M);
+        P[(long)(q0 + q) * (HD + 2) + HD] = M;
+        P[(long)(q0 + q) * (HD + 2) + HD + 1] = L;
+      }
+    }
+    __syncthreads();  // sm, sl, sO are reused by the next pass
+  }
+}
+
 // Merge the split partials of one (row, query head): o = sum_s o_s e^{m_s - M} / sum_s l_s e^{m_s - M}.
 template <int HD>
 __global__ __launch_bounds__(HD) void k_attn_combine(AttnArgs a, float* out) {
@@ -230,22 +453,27 @@ __global__ __launch_bounds__(HD) void k_attn_combine(AttnArgs a, float* out) {
   out[((long)row * a.nq + h) * HD + d] = O / L;
 }
 
-hipError_t run_attention(const AttnArgs& a, int hd, int wdtype, float* out, hipStream_t st) {
+// bf16 caches take the MFMA kernel (one query tile per pass when a sequence's queries fit in
+// 16, else two); fp32 caches the VALU kernel.
+template <int HD>
+void launch_attention(const AttnArgs& a, int wdtype, float* out, hipStream_t st) {
   dim3 grid(a.nsplit, a.nkv, a.B);
-  const int items = a.B * a.rps * a.nq;
-  if (hd == 128) {
-    if (wdtype == MTP_BF16)
-      hipLaunchKernelGGL((k_attn<BF16, 128>), grid, dim3(kWG), 0, st, a);
+  if (wdtype == MTP_BF16) {
+    if (a.qstride <= 16)
+      hipLaunchKernelGGL((k_attn_mfma<HD, 1>), grid, dim3(kWG), 0, st, a);
     else
-      hipLaunchKernelGGL((k_attn<F32, 128>), grid, dim3(kWG), 0, st, a);
-    hipLaunchKernelGGL((k_attn_combine<128>), dim3(items), dim3(128), 0, st, a, out);
+      hipLaunchKernelGGL((k_attn_mfma<HD, 2>), grid, dim3(kWG), 0, st, a);
   } else {
-    if (wdtype == MTP_BF16)
-      hipLaunchKernelGGL((k_attn<BF16, 64>), grid, dim3(kWG), 0, st, a);
-    else
-      hipLaunchKernelGGL((k_attn<F32, 64>), grid, dim3(kWG), 0, st, a);
-    hipLaunchKernelGGL((k_attn_combine<64>), dim3(items), dim3(64), 0, st, a, out);
+    hipLaunchKernelGGL((k_attn<F32, HD>), grid, dim3(kWG), 0, st, a);
   }
+  hipLaunchKernelGGL((k_attn_combine<HD>), dim3(a.B * a.rps * a.nq), dim3(HD), 0, st, a, out);
+}
+
+hipError_t run_attention(const AttnArgs& a, int hd, int wdtype, float* out, hipStream_t st) {
+  if (hd == 128)
+    launch_attention<128>(a, wdtype, out, st);
+  else
+    launch_attention<64>(a, wdtype, out, st);
   return hipGetLastError();
 }
 

@@ -93,7 +93,7 @@ int check_kv(const mtp_kv* kv) {
   if (!kv->k || !kv->v || !kv->len || !aligned16(kv->k) || !aligned16(kv->v))
     return fail(MTP_ERR_ARG, "kv pointers must be non-NULL and 16-byte aligned");
   if (kv->batch < 1 || kv->batch > kMaxBatch) return fail(MTP_ERR_ARG, "kv.batch must be in [1, %d]", kMaxBatch);
-  if (kv->max_len < 1) return fail(MTP_ERR_ARG, "kv.max_len must be positive");
+  if (kv->max_len < 8 || kv->max_len % 8) return fail(MTP_ERR_ARG, "kv.max_len must be a positive multiple of 8");
   return MTP_OK;
 }
 

@@ -30,6 +30,14 @@ struct BF16 {
     f[7] = __uint_as_float(v.w & 0xffff0000u);
   }
   __device__ __forceinline__ static float get(const T* p, long i) { return __uint_as_float(uint32_t(p[i]) << 16); }
+  // the first k elements of a vector, the rest zero
+  __device__ __forceinline__ static uint4 keep_first(uint4 v, int k) {
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (e >= k) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  }
   // round-to-nearest-even float -> bf16 (finite inputs; NaN stays NaN)
   __device__ __forceinline__ static T put(float f) {
     uint32_t u = __float_as_uint(f);
@@ -42,6 +50,9 @@ struct BF16 {
 struct F32 {
   using T = float;
   static constexpr int VE = 4;
+  __device__ __forceinline__ static uint4 keep_first(uint4 v, int k) {
+    return make_uint4(k > 0 ? v.x : 0u, k > 1 ? v.y : 0u, k > 2 ? v.z : 0u, k > 3 ? v.w : 0u);
+  }
   __device__ __forceinline__ static void cvt(const uint4 v, float (&f)[4]) {
     f[0] = __uint_as_float(v.x);
     f[1] = __uint_as_float(v.y);
@@ -130,6 +141,33 @@ __device__ __forceinline__ int count_rows(const int32_t* tok, int rps, int V, in
   }
   if (flags) *flags = f;
   return rps;
+}
+
+// ---- MFMA operands (v_mfma_f32_16x16x32_bf16)
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// float -> bf16 bits, round to nearest even (finite inputs)
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+// Eight floats as two bf16x8 operands hi = bf16(x), lo = bf16(x - hi): hi + lo carries x to
+// about 2^-17 relative, so two MFMAs give a near-fp32 product with a bf16 operand.
+__device__ __forceinline__ void split_bf16x8(const float (&x)[8], bf16x8_t& hi, bf16x8_t& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint16_t h0 = bf16_rne(x[2 * e]), h1 = bf16_rne(x[2 * e + 1]);
+    const uint16_t l0 = bf16_rne(x[2 * e] - __uint_as_float(uint32_t(h0) << 16));
+    const uint16_t l1 = bf16_rne(x[2 * e + 1] - __uint_as_float(uint32_t(h1) << 16));
+    h[e] = uint32_t(h0) | (uint32_t(h1) << 16);
+    l[e] = uint32_t(l0) | (uint32_t(l1) << 16);
+  }
+  hi = __builtin_bit_cast(bf16x8_t, make_uint4(h[0], h[1], h[2], h[3]));
+  lo = __builtin_bit_cast(bf16x8_t, make_uint4(l[0], l[1], l[2], l[3]));
 }
 
 }  // namespace mtp

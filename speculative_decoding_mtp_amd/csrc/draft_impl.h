@@ -97,7 +97,7 @@ struct PQKV : PBase<W> {
   int H, nq, nkv, hd;
   double log_theta;
   float* qout;
-  T *kc, *vc;  // this layer's cache [B][nkv][max_len][hd]
+  T *kc, *vc;  // this layer's cache: keys [B][nkv][max_len][hd], values [B][nkv][hd][max_len]
 
   __device__ void load_x(int row, int k, float (&f)[W::VE]) const { load_f32_vec<W::VE>(xin + (long)row * H + k, f); }
   __device__ void gain_vec(int k, float (&f)[W::VE]) const { W::cvt(ld16(g + k), f); }
@@ -125,11 +125,14 @@ struct PQKV : PBase<W> {
       float* qp = qout + (long)row * nq * hd + (long)head * hd;
       qp[u] = v0;
       qp[u + half] = v1;
-    } else {
-      const int kvh = head < nq + nkv ? head - nq : head - nq - nkv;
-      T* dst = (head < nq + nkv ? kc : vc) + (((long)b * nkv + kvh) * this->max_len + pos) * hd;
+    } else if (head < nq + nkv) {  // key row at position pos
+      T* dst = kc + (((long)b * nkv + head - nq) * this->max_len + pos) * hd;
       dst[u] = W::put(v0);
       dst[u + half] = W::put(v1);
+    } else {  // value channels u and u + hd/2 at position pos (values are stored transposed)
+      T* dst = vc + ((long)b * nkv + head - nq - nkv) * this->max_len * hd + pos;
+      dst[(long)u * this->max_len] = W::put(v0);
+      dst[(long)(u + half) * this->max_len] = W::put(v1);
     }
   }
 };

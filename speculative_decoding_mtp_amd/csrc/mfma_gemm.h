@@ -27,9 +27,6 @@
 
 namespace mtp {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
 constexpr int kMfmaKC = 128;          // K per LDS chunk
 constexpr int kMfmaLdr = kMfmaKC + 8; // padded LDS row (bf16 elements)
 
@@ -42,12 +39,6 @@ struct MfmaBufs {
   int ksplit, cap;      // K ranges; activation rows the partial buffer is laid out for
   long part_cap;        // floats available at part
 };
-
-__device__ __forceinline__ uint16_t bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
-}
 
 // One workgroup per activation index a (grid = nact).
 template <class W, class P>

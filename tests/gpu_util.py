@@ -32,7 +32,7 @@ def upload_weights(cfg: MTPConfig, w) -> M.Weights:
 def kv_from_numpy(cfg: MTPConfig, K: np.ndarray, V: np.ndarray, length: int, max_len: int) -> M.KVCache:
     kv = M.KVCache(config(cfg), K.shape[1], max_len)
     kv.k[:, :, :, :length] = to_dev(K[:, :, :, :length], cfg.wdtype)
-    kv.v[:, :, :, :length] = to_dev(V[:, :, :, :length], cfg.wdtype)
+    kv.v[:, :, :, :, :length] = to_dev(np.swapaxes(V[:, :, :, :length], -1, -2), cfg.wdtype)
     kv.len.fill_(length)
     return kv
 

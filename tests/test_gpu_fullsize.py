@@ -27,7 +27,7 @@ def _round(cfg, seqs, rounds=1):
     w = make_weights(cfg)
     c, gw = config(cfg), upload_weights(cfg, w)
     B, D, H, V = cfg.batch, cfg.D, cfg.hidden, cfg.vocab
-    max_len = cfg.ctx + rounds * (D + 1) + 8
+    max_len = M.round_max_len(cfg.ctx + rounds * (D + 1) + 8)
     K, Vv = make_kv_prefix(cfg)
     kv = kv_from_numpy(cfg, K, Vv, cfg.ctx, max_len)
     model = O.OracleModel(cfg, w)
