@@ -127,7 +127,7 @@ __global__ __launch_bounds__(kWG) void k_prep(P p, MfmaBufs mb) {
 
 // NT weight-row tiles (16 rows each) per wave, MG activation tiles (16 compact rows) per pass.
 template <class P, int NT, int MG>
-__global__ __launch_bounds__(kWG) void k_gemm_mfma(P p, MfmaBufs mb) {
+__global__ __launch_bounds__(kWG, MG <= 2 ? P::kMfmaWaves : 1) void k_gemm_mfma(P p, MfmaBufs mb) {
   using T = uint16_t;
   __shared__ __align__(16) uint16_t sA[2][MG * 16 * kMfmaLdr];  // [hi/lo][row][k]
   __shared__ int s_n[kMaxBatch];
@@ -162,8 +162,11 @@ __global__ __launch_bounds__(kWG) void k_gemm_mfma(P p, MfmaBufs mb) {
       for (int t = 0; t < NT; ++t) wrow[t] = p.wrow(min(n0 + t * 16 + jl, p.N - 1));
       // weights of a chunk: 64 bytes of each of the NT rows of this lane; the next chunk's are
       // requested before this chunk's activations are staged and multiplied
+      // With few activation tiles (MG <= 2) four workgroups fit per compute unit and hide each
+      // other's weight latency; larger MG keeps the next chunk's weights in flight instead.
+      constexpr bool kPrefetch = MG > 2;
       uint4 wv[NT][4], wn[NT][4];
-      if (kc_beg < kc_end) {
+      if (kPrefetch && kc_beg < kc_end) {
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -171,15 +174,22 @@ __global__ __launch_bounds__(kWG) void k_gemm_mfma(P p, MfmaBufs mb) {
       }
       for (int kc = kc_beg; kc < kc_end; ++kc) {
         const int k0 = kc * kMfmaKC;
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-          for (int s = 0; s < 4; ++s) wv[t][s] = wn[t][s];
-        if (kc + 1 < kc_end) {
+        if (kPrefetch) {
 #pragma unroll
           for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int s = 0; s < 4; ++s) wn[t][s] = ld_stream(wrow[t] + k0 + kMfmaKC + 32 * s + 8 * hq);
+            for (int s = 0; s < 4; ++s) wv[t][s] = wn[t][s];
+          if (kc + 1 < kc_end) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+              for (int s = 0; s < 4; ++s) wn[t][s] = ld_stream(wrow[t] + k0 + kMfmaKC + 32 * s + 8 * hq);
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) wv[t][s] = ld_stream(wrow[t] + k0 + 32 * s + 8 * hq);
         }
         // stage the chunk's activations (hi, lo) of this pass in LDS; rows past the pass's
         // count within its last tile are zero
