@@ -93,7 +93,7 @@ struct PQKV : PBase<W> {
   using T = typename W::T;
   static constexpr int kNorm = 1;
   static constexpr bool kPair = true;
-  static constexpr int kMfmaWaves = 3;  // the RoPE epilogue needs the registers
+  static constexpr int kMfmaWaves = 2;  // the RoPE epilogue needs the registers
   const T *g, *wq, *wk, *wv;
   const float* xin;
   int H, nq, nkv, hd;
@@ -302,7 +302,7 @@ constexpr int kMfmaItems = 1024;  // (row group, K range) items a launch aims fo
 
 template <class P, int MG>
 hipError_t launch_mfma(P& p, hipStream_t st, int* grid_used, const MfmaBufs& mb) {
-  constexpr int NT = 2;
+  constexpr int NT = P::kArgmax ? 2 : 1;  // 128 weight rows per workgroup for lm_head, else 64
   MfmaBufs m = mb;
   const int groups = (p.N + 4 * NT * 16 - 1) / (4 * NT * 16);
   int ks = 1;
@@ -335,8 +335,10 @@ hipError_t launch_gemv(P& p, hipStream_t st, int* grid_used = nullptr, const Mfm
     if (use_mfma<W>(p, mb)) {
       hipLaunchKernelGGL((k_prep<W, P>), dim3(p.nact), dim3(kWG), 0, st, p, *mb);
       // activation tiles per pass from the activation count (an upper bound of the valid rows)
+      // (up to 128 rows take 64-row passes: a catch-up's valid rows are usually far fewer
+      // than its padded count)
       if (p.nact <= 32) return launch_mfma<P, 2>(p, st, grid_used, *mb);
-      if (p.nact <= 64) return launch_mfma<P, 4>(p, st, grid_used, *mb);
+      if (p.nact <= 128) return launch_mfma<P, 4>(p, st, grid_used, *mb);
       return launch_mfma<P, 8>(p, st, grid_used, *mb);
     }
   }

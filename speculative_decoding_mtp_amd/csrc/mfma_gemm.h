@@ -129,18 +129,27 @@ __global__ __launch_bounds__(kWG) void k_prep(P p, MfmaBufs mb) {
 template <class P, int NT, int MG>
 __global__ __launch_bounds__(kWG, MG <= 2 ? P::kMfmaWaves : 1) void k_gemm_mfma(P p, MfmaBufs mb) {
   using T = uint16_t;
-  __shared__ __align__(16) uint16_t sA[2][MG * 16 * kMfmaLdr];  // [hi/lo][row][k]
+  constexpr int WR = NT * 16;          // weight rows per wave
+  constexpr int WL = WR / 4;           // weight loads per lane and chunk (four rows per load)
+  constexpr bool DB = MG <= 2;         // double-buffered activation staging
+  constexpr bool RP = MG == 4;         // single buffer, next chunk's activations held in registers
+  constexpr int NB = DB ? 2 : 1;
+  constexpr int AV = 2 * MG * 16 * (kMfmaKC / 8);  // 16-byte activation vectors per chunk (hi + lo)
+  constexpr int PER = (AV + kWG - 1) / kWG;
+  __shared__ __align__(16) uint16_t sA[NB][2][MG * 16 * kMfmaLdr];  // [buffer][hi/lo][row][k]
+  __shared__ __align__(16) uint16_t sW[4][WR * kMfmaLdr];            // each wave's weight tile
   __shared__ int s_n[kMaxBatch];
   __shared__ int s_len[kMaxBatch];
   __shared__ float s_bv[4 * MG * 16];
   __shared__ int s_bi[4 * MG * 16];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int jl = lane & 15, hq = lane >> 4;  // column of the tile, quarter of the wave
+  uint16_t* myW = sW[wid];
   p.setup(s_n, s_len);
   const int count = *mb.count;
   __syncthreads();
   const int Kc = p.K / kMfmaKC;  // K is a multiple of 128 on this path
-  const int rows_per_wg = 4 * NT * 16;
+  const int rows_per_wg = 4 * WR;
   const int ngroups = (p.N + rows_per_wg - 1) / rows_per_wg;
   const int ks = mb.part ? mb.ksplit : 1;           // K ranges per row group
   const int kper = (Kc + ks - 1) / ks;
@@ -148,78 +157,96 @@ __global__ __launch_bounds__(kWG, MG <= 2 ? P::kMfmaWaves : 1) void k_gemm_mfma(
   for (int mg0 = 0; mg0 < count; mg0 += MG * 16) {
     const int mrows = min(MG * 16, count - mg0);
     const int mt = (mrows + 15) / 16;
+    const int srows = mt * 16;                        // staged rows (zero past mrows)
+    const int nav = 2 * srows * (kMfmaKC / 8);        // staged vectors per chunk
+    uint4 st[PER];
+    // the pass's activations of chunk kc: vector idx -> (hi/lo, row, 8-column group)
+    auto aload = [&](int kc) {
+#pragma unroll
+      for (int v = 0; v < PER; ++v) {
+        const int idx = tid + kWG * v;
+        const int half = idx / (srows * (kMfmaKC / 8)), rem = idx - half * (srows * (kMfmaKC / 8));
+        const int r = rem / (kMfmaKC / 8), cv = rem - r * (kMfmaKC / 8);
+        st[v] = (idx < nav && r < mrows)
+                    ? ld16((half ? mb.xlo : mb.xhi) + (long)(mg0 + r) * p.K + kc * kMfmaKC + cv * 8)
+                    : make_uint4(0, 0, 0, 0);
+      }
+    };
+    auto astore = [&](int buf) {
+#pragma unroll
+      for (int v = 0; v < PER; ++v) {
+        const int idx = tid + kWG * v;
+        const int half = idx / (srows * (kMfmaKC / 8)), rem = idx - half * (srows * (kMfmaKC / 8));
+        const int r = rem / (kMfmaKC / 8), cv = rem - r * (kMfmaKC / 8);
+        if (idx < nav) *reinterpret_cast<uint4*>(&sA[buf][half][r * kMfmaLdr + cv * 8]) = st[v];
+      }
+    };
     for (int gk = blockIdx.x; gk < ngroups * ks; gk += gridDim.x) {
       const int g = gk / ks, kpart = gk - g * ks;
       const int kc_beg = kpart * kper, kc_end = min(Kc, kc_beg + kper);
-      const int n0 = g * rows_per_wg + wid * NT * 16;
+      const int n0 = g * rows_per_wg + wid * WR;
       f32x4_t acc[MG][NT];
 #pragma unroll
       for (int m = 0; m < MG; ++m)
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[m][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const T* wrow[NT];
+      // Weights are read row-contiguous: load i of a lane takes 16 bytes at column 8 (l % 16) of
+      // the wave's row 4 i + l / 16, so sixteen lanes read 256 contiguous bytes of one row.  The
+      // wave moves them through its own LDS tile into the MFMA operand layout.
+      const T* wrow[WL];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) wrow[t] = p.wrow(min(n0 + t * 16 + jl, p.N - 1));
-      // weights of a chunk: 64 bytes of each of the NT rows of this lane; the next chunk's are
-      // requested before this chunk's activations are staged and multiplied
-      // With few activation tiles (MG <= 2) four workgroups fit per compute unit and hide each
-      // other's weight latency; larger MG keeps the next chunk's weights in flight instead.
-      constexpr bool kPrefetch = MG > 2;
-      uint4 wv[NT][4], wn[NT][4];
-      if (kPrefetch && kc_beg < kc_end) {
+      for (int i = 0; i < WL; ++i) wrow[i] = p.wrow(min(n0 + 4 * i + hq, p.N - 1)) + 8 * jl;
+      uint4 wn[WL];
+      auto wload = [&](int kc) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-          for (int s = 0; s < 4; ++s) wn[t][s] = ld_stream(wrow[t] + kc_beg * kMfmaKC + 32 * s + 8 * hq);
+        for (int i = 0; i < WL; ++i) wn[i] = ld_stream(wrow[i] + kc * kMfmaKC);
+      };
+      if (kc_beg < kc_end) {
+        __syncthreads();  // the previous item's readers are done with the staging buffers
+        wload(kc_beg);
+        aload(kc_beg);
+        astore(0);
+        __syncthreads();
       }
       for (int kc = kc_beg; kc < kc_end; ++kc) {
-        const int k0 = kc * kMfmaKC;
-        if (kPrefetch) {
+        const int buf = DB ? ((kc - kc_beg) & 1) : 0;
 #pragma unroll
-          for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int s = 0; s < 4; ++s) wv[t][s] = wn[t][s];
-          if (kc + 1 < kc_end) {
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-#pragma unroll
-              for (int s = 0; s < 4; ++s) wn[t][s] = ld_stream(wrow[t] + k0 + kMfmaKC + 32 * s + 8 * hq);
-          }
-        } else {
-#pragma unroll
-          for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int s = 0; s < 4; ++s) wv[t][s] = ld_stream(wrow[t] + k0 + 32 * s + 8 * hq);
+        for (int i = 0; i < WL; ++i)  // this chunk's weights into the wave's tile
+          *reinterpret_cast<uint4*>(&myW[(4 * i + hq) * kMfmaLdr + 8 * jl]) = wn[i];
+        if (!DB && !RP && kc > kc_beg) {  // single buffer: stage this chunk now
+          __syncthreads();
+          aload(kc);
+          astore(0);
+          __syncthreads();
         }
-        // stage the chunk's activations (hi, lo) of this pass in LDS; rows past the pass's
-        // count within its last tile are zero
-        __syncthreads();
-        const int srows = mt * 16;
-        for (int idx = tid; idx < 2 * srows * (kMfmaKC / 8); idx += kWG) {
-          const int half = idx / (srows * (kMfmaKC / 8));
-          const int rem = idx - half * (srows * (kMfmaKC / 8));
-          const int r = rem / (kMfmaKC / 8), cv = rem - r * (kMfmaKC / 8);
-          uint4 v = make_uint4(0, 0, 0, 0);
-          if (r < mrows) v = ld16((half ? mb.xlo : mb.xhi) + (long)(mg0 + r) * p.K + k0 + cv * 8);
-          *reinterpret_cast<uint4*>(&sA[half][r * kMfmaLdr + cv * 8]) = v;
+        if (kc + 1 < kc_end) {  // the next chunk in flight while this one is multiplied
+          wload(kc + 1);
+          if (DB || RP) aload(kc + 1);
         }
-        __syncthreads();
 #pragma unroll
         for (int m = 0; m < MG; ++m) {
           if (m < mt) {
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
               const int kk = 32 * s + 8 * hq;
-              const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(&sA[0][(m * 16 + jl) * kMfmaLdr + kk]);
-              const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(&sA[1][(m * 16 + jl) * kMfmaLdr + kk]);
+              const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(&sA[buf][0][(m * 16 + jl) * kMfmaLdr + kk]);
+              const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(&sA[buf][1][(m * 16 + jl) * kMfmaLdr + kk]);
 #pragma unroll
               for (int t = 0; t < NT; ++t) {
-                const bf16x8_t bw = __builtin_bit_cast(bf16x8_t, wv[t][s]);
+                const bf16x8_t bw = *reinterpret_cast<const bf16x8_t*>(&myW[(t * 16 + jl) * kMfmaLdr + kk]);
                 acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bw, acc[m][t], 0, 0, 0);
                 acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bw, acc[m][t], 0, 0, 0);
               }
             }
           }
+        }
+        if (DB) {
+          if (kc + 1 < kc_end) astore(buf ^ 1);
+          __syncthreads();
+        } else if (RP && kc + 1 < kc_end) {
+          __syncthreads();  // every wave is done with this chunk's activations
+          astore(0);
+          __syncthreads();
         }
       }
       if (mb.part) {  // split-K: raw partial sums, reduced and stored by k_splitk_reduce
