@@ -12,7 +12,9 @@ logits = draft logits + N(0, 0.5).
 
 Prints one JSON line: accepted tokens/s (sum over rounds and sequences of accepted drafts + 1,
 divided by the timed wall time), the lm_head kernel's HBM roofline and the CPU oracle timed on
-a bounded sample of the same workload.
+a bounded sample of the same workload.  --config names another head workload (drafter4: the
+4-layer 1024-hidden drafter with sampling verification; dsv3: the 7168-hidden head at batch 32)
+or, with --config stress, the verifier alone (B=256, D=4, vocab 151936, sampling).
 """
 import argparse
 import hashlib
@@ -55,6 +57,9 @@ def main():
         make_round_uniforms, make_state, make_weights
     from tests.gpu_util import config, f32, i32, kv_from_numpy, upload_weights
 
+    from synth import VERIFY_CONFIGS
+    if args.config in VERIFY_CONFIGS:
+        return bench_verify(args, VERIFY_CONFIGS[args.config])
     cfg = CONFIGS[args.config]
     B, D, H, V = cfg.batch, cfg.D, cfg.hidden, cfg.vocab
     state_bytes = cfg.state_bytes_per_seq if args.state_bytes is None else args.state_bytes
@@ -207,6 +212,64 @@ def main():
                      "traffic": traffic, "bytes_per_launch": lm_bytes,
                      "avg_launch_us": round(lm_avg_s * 1e6, 2), "launches": lm_n},
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_verify(args, vc, sigma=1.0):
+    """The verifier on its own (--config stress): spec_verify over B sequences of D drafts with
+    fp32 target logits resident in HBM, sampling with the workload's settings (q_mode 0, greedy
+    drafts = argmax of the draft logits).  Reports verified sequences/s and the logits scan rate."""
+    import torch
+    import speculative_decoding_mtp_amd as M
+    from synth import gen, make_verify_inputs
+    from tests.gpu_util import f32, i32
+
+    B, D, V, sp = vc.batch, vc.D, vc.vocab, vc.sampling
+    dl, tl_np, ctx_np = make_verify_inputs(vc, sigma)
+    drafts = i32(np.argmax(dl, axis=-1))
+    del dl
+    g = gen(vc.index, 6, int(sigma * 10))
+    ua, us = f32(g.random((B, D), dtype=np.float32)), f32(g.random(B, dtype=np.float32))
+    tl, ctx = f32(tl_np), i32(ctx_np)
+    del tl_np
+    csp = M.sampling(sp.temperature, sp.top_k, sp.top_p, sp.q_mode)
+    vws = M.new_workspace(M.spec_verify_workspace_size(B, D, V, csp))
+    n_acc = torch.zeros(B, dtype=torch.int32, device="cuda")
+    out = torch.zeros(B, D + 1, dtype=torch.int32, device="cuda")
+    crop = torch.zeros(B, dtype=torch.int32, device="cuda")
+
+    def step():
+        M.spec_verify(B, D, V, tl, drafts, None, csp, ua, us, ctx, n_acc, out, crop, vws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    M.mtp_timer_start(M.MTP_KERNEL_VERIFY, args.steps)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    v_ms, v_n = M.mtp_timer_read(M.MTP_KERNEL_VERIFY)
+    logits_bytes = B * (D + 1) * V * 4
+    achieved = logits_bytes / (v_ms / v_n * 1e-3) / 1e9
+    line = {
+        "metric": "spec_verify sequences/s; target-logits scan HBM GB/s vs MI355X peak",
+        "value": round(B * args.steps / wall, 1), "unit": "verified sequences/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded draft logits N(0,3), target = draft + N(0,1), uniforms)",
+        "config": {"workload": vc.name, "batch": B, "draft_tokens": D, "vocab": V,
+                   "verify": f"sampling T={sp.temperature} top_k={sp.top_k} top_p={sp.top_p} q_mode={sp.q_mode}",
+                   "target_noise_std": sigma},
+        "acceptance": round(float(n_acc.float().mean()) / D, 4),
+        "roofline": {"bound": "hbm", "kernel": "spec_verify (top-k scan, merge, decide)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": logits_bytes, "avg_launch_us": round(v_ms / v_n * 1e3, 2),
+                     "launches": v_n},
+        "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
 

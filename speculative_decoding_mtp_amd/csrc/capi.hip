@@ -300,8 +300,7 @@ int spec_verify_workspace_size(int32_t B, int32_t D, int32_t V, const mtp_sampli
   } else {
     const int K = sp->top_k;
     if (K < 1 || K > kMaxTopK) return fail(MTP_ERR_ARG, "top_k must be in [1, %d]", kMaxTopK);
-    const size_t nchunk = (V + kChunk - 1) / kChunk;
-    t += 2 * up256(rows * nchunk * K * 4) + 2 * up256(rows * K * 4) + up256(rows * 4);
+    t += 2 * up256(rows * K * 4) + up256(rows * 4);
   }
   *bytes = t;
   return MTP_OK;
@@ -355,15 +354,6 @@ int spec_verify(int32_t B, int32_t D, int32_t V, const float* target_logits, con
     a.dl = draft_logits;
     a.u_accept = u_accept;
     a.u_sample = u_sample;
-    a.chunk = kChunk;
-    a.nchunk = (V + kChunk - 1) / kChunk;
-    if ((long)a.nchunk * K > kTopCap)
-      return fail(MTP_ERR_ARG, "vocab %d with top_k %d exceeds the merge capacity %d", V, K, kTopCap);
-    const size_t cand = (size_t)rows * a.nchunk * K * 4;
-    a.cand_v = reinterpret_cast<float*>(base + o);
-    o += up256(cand);
-    a.cand_i = reinterpret_cast<int*>(base + o);
-    o += up256(cand);
     a.top_v = reinterpret_cast<float*>(base + o);
     o += up256((size_t)rows * K * 4);
     a.top_i = reinterpret_cast<int*>(base + o);

@@ -30,7 +30,6 @@ struct PBase {
   using T = typename W::T;
   static constexpr bool kPair = false;
   static constexpr bool kArgmax = false;
-  static constexpr int kMfmaWaves = 4;  // waves per SIMD the small-MG MFMA GEMM is compiled for
   const int32_t* tok;
   int tok_sb;
   int B, rps;
@@ -93,7 +92,6 @@ struct PQKV : PBase<W> {
   using T = typename W::T;
   static constexpr int kNorm = 1;
   static constexpr bool kPair = true;
-  static constexpr int kMfmaWaves = 2;  // the RoPE epilogue needs the registers
   const T *g, *wq, *wk, *wv;
   const float* xin;
   int H, nq, nkv, hd;

@@ -127,7 +127,7 @@ __global__ __launch_bounds__(kWG) void k_prep(P p, MfmaBufs mb) {
 
 // NT weight-row tiles (16 rows each) per wave, MG activation tiles (16 compact rows) per pass.
 template <class P, int NT, int MG>
-__global__ __launch_bounds__(kWG, MG <= 2 ? P::kMfmaWaves : 1) void k_gemm_mfma(P p, MfmaBufs mb) {
+__global__ __launch_bounds__(kWG, MG <= 4 ? 2 : 1) void k_gemm_mfma(P p, MfmaBufs mb) {
   using T = uint16_t;
   constexpr int WR = NT * 16;          // weight rows per wave
   constexpr int WL = WR / 4;           // weight loads per lane and chunk (four rows per load)

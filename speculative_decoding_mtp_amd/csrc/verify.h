@@ -6,8 +6,8 @@
 
 namespace mtp {
 
-constexpr int kChunk = 4096;    // logits per workgroup in the sampling top-k pass
-constexpr int kTopCap = 8192;   // candidates one workgroup can merge (chunks * top_k)
+constexpr int kTopCap = 8192;   // LDS candidate buffer of the sampling top-k pass
+constexpr int kTopSmall = 1024; // second-level candidates ranked by counting
 constexpr int kMaxTopK = 128;   // largest top_k on the device path
 constexpr int kMaxDraft = 63;   // largest D on the device path
 
@@ -26,8 +26,6 @@ struct VerifyArgs {
   float* part_v;
   int* part_i;
   // sampling scratch
-  float* cand_v;  // [rows][nchunk][top_k]
-  int* cand_i;
   float* top_v;  // [rows][top_k]
   int* top_i;
   int* top_n;  // [rows]

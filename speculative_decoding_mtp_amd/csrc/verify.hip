@@ -111,13 +111,14 @@ __global__ __launch_bounds__(kWG) void k_verify_greedy_final(VerifyArgs a) {
 // ---------------------------------------------------------------------------------------------
 // sampling: top-k selection
 // ---------------------------------------------------------------------------------------------
-// LDS sized for the largest selection (kTopCap candidates) plus a 256-entry bitonic buffer.
+// LDS of the top-k pass: the candidate buffer and the per-thread maxima.
 struct TopkSmem {
   float v[kTopCap];
   int i[kTopCap];
   float tm[kWG];
-  int cnt;
-  int flag;
+  float v2[kTopSmall];  // second-level candidates of the final selection
+  int i2[kTopSmall];
+  int cnt, cnt2;
 };
 
 // bitonic sort of n (power of two <= kTopCap) (v, i) pairs in LDS, best first
@@ -161,51 +162,6 @@ __device__ void bitonic_sort_desc(float* v) {
       __syncthreads();
     }
   }
-}
-
-// Top K (value desc, id asc) of the items held by the workgroup (IPT per thread; id < 0 marks
-// an empty slot).  A lower bound on the K-th best value is the K-th best of the per-thread
-// maxima (K threads each hold an item at least that large); only items at or above it are
-// sorted.  Writes min(K, items) entries to out_v/out_i and returns that count (all threads).
-template <int IPT>
-__device__ int wg_topk(const float (&v)[IPT], const int (&id)[IPT], int K, TopkSmem& sm, float* out_v, int* out_i) {
-  float tmax = -INFINITY;
-  bool have = false;
-#pragma unroll
-  for (int e = 0; e < IPT; ++e)
-    if (id[e] >= 0) {
-      tmax = have ? fmaxf(tmax, v[e]) : v[e];
-      have = true;
-    }
-  sm.tm[threadIdx.x] = have ? tmax : -INFINITY;
-  if (threadIdx.x == 0) sm.cnt = 0;
-  __syncthreads();
-  bitonic_sort_desc(sm.tm);
-  const float lb = sm.tm[K - 1];
-#pragma unroll
-  for (int e = 0; e < IPT; ++e)
-    if (id[e] >= 0 && v[e] >= lb) {
-      const int pos = atomicAdd(&sm.cnt, 1);
-      sm.v[pos] = v[e];
-      sm.i[pos] = id[e];
-    }
-  __syncthreads();
-  const int S = sm.cnt;
-  int n2 = 1;
-  while (n2 < S) n2 <<= 1;
-  for (int t = S + threadIdx.x; t < n2; t += kWG) {
-    sm.v[t] = -INFINITY;
-    sm.i[t] = 0x7fffffff;
-  }
-  __syncthreads();
-  bitonic_sort_pairs(sm.v, sm.i, n2);
-  const int n = min(K, S);
-  for (int t = threadIdx.x; t < n; t += kWG) {
-    out_v[t] = sm.v[t];
-    out_i[t] = sm.i[t];
-  }
-  __syncthreads();
-  return n;
 }
 
 // Warped distribution of one row from its sorted top-k candidates: probabilities of the kept
@@ -269,52 +225,142 @@ __device__ int draw_ascending(int* ids, float* w, int m, float u) {
   return last;  // u * S rounded onto S
 }
 
-__global__ __launch_bounds__(kWG) void k_topk_chunks(VerifyArgs a) {
-  __shared__ TopkSmem sm;
-  const int c = blockIdx.x, row = blockIdx.y;
-  const int K = a.top_k;
-  const int tgt_rows = a.B * (a.D + 1);
-  const float* x = row < tgt_rows ? a.tl + (long)row * a.V : a.dl + (long)(row - tgt_rows) * a.V;
-  {  // chunk candidates
-    constexpr int IPT = kChunk / kWG;
-    float v[IPT];
-    int id[IPT];
-    const int beg = c * kChunk;
+// One workgroup per row streams the row once.  Items at or above a threshold are appended to an
+// LDS candidate buffer; the threshold starts as the K-th largest of the per-thread maxima of the
+// first tile (K threads hold an item at least that large, so it never exceeds the row's K-th
+// best) and rises to the K-th best candidate whenever the buffer has to be compacted.  At the
+// end the candidates are sorted (value desc, id asc) and the first K written.
+constexpr int kTile = kWG * 16;  // items per tile: four float4 per thread
+
+// Item e of tile `base` for thread t: ids base + 4 (t + kWG q) + r, e = 4 q + r.
+__device__ __forceinline__ void load_tile(const float* x, int V, int base, bool vec, float (&v)[16]) {
 #pragma unroll
-    for (int e = 0; e < IPT; ++e) {
-      const int k = beg + threadIdx.x + e * kWG;
-      id[e] = k < a.V ? k : -1;
-      v[e] = k < a.V ? x[k] : -INFINITY;
-    }
-    float* ov = a.cand_v + ((long)row * a.nchunk + c) * K;
-    int* oi = a.cand_i + ((long)row * a.nchunk + c) * K;
-    const int n = wg_topk<IPT>(v, id, K, sm, ov, oi);
-    for (int t = n + threadIdx.x; t < K; t += kWG) {
-      ov[t] = -INFINITY;
-      oi[t] = -1;
+  for (int q = 0; q < 4; ++q) {
+    const int k0 = base + 4 * (threadIdx.x + kWG * q);
+    if (vec && k0 + 3 < V) {
+      const float4 f = *reinterpret_cast<const float4*>(x + k0);
+      v[4 * q] = f.x;
+      v[4 * q + 1] = f.y;
+      v[4 * q + 2] = f.z;
+      v[4 * q + 3] = f.w;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[4 * q + r] = k0 + r < V ? x[k0 + r] : -INFINITY;
     }
   }
 }
 
-// one workgroup per row: the top-k of the row from its chunks' candidates
-__global__ __launch_bounds__(kWG) void k_topk_rows(VerifyArgs a) {
-  __shared__ TopkSmem sm;
-  const int row = blockIdx.x;
-  const int K = a.top_k;
-  {  // merge the row's candidates
-    constexpr int IPT = kTopCap / kWG;
-    float v[IPT];
-    int id[IPT];
-    const int total = a.nchunk * K;
-#pragma unroll
-    for (int e = 0; e < IPT; ++e) {
-      const int k = threadIdx.x + e * kWG;
-      v[e] = k < total ? a.cand_v[(long)row * a.nchunk * K + k] : -INFINITY;
-      id[e] = k < total ? a.cand_i[(long)row * a.nchunk * K + k] : -1;
-    }
-    const int n = wg_topk<IPT>(v, id, K, sm, a.top_v + (long)row * K, a.top_i + (long)row * K);
-    if (threadIdx.x == 0) a.top_n[row] = n;
+// Sort the S buffered candidates (padded to a power of two) best first; keeps the first `keep`.
+__device__ int sort_candidates(TopkSmem& sm, int S, int keep) {
+  int n2 = 1;
+  while (n2 < S) n2 <<= 1;
+  for (int t = S + threadIdx.x; t < n2; t += kWG) {
+    sm.v[t] = -INFINITY;
+    sm.i[t] = 0x7fffffff;
   }
+  __syncthreads();
+  bitonic_sort_pairs(sm.v, sm.i, n2);
+  return min(keep, S);
+}
+
+__global__ __launch_bounds__(kWG) void k_topk_stream(VerifyArgs a) {
+  __shared__ TopkSmem sm;
+  const int row = blockIdx.x, K = a.top_k, V = a.V;
+  const int tgt_rows = a.B * (a.D + 1);
+  const float* x = row < tgt_rows ? a.tl + (long)row * V : a.dl + (long)(row - tgt_rows) * V;
+  const bool vec = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
+  float cur[16], nxt[16];
+  load_tile(x, V, 0, vec, cur);
+  {  // threshold from the first tile
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, cur[e]);
+    sm.tm[threadIdx.x] = tmax;
+    if (threadIdx.x == 0) sm.cnt = 0;
+    __syncthreads();
+    bitonic_sort_desc(sm.tm);
+  }
+  float theta = sm.tm[K - 1];
+  // Append the tile's items at or above the threshold, then compact if the next tile might not
+  // fit in the buffer.  Tiles alternate between two register buffers, so the next tile's loads
+  // stay in flight while this one is filtered.
+  auto filter = [&](const float (&v)[16], int base) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int k = base + 4 * (threadIdx.x + kWG * (e >> 2)) + (e & 3);
+      if (k < V && v[e] >= theta) {
+        const int pos = atomicAdd(&sm.cnt, 1);
+        sm.v[pos] = v[e];
+        sm.i[pos] = k;
+      }
+    }
+    __syncthreads();
+    const int S = sm.cnt;
+    __syncthreads();  // every thread has read the count before the next tile appends
+    if (S > kTopCap - kTile && base + kTile < V) {
+      const int n = sort_candidates(sm, S, K);
+      if (n == K) theta = sm.v[K - 1];
+      __syncthreads();
+      if (threadIdx.x == 0) sm.cnt = n;
+      __syncthreads();
+    }
+  };
+  for (int base = 0; base < V; base += 2 * kTile) {
+    if (base + kTile < V) load_tile(x, V, base + kTile, vec, nxt);
+    filter(cur, base);
+    if (base + kTile >= V) break;
+    if (base + 2 * kTile < V) load_tile(x, V, base + 2 * kTile, vec, cur);
+    filter(nxt, base + kTile);
+  }
+  // Final selection.  The K-th largest of the per-thread maxima over the S candidates bounds
+  // the K-th best from below again; the few candidates at or above it are ranked by counting
+  // (rank = candidates ranked before it, value desc, id asc) straight into their output slots.
+  // If too many remain (ties), the whole buffer is sorted instead.
+  const int S = sm.cnt;
+  float* ov = a.top_v + (long)row * K;
+  int* oi = a.top_i + (long)row * K;
+  float tmax = -INFINITY;
+  for (int c = threadIdx.x; c < S; c += kWG) tmax = fmaxf(tmax, sm.v[c]);
+  sm.tm[threadIdx.x] = tmax;
+  if (threadIdx.x == 0) sm.cnt2 = 0;
+  __syncthreads();
+  bitonic_sort_desc(sm.tm);
+  const float theta2 = sm.tm[K - 1];
+  for (int c = threadIdx.x; c < S; c += kWG)
+    if (sm.v[c] >= theta2) {
+      const int pos = atomicAdd(&sm.cnt2, 1);
+      if (pos < kTopSmall) {
+        sm.v2[pos] = sm.v[c];
+        sm.i2[pos] = sm.i[c];
+      }
+    }
+  __syncthreads();
+  const int S2 = sm.cnt2;
+  int n;
+  if (S2 <= kTopSmall) {
+    n = min(K, S2);
+    for (int c = threadIdx.x; c < S2; c += kWG) {
+      const float cv = sm.v2[c];
+      const int ci = sm.i2[c];
+      int r = 0;
+      for (int d = 0; d < S2; ++d) r += better(sm.v2[d], sm.i2[d], cv, ci) ? 1 : 0;
+      if (r < K) {
+        ov[r] = cv;
+        oi[r] = ci;
+      }
+    }
+  } else {
+    n = sort_candidates(sm, S, K);
+    for (int t = threadIdx.x; t < n; t += kWG) {
+      ov[t] = sm.v[t];
+      oi[t] = sm.i[t];
+    }
+  }
+  for (int t = n + threadIdx.x; t < K; t += kWG) {
+    ov[t] = -INFINITY;
+    oi[t] = -1;
+  }
+  if (threadIdx.x == 0) a.top_n[row] = n;
 }
 
 // one workgroup per sequence (one thread does the work): accept / reject / draw
@@ -387,8 +433,7 @@ hipError_t run_verify(const VerifyArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(k_verify_greedy_final, dim3(a.B), dim3(kWG), 0, st, a);
   } else {
     const int rows = a.B * (a.D + 1) + (a.q_mode == 1 ? a.B * a.D : 0);
-    hipLaunchKernelGGL(k_topk_chunks, dim3(a.nchunk, rows), dim3(kWG), 0, st, a);
-    hipLaunchKernelGGL(k_topk_rows, dim3(rows), dim3(kWG), 0, st, a);
+    hipLaunchKernelGGL(k_topk_stream, dim3(rows), dim3(kWG), 0, st, a);
     hipLaunchKernelGGL(k_sample_decide, dim3(a.B), dim3(64), 0, st, a);
   }
   return hipGetLastError();
