@@ -6,8 +6,8 @@
 
 namespace mtp {
 
-constexpr int kTopCap = 8192;   // LDS candidate buffer of the sampling top-k pass
-constexpr int kTopSmall = 1024; // second-level candidates ranked by counting
+constexpr int kTopCap = 2048;   // LDS candidate buffer of the sampling top-k pass
+constexpr int kTopSmall = 512;  // second-level candidates ranked by counting
 constexpr int kMaxTopK = 128;   // largest top_k on the device path
 constexpr int kMaxDraft = 63;   // largest D on the device path
 

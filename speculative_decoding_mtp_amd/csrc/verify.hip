@@ -164,65 +164,104 @@ __device__ void bitonic_sort_desc(float* v) {
   }
 }
 
-// Warped distribution of one row from its sorted top-k candidates: probabilities of the kept
-// prefix (temperature softmax over the k candidates, then top-p: a candidate stays while the
-// mass ranked before it is below p; the first always stays), renormalised.  Runs on one thread.
-__device__ int warp_row(const float* tv, int n, float T, float top_p, float* prob) {
-  float S = 0.f;
-  for (int k = 0; k < n; ++k) {
-    prob[k] = expf((tv[k] - tv[0]) / T);
-    S += prob[k];
+// ---- wave-parallel pieces of the decision (one wave per sequence; candidate k of a row sits in
+// lane k % 64, slot k / 64, so K <= 128 takes two slots per lane)
+
+__device__ __forceinline__ float wave_incl_scan(float v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
   }
+  return v;
+}
+
+// A row's warped distribution from its sorted top-k candidates (value desc): temperature
+// softmax over the n candidates, then top-p (a candidate stays while the mass ranked before it
+// is below p; the first always stays), renormalised.  p[s] is candidate 64 s + lane's
+// probability (0 outside the kept prefix); returns the kept count m.
+__device__ int warp_row_wave(const float* tv, const int n, float T, float top_p, float (&p)[2]) {
+  const int lane = threadIdx.x & 63;
+  const float t0 = tv[0];
+  float e[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int k = 64 * s + lane;
+    e[s] = k < n ? expf((tv[k] - t0) / T) : 0.f;
+  }
+  const float c0 = wave_incl_scan(e[0]);
+  const float tot0 = __shfl(c0, 63, 64);
+  const float c1 = wave_incl_scan(e[1]) + tot0;
+  const float S = __shfl(c1, 63, 64);
   int m = n;
   if (top_p < 1.f) {
-    float before = 0.f;
-    m = 0;
-    for (int k = 0; k < n; ++k) {
-      const float pk = prob[k] / S;
-      if (k > 0 && !(before < top_p)) break;
-      before += pk;
-      ++m;
+    const float before[2] = {c0 - e[0], c1 - e[1]};
+    int kept = 0;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int k = 64 * s + lane;
+      kept += (k < n && (k == 0 || before[s] / S < top_p)) ? 1 : 0;
     }
+    m = (int)wave_sum((float)kept);
   }
-  float Z = 0.f;
-  for (int k = 0; k < m; ++k) Z += prob[k];
-  for (int k = 0; k < m; ++k) prob[k] = prob[k] / Z;
+  float z = 0.f;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) z += (64 * s + lane < m) ? e[s] : 0.f;
+  const float Z = wave_sum(z);
+#pragma unroll
+  for (int s = 0; s < 2; ++s) p[s] = (64 * s + lane < m) ? e[s] / Z : 0.f;
   return m;
 }
 
-__device__ float lookup(const int* ids, const float* prob, int m, int tok) {
-  for (int k = 0; k < m; ++k)
-    if (ids[k] == tok) return prob[k];
-  return 0.f;
-}
-
-// Inverse-CDF draw over (id, weight) pairs in ascending id order: the smallest id whose
-// cumulative weight exceeds u * total.  Sorts the pairs by id in place.
-__device__ int draw_ascending(int* ids, float* w, int m, float u) {
-  for (int a = 1; a < m; ++a) {  // insertion sort by id (m <= 128)
-    const int ki = ids[a];
-    const float kw = w[a];
-    int b = a - 1;
-    while (b >= 0 && ids[b] > ki) {
-      ids[b + 1] = ids[b];
-      w[b + 1] = w[b];
-      --b;
+// Inverse-CDF draw over the weights w of ids (candidate slots as above, m of them) in ascending
+// id order: the smallest id whose cumulative weight exceeds u * total; weights <= 0 are never
+// drawn (if u * total rounds onto the total, the last positive one is).  sw/si: LDS, 128 each.
+__device__ int draw_ascending_wave(const int (&id)[2], const float (&w)[2], int m, float u, float* sw, int* si) {
+  const int lane = threadIdx.x & 63;
+  // rank of each candidate by id among the m (ids are distinct)
+  int r[2] = {0, 0};
+#pragma unroll
+  for (int s = 0; s < 2; ++s) si[64 * s + lane] = id[s];
+  __syncthreads();
+  for (int j = 0; j < m; ++j) {
+    const int o = si[j];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) r[s] += o < id[s] ? 1 : 0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+    if (64 * s + lane < m) {
+      sw[r[s]] = w[s] > 0.f ? w[s] : 0.f;
+      si[r[s]] = id[s];
     }
-    ids[b + 1] = ki;
-    w[b + 1] = kw;
-  }
-  float S = 0.f;
-  for (int k = 0; k < m; ++k) S += w[k];
+  __syncthreads();
+  float x[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) x[s] = 64 * s + lane < m ? sw[64 * s + lane] : 0.f;
+  const float c0 = wave_incl_scan(x[0]);
+  const float tot0 = __shfl(c0, 63, 64);
+  const float c1 = wave_incl_scan(x[1]) + tot0;
+  const float S = __shfl(c1, 63, 64);
   const float t = u * S;
-  float c = 0.f;
-  int last = -1;
-  for (int k = 0; k < m; ++k) {
-    if (w[k] <= 0.f) continue;
-    c += w[k];
-    last = ids[k];
-    if (c > t) return ids[k];
+  const unsigned long long hit0 = __ballot(x[0] > 0.f && c0 > t);
+  const unsigned long long hit1 = __ballot(x[1] > 0.f && c1 > t);
+  int pos = -1;
+  if (hit0)
+    pos = __ffsll((long long)hit0) - 1;
+  else if (hit1)
+    pos = 64 + __ffsll((long long)hit1) - 1;
+  else {  // the last positive weight
+    const unsigned long long pz0 = __ballot(x[0] > 0.f), pz1 = __ballot(x[1] > 0.f);
+    if (pz1)
+      pos = 64 + 63 - __clzll((long long)pz1);
+    else if (pz0)
+      pos = 63 - __clzll((long long)pz0);
   }
-  return last;  // u * S rounded onto S
+  const int tok = pos >= 0 ? si[pos] : -1;
+  __syncthreads();
+  return tok;
 }
 
 // One workgroup per row streams the row once.  Items at or above a threshold are appended to an
@@ -231,6 +270,9 @@ __device__ int draw_ascending(int* ids, float* w, int m, float u) {
 // best) and rises to the K-th best candidate whenever the buffer has to be compacted.  At the
 // end the candidates are sorted (value desc, id asc) and the first K written.
 constexpr int kTile = kWG * 16;  // items per tile: four float4 per thread
+static_assert(kTopCap >= kMaxTopK + kTile / 4, "the slow pass appends a quarter tile after a compaction");
+static_assert((kTopCap & (kTopCap - 1)) == 0, "the candidate sort pads to a power of two");
+static_assert(kMaxTopK <= 128, "the decision keeps two candidates per lane");
 
 // Item e of tile `base` for thread t: ids base + 4 (t + kWG q) + r, e = 4 q + r.
 __device__ __forceinline__ void load_tile(const float* x, int V, int base, bool vec, float (&v)[16]) {
@@ -271,46 +313,78 @@ __global__ __launch_bounds__(kWG) void k_topk_stream(VerifyArgs a) {
   const bool vec = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
   float cur[16], nxt[16];
   load_tile(x, V, 0, vec, cur);
-  {  // threshold from the first tile
-    float tmax = -INFINITY;
+  float rmax = -INFINITY;  // this thread's running maximum
 #pragma unroll
-    for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, cur[e]);
-    sm.tm[threadIdx.x] = tmax;
-    if (threadIdx.x == 0) sm.cnt = 0;
+  for (int e = 0; e < 16; ++e) rmax = fmaxf(rmax, cur[e]);
+  // K-th largest of the per-thread maxima: K distinct items are at least this large
+  auto bound = [&]() {
+    sm.tm[threadIdx.x] = rmax;
     __syncthreads();
     bitonic_sort_desc(sm.tm);
-  }
-  float theta = sm.tm[K - 1];
-  // Append the tile's items at or above the threshold, then compact if the next tile might not
-  // fit in the buffer.  Tiles alternate between two register buffers, so the next tile's loads
-  // stay in flight while this one is filtered.
-  auto filter = [&](const float (&v)[16], int base) {
+    const float b = sm.tm[K - 1];
+    __syncthreads();
+    return b;
+  };
+  if (threadIdx.x == 0) sm.cnt = 0;
+  float theta = bound();
+  // Fast pass: no barriers while streaming (the threshold is raised once, after four tiles);
+  // appends past the buffer are counted, not stored, and send the row to the slow pass.
+  auto append = [&](const float (&v)[16], int base) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int k = base + 4 * (threadIdx.x + kWG * (e >> 2)) + (e & 3);
-      if (k < V && v[e] >= theta) {
-        const int pos = atomicAdd(&sm.cnt, 1);
-        sm.v[pos] = v[e];
-        sm.i[pos] = k;
+      if (k < V) {
+        rmax = fmaxf(rmax, v[e]);
+        if (v[e] >= theta) {
+          const int pos = atomicAdd(&sm.cnt, 1);
+          if (pos < kTopCap) {
+            sm.v[pos] = v[e];
+            sm.i[pos] = k;
+          }
+        }
       }
-    }
-    __syncthreads();
-    const int S = sm.cnt;
-    __syncthreads();  // every thread has read the count before the next tile appends
-    if (S > kTopCap - kTile && base + kTile < V) {
-      const int n = sort_candidates(sm, S, K);
-      if (n == K) theta = sm.v[K - 1];
-      __syncthreads();
-      if (threadIdx.x == 0) sm.cnt = n;
-      __syncthreads();
     }
   };
   for (int base = 0; base < V; base += 2 * kTile) {
-    if (base + kTile < V) load_tile(x, V, base + kTile, vec, nxt);
-    filter(cur, base);
+    if (base + kTile < V) load_tile(x, V, base + kTile, vec, nxt);  // in flight meanwhile
+    append(cur, base);
     if (base + kTile >= V) break;
     if (base + 2 * kTile < V) load_tile(x, V, base + 2 * kTile, vec, cur);
-    filter(nxt, base + kTile);
+    append(nxt, base + kTile);
+    if (base == 2 * kTile && base + 2 * kTile < V) theta = fmaxf(theta, bound());
+  }
+  __syncthreads();
+  if (sm.cnt > kTopCap) {
+    // Slow pass (the threshold let too many items through, e.g. heavy ties): stream the row
+    // again, compacting the buffer to its top K whenever the next tile might not fit.
+    __syncthreads();
+    if (threadIdx.x == 0) sm.cnt = 0;
+    __syncthreads();
+    for (int base = 0; base < V; base += kTile) {
+      load_tile(x, V, base, vec, cur);
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {  // a quarter tile (at most kTile / 4 appends) at a time
+#pragma unroll
+        for (int e = 4 * h; e < 4 * h + 4; ++e) {
+          const int k = base + 4 * (threadIdx.x + kWG * (e >> 2)) + (e & 3);
+          if (k < V && cur[e] >= theta) {
+            const int pos = atomicAdd(&sm.cnt, 1);
+            sm.v[pos] = cur[e];
+            sm.i[pos] = k;
+          }
+        }
+        __syncthreads();
+        const int S = sm.cnt;
+        __syncthreads();
+        if (S > kTopCap - kTile / 4) {
+          const int n = sort_candidates(sm, S, K);
+          if (n == K) theta = sm.v[K - 1];
+          __syncthreads();
+          if (threadIdx.x == 0) sm.cnt = n;
+          __syncthreads();
+        }
+      }
+    }
   }
   // Final selection.  The K-th largest of the per-thread maxima over the S candidates bounds
   // the K-th best from below again; the few candidates at or above it are ranked by counting
@@ -363,68 +437,84 @@ __global__ __launch_bounds__(kWG) void k_topk_stream(VerifyArgs a) {
   if (threadIdx.x == 0) a.top_n[row] = n;
 }
 
-// one workgroup per sequence (one thread does the work): accept / reject / draw
+// One wave per sequence: accept / reject / draw ([P2 "Speculative sampling"], [P3 rejection
+// sampler]).  P_j = warp(target row j); Q_j = one-hot at the draft (q_mode 0) or warp(draft row
+// j) (q_mode 1).  Draft j is accepted iff P_j(d) > 0 and U_j <= P_j(d) / Q_j(d); at the first
+// rejection a token is drawn from normalize(max(0, P_j - Q_j)) (P_j if that is all zero), and
+// if every draft holds, from P_D.
 __global__ __launch_bounds__(64) void k_sample_decide(VerifyArgs a) {
-  const int b = blockIdx.x;
+  __shared__ float sw[kMaxTopK], sq[kMaxTopK];
+  __shared__ int si[kMaxTopK], sqi[kMaxTopK];
+  const int b = blockIdx.x, lane = threadIdx.x;
   const int K = a.top_k;
   const int tgt_rows = a.B * (a.D + 1);
-  __shared__ float P[kMaxTopK], Q[kMaxTopK], w[kMaxTopK];  // probabilities, draft probs, residual
-  __shared__ int ids[kMaxTopK];
-  if (threadIdx.x != 0) return;
-  // ---- the sequence's decision, one thread, working in LDS ----
   const float T = a.temperature;
-  int32_t* out = a.out + (long)b * (a.D + 1);
-  int n_acc = 0;
-  int tok = -1;
-  for (int j = 0; j < a.D; ++j) {
-    const int tr = b * (a.D + 1) + j;
-    const float* tv = a.top_v + (long)tr * K;
-    const int* ti = a.top_i + (long)tr * K;
-    const int mP = warp_row(tv, a.top_n[tr], T, a.top_p, P);
+  int n_acc = 0, tok = -1;
+  float P[2];
+  int id[2];
+  auto load_row = [&](int r, float (&p)[2], int (&ids)[2]) {
+    const int m = warp_row_wave(a.top_v + (long)r * K, a.top_n[r], T, a.top_p, p);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int k = 64 * s + lane;
+      ids[s] = k < m ? a.top_i[(long)r * K + k] : -1;
+    }
+    return m;
+  };
+  for (int j = 0; j < a.D && tok < 0; ++j) {
+    const int mP = load_row(b * (a.D + 1) + j, P, id);
     const int d = a.drafts[(long)b * a.D + j];
-    const float Pd = lookup(ti, P, mP, d);
+    const float Pd = wave_sum((id[0] == d ? P[0] : 0.f) + (id[1] == d ? P[1] : 0.f));
     float Qd = 1.f;
     int mQ = 0;
-    const int* qi = nullptr;
     if (a.q_mode == 1) {
-      const int dr = tgt_rows + b * a.D + j;
-      qi = a.top_i + (long)dr * K;
-      mQ = warp_row(a.top_v + (long)dr * K, a.top_n[dr], T, a.top_p, Q);
-      Qd = lookup(qi, Q, mQ, d);
+      float Qp[2];
+      int qid[2];
+      mQ = load_row(tgt_rows + b * a.D + j, Qp, qid);
+      Qd = wave_sum((qid[0] == d ? Qp[0] : 0.f) + (qid[1] == d ? Qp[1] : 0.f));
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        sq[64 * s + lane] = Qp[s];
+        sqi[64 * s + lane] = qid[s];
+      }
+      __syncthreads();
     }
     const float u = a.u_accept[(long)b * a.D + j];
-    const bool accept = Pd > 0.f && (Qd == 0.f || u <= Pd / Qd);
-    if (accept) {
-      out[j] = d;
+    if (Pd > 0.f && (Qd == 0.f || u <= Pd / Qd)) {
+      if (lane == 0) a.out[(long)b * (a.D + 1) + j] = d;
       ++n_acc;
       continue;
     }
     // residual max(0, P - Q); its support lies inside P's kept set
-    float rs = 0.f;
-    for (int k = 0; k < mP; ++k) {
-      ids[k] = ti[k];
-      const float q = a.q_mode == 1 ? lookup(qi, Q, mQ, ti[k]) : (ti[k] == d ? 1.f : 0.f);
-      w[k] = fmaxf(P[k] - q, 0.f);
-      rs += w[k];
+    float w[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      float q = 0.f;
+      if (a.q_mode == 1) {
+        for (int k = 0; k < mQ; ++k) q = sqi[k] == id[s] ? sq[k] : q;
+      } else {
+        q = id[s] == d ? 1.f : 0.f;
+      }
+      w[s] = 64 * s + lane < mP ? fmaxf(P[s] - q, 0.f) : 0.f;
     }
-    if (!(rs > 0.f))
-      for (int k = 0; k < mP; ++k) w[k] = P[k];
-    tok = draw_ascending(ids, w, mP, a.u_sample[b]);
-    break;
-  }
-  if (tok < 0) {  // every draft held: one more token from row D
-    const int tr = b * (a.D + 1) + a.D;
-    const int mP = warp_row(a.top_v + (long)tr * K, a.top_n[tr], T, a.top_p, P);
-    for (int k = 0; k < mP; ++k) {
-      ids[k] = a.top_i[(long)tr * K + k];
-      w[k] = P[k];
+    if (!(wave_sum(w[0] + w[1]) > 0.f)) {
+      w[0] = P[0];
+      w[1] = P[1];
     }
-    tok = draw_ascending(ids, w, mP, a.u_sample[b]);
+    tok = draw_ascending_wave(id, w, mP, a.u_sample[b], sw, si);
+    if (tok < 0) tok = -2;  // nothing drawable: keep the row's outcome as a rejection
   }
-  out[n_acc] = tok;
-  for (int j = n_acc + 1; j <= a.D; ++j) out[j] = -1;
-  a.n_accept[b] = n_acc;
-  a.crop[b] = a.ctx_len[b] + 1 + n_acc;
+  if (tok == -1) {  // every draft held: one more token from row D
+    const int mP = load_row(b * (a.D + 1) + a.D, P, id);
+    tok = draw_ascending_wave(id, P, mP, a.u_sample[b], sw, si);
+  }
+  if (lane == 0) {
+    int32_t* out = a.out + (long)b * (a.D + 1);
+    out[n_acc] = tok < 0 ? -1 : tok;
+    for (int j = n_acc + 1; j <= a.D; ++j) out[j] = -1;
+    a.n_accept[b] = n_acc;
+    a.crop[b] = a.ctx_len[b] + 1 + n_acc;
+  }
 }
 
 hipError_t run_verify(const VerifyArgs& a, hipStream_t st) {

@@ -118,6 +118,28 @@ def test_verify_uniform_zero_and_near_one():
     assert np.array_equal(n, r.n_accept)
 
 
+@pytest.mark.parametrize("q_mode", [0, 1])
+def test_verify_heavy_ties_below_the_top(q_mode):
+    """Rows that are one repeated value except for 60 distinct larger logits placed past the
+    first 4096 ids: every item passes the first threshold, so the top-k pass overflows its
+    buffer and takes its compacting second pass; the top of each row is unambiguous."""
+    B, D, V = 4, 2, 20000
+    g = gen(61, 7, q_mode)
+    rows = B * (D + 1) + B * D
+    x = np.full((rows, V), -5.0, np.float32)
+    for r in range(rows):
+        pos = 4096 + g.choice(V - 4096, 60, replace=False)
+        x[r, pos] = (g.standard_normal(60) + 3.0).astype(np.float32)
+    tl = x[:B * (D + 1)].reshape(B, D + 1, V)
+    dl = x[B * (D + 1):].reshape(B, D, V)
+    sp = Sampling(0.7, 50, 0.9, q_mode)
+    drafts = np.argmax(dl, axis=-1).astype(np.int32) if q_mode == 0 else _sample_drafts(dl, sp, 5)
+    ua, us = g.random((B, D), dtype=np.float32), g.random(B, dtype=np.float32)
+    ctx = np.arange(1, B + 1, dtype=np.int32)
+    excl, _ = _compare(tl, drafts, dl if q_mode == 1 else None, sp, ua, us, ctx)
+    assert excl < B
+
+
 @pytest.mark.parametrize("sigma", [0.3, 1.0, 3.0])
 def test_verify_stress_full_size_sampled(sigma):
     """B=256, D=4, V=151936 (the verifier-only workload): every sequence runs on the GPU, a
