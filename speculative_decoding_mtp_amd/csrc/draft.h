@@ -97,7 +97,7 @@ struct StepArgs {
 // 16-byte vector) over N output rows.  kind 0: k_gemv_w with nj = NJ; kind 1: k_gemv_s with
 // nj = NXM.  The same plan sizes the lm_head partial buffer and launches the kernel.
 struct GemvPlan {
-  int kind, nj, rb, grid;
+  int kind, nj, rb, rw, grid;
 };
 GemvPlan plan_gemv(int nact, int K, int VE, int N);
 

@@ -21,12 +21,17 @@ GemvPlan plan_gemv(int nact, int K, int VE, int N) {
   const int Kc = K / VE;
   const int nj = (Kc + 63) / 64;
   GemvPlan pl;
+  pl.rw = 0;
   if (nj <= 8) {  // whole rows per wave: RW = 16 / NJ rows per pass keep 16 loads in flight
     pl.kind = 0;
     pl.nj = pow2_at_least(nj);
     const int rbmax = pl.nj <= 2 ? 4 : 2;
     pl.rb = pow2_at_most(nact < rbmax ? (nact < 1 ? 1 : nact) : rbmax);
-    const int rw = 16 / pl.nj;
+    int rw = 16 / pl.nj;
+    // a short matrix with 4 loads per row (fewer than 512 four-wave row groups) takes two rows
+    // per wave instead of four
+    if (pl.nj == 4 && (N + 4 * rw - 1) / (4 * rw) < 512) rw /= 2;
+    pl.rw = rw;
     const int groups = (N + rw - 1) / rw;
     const int wgs = (groups + 3) / 4;
     pl.grid = wgs < kMaxGemvGrid ? wgs : kMaxGemvGrid;

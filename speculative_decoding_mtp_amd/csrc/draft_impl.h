@@ -342,16 +342,17 @@ hipError_t launch_gemv(P& p, hipStream_t st, int* grid_used = nullptr, const Mfm
   }
   const GemvPlan pl = plan_gemv(p.nact, p.K, W::VE, p.N);
   if (pl.kind == 0) {
-#define MTP_W(NJ_, RB_)                                                                        \
-  if (pl.nj == NJ_ && pl.rb == RB_) {                                                          \
-    static int cap = 0;                                                                        \
-    const int grid = min(pl.grid, resident_cap(k_gemv_w<W, RB_, NJ_, 16 / NJ_, P>, &cap));    \
-    if (grid_used) *grid_used = grid;                                                          \
-    hipLaunchKernelGGL((k_gemv_w<W, RB_, NJ_, 16 / NJ_, P>), dim3(grid), dim3(kWG), 0, st, p); \
-    return hipGetLastError();                                                                  \
+#define MTP_W(NJ_, RB_, RW_)                                                                 \
+  if (pl.nj == NJ_ && pl.rb == RB_ && pl.rw == RW_) {                                         \
+    static int cap = 0;                                                                      \
+    const int grid = min(pl.grid, resident_cap(k_gemv_w<W, RB_, NJ_, RW_, P>, &cap));       \
+    if (grid_used) *grid_used = grid;                                                        \
+    hipLaunchKernelGGL((k_gemv_w<W, RB_, NJ_, RW_, P>), dim3(grid), dim3(kWG), 0, st, p);    \
+    return hipGetLastError();                                                                \
   }
-    MTP_W(1, 1) MTP_W(1, 2) MTP_W(1, 4) MTP_W(2, 1) MTP_W(2, 2) MTP_W(2, 4) MTP_W(4, 1) MTP_W(4, 2) MTP_W(8, 1)
-    MTP_W(8, 2)
+    MTP_W(1, 1, 16) MTP_W(1, 2, 16) MTP_W(1, 4, 16) MTP_W(2, 1, 8) MTP_W(2, 2, 8) MTP_W(2, 4, 8)
+    MTP_W(4, 1, 4) MTP_W(4, 2, 4) MTP_W(8, 1, 2) MTP_W(8, 2, 2)
+    MTP_W(4, 1, 2) MTP_W(4, 2, 2)  // short matrices: more waves across the compute units
 #undef MTP_W
   } else {
 #define MTP_S(NX_, RB_)                                                                    \
