@@ -23,6 +23,7 @@ __all__ = [
     "OracleModel", "KVCache", "decoder_block", "mtp_row", "draft_step", "draft_loop",
     "greedy_verify", "warp", "sample", "residual", "sampling_verify", "spec_verify",
     "kv_crop", "state_snapshot", "state_restore", "spec_decode", "VerifyResult",
+    "TargetModel", "target_row", "target_forward", "DenseTarget",
 ]
 
 
@@ -223,6 +224,92 @@ def mtp_row(model: OracleModel, cache: KVCache, b: int, tok: int, hidden, pos: i
     logits = model.lm_head @ g
     draft, margin = argmax_lowest(logits)
     return g, draft, logits, margin
+
+
+# --------------------------------------------------------------------------------------------
+# the target's verify forward (a dense stand-in main model)
+# --------------------------------------------------------------------------------------------
+class TargetModel:
+    """A dense main model sharing the MTP head's token embedding and output layer.
+
+    [HB14 "The draft head"]: the head takes the main model's embedding table and
+    lm_head, and the main model hands it its last hidden state; the main model
+    returns logits for every position it is given (the verify pass over the
+    current token and the D drafts).  The pages do not describe the main model's
+    layers.  Reading: a stack of the same pre-norm decoder blocks as the head's
+    (O3), a final RMSNorm, and the shared lm_head; its hidden is the post-norm
+    vector (the one its lm_head reads), as in the head."""
+
+    def __init__(self, cfg, target_weights):
+        self.cfg = cfg
+        f = lambda a: np.asarray(a, dtype=F64)
+        self.embed = target_weights.embed
+        self.layers = []
+        for lw in target_weights.layers:
+            self.layers.append(dict(in_norm=f(lw.in_norm), wq=f(lw.wq), wk=f(lw.wk), wv=f(lw.wv),
+                                    wo=f(lw.wo), post_norm=f(lw.post_norm), wgate=f(lw.wgate),
+                                    wup=f(lw.wup), wdown=f(lw.wdown)))
+        self.final_norm = f(target_weights.final_norm)
+        self.lm_head = f(target_weights.lm_head)
+
+
+def target_row(model: TargetModel, cache: KVCache, b: int, tok: int, pos: int):
+    """The target on one row: x = E[tok], every block at ``pos`` (appending its
+    K/V), g = rms(x; g_final), logits = W_lm g.  Returns (g, logits)."""
+    cfg = model.cfg
+    if not (0 <= tok < cfg.vocab):
+        raise IndexError(f"token {tok} outside the vocabulary")
+    x = np.asarray(model.embed[tok], dtype=F64)
+    for layer in range(cfg.n_layers):
+        x = decoder_block(model, layer, cache, b, x, pos)
+    g = rms_norm(x, model.final_norm, cfg.rms_eps)
+    return g, model.lm_head @ g
+
+
+def target_forward(model: TargetModel, cache: KVCache, tokens):
+    """The target over ``tokens[B][rows]`` (valid prefix of each row = the
+    non-negative tokens), row i of sequence b at position len[b] + i; len grows
+    by the valid rows.  Returns hiddens [B][rows][H] and logits [B][rows][V]
+    (zeros for invalid rows)."""
+    tokens = np.asarray(tokens)
+    B, R = tokens.shape
+    cfg = model.cfg
+    hid = np.zeros((B, R, cfg.hidden))
+    logits = np.zeros((B, R, cfg.vocab))
+    for b in range(B):
+        n = _valid_rows(tokens[b])
+        p0 = int(cache.len[b])
+        for i in range(n):
+            hid[b, i], logits[b, i] = target_row(model, cache, b, int(tokens[b, i]), p0 + i)
+        cache.len[b] = p0 + n
+    return hid, logits
+
+
+class DenseTarget:
+    """``spec_decode``'s target interface over a TargetModel (batch 1): the
+    state is its KV cache; there is no recurrent state (an empty table)."""
+
+    def __init__(self, model: TargetModel, max_len: int):
+        self.model, self.max_len = model, max_len
+
+    def new_state(self):
+        return KVCache(self.model.cfg, 1, self.max_len)
+
+    def forward(self, st, tokens):
+        h, lg = target_forward(self.model, st, np.asarray([list(tokens)]))
+        return lg[0], h[0]
+
+    def length(self, st):
+        return int(st.len[0])
+
+    def crop(self, st, n):
+        kv_crop(st, [n])
+
+    def recurrent(self, st):
+        return np.zeros((1, 0), np.uint8)
+
+    def set_recurrent(self, st, b):
+        pass
 
 
 # --------------------------------------------------------------------------------------------

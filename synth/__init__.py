@@ -23,7 +23,7 @@ from typing import Dict, Optional, Tuple
 import numpy as np
 
 # stream ids
-S_WEIGHTS, S_EMBED, S_HIDDEN, S_KV, S_TOKENS, S_NOISE, S_UNIF, S_VLOGITS, S_STATE = range(9)
+S_WEIGHTS, S_EMBED, S_HIDDEN, S_KV, S_TOKENS, S_NOISE, S_UNIF, S_VLOGITS, S_STATE, S_TARGET = range(10)
 
 
 @dataclass(frozen=True)
@@ -180,6 +180,28 @@ def make_weights(cfg: MTPConfig, std: float = 0.02) -> Weights:
     ge = gen(cfg.index, S_EMBED)
     embed = _as_wdtype(_normal(ge, (cfg.vocab, H), cfg.embed_std), cfg.wdtype)
     return Weights(embed, ones(H), ones(H), eh, layers, ones(H), lm)
+
+
+@dataclass
+class TargetWeights:
+    """A dense stand-in main model: its own decoder layers and final norm; the token embedding
+    and the output layer are the head's (shared, as the MTP head shares the main model's)."""
+    embed: np.ndarray       # [V][H]
+    layers: list
+    final_norm: np.ndarray  # [H]
+    lm_head: np.ndarray     # [V][H]
+
+
+def make_target_weights(cfg: MTPConfig, n_layers: int, head: Weights, std: float = 0.02) -> TargetWeights:
+    """n_layers target blocks with the head's dimensions, matrices N(0, std) in the config's
+    dtype, gains 1; embedding and lm_head taken from ``head``."""
+    g = gen(cfg.index, S_TARGET)
+    H, F = cfg.hidden, cfg.ffn
+    w = lambda *shape: _as_wdtype(_normal(g, shape, std), cfg.wdtype)
+    ones = lambda n: np.ones(n, dtype=np.float32)
+    layers = [LayerWeights(ones(H), w(cfg.q_dim, H), w(cfg.kv_dim, H), w(cfg.kv_dim, H), w(H, cfg.q_dim), ones(H),
+                           w(F, H), w(F, H), w(H, F)) for _ in range(n_layers)]
+    return TargetWeights(head.embed, layers, ones(H), head.lm_head)
 
 
 def make_kv_prefix(cfg: MTPConfig, length: Optional[int] = None):
