@@ -189,6 +189,37 @@ enum { MTP_KERNEL_LM_HEAD = 1, MTP_KERNEL_VERIFY = 2 };
 int mtp_timer_start(int32_t kernel, int32_t max_launches);
 int mtp_timer_read(int32_t kernel, float* total_ms, int32_t* launches);
 
+/* ---- The target's verify forward (a dense stand-in main model) ----
+ * [HB14 "The draft head"]: the main model scores the settled token and the D drafts in one pass,
+ * returns logits for each of those positions and hands the head its hidden states; the head
+ * shares the main model's token embedding and output layer.  The pages do not describe the main
+ * model's layers; this stand-in stacks the head's decoder block: x = E[tok]; cfg->n_layers
+ * blocks over the target's own KV cache (RoPE, append, GQA attention, o_proj, SwiGLU MLP);
+ * g = rms(x) * final_norm; logits = lm_head g.  cfg describes the target (n_layers = its layers).
+ * embed / lm_head [V][H], final_norm [H], `layers` a HOST array of cfg->n_layers entries. */
+typedef struct {
+  const void *embed, *final_norm, *lm_head;
+  const mtp_layer_weights* layers;
+} mtp_target_weights;
+
+/* Workspace bytes for mtp_target_forward on `batch` sequences of `rows_per_seq` rows with a
+ * cache of `max_len` positions. */
+int mtp_target_workspace_size(const mtp_config* cfg, int32_t batch, int32_t rows_per_seq, int32_t max_len,
+                              size_t* bytes);
+
+/* One target pass over tokens [B][rows_per_seq] (B = kv->batch): the valid rows of sequence b are
+ * the prefix of non-negative tokens (inside the vocabulary and the cache, as in mtp_draft_step;
+ * violations are reported through mtp_check); row i sits at position kv->len[b] + i, appends
+ * its K/V there and attends to positions 0 .. kv->len[b] + i; kv->len[b] grows by the valid rows.
+ *   hidden_out [B][rows_per_seq][H] or NULL: g of every valid row (what the head consumes).
+ *   logits_out [B][rows_per_seq][V]: logits of every valid row; rows past the valid prefix are
+ *                                   not written.
+ * For verification, tokens[b] = [x_n, d_1 .. d_D] (rows_per_seq = D + 1) gives spec_verify's
+ * target_logits directly; afterwards kv_crop(target kv, crop_len) drops the rejected positions. */
+int mtp_target_forward(const mtp_config* cfg, const mtp_target_weights* w, const mtp_kv* kv, int32_t rows_per_seq,
+                       const int32_t* tokens, float* hidden_out, float* logits_out, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

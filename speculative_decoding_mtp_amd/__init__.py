@@ -55,6 +55,11 @@ class MtpWeights(ctypes.Structure):
                 ("layers", ctypes.POINTER(MtpLayerWeights))]
 
 
+class MtpTargetWeights(ctypes.Structure):
+    _fields_ = [("embed", ctypes.c_void_p), ("final_norm", ctypes.c_void_p), ("lm_head", ctypes.c_void_p),
+                ("layers", ctypes.POINTER(MtpLayerWeights))]
+
+
 class MtpKV(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("len", ctypes.c_void_p),
                 ("batch", ctypes.c_int32), ("max_len", ctypes.c_int32)]
@@ -81,6 +86,9 @@ _sigs = {
     "mtp_state_snapshot": ([_P, _P, _SZ, _I, _P], _I),
     "mtp_state_restore": ([_P, _P, _SZ, _I, _P, _I, _P], _I),
     "mtp_check": ([_P, _P], _I),
+    "mtp_target_workspace_size": ([ctypes.POINTER(MtpConfig), _I, _I, _I, ctypes.POINTER(_SZ)], _I),
+    "mtp_target_forward": ([ctypes.POINTER(MtpConfig), ctypes.POINTER(MtpTargetWeights), ctypes.POINTER(MtpKV), _I,
+                            _P, _P, _P, _P, _SZ, _P], _I),
     "mtp_timer_start": ([_I, _I], _I),
     "mtp_timer_read": ([_I, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(_I)], _I),
 }
@@ -162,6 +170,24 @@ class Weights:
                             tensors["lm_head"].data_ptr(), self._layers)
 
 
+class TargetWeights:
+    """Device weight tensors of the dense stand-in target: ``tensors`` holds embed, final_norm,
+    lm_head and ``layers`` (as in Weights), kept alive with the C struct."""
+
+    def __init__(self, cfg: Config, tensors: dict):
+        self.cfg = cfg
+        self.t = tensors
+        dt = cfg.torch_dtype
+        for k in ("embed", "final_norm", "lm_head"):
+            _ptr(tensors[k], dt, k)
+        self._layers = (MtpLayerWeights * cfg.n_layers)()
+        for i, lw in enumerate(tensors["layers"]):
+            for k in ("in_norm", "wq", "wk", "wv", "wo", "post_norm", "wgate", "wup", "wdown"):
+                setattr(self._layers[i], k, _ptr(lw[k], dt, f"layers[{i}].{k}"))
+        self.c = MtpTargetWeights(tensors["embed"].data_ptr(), tensors["final_norm"].data_ptr(),
+                                  tensors["lm_head"].data_ptr(), self._layers)
+
+
 def round_max_len(n: int) -> int:
     """The smallest cache capacity >= n that the library accepts (a multiple of 8)."""
     return -(-int(n) // 8) * 8
@@ -199,6 +225,23 @@ def mtp_draft_workspace_size(cfg: Config, batch: int, rows_per_seq: int, D: int,
 def new_workspace(nbytes: int, device="cuda") -> torch.Tensor:
     """A zero-filled workspace (16-byte aligned: torch allocations are 256-byte aligned)."""
     return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+
+def mtp_target_workspace_size(cfg: Config, batch: int, rows_per_seq: int, max_len: int) -> int:
+    n = _SZ()
+    _check(_lib.mtp_target_workspace_size(ctypes.byref(cfg.c()), batch, rows_per_seq, max_len, ctypes.byref(n)))
+    return n.value
+
+
+def mtp_target_forward(cfg: Config, w: TargetWeights, kv: KVCache, rows_per_seq: int, tokens, hidden_out,
+                       logits_out, ws: torch.Tensor, stream=None) -> None:
+    B, H = kv.batch, cfg.hidden
+    R = B * rows_per_seq
+    _check(_lib.mtp_target_forward(
+        ctypes.byref(cfg.c()), ctypes.byref(w.c), ctypes.byref(kv.c()), rows_per_seq,
+        _ptr(tokens, torch.int32, "tokens", R), _ptr(hidden_out, torch.float32, "hidden_out", R * H),
+        _ptr(logits_out, torch.float32, "logits_out", R * cfg.vocab), _ptr(ws, None, "ws"), ws.numel(),
+        _stream(stream)))
 
 
 def mtp_draft_step(cfg: Config, w: Weights, kv: KVCache, rows_per_seq: int, tokens, hidden_in, hidden_out,

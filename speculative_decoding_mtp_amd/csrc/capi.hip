@@ -73,19 +73,31 @@ int check_cfg(const mtp_config* c) {
   return MTP_OK;
 }
 
-int check_weights(const mtp_config* c, const mtp_weights* w) {
-  if (!w) return fail(MTP_ERR_ARG, "weights is NULL");
-  const void* top[6] = {w->embed, w->enorm, w->hnorm, w->eh_proj, w->final_norm, w->lm_head};
-  for (const void* p : top)
-    if (!p || !aligned16(p)) return fail(MTP_ERR_ARG, "a weight pointer is NULL or not 16-byte aligned");
-  if (!w->layers) return fail(MTP_ERR_ARG, "weights.layers is NULL");
+int check_layers(const mtp_config* c, const mtp_layer_weights* layers) {
+  if (!layers) return fail(MTP_ERR_ARG, "weights.layers is NULL");
   for (int l = 0; l < c->n_layers; ++l) {
-    const mtp_layer_weights& L = w->layers[l];
+    const mtp_layer_weights& L = layers[l];
     const void* lp[9] = {L.in_norm, L.wq, L.wk, L.wv, L.wo, L.post_norm, L.wgate, L.wup, L.wdown};
     for (const void* p : lp)
       if (!p || !aligned16(p)) return fail(MTP_ERR_ARG, "layer %d: a weight pointer is NULL or misaligned", l);
   }
   return MTP_OK;
+}
+
+int check_weights(const mtp_config* c, const mtp_weights* w) {
+  if (!w) return fail(MTP_ERR_ARG, "weights is NULL");
+  const void* top[6] = {w->embed, w->enorm, w->hnorm, w->eh_proj, w->final_norm, w->lm_head};
+  for (const void* p : top)
+    if (!p || !aligned16(p)) return fail(MTP_ERR_ARG, "a weight pointer is NULL or not 16-byte aligned");
+  return check_layers(c, w->layers);
+}
+
+int check_target_weights(const mtp_config* c, const mtp_target_weights* w) {
+  if (!w) return fail(MTP_ERR_ARG, "target weights is NULL");
+  const void* top[3] = {w->embed, w->final_norm, w->lm_head};
+  for (const void* p : top)
+    if (!p || !aligned16(p)) return fail(MTP_ERR_ARG, "a target weight pointer is NULL or not 16-byte aligned");
+  return check_layers(c, w->layers);
 }
 
 int check_kv(const mtp_kv* kv) {
@@ -178,6 +190,8 @@ StepArgs base_step(const mtp_config* cfg, const mtp_weights* w, const mtp_kv* kv
   StepArgs s;
   s.cfg = *cfg;
   s.w = w;
+  s.tw = nullptr;
+  s.target = 0;
   s.kc = kv->k;
   s.vc = kv->v;
   s.kv_len = kv->len;
@@ -217,6 +231,42 @@ int mtp_draft_workspace_size(const mtp_config* cfg, int32_t batch, int32_t rows_
     return fail(MTP_ERR_ARG, "batch in [1, %d], rows_per_seq >= 1, max_len >= 1, D >= 0", kMaxBatch);
   *bytes = draft_layout(*cfg, batch, rows_per_seq, D, max_len).total;
   return MTP_OK;
+}
+
+int mtp_target_workspace_size(const mtp_config* cfg, int32_t batch, int32_t rows_per_seq, int32_t max_len,
+                              size_t* bytes) {
+  return mtp_draft_workspace_size(cfg, batch, rows_per_seq, 1, max_len, bytes);
+}
+
+int mtp_target_forward(const mtp_config* cfg, const mtp_target_weights* w, const mtp_kv* kv, int32_t rows_per_seq,
+                       const int32_t* tokens, float* hidden_out, float* logits_out, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  int rc;
+  if ((rc = check_cfg(cfg)) || (rc = check_target_weights(cfg, w)) || (rc = check_kv(kv))) return rc;
+  if (rows_per_seq < 1) return fail(MTP_ERR_ARG, "rows_per_seq must be >= 1");
+  if (!tokens) return fail(MTP_ERR_ARG, "tokens is NULL");
+  if (!logits_out || !aligned16(logits_out)) return fail(MTP_ERR_ARG, "logits_out NULL or misaligned");
+  if (hidden_out && !aligned16(hidden_out)) return fail(MTP_ERR_ARG, "hidden_out misaligned");
+  if (!ws || !aligned16(ws)) return fail(MTP_ERR_ARG, "workspace NULL or misaligned");
+  const DraftLayout L = draft_layout(*cfg, kv->batch, rows_per_seq, 1, kv->max_len);
+  if (ws_bytes < L.total) return fail(MTP_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, L.total);
+  StepArgs s = base_step(cfg, nullptr, kv, ws, L, stream);
+  s.tw = w;
+  s.target = 1;
+  s.rps = rows_per_seq;
+  s.tok = tokens;
+  s.tok_sb = rows_per_seq;
+  s.hin = nullptr;
+  s.hin_sb = 0;
+  s.hout = hidden_out;
+  s.hout_sb = rows_per_seq;
+  s.hout_last = 0;
+  s.draft = nullptr;
+  s.dr_sb = 0;
+  s.logits = logits_out;
+  s.lg_sb = cfg->vocab;
+  const hipError_t e = run_step(s);
+  return e == hipSuccess ? MTP_OK : hip_fail(e, "mtp_target_forward launch");
 }
 
 int mtp_draft_step(const mtp_config* cfg, const mtp_weights* w, const mtp_kv* kv, int32_t rows_per_seq,

@@ -74,7 +74,9 @@ struct DraftWs {
 
 struct StepArgs {
   mtp_config cfg;
-  const mtp_weights* w;
+  const mtp_weights* w;          // the head (target == 0)
+  const mtp_target_weights* tw;  // the target (target == 1)
+  int target;                    // 1: x = E[tok], logits of every valid row, no draft
   void *kc, *vc;
   int32_t* kv_len;
   int B, max_len, rps, nsplit;
@@ -86,7 +88,7 @@ struct StepArgs {
   int hout_sb, hout_last;
   int32_t* draft;  // draft of b at draft[b * dr_sb]
   int dr_sb;
-  float* logits;  // NULL or logits of b at logits + b * lg_sb
+  float* logits;  // head: NULL or logits of b at logits + b * lg_sb; target: row r at logits + r * V
   long lg_sb;
   DraftWs ws;
   hipStream_t stream;

@@ -216,6 +216,43 @@ struct PLmHead : PBase<W> {
   }
 };
 
+// The target's output layer: final RMSNorm + lm_head for every valid row, logits stored
+// [row][V] (row = b * rps + i).
+template <class W>
+struct PLogits : PBase<W> {
+  using T = typename W::T;
+  static constexpr int kNorm = 1;
+  const T *g, *w;
+  const float* xin;
+  int H;
+  float* logits;
+
+  __device__ void load_x(int row, int k, float (&f)[W::VE]) const { load_f32_vec<W::VE>(xin + (long)row * H + k, f); }
+  __device__ void gain_vec(int k, float (&f)[W::VE]) const { W::cvt(ld16(g + k), f); }
+  __device__ const T* wrow(int m) const { return w + (long)m * H; }
+  __device__ void store(int m, int, int row, float v) { logits[(long)row * this->N + m] = v; }
+};
+
+// The target's input: x[row] = E[tok] (fp32) for the valid rows; one workgroup per row.
+template <class W>
+__global__ __launch_bounds__(kWG) void k_embed_rows(const void* embed, const int32_t* tok, int rps, int V,
+                                                    const int32_t* len, int max_len, int H, float* x) {
+  using T = typename W::T;
+  constexpr int VE = W::VE;
+  __shared__ int s_n;
+  const int row = blockIdx.x, b = row / rps, i = row - b * rps;
+  if (threadIdx.x == 0) s_n = count_rows(tok + (long)b * rps, rps, V, len[b], max_len, nullptr);
+  __syncthreads();
+  if (i >= s_n) return;
+  const T* e = reinterpret_cast<const T*>(embed) + (long)tok[(long)b * rps + i] * H;
+  for (int k = threadIdx.x * VE; k < H; k += kWG * VE) {
+    float f[VE];
+    W::cvt(ld16(e + k), f);
+#pragma unroll
+    for (int j = 0; j < VE; ++j) x[(long)row * H + k + j] = f[j];
+  }
+}
+
 // After the lm_head: one workgroup per sequence reduces the per-workgroup argmax partials
 // (the lowest id among equal maxima), writes the draft, grows len[b], records device errors,
 // and writes the post-norm hidden of the rows the caller wants.
@@ -245,7 +282,7 @@ __global__ __launch_bounds__(kWG) void k_lm_finalize(LmFinal f) {
   }
   __syncthreads();
   const T* g = reinterpret_cast<const T*>(f.gain);
-  for (int i = (f.hout_last ? n - 1 : 0); i < n; ++i) {
+  for (int i = (f.hout_last ? n - 1 : 0); f.hout && i < n; ++i) {
     const float* xr = f.x + ((long)b * f.rps + i) * f.H;
     float ss[1] = {0.f};
     for (int k = tid; k < f.H; k += kWG) ss[0] += xr[k] * xr[k];
@@ -262,7 +299,7 @@ __global__ __launch_bounds__(kWG) void k_lm_finalize(LmFinal f) {
         v = sv[w];
         id = si[w];
       }
-    f.draft[(long)b * f.dr_sb] = n > 0 ? id : -1;
+    if (f.draft) f.draft[(long)b * f.dr_sb] = n > 0 ? id : -1;
     f.len[b] = f.len[b] + n;
     if (flags) atomicOr(f.status, flags);
   }
@@ -393,7 +430,11 @@ hipError_t run_step_t(const StepArgs& s) {
                          s.ws.kpart_cap};
   const MfmaBufs* mb = s.ws.xhi ? &mbuf : nullptr;
 
-  {  // eh_proj
+  if (s.target) {  // the target's input: token embeddings
+    hipLaunchKernelGGL((k_embed_rows<W>), dim3(R), dim3(kWG), 0, s.stream, s.tw->embed, s.tok, s.rps, c.vocab,
+                       s.kv_len, s.max_len, H, s.ws.x);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  } else {  // eh_proj
     PEhProj<W> p;
     fill_base<W>(p, s);
     p.K = 2 * H;
@@ -410,8 +451,9 @@ hipError_t run_step_t(const StepArgs& s) {
     p.xout = s.ws.x;
     if ((e = launch_gemv<W>(p, s.stream, nullptr, mb)) != hipSuccess) return e;
   }
+  const mtp_layer_weights* layers = s.target ? s.tw->layers : s.w->layers;
   for (int l = 0; l < c.n_layers; ++l) {
-    const mtp_layer_weights& lw = s.w->layers[l];
+    const mtp_layer_weights& lw = layers[l];
     const long layer_off = (long)l * s.B * nkv * s.max_len * hd;
     {  // q/k/v + RoPE + append
       PQKV<W> p;
@@ -490,6 +532,41 @@ hipError_t run_step_t(const StepArgs& s) {
       p.xres = s.ws.x;
       if ((e = launch_gemv<W>(p, s.stream, nullptr, mb)) != hipSuccess) return e;
     }
+  }
+  if (s.target) {  // final norm + lm_head over every valid row, hiddens, len
+    PLogits<W> p;
+    fill_base<W>(p, s);
+    p.K = H;
+    p.N = c.vocab;
+    p.nact = R;
+    p.g = (const T*)s.tw->final_norm;
+    p.w = (const T*)s.tw->lm_head;
+    p.xin = s.ws.x;
+    p.H = H;
+    p.logits = s.logits;
+    if ((e = launch_gemv<W>(p, s.stream, nullptr, mb)) != hipSuccess) return e;
+    LmFinal f;
+    f.tok = s.tok;
+    f.tok_sb = s.tok_sb;
+    f.rps = s.rps;
+    f.V = c.vocab;
+    f.len = s.kv_len;
+    f.max_len = s.max_len;
+    f.part_v = nullptr;
+    f.part_i = nullptr;
+    f.nparts = 0;
+    f.x = s.ws.x;
+    f.gain = s.tw->final_norm;
+    f.H = H;
+    f.eps = c.rms_eps;
+    f.hout = s.hout;
+    f.hout_sb = s.hout_sb;
+    f.hout_last = 0;
+    f.draft = nullptr;
+    f.dr_sb = 0;
+    f.status = s.ws.status;
+    hipLaunchKernelGGL((k_lm_finalize<W>), dim3(s.B), dim3(kWG), 0, s.stream, f);
+    return hipGetLastError();
   }
   {  // final norm + lm_head + argmax + finalisation
     PLmHead<W> p;

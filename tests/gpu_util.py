@@ -29,6 +29,16 @@ def upload_weights(cfg: MTPConfig, w) -> M.Weights:
     return M.Weights(config(cfg), t)
 
 
+def upload_target_weights(cfg: MTPConfig, tw) -> M.TargetWeights:
+    """``cfg`` describes the target (its n_layers)."""
+    d = lambda a: to_dev(a, cfg.wdtype)
+    t = dict(embed=d(tw.embed), final_norm=d(tw.final_norm), lm_head=d(tw.lm_head), layers=[])
+    for lw in tw.layers:
+        t["layers"].append(dict(in_norm=d(lw.in_norm), wq=d(lw.wq), wk=d(lw.wk), wv=d(lw.wv), wo=d(lw.wo),
+                                post_norm=d(lw.post_norm), wgate=d(lw.wgate), wup=d(lw.wup), wdown=d(lw.wdown)))
+    return M.TargetWeights(config(cfg), t)
+
+
 def kv_from_numpy(cfg: MTPConfig, K: np.ndarray, V: np.ndarray, length: int, max_len: int) -> M.KVCache:
     kv = M.KVCache(config(cfg), K.shape[1], max_len)
     kv.k[:, :, :, :length] = to_dev(K[:, :, :, :length], cfg.wdtype)
