@@ -15,6 +15,8 @@ divided by the timed wall time), the lm_head kernel's HBM roofline and the CPU o
 a bounded sample of the same workload.  --config names another head workload (drafter4: the
 4-layer 1024-hidden drafter with sampling verification; dsv3: the 7168-hidden head at batch 32)
 or, with --config stress, the verifier alone (B=256, D=4, vocab 151936, sampling).
+--target-layers L times the target's verify pass instead: a dense stand-in with the head's
+dimensions and L blocks, scoring 1, 2 or 7 positions per call.
 """
 import argparse
 import hashlib
@@ -41,6 +43,8 @@ def parse():
                                                       "lm_head_counters.json"),
                     help="counter-measured lm_head bytes per launch (ignored when the kernel sources changed)")
     ap.add_argument("--graph", type=int, default=0, help="capture this many rounds per HIP graph (0: eager)")
+    ap.add_argument("--target-layers", type=int, default=0,
+                    help="time the target's verify pass instead (a dense stand-in with this many layers)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB first (counter calibration)")
     return ap.parse_args()
@@ -61,6 +65,8 @@ def main():
     if args.config in VERIFY_CONFIGS:
         return bench_verify(args, VERIFY_CONFIGS[args.config])
     cfg = CONFIGS[args.config]
+    if args.target_layers > 0:
+        return bench_target(args, cfg, args.target_layers)
     B, D, H, V = cfg.batch, cfg.D, cfg.hidden, cfg.vocab
     state_bytes = cfg.state_bytes_per_seq if args.state_bytes is None else args.state_bytes
     rounds_total = args.warmup + args.steps
@@ -269,6 +275,73 @@ def bench_verify(args, vc, sigma=1.0):
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "bytes_per_launch": logits_bytes, "avg_launch_us": round(v_ms / v_n * 1e3, 2),
                      "launches": v_n},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_target(args, cfg, layers, row_counts=(1, 2, 7)):
+    """The target's verify pass (mtp_target_forward) on a dense stand-in with the head's
+    dimensions and ``layers`` blocks over a KV context of cfg.ctx positions (B = cfg.batch):
+    time per call when it scores 1, 2 or 7 positions per sequence ([P2]: seven positions cost
+    about as much as one, because the pass is bound by streaming the weights)."""
+    import dataclasses
+    import torch
+    import speculative_decoding_mtp_amd as M
+    from synth import gen, make_kv_prefix, make_target_weights, make_weights
+    from tests.gpu_util import config, i32, kv_from_numpy, upload_target_weights
+
+    B, H, V = cfg.batch, cfg.hidden, cfg.vocab
+    tcfg = dataclasses.replace(cfg, n_layers=layers)
+    w = make_weights(cfg)
+    tw = make_target_weights(cfg, layers, w)
+    c, gw = config(tcfg), upload_target_weights(tcfg, tw)
+    del w, tw
+    K, Vv = make_kv_prefix(tcfg)
+    max_len = M.round_max_len(cfg.ctx + max(row_counts) + 8)
+    kv = kv_from_numpy(tcfg, K, Vv, cfg.ctx, max_len)
+    del K, Vv
+    ctx = i32(np.full(B, cfg.ctx))
+    R = max(row_counts)
+    ws = M.new_workspace(M.mtp_target_workspace_size(c, B, R, max_len))
+    hid = torch.zeros(B, R, H, device="cuda")
+    lg = torch.zeros(B, R, V, device="cuda")
+    toks = i32(gen(cfg.index, 4, 77).integers(0, V, size=(B, R)))
+    ms = {}
+    for rows in row_counts:
+        t = toks[:, :rows].contiguous()
+        for _ in range(args.warmup):
+            M.mtp_target_forward(c, gw, kv, rows, t, hid, lg, ws)
+            M.kv_crop(kv, ctx)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            M.mtp_target_forward(c, gw, kv, rows, t, hid, lg, ws)
+            M.kv_crop(kv, ctx)
+        e1.record()
+        torch.cuda.synchronize()
+        ms[rows] = e0.elapsed_time(e1) / args.steps
+    M.mtp_check(ws)
+    wb = 2 if cfg.wdtype == "bf16" else 4
+    per_layer = ((cfg.q_dim + 2 * cfg.kv_dim) * H + H * cfg.q_dim + 3 * cfg.ffn * H) * wb
+    weight_bytes = layers * per_layer + V * H * wb
+    kv_bytes = layers * B * 2 * cfg.kv_dim * cfg.ctx * wb
+    r7 = max(row_counts)
+    achieved = (weight_bytes + kv_bytes) / (ms[r7] * 1e-3) / 1e9
+    line = {
+        "metric": "target verify pass: time for 7 scored positions relative to 1",
+        "value": round(ms[r7] / ms[min(row_counts)], 4), "unit": "ratio", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms[r7], 4), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.wdtype,
+        "data": "synthetic (seeded random-init dense target sharing the head's embedding and lm_head, random KV)",
+        "config": {"workload": f"target-{layers}layer-h{H}-v{V}-{cfg.wdtype}-b{B}-ctx{cfg.ctx}", "batch": B,
+                   "layers": layers, "kv_context": cfg.ctx},
+        "ms_per_call": {str(k): round(v, 4) for k, v in ms.items()},
+        "roofline": {"bound": "hbm", "kernel": f"mtp_target_forward at {r7} rows (all kernels)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": weight_bytes + kv_bytes},
         "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)

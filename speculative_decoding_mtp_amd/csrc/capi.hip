@@ -122,7 +122,7 @@ DraftLayout draft_layout(const mtp_config& c, int B, int rps, int D, int max_len
   size_t kmax = 2 * (size_t)c.hidden;
   if ((size_t)c.ffn > kmax) kmax = c.ffn;
   if ((size_t)c.n_heads * c.head_dim > kmax) kmax = (size_t)c.n_heads * c.head_dim;
-  const bool mfma = c.wdtype == MTP_BF16 && R >= 16;
+  const bool mfma = c.wdtype == MTP_BF16 && R >= 3;  // more rows than one VALU GEMV pass may hold
   const size_t sizes[15] = {
       256,                                                                   // status word
       R * c.hidden * 4,                                                      // x

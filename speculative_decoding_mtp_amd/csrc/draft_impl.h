@@ -98,6 +98,17 @@ struct PQKV : PBase<W> {
   double log_theta;
   float* qout;
   T *kc, *vc;  // this layer's cache: keys [B][nkv][max_len][hd], values [B][nkv][hd][max_len]
+  const double* inv_freq;  // theta^(-2u/hd), u < hd/2, in LDS (set by setup)
+
+  // Per-sequence rows and cache lengths, and the rotation frequencies (exp in double once per
+  // workgroup instead of once per output pair).
+  __device__ void setup(int* s_n, int* s_len) {
+    PBase<W>::setup(s_n, s_len);
+    __shared__ double s_inv_freq[64];  // head_dim <= 128
+    for (int u = threadIdx.x; u < (hd >> 1); u += kWG)
+      s_inv_freq[u] = exp(-2.0 * double(u) / double(hd) * log_theta);
+    inv_freq = s_inv_freq;
+  }
 
   __device__ void load_x(int row, int k, float (&f)[W::VE]) const { load_f32_vec<W::VE>(xin + (long)row * H + k, f); }
   __device__ void gain_vec(int k, float (&f)[W::VE]) const { W::cvt(ld16(g + k), f); }
@@ -112,11 +123,14 @@ struct PQKV : PBase<W> {
     const int head = m / hd, u = (m - head * hd) >> 1, half = hd >> 1;
     const int b = row / this->rps, i = row - b * this->rps;
     const int pos = this->lds_len[b] + i;
-    if (head < nq + nkv) {  // rotate q and k: angle pos * theta^(-2u/hd), computed in double
-      const double ang = double(pos) * exp(-2.0 * double(u) / double(hd) * log_theta);
-      double s, c;
-      sincos(ang, &s, &c);
-      const float cf = float(c), sf = float(s);
+    if (head < nq + nkv) {
+      // rotate q and k by pos * theta^(-2u/hd): the angle in double, reduced to [-pi, pi] in
+      // double (two-part 2 pi), then sine and cosine of the reduced angle in float
+      const double ang = double(pos) * inv_freq[u];
+      const double k2pi = rint(ang * 0.15915494309189535);  // 1 / (2 pi)
+      const double red = fma(-k2pi, 2.4492935982947064e-16, fma(-k2pi, 6.283185307179586, ang));
+      float sf, cf;
+      sincosf(float(red), &sf, &cf);
       const float a0 = v0 * cf - v1 * sf, a1 = v1 * cf + v0 * sf;
       v0 = a0;
       v1 = a1;
@@ -323,11 +337,14 @@ int resident_cap(K kernel, int* cache) {
 
 // Launch the planned variant with a grid of at most one resident wave of workgroups (the
 // kernels loop over row groups), so no partial second wave of workgroups trails the first.
-// The bf16 MFMA path serves activation counts of 16 and more (a batch of sequences) when K
-// is a multiple of the 128-wide chunk; fewer rows stream through the VALU GEMVs.
+// The bf16 MFMA path (K a multiple of the 128-wide chunk) serves every activation count the
+// VALU GEMVs cannot take in one pass over the weights.
+// bf16 weights take the MFMA path for 16 or more activation rows, and also for fewer when the
+// VALU GEMV would have to stream the weights more than once (more rows than it holds per pass).
 template <class W, class P>
 bool use_mfma(const P& p, const MfmaBufs* mb) {
-  return mb && std::is_same<W, BF16>::value && p.nact >= 16 && p.K % kMfmaKC == 0;
+  if (!mb || !std::is_same<W, BF16>::value || p.K % kMfmaKC != 0) return false;
+  return p.nact >= 16 || p.nact > plan_gemv(p.nact, p.K, W::VE, p.N).rb;
 }
 
 // MFMA GEMM with MG activation tiles per pass.  Few weight-row groups (N < 256 x 128): K is
