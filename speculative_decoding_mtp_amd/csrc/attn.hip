@@ -453,13 +453,15 @@ __global__ __launch_bounds__(HD) void k_attn_combine(AttnArgs a, float* out) {
   out[((long)row * a.nq + h) * HD + d] = O / L;
 }
 
-// bf16 caches take the MFMA kernel (one query tile per pass when a sequence's queries fit in
-// 16, else two); fp32 caches the VALU kernel.
+// bf16 caches take the MFMA kernel: one query tile per pass, or two when a sequence has more
+// than 16 queries and the cache is large enough that a second pass over it would cost more than
+// the two-tile kernel's lower occupancy (64 MB of keys and values); fp32 caches the VALU kernel.
 template <int HD>
 void launch_attention(const AttnArgs& a, int wdtype, float* out, hipStream_t st) {
   dim3 grid(a.nsplit, a.nkv, a.B);
   if (wdtype == MTP_BF16) {
-    if (a.qstride <= 16)
+    const double kv_bytes = 4.0 * a.B * a.nkv * (double)a.max_len * HD;
+    if (a.qstride <= 16 || kv_bytes < 64.0 * 1024 * 1024)
       hipLaunchKernelGGL((k_attn_mfma<HD, 1>), grid, dim3(kWG), 0, st, a);
     else
       hipLaunchKernelGGL((k_attn_mfma<HD, 2>), grid, dim3(kWG), 0, st, a);

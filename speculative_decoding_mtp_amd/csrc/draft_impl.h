@@ -30,6 +30,7 @@ struct PBase {
   using T = typename W::T;
   static constexpr bool kPair = false;
   static constexpr bool kArgmax = false;
+  static constexpr bool kVocab = false;  // output rows are a vocabulary (MFMA: 128 rows per workgroup)
   const int32_t* tok;
   int tok_sb;
   int B, rps;
@@ -236,6 +237,7 @@ template <class W>
 struct PLogits : PBase<W> {
   using T = typename W::T;
   static constexpr int kNorm = 1;
+  static constexpr bool kVocab = true;
   const T *g, *w;
   const float* xin;
   int H;
@@ -296,14 +298,16 @@ __global__ __launch_bounds__(kWG) void k_lm_finalize(LmFinal f) {
   }
   __syncthreads();
   const T* g = reinterpret_cast<const T*>(f.gain);
-  for (int i = (f.hout_last ? n - 1 : 0); f.hout && i < n; ++i) {
+  // output hiddens: wave w normalises rows first + w, first + w + 4, ... (no block barriers)
+  const int lane = tid & 63, wid = tid >> 6;
+  for (int i = (f.hout_last ? n - 1 : 0) + wid; f.hout && i < n; i += kWG / 64) {
     const float* xr = f.x + ((long)b * f.rps + i) * f.H;
-    float ss[1] = {0.f};
-    for (int k = tid; k < f.H; k += kWG) ss[0] += xr[k] * xr[k];
-    wg_sum<1>(ss, red);
-    const float sc = 1.0f / sqrtf(ss[0] / float(f.H) + f.eps);
+    float ss = 0.f;
+    for (int k = lane; k < f.H; k += 64) ss += xr[k] * xr[k];
+    ss = wave_sum(ss);
+    const float sc = 1.0f / sqrtf(ss / float(f.H) + f.eps);
     float* dst = f.hout + ((long)b * f.hout_sb + (f.hout_last ? 0 : i)) * f.H;
-    for (int k = tid; k < f.H; k += kWG) dst[k] = xr[k] * sc * W::get(g, k);
+    for (int k = lane; k < f.H; k += 64) dst[k] = xr[k] * sc * W::get(g, k);
   }
   if (tid == 0) {
     v = sv[0];
@@ -354,7 +358,7 @@ constexpr int kMfmaItems = 1024;  // (row group, K range) items a launch aims fo
 
 template <class P, int MG>
 hipError_t launch_mfma(P& p, hipStream_t st, int* grid_used, const MfmaBufs& mb) {
-  constexpr int NT = P::kArgmax ? 2 : 1;  // 128 weight rows per workgroup for lm_head, else 64
+  constexpr int NT = (P::kArgmax || P::kVocab) ? 2 : 1;  // 128 weight rows per workgroup for lm_head, else 64
   MfmaBufs m = mb;
   const int groups = (p.N + 4 * NT * 16 - 1) / (4 * NT * 16);
   int ks = 1;

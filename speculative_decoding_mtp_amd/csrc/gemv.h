@@ -78,6 +78,7 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
 //                                   [split, K) separately
 //   static constexpr bool kPair;    outputs come as logical-row pairs (m even, m + 1)
 //   static constexpr bool kArgmax;  track the argmax over logical rows of every activation row
+//   static constexpr bool kVocab;   output rows are a vocabulary (wider MFMA row groups)
 //   void setup(int* s_n, int* s_len) per-sequence row counts and cache lengths into LDS (the
 //                                   kernel then syncs)
 //   void act(int a, const int* s_n, int& row, bool& valid)
