@@ -210,7 +210,7 @@ StepArgs base_step(const mtp_config* cfg, const mtp_weights* w, const mtp_kv* kv
 
 namespace mtp {
 int attn_nsplit(int B, int nkv, int max_len) {
-  int n = (2048 + B * nkv - 1) / (B * nkv);
+  int n = (512 + B * nkv - 1) / (B * nkv);  // about two resident workgroups per compute unit
   if (n > kMaxSplit) n = kMaxSplit;
   const int cap = (max_len + 63) / 64;
   if (n > cap) n = cap;
