@@ -16,7 +16,8 @@ a bounded sample of the same workload.  --config names another head workload (dr
 4-layer 1024-hidden drafter with sampling verification; dsv3: the 7168-hidden head at batch 32)
 or, with --config stress, the verifier alone (B=256, D=4, vocab 151936, sampling).
 --target-layers L times the target's verify pass instead: a dense stand-in with the head's
-dimensions and L blocks, scoring 1, 2 or 7 positions per call.
+dimensions and L blocks, scoring 1, 2 or 7 positions per call.  --prefill-rows N times one MTP
+prefill call over N prompt rows.
 """
 import argparse
 import hashlib
@@ -43,6 +44,8 @@ def parse():
                                                       "lm_head_counters.json"),
                     help="counter-measured lm_head bytes per launch (ignored when the kernel sources changed)")
     ap.add_argument("--graph", type=int, default=0, help="capture this many rounds per HIP graph (0: eager)")
+    ap.add_argument("--prefill-rows", type=int, default=0,
+                    help="time one MTP prefill of this many rows per sequence instead (from an empty cache)")
     ap.add_argument("--target-layers", type=int, default=0,
                     help="time the target's verify pass instead (a dense stand-in with this many layers)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
@@ -67,6 +70,8 @@ def main():
     cfg = CONFIGS[args.config]
     if args.target_layers > 0:
         return bench_target(args, cfg, args.target_layers)
+    if args.prefill_rows > 0:
+        return bench_prefill(args, cfg, args.prefill_rows)
     B, D, H, V = cfg.batch, cfg.D, cfg.hidden, cfg.vocab
     state_bytes = cfg.state_bytes_per_seq if args.state_bytes is None else args.state_bytes
     rounds_total = args.warmup + args.steps
@@ -275,6 +280,62 @@ def bench_verify(args, vc, sigma=1.0):
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "bytes_per_launch": logits_bytes, "avg_launch_us": round(v_ms / v_n * 1e3, 2),
                      "launches": v_n},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_prefill(args, cfg, rows):
+    """One MTP prefill call (mtp_draft_step over ``rows`` rows per sequence, B = cfg.batch) from an
+    empty head cache, timed with HIP events; the cache length is reset between calls."""
+    import torch
+    import speculative_decoding_mtp_amd as M
+    from synth import make_prefill, make_weights
+    from tests.gpu_util import config, f32, i32, upload_weights
+
+    B, H, V = cfg.batch, cfg.hidden, cfg.vocab
+    w = make_weights(cfg)
+    c, gw = config(cfg), upload_weights(cfg, w)
+    del w
+    toks, hid = make_prefill(cfg, rows)
+    max_len = M.round_max_len(rows + 8)
+    kv = M.KVCache(c, B, max_len)
+    ws = M.new_workspace(M.mtp_draft_workspace_size(c, B, rows, 1, max_len))
+    t, h = i32(toks), f32(hid)
+    hout = torch.zeros(B, rows, H, device="cuda")
+    draft = torch.zeros(B, dtype=torch.int32, device="cuda")
+    zero = torch.zeros(B, dtype=torch.int32, device="cuda")
+
+    def call():
+        M.mtp_draft_step(c, gw, kv, rows, t, h, hout, draft, None, ws)
+        M.kv_crop(kv, zero)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    M.mtp_check(ws)
+    ms = e0.elapsed_time(e1) / args.steps
+    # algorithmic work: every row through eh_proj, the blocks and the final norm; causal
+    # attention; lm_head for each sequence's last row
+    per_row = 2 * H * H + cfg.n_layers * ((cfg.q_dim + 2 * cfg.kv_dim) * H + H * cfg.q_dim + 3 * cfg.ffn * H)
+    flops = 2.0 * B * rows * per_row + 2.0 * B * V * H
+    flops += cfg.n_layers * B * 4.0 * cfg.q_dim * rows * (rows + 1) / 2
+    tflops = flops / (ms * 1e-3) / 1e12
+    line = {
+        "metric": "MTP prefill rows/s (one call over the prompt)", "value": round(B * rows / (ms * 1e-3), 1),
+        "unit": "rows/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.wdtype,
+        "data": "synthetic (seeded random-init head, uniform tokens, N(0,1) hiddens)",
+        "config": {"workload": f"{cfg.name}-prefill{rows}", "batch": B, "rows": rows},
+        "roofline": {"bound": "mfma", "kernel": "mtp_draft_step over the prompt (all kernels)",
+                     "achieved": round(tflops, 2), "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": round(tflops / 2500.0, 4), "traffic": None, "flops_per_launch": flops},
         "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)

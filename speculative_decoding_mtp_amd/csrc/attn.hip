@@ -41,10 +41,13 @@ __global__ __launch_bounds__(kWG) void k_attn(AttnArgs a) {
   __shared__ int s_n;
 
   const int tid = threadIdx.x;
-  const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  // blockIdx.y = kv head + nkv * (query-block group): many queries (a prefill) also spread over
+  // the grid: this workgroup takes query blocks qgrp, qgrp + nqgrp, ... of the sequence
+  const int s = blockIdx.x, kvh = blockIdx.y % a.nkv, b = blockIdx.z;
+  const int qgrp = blockIdx.y / a.nkv, nqgrp = gridDim.y / a.nkv;
   const int G = a.nq / a.nkv;
   const int L0 = a.len[b];
-  if (tid == 0) s_n = count_rows(a.tok + (long)b * a.tok_sb, a.rps, a.V, L0, a.max_len, nullptr);
+  if (tid == 0) s_n = a.rows ? a.rows[b] : count_rows(a.tok + (long)b * a.tok_sb, a.rps, a.V, L0, a.max_len, nullptr);
   __syncthreads();
   const int n = s_n;
   if (n == 0) return;
@@ -59,8 +62,10 @@ __global__ __launch_bounds__(kWG) void k_attn(AttnArgs a) {
   const float scale = 1.0f / sqrtf(float(HD));
   const int dpv = tid % HD, qg = tid / HD;
 
-  for (int q0 = 0; q0 < NQ; q0 += kQB) {
+  for (int q0 = qgrp * kQB; q0 < NQ; q0 += kQB * nqgrp) {
     const int nqb = min(kQB, NQ - q0);
+    // positions past the last row of this pass are masked for every query: not visited
+    const int p_stop = min(p_end, L0 + (q0 + nqb - 1) / G + 1);
     uint4 kr[NV], vr[NV];
     auto fetch = [&](int t0) {
 #pragma unroll
@@ -95,7 +100,7 @@ __global__ __launch_bounds__(kWG) void k_attn(AttnArgs a) {
 #pragma unroll
     for (int k = 0; k < QPT; ++k) o[k] = 0.f;
 
-    for (int t0 = p_beg; t0 < p_end; t0 += kTile) {
+    for (int t0 = p_beg; t0 < p_stop; t0 += kTile) {
       __syncthreads();  // the previous tile is no longer read
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
@@ -108,7 +113,7 @@ __global__ __launch_bounds__(kWG) void k_attn(AttnArgs a) {
         for (int e = 0; e < VE; ++e) sV[(pl + e) * LDR + d] = ve[e];  // transposed into [p][d]
       }
       __syncthreads();
-      if (t0 + kTile < p_end) fetch(t0 + kTile);  // in flight while this tile is used
+      if (t0 + kTile < p_stop) fetch(t0 + kTile);  // in flight while this tile is used
       {  // scores: thread -> position pl, queries qs + 4k
         const int pl = tid & (kTile - 1), qs = tid >> 6;
         float acc[SPT];
@@ -225,10 +230,13 @@ __global__ __launch_bounds__(kWG) void k_attn_mfma(AttnArgs a) {
   __shared__ __align__(16) __bf16 sQ[2 * QB * QP];  // [hi/lo][query][channel]
   __shared__ int s_n;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, j = lane & 15, hq = lane >> 4;
-  const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  // blockIdx.y = kv head + nkv * (query-block group): many queries (a prefill) also spread over
+  // the grid: this workgroup takes query blocks qgrp, qgrp + nqgrp, ... of the sequence
+  const int s = blockIdx.x, kvh = blockIdx.y % a.nkv, b = blockIdx.z;
+  const int qgrp = blockIdx.y / a.nkv, nqgrp = gridDim.y / a.nkv;
   const int G = a.nq / a.nkv;
   const int L0 = a.len[b];
-  if (tid == 0) s_n = count_rows(a.tok + (long)b * a.tok_sb, a.rps, a.V, L0, a.max_len, nullptr);
+  if (tid == 0) s_n = a.rows ? a.rows[b] : count_rows(a.tok + (long)b * a.tok_sb, a.rps, a.V, L0, a.max_len, nullptr);
   __syncthreads();
   const int n = s_n;
   if (n == 0) return;
@@ -243,7 +251,9 @@ __global__ __launch_bounds__(kWG) void k_attn_mfma(AttnArgs a) {
   const float scale = 1.0f / sqrtf(float(HD));
   const int krow = 8 * (j >> 2) + (j & 3);  // this lane's K row in sub-tile 0 (+4 in sub-tile 1)
 
-  for (int q0 = 0; q0 < NQ; q0 += QB) {
+  for (int q0 = qgrp * QB; q0 < NQ; q0 += QB * nqgrp) {
+    // positions past the last row of this pass are masked for every query: not visited
+    const int p_stop = min(p_end, L0 + (min(NQ, q0 + QB) - 1) / G + 1);
     // queries of this pass as bf16 hi + lo in LDS (B operand of the scores); absent ones zero
     for (int idx = tid; idx < QB * (HD / 8); idx += kWG) {
       const int q = idx / (HD / 8), c = idx - q * (HD / 8), qi = q0 + q;
@@ -299,7 +309,7 @@ __global__ __launch_bounds__(kWG) void k_attn_mfma(AttnArgs a) {
     };
     // Two waves per SIMD hide the load latency of each other's slices (a register prefetch of
     // the next slice would cost that occupancy).
-    for (int pw = p_beg + 32 * wid; pw < p_end; pw += 128) {
+    for (int pw = p_beg + 32 * wid; pw < p_stop; pw += 128) {
       load(pw, ck, cv);
       __builtin_amdgcn_sched_barrier(0);  // all of the slice's loads are issued before any use
 #pragma unroll
@@ -398,19 +408,37 @@ __global__ __launch_bounds__(kWG) void k_attn_mfma(AttnArgs a) {
       }
       __syncthreads();
     }
-    float* P = a.part + (((long)b * a.nkv + kvh) * a.nsplit + s) * (long)a.qstride * (HD + 2);
-    for (int idx = tid; idx < QB * HD; idx += kWG) {
-      const int q = idx / HD, d = idx - q * HD;
-      if (q0 + q < NQ) P[(long)(q0 + q) * (HD + 2) + d] = sO[q * OP + d];
-    }
-    for (int q = tid; q < QB; q += kWG) {
-      if (q0 + q < NQ) {
+    if (a.out) {  // the only split: normalise here and write the output rows (no combine pass)
+      for (int q = tid; q < QB; q += kWG) {  // thread q alone reads and writes column q
         const float M = fmaxf(fmaxf(sm[0][q], sm[1][q]), fmaxf(sm[2][q], sm[3][q]));
         float L = 0.f;
         for (int w = 0; w < 4; ++w)
           if (sm[w][q] != -INFINITY) L += sl[w][q] * expf(sm[w][q] - M);
-        P[(long)(q0 + q) * (HD + 2) + HD] = M;
-        P[(long)(q0 + q) * (HD + 2) + HD + 1] = L;
+        sl[0][q] = L;
+      }
+      __syncthreads();
+      for (int idx = tid; idx < QB * HD; idx += kWG) {
+        const int q = idx / HD, d = idx - q * HD, qi = q0 + q;
+        if (qi < NQ) {
+          const int i = qi / G, g = qi - i * G;
+          a.out[(((long)b * a.rps + i) * a.nq + kvh * G + g) * HD + d] = sO[q * OP + d] / sl[0][q];
+        }
+      }
+    } else {
+      float* P = a.part + (((long)b * a.nkv + kvh) * a.nsplit + s) * (long)a.qstride * (HD + 2);
+      for (int idx = tid; idx < QB * HD; idx += kWG) {
+        const int q = idx / HD, d = idx - q * HD;
+        if (q0 + q < NQ) P[(long)(q0 + q) * (HD + 2) + d] = sO[q * OP + d];
+      }
+      for (int q = tid; q < QB; q += kWG) {
+        if (q0 + q < NQ) {
+          const float M = fmaxf(fmaxf(sm[0][q], sm[1][q]), fmaxf(sm[2][q], sm[3][q]));
+          float L = 0.f;
+          for (int w = 0; w < 4; ++w)
+            if (sm[w][q] != -INFINITY) L += sl[w][q] * expf(sm[w][q] - M);
+          P[(long)(q0 + q) * (HD + 2) + HD] = M;
+          P[(long)(q0 + q) * (HD + 2) + HD + 1] = L;
+        }
       }
     }
     __syncthreads();  // sm, sl, sO are reused by the next pass
@@ -425,7 +453,7 @@ __global__ __launch_bounds__(HD) void k_attn_combine(AttnArgs a, float* out) {
   const int item = blockIdx.x, d = threadIdx.x;
   const int row = item / a.nq, h = item - row * a.nq;
   const int b = row / a.rps, i = row - b * a.rps;
-  const int n = count_rows(a.tok + (long)b * a.tok_sb, a.rps, a.V, a.len[b], a.max_len, nullptr);
+  const int n = a.rows ? a.rows[b] : count_rows(a.tok + (long)b * a.tok_sb, a.rps, a.V, a.len[b], a.max_len, nullptr);
   if (i >= n) return;
   const int G = a.nq / a.nkv, kvh = h / G, qi = i * G + (h - kvh * G);
   const int Tn = a.len[b] + n;
@@ -456,19 +484,33 @@ __global__ __launch_bounds__(HD) void k_attn_combine(AttnArgs a, float* out) {
 // bf16 caches take the MFMA kernel: one query tile per pass, or two when a sequence has more
 // than 16 queries and the cache is large enough that a second pass over it would cost more than
 // the two-tile kernel's lower occupancy (64 MB of keys and values); fp32 caches the VALU kernel.
+// Query-block groups per (split, kv head, sequence): enough to give the launch ~2048 workgroups
+// when a sequence has many query blocks.
+inline int attn_qgroups(const AttnArgs& a, int qb) {
+  const int blocks = (a.qstride + qb - 1) / qb;
+  const int want = 2048 / (a.nsplit * a.nkv * a.B);
+  const int g = blocks < want ? blocks : want;
+  return g < 1 ? 1 : g;
+}
+
 template <int HD>
-void launch_attention(const AttnArgs& a, int wdtype, float* out, hipStream_t st) {
-  dim3 grid(a.nsplit, a.nkv, a.B);
+void launch_attention(AttnArgs a, int wdtype, float* out, hipStream_t st) {
+  a.out = nullptr;
   if (wdtype == MTP_BF16) {
+    if (a.nsplit == 1) a.out = out;
     const double kv_bytes = 4.0 * a.B * a.nkv * (double)a.max_len * HD;
-    if (a.qstride <= 16 || kv_bytes < 64.0 * 1024 * 1024)
+    if (a.qstride <= 16 || kv_bytes < 64.0 * 1024 * 1024) {
+      dim3 grid(a.nsplit, a.nkv * attn_qgroups(a, 16), a.B);
       hipLaunchKernelGGL((k_attn_mfma<HD, 1>), grid, dim3(kWG), 0, st, a);
-    else
+    } else {
+      dim3 grid(a.nsplit, a.nkv * attn_qgroups(a, 32), a.B);
       hipLaunchKernelGGL((k_attn_mfma<HD, 2>), grid, dim3(kWG), 0, st, a);
+    }
   } else {
+    dim3 grid(a.nsplit, a.nkv * attn_qgroups(a, kQB), a.B);
     hipLaunchKernelGGL((k_attn<F32, HD>), grid, dim3(kWG), 0, st, a);
   }
-  hipLaunchKernelGGL((k_attn_combine<HD>), dim3(a.B * a.rps * a.nq), dim3(HD), 0, st, a, out);
+  if (!a.out) hipLaunchKernelGGL((k_attn_combine<HD>), dim3(a.B * a.rps * a.nq), dim3(HD), 0, st, a, out);
 }
 
 hipError_t run_attention(const AttnArgs& a, int hd, int wdtype, float* out, hipStream_t st) {

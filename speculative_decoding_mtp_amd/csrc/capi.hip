@@ -113,18 +113,19 @@ int check_kv(const mtp_kv* kv) {
 struct DraftLayout {
   size_t off[15];
   size_t total;
+  int nsplit;  // attention splits the partial buffer is laid out for
 };
 
 DraftLayout draft_layout(const mtp_config& c, int B, int rps, int D, int max_len) {
   const size_t R = (size_t)B * (rps < 1 ? 1 : rps);
-  const int nsplit = attn_nsplit(B, c.n_kv_heads, max_len);
+  const int nsplit = attn_nsplit(B, c.n_kv_heads, max_len, (rps < 1 ? 1 : rps) * (c.n_heads / c.n_kv_heads));
   const size_t G = c.n_heads / c.n_kv_heads;
   size_t kmax = 2 * (size_t)c.hidden;
   if ((size_t)c.ffn > kmax) kmax = c.ffn;
   if ((size_t)c.n_heads * c.head_dim > kmax) kmax = (size_t)c.n_heads * c.head_dim;
   const bool mfma = c.wdtype == MTP_BF16 && R >= 3;  // more rows than one VALU GEMV pass may hold
   const size_t sizes[15] = {
-      256,                                                                   // status word
+      256 + (size_t)B * 8,                                                   // status word, row counts
       R * c.hidden * 4,                                                      // x
       R * c.n_heads * c.head_dim * 4,                                        // q
       (size_t)B * c.n_kv_heads * nsplit * (rps * G) * (c.head_dim + 2) * 4, // attention partials
@@ -146,6 +147,7 @@ DraftLayout draft_layout(const mtp_config& c, int B, int rps, int D, int max_len
     o += up256(sizes[i]);
   }
   L.total = o;
+  L.nsplit = nsplit;
   return L;
 }
 
@@ -153,6 +155,7 @@ DraftWs carve(void* ws, const DraftLayout& L) {
   char* base = static_cast<char*>(ws);
   DraftWs w;
   w.status = reinterpret_cast<int*>(base);
+  w.rows = reinterpret_cast<int*>(base + 256);
   w.x = reinterpret_cast<float*>(base + L.off[1]);
   w.q = reinterpret_cast<float*>(base + L.off[2]);
   w.attn_part = reinterpret_cast<float*>(base + L.off[3]);
@@ -197,7 +200,7 @@ StepArgs base_step(const mtp_config* cfg, const mtp_weights* w, const mtp_kv* kv
   s.kv_len = kv->len;
   s.B = kv->batch;
   s.max_len = kv->max_len;
-  s.nsplit = attn_nsplit(kv->batch, cfg->n_kv_heads, kv->max_len);
+  s.nsplit = L.nsplit;
   s.ws = carve(ws, L);
   s.stream = st;
   s.logits = nullptr;
@@ -209,9 +212,12 @@ StepArgs base_step(const mtp_config* cfg, const mtp_weights* w, const mtp_kv* kv
 }  // namespace
 
 namespace mtp {
-int attn_nsplit(int B, int nkv, int max_len) {
+int attn_nsplit(int B, int nkv, int max_len, int qrows) {
   int n = (512 + B * nkv - 1) / (B * nkv);  // about two resident workgroups per compute unit
   if (n > kMaxSplit) n = kMaxSplit;
+  // many queries per kv head (a long prefill): bound the partials to 8192 query rows per head
+  const int qcap = 8192 / (qrows < 1 ? 1 : qrows);
+  if (n > qcap) n = qcap;
   const int cap = (max_len + 63) / 64;
   if (n > cap) n = cap;
   return n < 1 ? 1 : n;

@@ -15,6 +15,9 @@ constexpr int kMaxSplit = 128;     // attention splits per (sequence, kv head)
 constexpr int kMaxGemvGrid = 2048; // workgroups of one GEMV launch (also sizes the lm_head partials)
 constexpr int kMaxKSplit = 16;     // K ranges of a split-K MFMA GEMM
 constexpr long kPartCols = 98304;  // split-K partial columns per activation row (ksplit x N)
+// Calls with more rows per sequence than this (a prefill) count each sequence's valid rows once
+// per step into the workspace; shorter ones count them inside every kernel.
+constexpr int kInlineRows = 16;
 
 // Positions per attention split for a sequence of T cached positions (a multiple of 64).
 __host__ __device__ inline int attn_chunk(int T, int nsplit) {
@@ -30,11 +33,14 @@ struct AttnArgs {
   int tok_sb;
   const int32_t* len;
   int B, rps, nq, nkv, max_len, V, nsplit, qstride;
-  float* part;  // [B][nkv][nsplit][qstride][hd + 2]
+  float* part;       // [B][nkv][nsplit][qstride][hd + 2]
+  const int* rows;   // NULL, or the valid rows of sequence b at rows[b]
+  float* out;        // set by run_attention: one split of a bf16 cache writes the output rows here
 };
 
 // Arguments of the lm_head finalisation kernel.
 struct LmFinal {
+  int B;
   const int32_t* tok;
   int tok_sb, rps, V;
   int32_t* len;
@@ -51,11 +57,13 @@ struct LmFinal {
   int32_t* draft;
   int dr_sb;
   int* status;
+  const int* rows;  // NULL, or rows[b] = valid rows, rows[B + b] = the flags that ended them
 };
 
 // Carved out of the caller's workspace.
 struct DraftWs {
   int* status;
+  int* rows;  // [2B] per-sequence valid rows and flags of many-row calls
   float* x;
   float* q;
   float* attn_part;
@@ -103,9 +111,10 @@ struct GemvPlan {
 };
 GemvPlan plan_gemv(int nact, int K, int VE, int N);
 
-int attn_nsplit(int B, int nkv, int max_len);
+int attn_nsplit(int B, int nkv, int max_len, int qrows);
 hipError_t run_attention(const AttnArgs& a, int hd, int wdtype, float* out, hipStream_t st);
 hipError_t run_step(const StepArgs& s);
+hipError_t count_step_rows(const StepArgs& s);  // k_count_rows into s.ws.rows
 
 struct BF16;
 struct F32;

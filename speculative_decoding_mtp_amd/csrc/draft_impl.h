@@ -38,13 +38,14 @@ struct PBase {
   int max_len, V;
   int K, N, nact, split;
   float eps;
+  const int* rows;      // NULL, or valid rows counted once for the step
   const int* lds_len;  // cache lengths in LDS, set by setup()
 
   __device__ void setup(int* s_n, int* s_len) {
     for (int b = threadIdx.x; b < B; b += kWG) {
       const int l = len[b];
       s_len[b] = l;
-      s_n[b] = count_rows(tok + (long)b * tok_sb, rps, V, l, max_len, nullptr);
+      s_n[b] = rows ? rows[b] : count_rows(tok + (long)b * tok_sb, rps, V, l, max_len, nullptr);
     }
     lds_len = s_len;
   }
@@ -251,16 +252,18 @@ struct PLogits : PBase<W> {
 
 // The target's input: x[row] = E[tok] (fp32) for the valid rows; one workgroup per row.
 template <class W>
-__global__ __launch_bounds__(kWG) void k_embed_rows(const void* embed, const int32_t* tok, int rps, int V,
-                                                    const int32_t* len, int max_len, int H, float* x) {
+__global__ __launch_bounds__(kWG) void k_embed_rows(const void* embed, const int32_t* tok, int tok_sb, int rps,
+                                                    int V, const int32_t* len, int max_len, int H, float* x,
+                                                    const int* rows) {
   using T = typename W::T;
   constexpr int VE = W::VE;
   __shared__ int s_n;
   const int row = blockIdx.x, b = row / rps, i = row - b * rps;
-  if (threadIdx.x == 0) s_n = count_rows(tok + (long)b * rps, rps, V, len[b], max_len, nullptr);
+  if (threadIdx.x == 0)
+    s_n = rows ? rows[b] : count_rows(tok + (long)b * tok_sb, rps, V, len[b], max_len, nullptr);
   __syncthreads();
   if (i >= s_n) return;
-  const T* e = reinterpret_cast<const T*>(embed) + (long)tok[(long)b * rps + i] * H;
+  const T* e = reinterpret_cast<const T*>(embed) + (long)tok[(long)b * tok_sb + i] * H;
   for (int k = threadIdx.x * VE; k < H; k += kWG * VE) {
     float f[VE];
     W::cvt(ld16(e + k), f);
@@ -277,10 +280,10 @@ __global__ __launch_bounds__(kWG) void k_lm_finalize(LmFinal f) {
   using T = typename W::T;
   __shared__ float sv[4];
   __shared__ int si[4];
-  __shared__ float red[8];
   const int b = blockIdx.x, tid = threadIdx.x;
   int flags = 0;
-  const int n = count_rows(f.tok + (long)b * f.tok_sb, f.rps, f.V, f.len[b], f.max_len, &flags);
+  const int n = f.rows ? f.rows[b] : count_rows(f.tok + (long)b * f.tok_sb, f.rps, f.V, f.len[b], f.max_len, &flags);
+  if (f.rows) flags = f.rows[f.B + b];
   float v = -INFINITY;
   int id = 0x7fffffff;
   for (int k = tid; k < f.nparts; k += kWG) {
@@ -323,6 +326,38 @@ __global__ __launch_bounds__(kWG) void k_lm_finalize(LmFinal f) {
   }
 }
 
+// The post-norm hiddens of many rows (a prefill): one wave per row of the flattened [B][rps]
+// rows, launched before k_lm_finalize grows the cache lengths.
+template <class W>
+__global__ __launch_bounds__(kWG) void k_hidden_out(LmFinal f) {
+  using T = typename W::T;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * (kWG / 64) + (threadIdx.x >> 6);
+  if (row >= f.B * f.rps) return;
+  const int b = row / f.rps, i = row - b * f.rps;
+  const int n = f.rows ? f.rows[b] : count_rows(f.tok + (long)b * f.tok_sb, f.rps, f.V, f.len[b], f.max_len, nullptr);
+  if (i >= n || (f.hout_last && i != n - 1)) return;
+  const float* xr = f.x + (long)row * f.H;
+  float ss = 0.f;
+  for (int k = lane; k < f.H; k += 64) ss += xr[k] * xr[k];
+  ss = wave_sum(ss);
+  const float sc = 1.0f / sqrtf(ss / float(f.H) + f.eps);
+  const T* g = reinterpret_cast<const T*>(f.gain);
+  float* dst = f.hout + ((long)b * f.hout_sb + (f.hout_last ? 0 : i)) * f.H;
+  for (int k = lane; k < f.H; k += 64) dst[k] = xr[k] * sc * W::get(g, k);
+}
+
+// k_lm_finalize, with the hiddens of many-row calls written by k_hidden_out first.
+template <class W>
+hipError_t launch_finalize(LmFinal f, hipStream_t st) {
+  if (f.hout && f.rps >= 8) {
+    hipLaunchKernelGGL((k_hidden_out<W>), dim3((f.B * f.rps + kWG / 64 - 1) / (kWG / 64)), dim3(kWG), 0, st, f);
+    f.hout = nullptr;
+  }
+  hipLaunchKernelGGL((k_lm_finalize<W>), dim3(f.B), dim3(kWG), 0, st, f);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------------------------
 // launch selection
 // ---------------------------------------------------------------------------------------------
@@ -361,9 +396,13 @@ hipError_t launch_mfma(P& p, hipStream_t st, int* grid_used, const MfmaBufs& mb)
   constexpr int NT = (P::kArgmax || P::kVocab) ? 2 : 1;  // 128 weight rows per workgroup for lm_head, else 64
   MfmaBufs m = mb;
   const int groups = (p.N + 4 * NT * 16 - 1) / (4 * NT * 16);
+  // passes of MG activation tiles (at most: the valid rows are counted on the device); long
+  // prefills spread their passes over the grid instead of splitting K
+  const int npass = P::kArgmax ? 1 : (p.nact + MG * 16 - 1) / (MG * 16);
+  const int par = npass > 2 ? npass * groups : groups;
   int ks = 1;
-  if (!P::kArgmax && groups < kMfmaItems && m.part) {
-    ks = (kMfmaItems + groups - 1) / groups;
+  if (!P::kArgmax && par < kMfmaItems && m.part) {
+    ks = (kMfmaItems + par - 1) / par;
     const int kc = p.K / kMfmaKC;
     if (ks > kc) ks = kc;
     if (ks > kMaxKSplit) ks = kMaxKSplit;
@@ -373,7 +412,7 @@ hipError_t launch_mfma(P& p, hipStream_t st, int* grid_used, const MfmaBufs& mb)
   if (ks <= 1) m.part = nullptr;
   m.ksplit = ks;
   static int cap = 0;
-  int grid = min(groups * ks, resident_cap(k_gemm_mfma<P, NT, MG>, &cap));
+  int grid = min(npass * groups * ks, resident_cap(k_gemm_mfma<P, NT, MG>, &cap));
   grid = min(grid, kMaxGemvGrid);
   if (grid_used) *grid_used = grid;
   hipLaunchKernelGGL((k_gemm_mfma<P, NT, MG>), dim3(grid), dim3(kWG), 0, st, p, m);
@@ -427,6 +466,9 @@ hipError_t launch_gemv(P& p, hipStream_t st, int* grid_used = nullptr, const Mfm
   return hipErrorInvalidValue;
 }
 
+// The per-step row counts when the call has many rows per sequence, else NULL.
+inline const int* step_rows(const StepArgs& s) { return s.rps > kInlineRows ? s.ws.rows : nullptr; }
+
 template <class W, class P>
 void fill_base(P& p, const StepArgs& s) {
   p.tok = s.tok;
@@ -438,6 +480,7 @@ void fill_base(P& p, const StepArgs& s) {
   p.V = s.cfg.vocab;
   p.eps = s.cfg.rms_eps;
   p.split = 0;
+  p.rows = step_rows(s);
 }
 
 template <class W>
@@ -451,9 +494,10 @@ hipError_t run_step_t(const StepArgs& s) {
                          s.ws.kpart_cap};
   const MfmaBufs* mb = s.ws.xhi ? &mbuf : nullptr;
 
+  if (step_rows(s) && (e = count_step_rows(s)) != hipSuccess) return e;
   if (s.target) {  // the target's input: token embeddings
-    hipLaunchKernelGGL((k_embed_rows<W>), dim3(R), dim3(kWG), 0, s.stream, s.tw->embed, s.tok, s.rps, c.vocab,
-                       s.kv_len, s.max_len, H, s.ws.x);
+    hipLaunchKernelGGL((k_embed_rows<W>), dim3(R), dim3(kWG), 0, s.stream, s.tw->embed, s.tok, s.tok_sb, s.rps,
+                       c.vocab, s.kv_len, s.max_len, H, s.ws.x, step_rows(s));
     if ((e = hipGetLastError()) != hipSuccess) return e;
   } else {  // eh_proj
     PEhProj<W> p;
@@ -514,6 +558,7 @@ hipError_t run_step_t(const StepArgs& s) {
       a.nsplit = s.nsplit;
       a.qstride = s.rps * (nq / nkv);
       a.part = s.ws.attn_part;
+      a.rows = step_rows(s);
       if ((e = run_attention(a, hd, c.wdtype, s.ws.attn_out, s.stream)) != hipSuccess) return e;
     }
     {  // o_proj + residual
@@ -567,6 +612,7 @@ hipError_t run_step_t(const StepArgs& s) {
     p.logits = s.logits;
     if ((e = launch_gemv<W>(p, s.stream, nullptr, mb)) != hipSuccess) return e;
     LmFinal f;
+    f.B = s.B;
     f.tok = s.tok;
     f.tok_sb = s.tok_sb;
     f.rps = s.rps;
@@ -586,8 +632,8 @@ hipError_t run_step_t(const StepArgs& s) {
     f.draft = nullptr;
     f.dr_sb = 0;
     f.status = s.ws.status;
-    hipLaunchKernelGGL((k_lm_finalize<W>), dim3(s.B), dim3(kWG), 0, s.stream, f);
-    return hipGetLastError();
+    f.rows = step_rows(s);
+    return launch_finalize<W>(f, s.stream);
   }
   {  // final norm + lm_head + argmax + finalisation
     PLmHead<W> p;
@@ -609,6 +655,7 @@ hipError_t run_step_t(const StepArgs& s) {
     if (s.ev_end) (void)hipEventRecord(s.ev_end, s.stream);
     if (e != hipSuccess) return e;
     LmFinal f;
+    f.B = s.B;
     f.tok = s.tok;
     f.tok_sb = s.tok_sb;
     f.rps = s.rps;
@@ -628,8 +675,8 @@ hipError_t run_step_t(const StepArgs& s) {
     f.draft = s.draft;
     f.dr_sb = s.dr_sb;
     f.status = s.ws.status;
-    hipLaunchKernelGGL((k_lm_finalize<W>), dim3(s.B), dim3(kWG), 0, s.stream, f);
-    e = hipGetLastError();
+    f.rows = step_rows(s);
+    e = launch_finalize<W>(f, s.stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -154,7 +154,17 @@ __global__ __launch_bounds__(kWG, MG <= 4 ? 2 : 1) void k_gemm_mfma(P p, MfmaBuf
   const int ks = mb.part ? mb.ksplit : 1;           // K ranges per row group
   const int kper = (Kc + ks - 1) / ks;
 
-  for (int mg0 = 0; mg0 < count; mg0 += MG * 16) {
+  const int npass = (count + MG * 16 - 1) / (MG * 16);  // passes of MG activation tiles
+  const int per_pass = ngroups * ks;
+  // lm_head (argmax) walks the passes in order (each workgroup's running bests are flushed per
+  // pass); the other policies spread their (pass, row group, K range) items over the grid
+  const int outer = P::kArgmax ? npass : (npass > 0 ? 1 : 0);
+  for (int op = 0; op < outer; ++op) {
+   const int n_items = P::kArgmax ? per_pass : npass * per_pass;
+   for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
+    const int pass = P::kArgmax ? op : it / per_pass;
+    const int gk = P::kArgmax ? it : it - pass * per_pass;
+    const int mg0 = pass * MG * 16;
     const int mrows = min(MG * 16, count - mg0);
     const int mt = (mrows + 15) / 16;
     const int srows = mt * 16;                        // staged rows (zero past mrows)
@@ -181,7 +191,7 @@ __global__ __launch_bounds__(kWG, MG <= 4 ? 2 : 1) void k_gemm_mfma(P p, MfmaBuf
         if (idx < nav) *reinterpret_cast<uint4*>(&sA[buf][half][r * kMfmaLdr + cv * 8]) = st[v];
       }
     };
-    for (int gk = blockIdx.x; gk < ngroups * ks; gk += gridDim.x) {
+    {
       const int g = gk / ks, kpart = gk - g * ks;
       const int kc_beg = kpart * kper, kc_end = min(Kc, kc_beg + kper);
       const int n0 = g * rows_per_wg + wid * WR;
@@ -327,7 +337,9 @@ __global__ __launch_bounds__(kWG, MG <= 4 ? 2 : 1) void k_gemm_mfma(P p, MfmaBuf
         }
       }
     }
+   }
     if constexpr (P::kArgmax) {
+      const int mg0 = op * MG * 16, mrows = min(MG * 16, count - mg0);
       __syncthreads();
       for (int k = tid; k < mrows; k += kWG) {
         float v = -INFINITY;
