@@ -24,6 +24,7 @@ __all__ = [
     "greedy_verify", "warp", "sample", "residual", "sampling_verify", "spec_verify",
     "kv_crop", "state_snapshot", "state_restore", "spec_decode", "VerifyResult",
     "TargetModel", "target_row", "target_forward", "DenseTarget",
+    "shared_block", "mtp_row_shared", "draft_loop_shared",
 ]
 
 
@@ -389,6 +390,91 @@ def draft_loop(model: OracleModel, cache: KVCache, tokens, hiddens, D: int, want
         hid[:, k] = hout[:, 0]
         if want_logits:
             logits[:, k] = lg
+    return drafts, hid, logits, margins
+
+
+# --------------------------------------------------------------------------------------------
+# a head with no cache of its own: it reads the main model's keys and values
+# --------------------------------------------------------------------------------------------
+def shared_block(model: OracleModel, layer: int, tcache: KVCache, tlayer: int, b: int, x, pos: int) -> np.ndarray:
+    """The head's decoder block when it keeps no K/V ([DLM "MTP speculative
+    decoding"] item 1: the drafter has no KV cache and reads the main model's
+    keys and values).  q = W_q rms(x), rotated at ``pos``; the keys and values
+    are the main model's cache of layer ``tlayer`` for sequence ``b``, positions
+    [0, len_b); nothing is appended.  Readings: every cached position is visible
+    (the main model has only cached positions before the row's); the head's own
+    q/kv head grouping is used over the main model's kv heads (same count and
+    head size); an empty cache contributes a zero attention output.  The output
+    projection and the SwiGLU part are those of the ordinary block."""
+    cfg = model.cfg
+    w = model.layers[layer]
+    nq, nkv, hd = cfg.n_heads, cfg.n_kv_heads, cfg.head_dim
+    x = np.asarray(x, dtype=F64)
+    a = rms_norm(x, w["in_norm"], cfg.rms_eps)
+    q = rope((w["wq"] @ a).reshape(nq, hd), pos, cfg.rope_theta)
+    L = int(tcache.len[b])
+    group = nq // nkv
+    o = np.zeros((nq, hd), dtype=F64)
+    if L > 0:
+        for h in range(nq):
+            g = h // group
+            o[h] = attend(q[h], tcache.K[tlayer, b, g, :L], tcache.V[tlayer, b, g, :L])
+    x = x + w["wo"] @ o.reshape(-1)
+    m = rms_norm(x, w["post_norm"], cfg.rms_eps)
+    x = x + w["wdown"] @ (silu(w["wgate"] @ m) * (w["wup"] @ m))
+    return x
+
+
+def mtp_row_shared(model: OracleModel, tcache: KVCache, kv_layers, b: int, tok: int, hidden, pos: int):
+    """``mtp_row`` for a head that reads the main model's cache: head layer l
+    attends over the main model's layer ``kv_layers[l]``.  Returns (g, draft,
+    logits, margin)."""
+    cfg = model.cfg
+    if not (0 <= tok < cfg.vocab):
+        raise IndexError(f"token {tok} outside the vocabulary")
+    e = np.asarray(model.embed[tok], dtype=F64)
+    cat = np.concatenate([rms_norm(e, model.enorm, cfg.rms_eps),
+                          rms_norm(hidden, model.hnorm, cfg.rms_eps)])
+    x = model.eh_proj @ cat
+    for layer in range(cfg.n_layers):
+        x = shared_block(model, layer, tcache, int(kv_layers[layer]), b, x, pos)
+    g = rms_norm(x, model.final_norm, cfg.rms_eps)
+    logits = model.lm_head @ g
+    draft, margin = argmax_lowest(logits)
+    return g, draft, logits, margin
+
+
+def draft_loop_shared(model: OracleModel, tcache: KVCache, kv_layers, tokens, hiddens, D: int,
+                      want_logits: bool = True):
+    """D serial draft steps of a head that reads the main model's cache.
+
+    tokens [B]: the settled next token x_n (negative: no drafts for the
+    sequence); hiddens [B][H]: the main model's hidden at its last cached
+    position.  With no cache of its own the head needs no catch-up rows: step 1
+    is the row (x_n, h) at the main model's last cached position len_b - 1,
+    step k (k >= 2) the row (d_{k-1}, g_{k-1}) one position later each time
+    ([YL 三 stage 2] feeding, as in ``draft_loop``).  The main model's cache
+    and its length are read only.  A sequence whose main-model cache is empty
+    has no hidden to start from and gets no drafts.  Returns drafts [B][D],
+    hiddens [B][D][H], logits [B][D][V], margins [B][D]."""
+    tokens = np.asarray(tokens).reshape(-1)
+    B = tokens.shape[0]
+    H, V = model.cfg.hidden, model.cfg.vocab
+    drafts = np.full((B, D), -1, dtype=np.int64)
+    hid = np.zeros((B, D, H), dtype=F64)
+    logits = np.zeros((B, D, V), dtype=F64) if want_logits else None
+    margins = np.full((B, D), np.inf)
+    for b in range(B):
+        L = int(tcache.len[b])
+        if tokens[b] < 0 or L == 0:
+            continue
+        tok, h = int(tokens[b]), hiddens[b]
+        for k in range(D):
+            g, d, lg, mg = mtp_row_shared(model, tcache, kv_layers, b, tok, h, L - 1 + k)
+            drafts[b, k], hid[b, k], margins[b, k] = d, g, mg
+            if want_logits:
+                logits[b, k] = lg
+            tok, h = d, g
     return drafts, hid, logits, margins
 
 
