@@ -17,7 +17,9 @@ a bounded sample of the same workload.  --config names another head workload (dr
 or, with --config stress, the verifier alone (B=256, D=4, vocab 151936, sampling).
 --target-layers L times the target's verify pass instead: a dense stand-in with the head's
 dimensions and L blocks, scoring 1, 2 or 7 positions per call.  --prefill-rows N times one MTP
-prefill call over N prompt rows.
+prefill call over N prompt rows.  --shared-kv T runs the same rounds with a head that keeps no
+cache of its own and reads a T-layer main-model cache (head layer l reads layer l mod T) through
+mtp_draft_loop_shared_kv; the main model's cache length then follows the verifier's crop length.
 """
 import argparse
 import hashlib
@@ -48,6 +50,8 @@ def parse():
                     help="time one MTP prefill of this many rows per sequence instead (from an empty cache)")
     ap.add_argument("--target-layers", type=int, default=0,
                     help="time the target's verify pass instead (a dense stand-in with this many layers)")
+    ap.add_argument("--shared-kv", type=int, default=0,
+                    help="the head keeps no cache and reads a main-model cache of this many layers instead")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB first (counter calibration)")
     return ap.parse_args()
@@ -80,8 +84,21 @@ def main():
     w = make_weights(cfg)
     c = config(cfg)
     gw = upload_weights(cfg, w)
-    K, Vv = make_kv_prefix(cfg)
-    kv = kv_from_numpy(cfg, K, Vv, cfg.ctx, max_len)
+    T = args.shared_kv
+    if T:
+        # the main model's cache: seeded N(0,1) keys and values in every slot, ctx + 1 positions
+        # cached at the start (the settled token's predecessor included)
+        kv = M.KVCache(c, B, max_len, n_layers=T)
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(1000 * cfg.index + 3)
+        kv.k.copy_(torch.randn(kv.k.shape, generator=gen, device="cuda"))
+        kv.v.copy_(torch.randn(kv.v.shape, generator=gen, device="cuda"))
+        kv.len.fill_(cfg.ctx + 1)
+        kv_layer = [l % T for l in range(cfg.n_layers)]
+        K = Vv = None
+    else:
+        K, Vv = make_kv_prefix(cfg)
+        kv = kv_from_numpy(cfg, K, Vv, cfg.ctx, max_len)
     print(f"[bench] inputs ready in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
 
     if args.calib_copy_mb:
@@ -103,7 +120,11 @@ def main():
     noise_bufs = [f32(make_round_noise(cfg, r)) for r in range(NBUF)]
     tokens = i32(tok_pad)
     hidden0 = f32(hid_pad)
-    ws = M.new_workspace(M.mtp_draft_workspace_size(c, B, rps, D, max_len))
+    ws = M.new_workspace(M.mtp_draft_workspace_size(c, B, 1 if T else rps, D, max_len))
+    if T:  # one settled token and one main-model hidden per sequence and round
+        tok_shared = i32(toks0[:, 0])
+        hid_shared = [f32(np.ascontiguousarray(make_round_hiddens(cfg, r)[:, 0])) for r in range(NBUF)]
+        hid_shared0 = f32(np.ascontiguousarray(hid0[:, 0]))
     sp = cfg.sampling
     csp = None if sp is None else M.sampling(sp.temperature, sp.top_k, sp.top_p, sp.q_mode)
     vws = M.new_workspace(M.spec_verify_workspace_size(B, D, V, csp))
@@ -123,9 +144,15 @@ def main():
 
     def step(r):
         cur, nxt = r % 2, (r + 1) % 2
-        tk = tokens if r == 0 else out_tok[cur]
-        hin = hidden0 if r == 0 else hid_bufs[r % NBUF]
-        M.mtp_draft_loop(c, gw, kv, D, rps, tk, hin, drafts, hiddens, dlog, ws)
+        if T:
+            if r > 0:  # the last emitted token of the previous round is the settled one
+                torch.gather(out_tok[cur], 1, hist[r - 1].long().unsqueeze(1), out=tok_shared.view(B, 1))
+            hin = hid_shared0 if r == 0 else hid_shared[r % NBUF]
+            M.mtp_draft_loop_shared_kv(c, gw, kv, kv_layer, D, tok_shared, hin, drafts, hiddens, dlog, ws)
+        else:
+            tk = tokens if r == 0 else out_tok[cur]
+            hin = hidden0 if r == 0 else hid_bufs[r % NBUF]
+            M.mtp_draft_loop(c, gw, kv, D, rps, tk, hin, drafts, hiddens, dlog, ws)
         # stand-in target forward: target row j = draft logits of step j+1 + noise (row D
         # reuses step D's logits), one elementwise kernel for D = 1
         noise = noise_bufs[r % NBUF]
@@ -141,7 +168,10 @@ def main():
         M.spec_verify(B, D, V, tl, drafts, None, csp, ua, us, ctx[cur], n_acc, out_tok[nxt], ctx[nxt], vws)
         if state is not None:
             M.mtp_state_restore(state, snap, state_bytes, B, n_acc, D)
-        M.kv_crop(kv, ctx[cur])
+        if T:  # stand-in for the main model's verify pass + crop: its cache now ends at crop_len
+            kv.len.copy_(ctx[nxt])
+        else:
+            M.kv_crop(kv, ctx[cur])
 
     for r in range(args.warmup):
         step(r)
@@ -202,7 +232,7 @@ def main():
             traffic = rec.get("bytes_per_launch")
 
     cpu = None
-    if args.cpu_seconds > 0:
+    if args.cpu_seconds > 0 and not T:
         cpu = cpu_baseline(cfg, w, K, Vv, args.cpu_seconds)
 
     line = {
@@ -210,7 +240,9 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded random-init weights, KV prefix, hiddens and target-logit noise)",
-        "config": {"workload": cfg.name, "batch": B, "draft_tokens": D, "kv_context": cfg.ctx,
+        "config": {"workload": cfg.name + (f"-sharedkv{T}" if T else ""), "batch": B, "draft_tokens": D,
+                   "kv_context": cfg.ctx,
+                   "head_kv": f"reads a {T}-layer main-model cache (layer l mod {T})" if T else "own cache",
                    "target_noise_std": cfg.noise_std,
                    "verify": "greedy" if sp is None else
                    f"sampling T={sp.temperature} top_k={sp.top_k} top_p={sp.top_p} q_mode={sp.q_mode}",

@@ -143,6 +143,28 @@ int mtp_draft_loop(const mtp_config* cfg, const mtp_weights* w, const mtp_kv* kv
                    int32_t rows_per_seq, const int32_t* tokens, const float* hidden_in, int32_t* drafts,
                    float* hiddens, float* draft_logits, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* The D-step draft loop of a head that keeps no KV cache of its own and reads the main model's
+ * keys and values ([DLM "MTP speculative decoding"] item 1: the drafter has no cache and reads the
+ * model's keys and values directly; its input is the last token's embedding beside the model's
+ * last hidden).  target_kv is the main model's cache: `target_layers` layers in the mtp_kv layout,
+ * with cfg->n_kv_heads and cfg->head_dim, B = target_kv->batch.  Head layer l attends over layer
+ * kv_layer[l] (HOST array of cfg->n_layers entries in [0, target_layers)) at positions
+ * 0 .. target_kv->len[b] - 1.  The head projects q only (w->layers[l].wk / .wv are not read and
+ * may be NULL), appends nothing, and leaves target_kv->len unchanged.
+ *   tokens    [B]     the settled next token of each sequence; negative: no drafts.
+ *   hidden_in [B][H]  the main model's post-final-norm hidden at its last cached position.
+ * Step 1 is the row (tokens[b], hidden_in[b]) at position len[b] - 1; step k >= 2 the row
+ * (draft k-1, output hidden k-1) at position len[b] + k - 2.  A sequence whose cache is empty
+ * (len[b] == 0) gets no drafts.  No catch-up rows are needed: there is no head cache to fill.
+ *   drafts [B][D], hiddens [B][D][H] or NULL, draft_logits [B][D][V] or NULL: as in
+ *   mtp_draft_loop (-1 / untouched for sequences without drafts).
+ * Workspace: mtp_draft_workspace_size(cfg, B, 1, D, target_kv->max_len).  A token id >= vocab is
+ * reported through mtp_check (MTP_ERR_TOKEN); there is no capacity error. */
+int mtp_draft_loop_shared_kv(const mtp_config* cfg, const mtp_weights* w, const mtp_kv* target_kv,
+                             int32_t target_layers, const int32_t* kv_layer, int32_t D, const int32_t* tokens,
+                             const float* hidden_in, int32_t* drafts, float* hiddens, float* draft_logits, void* ws,
+                             size_t ws_bytes, hipStream_t stream);
+
 /* Bytes of workspace spec_verify needs. */
 int spec_verify_workspace_size(int32_t B, int32_t D, int32_t V, const mtp_sampling* sp, size_t* bytes);
 

@@ -80,6 +80,8 @@ _sigs = {
                         _P, _P, _P, _SZ, _P], _I),
     "mtp_draft_loop": ([ctypes.POINTER(MtpConfig), ctypes.POINTER(MtpWeights), ctypes.POINTER(MtpKV), _I, _I, _P, _P,
                         _P, _P, _P, _P, _SZ, _P], _I),
+    "mtp_draft_loop_shared_kv": ([ctypes.POINTER(MtpConfig), ctypes.POINTER(MtpWeights), ctypes.POINTER(MtpKV), _I,
+                                  ctypes.POINTER(_I), _I, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
     "spec_verify_workspace_size": ([_I, _I, _I, ctypes.POINTER(MtpSampling), ctypes.POINTER(_SZ)], _I),
     "spec_verify": ([_I, _I, _I, _P, _P, _P, ctypes.POINTER(MtpSampling), _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
     "kv_crop": ([ctypes.POINTER(MtpKV), _P, _P], _I),
@@ -197,13 +199,13 @@ class KVCache:
     """The head's cache: keys [n_layers][batch][n_kv_heads][max_len][head_dim], values transposed
     [n_layers][batch][n_kv_heads][head_dim][max_len], lengths [batch].  max_len: multiple of 8."""
 
-    def __init__(self, cfg: Config, batch: int, max_len: int, device="cuda"):
+    def __init__(self, cfg: Config, batch: int, max_len: int, device="cuda", n_layers: Optional[int] = None):
         if max_len < 8 or max_len % 8:
             raise MTPError(-1, f"max_len must be a positive multiple of 8, got {max_len}")
-        self.k = torch.zeros((cfg.n_layers, batch, cfg.n_kv_heads, max_len, cfg.head_dim),
-                             dtype=cfg.torch_dtype, device=device)
-        self.v = torch.zeros((cfg.n_layers, batch, cfg.n_kv_heads, cfg.head_dim, max_len),
-                             dtype=cfg.torch_dtype, device=device)
+        L = cfg.n_layers if n_layers is None else n_layers
+        self.k = torch.zeros((L, batch, cfg.n_kv_heads, max_len, cfg.head_dim), dtype=cfg.torch_dtype, device=device)
+        self.v = torch.zeros((L, batch, cfg.n_kv_heads, cfg.head_dim, max_len), dtype=cfg.torch_dtype, device=device)
+        self.n_layers = L
         self.len = torch.zeros(batch, dtype=torch.int32, device=device)
         self.batch, self.max_len = batch, max_len
 
@@ -263,6 +265,20 @@ def mtp_draft_loop(cfg: Config, w: Weights, kv: KVCache, D: int, rows_per_seq: i
     _check(_lib.mtp_draft_loop(
         ctypes.byref(cfg.c()), ctypes.byref(w.c), ctypes.byref(kv.c()), D, rows_per_seq,
         _ptr(tokens, torch.int32, "tokens", R), _ptr(hidden_in, torch.float32, "hidden_in", R * H),
+        _ptr(drafts, torch.int32, "drafts", B * D), _ptr(hiddens, torch.float32, "hiddens", B * D * H),
+        _ptr(draft_logits, torch.float32, "draft_logits", B * D * cfg.vocab), _ptr(ws, None, "ws"), ws.numel(),
+        _stream(stream)))
+
+
+def mtp_draft_loop_shared_kv(cfg: Config, w: Weights, target_kv: KVCache, kv_layer, D: int, tokens, hidden_in,
+                             drafts, hiddens, draft_logits, ws: torch.Tensor, stream=None) -> None:
+    B, H = target_kv.batch, cfg.hidden
+    if len(kv_layer) != cfg.n_layers:
+        raise MTPError(-1, f"kv_layer needs {cfg.n_layers} entries")
+    layers = (_I * cfg.n_layers)(*[int(x) for x in kv_layer])
+    _check(_lib.mtp_draft_loop_shared_kv(
+        ctypes.byref(cfg.c()), ctypes.byref(w.c), ctypes.byref(target_kv.c()), target_kv.n_layers, layers, D,
+        _ptr(tokens, torch.int32, "tokens", B), _ptr(hidden_in, torch.float32, "hidden_in", B * H),
         _ptr(drafts, torch.int32, "drafts", B * D), _ptr(hiddens, torch.float32, "hiddens", B * D * H),
         _ptr(draft_logits, torch.float32, "draft_logits", B * D * cfg.vocab), _ptr(ws, None, "ws"), ws.numel(),
         _stream(stream)))

@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kWG) void k_attn(AttnArgs a) {
   __syncthreads();
   const int n = s_n;
   if (n == 0) return;
-  const int Tn = L0 + n;
+  const int Tn = L0 + (a.shared ? 0 : n);
   const int chunk = attn_chunk(Tn, a.nsplit);
   const int p_beg = s * chunk;
   if (p_beg >= Tn) return;
@@ -240,7 +240,7 @@ __global__ __launch_bounds__(kWG) void k_attn_mfma(AttnArgs a) {
   __syncthreads();
   const int n = s_n;
   if (n == 0) return;
-  const int Tn = L0 + n;
+  const int Tn = L0 + (a.shared ? 0 : n);
   const int chunk = attn_chunk(Tn, a.nsplit);
   const int p_beg = s * chunk;
   if (p_beg >= Tn) return;
@@ -446,22 +446,26 @@ __global__ __launch_bounds__(kWG) void k_attn_mfma(AttnArgs a) {
 }
 
 // Merge the split partials of one (row, query head): o = sum_s o_s e^{m_s - M} / sum_s l_s e^{m_s - M}.
+// kWG / HD thread groups take every (kWG / HD)-th split, summed in LDS at the end.
 template <int HD>
-__global__ __launch_bounds__(HD) void k_attn_combine(AttnArgs a, float* out) {
+__global__ __launch_bounds__(kWG) void k_attn_combine(AttnArgs a, float* out) {
+  constexpr int NG = kWG / HD;
   __shared__ float sw[kMaxSplit];
   __shared__ float sl[kMaxSplit];
-  const int item = blockIdx.x, d = threadIdx.x;
+  __shared__ float so[NG][HD];
+  __shared__ float sL[NG];
+  const int item = blockIdx.x, tid = threadIdx.x, d = tid % HD, grp = tid / HD;
   const int row = item / a.nq, h = item - row * a.nq;
   const int b = row / a.rps, i = row - b * a.rps;
   const int n = a.rows ? a.rows[b] : count_rows(a.tok + (long)b * a.tok_sb, a.rps, a.V, a.len[b], a.max_len, nullptr);
   if (i >= n) return;
   const int G = a.nq / a.nkv, kvh = h / G, qi = i * G + (h - kvh * G);
-  const int Tn = a.len[b] + n;
+  const int Tn = a.len[b] + (a.shared ? 0 : n);
   const int chunk = attn_chunk(Tn, a.nsplit);
   const int ns = min(a.nsplit, (Tn + chunk - 1) / chunk);
   const long sstride = (long)a.qstride * (HD + 2);
   const float* P = a.part + ((long)b * a.nkv + kvh) * a.nsplit * sstride + (long)qi * (HD + 2);
-  for (int s = d; s < ns; s += HD) {
+  for (int s = tid; s < ns; s += kWG) {
     const float l = P[s * sstride + HD + 1];
     sw[s] = l > 0.f ? P[s * sstride + HD] : -INFINITY;
     sl[s] = l;
@@ -470,15 +474,26 @@ __global__ __launch_bounds__(HD) void k_attn_combine(AttnArgs a, float* out) {
   float M = -INFINITY;
   for (int s = 0; s < ns; ++s) M = fmaxf(M, sw[s]);
   __syncthreads();
-  for (int s = d; s < ns; s += HD) sw[s] = sl[s] > 0.f ? expf(sw[s] - M) : 0.f;
+  for (int s = tid; s < ns; s += kWG) sw[s] = sl[s] > 0.f ? expf(sw[s] - M) : 0.f;
   __syncthreads();
   float L = 0.f, O = 0.f;
 #pragma unroll 8
-  for (int s = 0; s < ns; ++s) {
+  for (int s = grp; s < ns; s += NG) {
     L = fmaf(sl[s], sw[s], L);
     O = fmaf(P[s * sstride + d], sw[s], O);
   }
-  out[((long)row * a.nq + h) * HD + d] = O / L;
+  so[grp][d] = O;
+  if (d == 0) sL[grp] = L;
+  __syncthreads();
+  if (grp == 0) {
+    float Ot = so[0][d], Lt = sL[0];
+#pragma unroll
+    for (int q = 1; q < NG; ++q) {
+      Ot += so[q][d];
+      Lt += sL[q];
+    }
+    out[((long)row * a.nq + h) * HD + d] = Ot / Lt;
+  }
 }
 
 // bf16 caches take the MFMA kernel: one query tile per pass, or two when a sequence has more
@@ -510,7 +525,7 @@ void launch_attention(AttnArgs a, int wdtype, float* out, hipStream_t st) {
     dim3 grid(a.nsplit, a.nkv * attn_qgroups(a, kQB), a.B);
     hipLaunchKernelGGL((k_attn<F32, HD>), grid, dim3(kWG), 0, st, a);
   }
-  if (!a.out) hipLaunchKernelGGL((k_attn_combine<HD>), dim3(a.B * a.rps * a.nq), dim3(HD), 0, st, a, out);
+  if (!a.out) hipLaunchKernelGGL((k_attn_combine<HD>), dim3(a.B * a.rps * a.nq), dim3(kWG), 0, st, a, out);
 }
 
 hipError_t run_attention(const AttnArgs& a, int hd, int wdtype, float* out, hipStream_t st) {

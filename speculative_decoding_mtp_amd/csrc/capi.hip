@@ -73,23 +73,24 @@ int check_cfg(const mtp_config* c) {
   return MTP_OK;
 }
 
-int check_layers(const mtp_config* c, const mtp_layer_weights* layers) {
+// need_kv = 0: a head reading another model's cache never reads wk / wv.
+int check_layers(const mtp_config* c, const mtp_layer_weights* layers, bool need_kv = true) {
   if (!layers) return fail(MTP_ERR_ARG, "weights.layers is NULL");
   for (int l = 0; l < c->n_layers; ++l) {
     const mtp_layer_weights& L = layers[l];
-    const void* lp[9] = {L.in_norm, L.wq, L.wk, L.wv, L.wo, L.post_norm, L.wgate, L.wup, L.wdown};
-    for (const void* p : lp)
-      if (!p || !aligned16(p)) return fail(MTP_ERR_ARG, "layer %d: a weight pointer is NULL or misaligned", l);
+    const void* lp[9] = {L.in_norm, L.wq, L.wo, L.post_norm, L.wgate, L.wup, L.wdown, L.wk, L.wv};
+    for (int i = 0; i < (need_kv ? 9 : 7); ++i)
+      if (!lp[i] || !aligned16(lp[i])) return fail(MTP_ERR_ARG, "layer %d: a weight pointer is NULL or misaligned", l);
   }
   return MTP_OK;
 }
 
-int check_weights(const mtp_config* c, const mtp_weights* w) {
+int check_weights(const mtp_config* c, const mtp_weights* w, bool need_kv = true) {
   if (!w) return fail(MTP_ERR_ARG, "weights is NULL");
   const void* top[6] = {w->embed, w->enorm, w->hnorm, w->eh_proj, w->final_norm, w->lm_head};
   for (const void* p : top)
     if (!p || !aligned16(p)) return fail(MTP_ERR_ARG, "a weight pointer is NULL or not 16-byte aligned");
-  return check_layers(c, w->layers);
+  return check_layers(c, w->layers, need_kv);
 }
 
 int check_target_weights(const mtp_config* c, const mtp_target_weights* w) {
@@ -206,6 +207,9 @@ StepArgs base_step(const mtp_config* cfg, const mtp_weights* w, const mtp_kv* kv
   s.logits = nullptr;
   s.lg_sb = 0;
   s.ev_begin = s.ev_end = nullptr;
+  s.shared = 0;
+  s.pos_off = 0;
+  s.kv_layer = nullptr;
   return s;
 }
 
@@ -339,6 +343,51 @@ int mtp_draft_loop(const mtp_config* cfg, const mtp_weights* w, const mtp_kv* kv
     timer_events(MTP_KERNEL_LM_HEAD, &s.ev_begin, &s.ev_end);
     const hipError_t e = run_step(s);
     if (e != hipSuccess) return hip_fail(e, "mtp_draft_loop launch");
+  }
+  return MTP_OK;
+}
+
+int mtp_draft_loop_shared_kv(const mtp_config* cfg, const mtp_weights* w, const mtp_kv* target_kv,
+                             int32_t target_layers, const int32_t* kv_layer, int32_t D, const int32_t* tokens,
+                             const float* hidden_in, int32_t* drafts, float* hiddens, float* draft_logits, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  int rc;
+  if ((rc = check_cfg(cfg)) || (rc = check_weights(cfg, w, false)) || (rc = check_kv(target_kv))) return rc;
+  if (D < 1) return fail(MTP_ERR_ARG, "D must be >= 1");
+  if (target_layers < 1) return fail(MTP_ERR_ARG, "target_layers must be >= 1");
+  if (!kv_layer) return fail(MTP_ERR_ARG, "kv_layer is NULL");
+  for (int l = 0; l < cfg->n_layers; ++l)
+    if (kv_layer[l] < 0 || kv_layer[l] >= target_layers)
+      return fail(MTP_ERR_ARG, "kv_layer[%d] = %d outside [0, %d)", l, kv_layer[l], target_layers);
+  if (!tokens || !hidden_in || !aligned16(hidden_in)) return fail(MTP_ERR_ARG, "tokens / hidden_in NULL or misaligned");
+  if (!drafts) return fail(MTP_ERR_ARG, "drafts is NULL");
+  if ((hiddens && !aligned16(hiddens)) || (draft_logits && !aligned16(draft_logits)))
+    return fail(MTP_ERR_ARG, "hiddens / draft_logits misaligned");
+  if (!ws || !aligned16(ws)) return fail(MTP_ERR_ARG, "workspace NULL or misaligned");
+  const DraftLayout L = draft_layout(*cfg, target_kv->batch, 1, D, target_kv->max_len);
+  if (ws_bytes < L.total) return fail(MTP_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, L.total);
+  StepArgs s = base_step(cfg, w, target_kv, ws, L, stream);
+  s.shared = 1;
+  s.kv_layer = kv_layer;
+  s.rps = 1;
+  const int H = cfg->hidden;
+  float* hbuf = hiddens ? hiddens : s.ws.hid_fb;
+  for (int k = 0; k < D; ++k) {
+    s.pos_off = k - 1;  // step k + 1 sits at len[b] - 1 + k
+    s.tok = k == 0 ? tokens : drafts + (k - 1);
+    s.tok_sb = k == 0 ? 1 : D;
+    s.hin = k == 0 ? hidden_in : hbuf + (long)(k - 1) * H;
+    s.hin_sb = k == 0 ? 1 : D;
+    s.hout = hbuf + (long)k * H;
+    s.hout_sb = D;
+    s.hout_last = 1;
+    s.draft = drafts + k;
+    s.dr_sb = D;
+    s.logits = draft_logits ? draft_logits + (long)k * cfg->vocab : nullptr;
+    s.lg_sb = (long)D * cfg->vocab;
+    timer_events(MTP_KERNEL_LM_HEAD, &s.ev_begin, &s.ev_end);
+    const hipError_t e = run_step(s);
+    if (e != hipSuccess) return hip_fail(e, "mtp_draft_loop_shared_kv launch");
   }
   return MTP_OK;
 }

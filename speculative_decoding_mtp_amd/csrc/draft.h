@@ -36,6 +36,7 @@ struct AttnArgs {
   float* part;       // [B][nkv][nsplit][qstride][hd + 2]
   const int* rows;   // NULL, or the valid rows of sequence b at rows[b]
   float* out;        // set by run_attention: one split of a bf16 cache writes the output rows here
+  int shared;        // 1: the rows read a cache they do not append to (keys 0 .. len[b] - 1 only)
 };
 
 // Arguments of the lm_head finalisation kernel.
@@ -58,6 +59,7 @@ struct LmFinal {
   int dr_sb;
   int* status;
   const int* rows;  // NULL, or rows[b] = valid rows, rows[B + b] = the flags that ended them
+  int grow;         // 1: len[b] grows by the valid rows (0 for a head reading another model's cache)
 };
 
 // Carved out of the caller's workspace.
@@ -101,6 +103,11 @@ struct StepArgs {
   DraftWs ws;
   hipStream_t stream;
   hipEvent_t ev_begin, ev_end;  // optional, around the lm_head launch
+  // A head without a cache of its own: kc/vc/kv_len are the main model's cache, read only; head
+  // layer l reads its layer kv_layer[l] (host array); rows sit at kv_len[b] + i + pos_off.
+  int shared;
+  int pos_off;
+  const int32_t* kv_layer;
 };
 
 // Which GEMV layout, variant and grid serve nact activation rows of width K (VE elements per

@@ -20,8 +20,10 @@ int pow2_at_most(int n) {
 // Valid rows of each sequence of a many-row call, counted once per step: the workgroup of sequence b
 // scans its tokens together and keeps the first row that ends the prefix (the rule of count_rows),
 // writing the count to rows[b] and the flags that ended it to rows[B + b].
+// A head reading another model's cache (shared) appends nothing: no capacity limit, but a sequence
+// whose cache is empty has no rows.
 __global__ __launch_bounds__(kWG) void k_count_rows(const int32_t* tok, int tok_sb, int rps, int V,
-                                                    const int32_t* len, int max_len, int B, int* rows) {
+                                                    const int32_t* len, int max_len, int B, int shared, int* rows) {
   __shared__ int s_first;
   const int b = blockIdx.x;
   if (threadIdx.x == 0) s_first = rps;
@@ -30,7 +32,7 @@ __global__ __launch_bounds__(kWG) void k_count_rows(const int32_t* tok, int tok_
   const int32_t* t = tok + (long)b * tok_sb;
   for (int i = threadIdx.x; i < rps; i += kWG) {
     const int v = t[i];
-    if (v < 0 || v >= V || l + i >= max_len) {  // rows rise with i: this thread's first is its least
+    if (v < 0 || v >= V || (shared ? l == 0 : l + i >= max_len)) {  // this thread's first is its least
       atomicMin(&s_first, i);
       break;
     }
@@ -39,7 +41,7 @@ __global__ __launch_bounds__(kWG) void k_count_rows(const int32_t* tok, int tok_
   if (threadIdx.x == 0) {
     const int n = s_first;
     int f = 0;
-    if (n < rps && t[n] >= 0) f = t[n] >= V ? kFlagToken : kFlagCapacity;
+    if (n < rps && t[n] >= 0) f = t[n] >= V ? kFlagToken : (shared ? 0 : kFlagCapacity);
     rows[b] = n;
     rows[B + b] = f;
   }
@@ -47,7 +49,7 @@ __global__ __launch_bounds__(kWG) void k_count_rows(const int32_t* tok, int tok_
 
 hipError_t count_step_rows(const StepArgs& s) {
   hipLaunchKernelGGL(k_count_rows, dim3(s.B), dim3(kWG), 0, s.stream, s.tok, s.tok_sb, s.rps, s.cfg.vocab, s.kv_len,
-                     s.max_len, s.B, s.ws.rows);
+                     s.max_len, s.B, s.shared, s.ws.rows);
   return hipGetLastError();
 }
 

@@ -82,7 +82,7 @@ struct PEhProj : PBase<W> {
       load_f32_vec<W::VE>(hin + ((long)b * hin_sb + i) * H + (k - H), f);
     }
   }
-  __device__ void gain_vec(int k, float (&f)[W::VE]) const { W::cvt(ld16(k < H ? enorm + k : hnorm + (k - H)), f); }
+  __device__ uint4 gain_raw(int k) const { return ld16(k < H ? enorm + k : hnorm + (k - H)); }
   __device__ const T* wrow(int m) const { return w + (long)m * (2 * H); }
   __device__ void store(int m, int, int row, float v) { xout[(long)row * H + m] = v; }
 };
@@ -100,6 +100,7 @@ struct PQKV : PBase<W> {
   double log_theta;
   float* qout;
   T *kc, *vc;  // this layer's cache: keys [B][nkv][max_len][hd], values [B][nkv][hd][max_len]
+  int pos_off;  // row i of sequence b sits at position len[b] + i + pos_off
   const double* inv_freq;  // theta^(-2u/hd), u < hd/2, in LDS (set by setup)
 
   // Per-sequence rows and cache lengths, and the rotation frequencies (exp in double once per
@@ -113,7 +114,7 @@ struct PQKV : PBase<W> {
   }
 
   __device__ void load_x(int row, int k, float (&f)[W::VE]) const { load_f32_vec<W::VE>(xin + (long)row * H + k, f); }
-  __device__ void gain_vec(int k, float (&f)[W::VE]) const { W::cvt(ld16(g + k), f); }
+  __device__ uint4 gain_raw(int k) const { return ld16(g + k); }
   __device__ const T* wrow(int m) const {
     const int head = m / hd, mm = m - head * hd;
     const int dim = (mm >> 1) + (mm & 1) * (hd >> 1);
@@ -124,7 +125,7 @@ struct PQKV : PBase<W> {
   __device__ void store_pair(int m, int, int row, float v0, float v1) {
     const int head = m / hd, u = (m - head * hd) >> 1, half = hd >> 1;
     const int b = row / this->rps, i = row - b * this->rps;
-    const int pos = this->lds_len[b] + i;
+    const int pos = this->lds_len[b] + i + pos_off;
     if (head < nq + nkv) {
       // rotate q and k by pos * theta^(-2u/hd): the angle in double, reduced to [-pi, pi] in
       // double (two-part 2 pi), then sine and cosine of the reduced angle in float
@@ -165,10 +166,6 @@ struct PResidual : PBase<W> {
   __device__ void load_x(int row, int k, float (&f)[W::VE]) const {
     load_f32_vec<W::VE>(ain + (long)row * this->K + k, f);
   }
-  __device__ void gain_vec(int, float (&f)[W::VE]) const {
-#pragma unroll
-    for (int e = 0; e < W::VE; ++e) f[e] = 1.f;
-  }
   __device__ const T* wrow(int m) const { return w + (long)m * this->K; }
   __device__ void store(int m, int, int row, float v) { xres[(long)row * this->N + m] += v; }
 };
@@ -185,7 +182,7 @@ struct PGateUp : PBase<W> {
   float* aout;  // [R][F]
 
   __device__ void load_x(int row, int k, float (&f)[W::VE]) const { load_f32_vec<W::VE>(xin + (long)row * H + k, f); }
-  __device__ void gain_vec(int k, float (&f)[W::VE]) const { W::cvt(ld16(g + k), f); }
+  __device__ uint4 gain_raw(int k) const { return ld16(g + k); }
   __device__ const T* wrow(int m) const { return ((m & 1) ? wu : wg) + (long)(m >> 1) * H; }
   __device__ void store_pair(int m, int, int row, float gt, float up) {
     aout[(long)row * F + (m >> 1)] = gt / (1.0f + expf(-gt)) * up;
@@ -211,7 +208,7 @@ struct PLmHead : PBase<W> {
     row = valid ? a * this->rps + s_n[a] - 1 : 0;
   }
   __device__ void load_x(int row, int k, float (&f)[W::VE]) const { load_f32_vec<W::VE>(xin + (long)row * H + k, f); }
-  __device__ void gain_vec(int k, float (&f)[W::VE]) const { W::cvt(ld16(g + k), f); }
+  __device__ uint4 gain_raw(int k) const { return ld16(g + k); }
   __device__ const T* wrow(int m) const { return w + (long)m * H; }
   __device__ void store(int m, int a, int, float v) {
     if (logits) logits[(long)a * lg_sb + m] = v;
@@ -245,7 +242,7 @@ struct PLogits : PBase<W> {
   float* logits;
 
   __device__ void load_x(int row, int k, float (&f)[W::VE]) const { load_f32_vec<W::VE>(xin + (long)row * H + k, f); }
-  __device__ void gain_vec(int k, float (&f)[W::VE]) const { W::cvt(ld16(g + k), f); }
+  __device__ uint4 gain_raw(int k) const { return ld16(g + k); }
   __device__ const T* wrow(int m) const { return w + (long)m * H; }
   __device__ void store(int m, int, int row, float v) { logits[(long)row * this->N + m] = v; }
 };
@@ -269,6 +266,31 @@ __global__ __launch_bounds__(kWG) void k_embed_rows(const void* embed, const int
     W::cvt(ld16(e + k), f);
 #pragma unroll
     for (int j = 0; j < VE; ++j) x[(long)row * H + k + j] = f[j];
+  }
+}
+
+// dst = rms(x) * g over one row of H floats (H a multiple of 8) by one wave: float4 loads, four
+// in flight per lane, the row read twice (the second time from cache).
+template <class W>
+__device__ __forceinline__ void wave_rms_row(const float* x, float* dst, const typename W::T* g, int H, float eps,
+                                             int lane) {
+  const float4* xr = reinterpret_cast<const float4*>(x);
+  float4* d4 = reinterpret_cast<float4*>(dst);
+  const int H4 = H >> 2;
+  float ss = 0.f;
+#pragma unroll 4
+  for (int c = lane; c < H4; c += 64) {
+    const float4 v = xr[c];
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  ss = wave_sum(ss);
+  const float sc = 1.0f / sqrtf(ss / float(H) + eps);
+#pragma unroll 4
+  for (int c = lane; c < H4; c += 64) {
+    const float4 v = xr[c];
+    const int k = 4 * c;
+    d4[c] = make_float4(v.x * sc * W::get(g, k), v.y * sc * W::get(g, k + 1), v.z * sc * W::get(g, k + 2),
+                        v.w * sc * W::get(g, k + 3));
   }
 }
 
@@ -300,28 +322,55 @@ __global__ __launch_bounds__(kWG) void k_lm_finalize(LmFinal f) {
     si[tid >> 6] = id;
   }
   __syncthreads();
-  const T* g = reinterpret_cast<const T*>(f.gain);
-  // output hiddens: wave w normalises rows first + w, first + w + 4, ... (no block barriers)
-  const int lane = tid & 63, wid = tid >> 6;
-  for (int i = (f.hout_last ? n - 1 : 0) + wid; f.hout && i < n; i += kWG / 64) {
-    const float* xr = f.x + ((long)b * f.rps + i) * f.H;
-    float ss = 0.f;
-    for (int k = lane; k < f.H; k += 64) ss += xr[k] * xr[k];
-    ss = wave_sum(ss);
-    const float sc = 1.0f / sqrtf(ss / float(f.H) + f.eps);
-    float* dst = f.hout + ((long)b * f.hout_sb + (f.hout_last ? 0 : i)) * f.H;
-    for (int k = lane; k < f.H; k += 64) dst[k] = xr[k] * sc * W::get(g, k);
-  }
-  if (tid == 0) {
+  if (tid == 0) {  // the argmax of the workgroup, before sv is reused for the norm
+    for (int w = 1; w < 4; ++w)
+      if (better(sv[w], si[w], sv[0], si[0])) {
+        sv[0] = sv[w];
+        si[0] = si[w];
+      }
     v = sv[0];
     id = si[0];
-    for (int w = 1; w < 4; ++w)
-      if (better(sv[w], si[w], v, id)) {
-        v = sv[w];
-        id = si[w];
+  }
+  __syncthreads();
+  const T* g = reinterpret_cast<const T*>(f.gain);
+  const int lane = tid & 63, wid = tid >> 6;
+  if (f.hout && f.hout_last && n > 0 && f.H <= 8 * 4 * kWG) {
+    // the last row only (a draft step's fed-back hidden): the whole workgroup, float4 loads held
+    // in registers across the norm reduction
+    const float4* xr = reinterpret_cast<const float4*>(f.x + ((long)b * f.rps + n - 1) * f.H);
+    float4* dst = reinterpret_cast<float4*>(f.hout + (long)b * f.hout_sb * f.H);
+    const int H4 = f.H >> 2;
+    float4 xv[8];
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int c = tid + j * kWG;
+      xv[j] = c < H4 ? xr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ss += xv[j].x * xv[j].x + xv[j].y * xv[j].y + xv[j].z * xv[j].z + xv[j].w * xv[j].w;
+    ss = wave_sum(ss);
+    if (lane == 0) sv[wid] = ss;
+    __syncthreads();
+    const float sc = 1.0f / sqrtf((sv[0] + sv[1] + sv[2] + sv[3]) / float(f.H) + f.eps);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int c = tid + j * kWG;
+      if (c < H4) {
+        const int k = 4 * c;
+        dst[c] = make_float4(xv[j].x * sc * W::get(g, k), xv[j].y * sc * W::get(g, k + 1),
+                             xv[j].z * sc * W::get(g, k + 2), xv[j].w * sc * W::get(g, k + 3));
       }
+    }
+  } else if (f.hout) {
+    // every valid row (or the last of a wider one): wave w normalises rows first + w, first + w + 4, ...
+    for (int i = (f.hout_last ? n - 1 : 0) + wid; i < n; i += kWG / 64)
+      wave_rms_row<W>(f.x + ((long)b * f.rps + i) * f.H, f.hout + ((long)b * f.hout_sb + (f.hout_last ? 0 : i)) * f.H,
+                      g, f.H, f.eps, lane);
+  }
+  if (tid == 0) {
     if (f.draft) f.draft[(long)b * f.dr_sb] = n > 0 ? id : -1;
-    f.len[b] = f.len[b] + n;
+    if (f.grow) f.len[b] = f.len[b] + n;
     if (flags) atomicOr(f.status, flags);
   }
 }
@@ -337,14 +386,8 @@ __global__ __launch_bounds__(kWG) void k_hidden_out(LmFinal f) {
   const int b = row / f.rps, i = row - b * f.rps;
   const int n = f.rows ? f.rows[b] : count_rows(f.tok + (long)b * f.tok_sb, f.rps, f.V, f.len[b], f.max_len, nullptr);
   if (i >= n || (f.hout_last && i != n - 1)) return;
-  const float* xr = f.x + (long)row * f.H;
-  float ss = 0.f;
-  for (int k = lane; k < f.H; k += 64) ss += xr[k] * xr[k];
-  ss = wave_sum(ss);
-  const float sc = 1.0f / sqrtf(ss / float(f.H) + f.eps);
-  const T* g = reinterpret_cast<const T*>(f.gain);
-  float* dst = f.hout + ((long)b * f.hout_sb + (f.hout_last ? 0 : i)) * f.H;
-  for (int k = lane; k < f.H; k += 64) dst[k] = xr[k] * sc * W::get(g, k);
+  wave_rms_row<W>(f.x + (long)row * f.H, f.hout + ((long)b * f.hout_sb + (f.hout_last ? 0 : i)) * f.H,
+                  reinterpret_cast<const T*>(f.gain), f.H, f.eps, lane);
 }
 
 // k_lm_finalize, with the hiddens of many-row calls written by k_hidden_out first.
@@ -467,7 +510,7 @@ hipError_t launch_gemv(P& p, hipStream_t st, int* grid_used = nullptr, const Mfm
 }
 
 // The per-step row counts when the call has many rows per sequence, else NULL.
-inline const int* step_rows(const StepArgs& s) { return s.rps > kInlineRows ? s.ws.rows : nullptr; }
+inline const int* step_rows(const StepArgs& s) { return s.shared || s.rps > kInlineRows ? s.ws.rows : nullptr; }
 
 template <class W, class P>
 void fill_base(P& p, const StepArgs& s) {
@@ -519,12 +562,12 @@ hipError_t run_step_t(const StepArgs& s) {
   const mtp_layer_weights* layers = s.target ? s.tw->layers : s.w->layers;
   for (int l = 0; l < c.n_layers; ++l) {
     const mtp_layer_weights& lw = layers[l];
-    const long layer_off = (long)l * s.B * nkv * s.max_len * hd;
+    const long layer_off = (long)(s.kv_layer ? s.kv_layer[l] : l) * s.B * nkv * s.max_len * hd;
     {  // q/k/v + RoPE + append
       PQKV<W> p;
       fill_base<W>(p, s);
       p.K = H;
-      p.N = (nq + 2 * nkv) * hd;
+      p.N = (nq + (s.shared ? 0 : 2 * nkv)) * hd;  // a head reading another cache projects q only
       p.nact = R;
       p.g = (const T*)lw.in_norm;
       p.wq = (const T*)lw.wq;
@@ -539,6 +582,7 @@ hipError_t run_step_t(const StepArgs& s) {
       p.qout = s.ws.q;
       p.kc = (T*)s.kc + layer_off;
       p.vc = (T*)s.vc + layer_off;
+      p.pos_off = s.pos_off;
       if ((e = launch_gemv<W>(p, s.stream, nullptr, mb)) != hipSuccess) return e;
     }
     {  // attention
@@ -559,6 +603,7 @@ hipError_t run_step_t(const StepArgs& s) {
       a.qstride = s.rps * (nq / nkv);
       a.part = s.ws.attn_part;
       a.rows = step_rows(s);
+      a.shared = s.shared;
       if ((e = run_attention(a, hd, c.wdtype, s.ws.attn_out, s.stream)) != hipSuccess) return e;
     }
     {  // o_proj + residual
@@ -633,6 +678,7 @@ hipError_t run_step_t(const StepArgs& s) {
     f.dr_sb = 0;
     f.status = s.ws.status;
     f.rows = step_rows(s);
+    f.grow = !s.shared;
     return launch_finalize<W>(f, s.stream);
   }
   {  // final norm + lm_head + argmax + finalisation
@@ -676,6 +722,7 @@ hipError_t run_step_t(const StepArgs& s) {
     f.dr_sb = s.dr_sb;
     f.status = s.ws.status;
     f.rows = step_rows(s);
+    f.grow = !s.shared;
     e = launch_finalize<W>(f, s.stream);
     if (e != hipSuccess) return e;
   }

@@ -83,7 +83,7 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
 //                                   kernel then syncs)
 //   void act(int a, const int* s_n, int& row, bool& valid)
 //   void load_x(int row, int k, float (&f)[VE])     raw activations k..k+VE-1 of a row
-//   void gain_vec(int k, float (&g)[VE])            norm gains (kNorm > 0)
+//   uint4 gain_raw(int k)                            16 bytes of norm gains from column k (kNorm > 0)
 //   const T* wrow(int m)                            weight row of logical row m < N
 //   void store(int m, int a, int row, float v)      (!kPair)
 //   void store_pair(int m, int a, int row, float v0, float v1)   (kPair)
@@ -97,6 +97,13 @@ template <class W, int RB, int NJ, class P, class Reduce>
 __device__ __forceinline__ void load_slice(const P& p, const int (&rows)[RB], const bool (&valid)[RB], int cbase,
                                            int cstride, int Kc, float (&x)[RB][NJ][W::VE], Reduce reduce) {
   constexpr int VE = W::VE;
+  // the norm gains of this thread's columns are fetched with the activations (one memory round
+  // trip before the reduction, not a second one after it)
+  uint4 graw[NJ];
+  if constexpr (P::kNorm > 0) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) graw[j] = p.gain_raw(min(cbase + j * cstride, Kc - 1) * VE);
+  }
 #pragma unroll
   for (int r = 0; r < RB; ++r) {
     float s0 = 0.f, s1 = 0.f;
@@ -135,7 +142,7 @@ __device__ __forceinline__ void load_slice(const P& p, const int (&rows)[RB], co
           const int k0 = c * VE;
           const float sc = (P::kNorm == 2 && k0 >= p.split) ? sc1 : sc0;
           float gv[VE];
-          p.gain_vec(k0, gv);
+          W::cvt(graw[j], gv);
 #pragma unroll
           for (int e = 0; e < VE; ++e) x[r][j][e] = x[r][j][e] * sc * gv[e];
         }

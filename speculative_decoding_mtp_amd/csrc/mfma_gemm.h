@@ -72,18 +72,37 @@ __global__ __launch_bounds__(kWG) void k_prep(P p, MfmaBufs mb) {
   if (a == 0 && tid == 0) *mb.count = total;
   if (!valid) return;
   const int Kc = p.K / VE;
+  // The first KEEP chunks of each thread (K <= KEEP * kWG * VE: every width here but the widest
+  // FFN) stay in registers, with their gains, across the norm reduction: one memory round trip.
+  constexpr int KEEP = 4;
+  float keep[KEEP][VE];
+  uint4 gk[KEEP];
   float ss[2] = {0.f, 0.f};
+  auto sumsq = [&](const float (&f)[VE], int ch) {
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < VE; ++e) s = fmaf(f[e], f[e], s);
+    if (P::kNorm == 2 && ch * VE >= p.split)
+      ss[1] += s;
+    else
+      ss[0] += s;
+  };
+#pragma unroll
+  for (int i = 0; i < KEEP; ++i) {
+    const int ch = tid + i * kWG;
+    if (ch < Kc) {
+      p.load_x(row, ch * VE, keep[i]);
+      if constexpr (P::kNorm > 0) gk[i] = p.gain_raw(ch * VE);
+    }
+  }
   if constexpr (P::kNorm > 0) {
-    for (int ch = tid; ch < Kc; ch += kWG) {
+#pragma unroll
+    for (int i = 0; i < KEEP; ++i)
+      if (tid + i * kWG < Kc) sumsq(keep[i], tid + i * kWG);
+    for (int ch = tid + KEEP * kWG; ch < Kc; ch += kWG) {
       float f[VE];
       p.load_x(row, ch * VE, f);
-      float s = 0.f;
-#pragma unroll
-      for (int e = 0; e < VE; ++e) s = fmaf(f[e], f[e], s);
-      if (P::kNorm == 2 && ch * VE >= p.split)
-        ss[1] += s;
-      else
-        ss[0] += s;
+      sumsq(f, ch);
     }
     wg_sum<2>(ss, red);
   }
@@ -96,11 +115,10 @@ __global__ __launch_bounds__(kWG) void k_prep(P p, MfmaBufs mb) {
   }
   uint16_t* hi = mb.xhi + (long)c * p.K;
   uint16_t* lo = mb.xlo + (long)c * p.K;
-  for (int ch = tid; ch < Kc; ch += kWG) {
-    float f[VE], g[VE];
-    p.load_x(row, ch * VE, f);
+  auto emit = [&](const float (&f)[VE], const uint4& graw, int ch) {
+    float g[VE];
     if constexpr (P::kNorm > 0) {
-      p.gain_vec(ch * VE, g);
+      W::cvt(graw, g);
     } else {
 #pragma unroll
       for (int e = 0; e < VE; ++e) g[e] = 1.f;
@@ -118,6 +136,16 @@ __global__ __launch_bounds__(kWG) void k_prep(P p, MfmaBufs mb) {
       hi[ch * VE + e] = h16[e];
       lo[ch * VE + e] = l16[e];
     }
+  };
+#pragma unroll
+  for (int i = 0; i < KEEP; ++i)
+    if (tid + i * kWG < Kc) emit(keep[i], gk[i], tid + i * kWG);
+  for (int ch = tid + KEEP * kWG; ch < Kc; ch += kWG) {
+    float f[VE];
+    p.load_x(row, ch * VE, f);
+    uint4 graw = make_uint4(0, 0, 0, 0);
+    if constexpr (P::kNorm > 0) graw = p.gain_raw(ch * VE);
+    emit(f, graw, ch);
   }
   if (tid == 0) {
     mb.rowmap[c] = row;

@@ -1,0 +1,111 @@
+"""GPU parity of the draft head that keeps no cache of its own and reads the main model's keys and
+values ([DLM "MTP speculative decoding"] item 1), through mtp_draft_loop_shared_kv.
+
+Bar as for the own-cache head: drafts bit-exact while the oracle's top-2 gap is at least 1e-4
+(after a smaller gap the later steps may follow another token and are not compared); hiddens and
+logits within max relative error 1e-4 (fp32) or 2e-2 (bf16).  The main model's cache and lengths
+must come back bit-identical."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from synth import CONFIGS, make_kv_prefix, make_weights
+
+pytestmark = pytest.mark.gpu
+
+M = pytest.importorskip("speculative_decoding_mtp_amd")
+from tests.gpu_util import MARGIN, config, f32, i32, max_rel, to_dev, upload_weights  # noqa: E402
+
+
+def _target_cache(cfg, T, lens, max_len):
+    """Seeded main-model K/V for T layers (N(0,1) in the KV dtype), per-sequence lengths."""
+    tcfg = cfg.replace(n_layers=T, index=cfg.index + 50)
+    K, V = make_kv_prefix(tcfg, max_len)
+    kv = M.KVCache(config(cfg), cfg.batch, max_len, n_layers=T)
+    kv.k.copy_(to_dev(K, cfg.wdtype))
+    kv.v.copy_(to_dev(np.ascontiguousarray(np.swapaxes(V, -1, -2)), cfg.wdtype))
+    kv.len.copy_(i32(lens))
+    ref = O.KVCache(tcfg, cfg.batch, max_len)
+    ref.K[:], ref.V[:] = K, V
+    ref.len[:] = lens
+    return kv, ref
+
+
+def _run(cfg, T, kv_layer, lens, toks, D, drop_kv_weights=False):
+    w = make_weights(cfg)
+    model = O.OracleModel(cfg, w)
+    c, gw = config(cfg), upload_weights(cfg, w)
+    if drop_kv_weights:   # the head reads no wk / wv: they may be absent
+        for lw in gw.t["layers"]:
+            lw["wk"] = lw["wv"] = None
+        gw = M.Weights(c, gw.t)
+    B, H, V = cfg.batch, cfg.hidden, cfg.vocab
+    max_len = 256
+    kv, ref = _target_cache(cfg, T, lens, max_len)
+    k0, v0 = kv.k.clone(), kv.v.clone()
+    hid = np.random.default_rng(cfg.index).standard_normal((B, H)).astype(np.float32)
+    ws = M.new_workspace(M.mtp_draft_workspace_size(c, B, 1, D, max_len))
+    drafts = torch.full((B, D), -7, dtype=torch.int32, device="cuda")
+    hs = torch.zeros(B, D, H, device="cuda")
+    lg = torch.zeros(B, D, V, device="cuda")
+    M.mtp_draft_loop_shared_kv(c, gw, kv, kv_layer, D, i32(toks), f32(hid), drafts, hs, lg, ws)
+    M.mtp_check(ws)
+    d_o, h_o, l_o, m_o = O.draft_loop_shared(model, ref, kv_layer, toks, hid, D)
+    assert torch.equal(kv.k, k0) and torch.equal(kv.v, v0)
+    assert kv.len.cpu().tolist() == list(lens)
+    tol = 1e-4 if cfg.wdtype == "f32" else 2e-2
+    dg, hg, lgg = drafts.cpu().numpy(), hs.cpu().numpy(), lg.cpu().numpy()
+    compared = 0
+    for b in range(B):
+        if d_o[b, 0] < 0:
+            assert (dg[b] == -1).all(), b
+            continue
+        for k in range(D):
+            assert max_rel(hg[b, k], h_o[b, k]) < tol, (b, k)
+            assert max_rel(lgg[b, k], l_o[b, k]) < tol, (b, k)
+            if m_o[b, k] < MARGIN:
+                break
+            assert dg[b, k] == d_o[b, k], (b, k)
+            compared += 1
+    return compared
+
+
+def test_tiny_fp32_shared_kv_loop():
+    cfg = CONFIGS["tiny"].replace(index=61, batch=4)
+    lens = [37, 1, 0, 200]
+    toks = np.array([5, 4000, 17, -1], np.int32)
+    assert _run(cfg, 2, [1], lens, toks, 4) >= 6
+
+
+@pytest.mark.parametrize("B", [1, 5])
+def test_four_layer_bf16_head_over_a_two_layer_cache(B):
+    # B 5: five rows per step take the MFMA GEMM path
+    cfg = CONFIGS["tiny"].replace(index=62, wdtype="bf16", n_layers=4, n_heads=8, n_kv_heads=2, head_dim=128,
+                                  hidden=512, ffn=1024, vocab=5000, batch=B)
+    lens = [129, 64, 250, 3, 1][:B]
+    toks = (np.arange(B, dtype=np.int32) * 977 + 11) % cfg.vocab
+    assert _run(cfg, 2, [0, 1, 0, 1], lens, toks, 6, drop_kv_weights=True) >= B
+
+
+def test_shared_kv_argument_errors():
+    cfg = CONFIGS["tiny"].replace(index=63, batch=2)
+    c, gw = config(cfg), upload_weights(cfg, make_weights(cfg))
+    kv = M.KVCache(c, 2, 64, n_layers=2)
+    ws = M.new_workspace(M.mtp_draft_workspace_size(c, 2, 1, 2, 64))
+    toks = i32([1, 2])
+    hid = torch.zeros(2, cfg.hidden, device="cuda")
+    d = torch.zeros(2, 2, dtype=torch.int32, device="cuda")
+    with pytest.raises(M.MTPError) as e:
+        M.mtp_draft_loop_shared_kv(c, gw, kv, [2], 2, toks, hid, d, None, None, ws)
+    assert e.value.code == -1
+    with pytest.raises(M.MTPError) as e:
+        M.mtp_draft_loop_shared_kv(c, gw, kv, [0], 2, toks, hid, d, None, None, M.new_workspace(256))
+    assert e.value.code == -5
+    kv.len.copy_(i32([3, 3]))
+    M.mtp_draft_loop_shared_kv(c, gw, kv, [0], 2, i32([1, cfg.vocab]), hid, d, None, None, ws)
+    with pytest.raises(M.MTPError) as e:
+        M.mtp_check(ws)
+    assert e.value.code == -7
+    assert d[1].cpu().tolist() == [-1, -1]
+    assert kv.len.cpu().tolist() == [3, 3]
