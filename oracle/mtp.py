@@ -24,7 +24,7 @@ __all__ = [
     "greedy_verify", "warp", "sample", "residual", "sampling_verify", "spec_verify",
     "kv_crop", "state_snapshot", "state_restore", "spec_decode", "VerifyResult",
     "TargetModel", "target_row", "target_forward", "DenseTarget",
-    "shared_block", "mtp_row_shared", "draft_loop_shared",
+    "shared_block", "mtp_row_shared", "draft_loop_shared", "draft_loop_multi",
 ]
 
 
@@ -390,6 +390,70 @@ def draft_loop(model: OracleModel, cache: KVCache, tokens, hiddens, D: int, want
         hid[:, k] = hout[:, 0]
         if want_logits:
             logits[:, k] = lg
+    return drafts, hid, logits, margins
+
+
+# --------------------------------------------------------------------------------------------
+# several MTP modules: one per draft position
+# --------------------------------------------------------------------------------------------
+def draft_loop_multi(models: Sequence[OracleModel], caches: Sequence[KVCache], tokens, hiddens, D: int,
+                     want_logits: bool = True):
+    """The D-step draft loop over M modules, each with its own cache.
+
+    [YL 二.3]: the predictor holds several MTP layers; a single module is
+    reused for every step, the layer chosen by the step index modulo the
+    number of layers, and multi-module MTP gives each draft position its own
+    layer.  [YL 五]: the multi-module form needs a re-prefill to repair the
+    stale KV that rejected tokens leave.  Readings: step k (1-based) uses
+    module (k-1) mod M at the position the single-module loop gives it (one
+    past step k-1); every module keeps, like the single module's cache, the
+    K/V of every row of the sequence it is asked about:
+      * catch-up (re-prefill after a verification): every module appends the
+        catch-up rows (the settled positions, with the main model's hiddens);
+        module 0's last row gives draft 1;
+      * step k >= 2: module m = (k-1) mod M first appends the rows of this
+        round's chain it has not seen yet (positions of steps s_m+1 .. k-1,
+        fed (d_j, g_j) as the single module is), then its own row; the last
+        row gives draft k.
+    A stale row (a rejected draft's) is removed by the caller's crop of every
+    module's cache and recomputed by the next catch-up.  With M = 1 this is
+    ``draft_loop``; with M identical modules it equals ``draft_loop`` exactly.
+    tokens/hiddens: the catch-up rows as in ``draft_step``.  Returns drafts
+    [B][D], hiddens [B][D][H], logits [B][D][V], margins [B][D]."""
+    M = len(models)
+    assert M >= 1 and len(caches) == M
+    tokens = np.asarray(tokens)
+    B = tokens.shape[0]
+    H, V = models[0].cfg.hidden, models[0].cfg.vocab
+    drafts = np.full((B, D), -1, dtype=np.int64)
+    hid = np.zeros((B, D, H), dtype=F64)
+    logits = np.zeros((B, D, V), dtype=F64) if want_logits else None
+    margins = np.full((B, D), np.inf)
+    for m in range(M):
+        hout, d, lg, mg = draft_step(models[m], caches[m], tokens, hiddens, want_logits)
+        if m == 0:
+            for b in range(B):
+                n = _valid_rows(tokens[b])
+                if n:
+                    hid[b, 0] = hout[b, n - 1]
+            drafts[:, 0], margins[:, 0] = d, mg
+            if want_logits:
+                logits[:, 0] = lg
+    seen = [1] * M  # chain steps whose rows each module holds (the catch-up's last row is step 1's)
+    for k in range(2, D + 1):
+        m = (k - 1) % M
+        lo = seen[m]
+        # rows of steps lo+1 .. k: step j's row is fed (d_{j-1}, g_{j-1})
+        tk = np.where(drafts[:, lo - 1:k - 1] >= 0, drafts[:, lo - 1:k - 1], -1)
+        hout, d, lg, mg = draft_step(models[m], caches[m], tk, hid[:, lo - 1:k - 1], want_logits)
+        for b in range(B):
+            n = _valid_rows(tk[b])
+            if n:
+                hid[b, k - 1] = hout[b, n - 1]
+        drafts[:, k - 1], margins[:, k - 1] = d, mg
+        if want_logits:
+            logits[:, k - 1] = lg
+        seen[m] = k
     return drafts, hid, logits, margins
 
 
