@@ -20,6 +20,8 @@ dimensions and L blocks, scoring 1, 2 or 7 positions per call.  --prefill-rows N
 prefill call over N prompt rows.  --shared-kv T runs the same rounds with a head that keeps no
 cache of its own and reads a T-layer main-model cache (head layer l reads layer l mod T) through
 mtp_draft_loop_shared_kv; the main model's cache length then follows the verifier's crop length.
+--modules M drafts with M MTP modules (step k by module (k-1) mod M, each with its own cache,
+re-prefilled by every catch-up) through mtp_draft_loop_multi.
 """
 import argparse
 import hashlib
@@ -50,6 +52,8 @@ def parse():
                     help="time one MTP prefill of this many rows per sequence instead (from an empty cache)")
     ap.add_argument("--target-layers", type=int, default=0,
                     help="time the target's verify pass instead (a dense stand-in with this many layers)")
+    ap.add_argument("--modules", type=int, default=1,
+                    help="draft with this many MTP modules, step k by module (k-1) mod M (mtp_draft_loop_multi)")
     ap.add_argument("--shared-kv", type=int, default=0,
                     help="the head keeps no cache and reads a main-model cache of this many layers instead")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
@@ -99,6 +103,29 @@ def main():
     else:
         K, Vv = make_kv_prefix(cfg)
         kv = kv_from_numpy(cfg, K, Vv, cfg.ctx, max_len)
+    MODS = max(1, args.modules)
+    gws, kvs = [gw], [kv]
+    if MODS > 1:
+        # modules 1.. : seeded on the device (same init as make_weights: N(0, 0.02) matrices, unit
+        # gains), sharing module 0's embedding and lm_head; their caches hold seeded N(0,1) K/V
+        gen = torch.Generator(device="cuda")
+        dt = c.torch_dtype
+        for m in range(1, MODS):
+            gen.manual_seed(1000 * cfg.index + 7 + m)
+            rnd = lambda *shape: (torch.randn(shape, generator=gen, device="cuda") * 0.02).to(dt)
+            ones = lambda n: torch.ones(n, device="cuda", dtype=dt)
+            t = dict(embed=gw.t["embed"], lm_head=gw.t["lm_head"], enorm=ones(H), hnorm=ones(H),
+                     final_norm=ones(H), eh_proj=rnd(H, 2 * H), layers=[])
+            for _ in range(cfg.n_layers):
+                t["layers"].append(dict(in_norm=ones(H), wq=rnd(cfg.q_dim, H), wk=rnd(cfg.kv_dim, H),
+                                        wv=rnd(cfg.kv_dim, H), wo=rnd(H, cfg.q_dim), post_norm=ones(H),
+                                        wgate=rnd(cfg.ffn, H), wup=rnd(cfg.ffn, H), wdown=rnd(H, cfg.ffn)))
+            gws.append(M.Weights(c, t))
+            km = M.KVCache(c, B, max_len)
+            km.k.copy_(torch.randn(km.k.shape, generator=gen, device="cuda"))
+            km.v.copy_(torch.randn(km.v.shape, generator=gen, device="cuda"))
+            km.len.fill_(cfg.ctx)
+            kvs.append(km)
     print(f"[bench] inputs ready in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
 
     if args.calib_copy_mb:
@@ -120,7 +147,7 @@ def main():
     noise_bufs = [f32(make_round_noise(cfg, r)) for r in range(NBUF)]
     tokens = i32(tok_pad)
     hidden0 = f32(hid_pad)
-    ws = M.new_workspace(M.mtp_draft_workspace_size(c, B, 1 if T else rps, D, max_len))
+    ws = M.new_workspace(M.mtp_draft_workspace_size(c, B, 1 if T else max(rps, D - 1), D, max_len))
     if T:  # one settled token and one main-model hidden per sequence and round
         tok_shared = i32(toks0[:, 0])
         hid_shared = [f32(np.ascontiguousarray(make_round_hiddens(cfg, r)[:, 0])) for r in range(NBUF)]
@@ -152,7 +179,10 @@ def main():
         else:
             tk = tokens if r == 0 else out_tok[cur]
             hin = hidden0 if r == 0 else hid_bufs[r % NBUF]
-            M.mtp_draft_loop(c, gw, kv, D, rps, tk, hin, drafts, hiddens, dlog, ws)
+            if MODS > 1:
+                M.mtp_draft_loop_multi(c, gws, kvs, D, rps, tk, hin, drafts, hiddens, dlog, ws)
+            else:
+                M.mtp_draft_loop(c, gw, kv, D, rps, tk, hin, drafts, hiddens, dlog, ws)
         # stand-in target forward: target row j = draft logits of step j+1 + noise (row D
         # reuses step D's logits), one elementwise kernel for D = 1
         noise = noise_bufs[r % NBUF]
@@ -171,7 +201,8 @@ def main():
         if T:  # stand-in for the main model's verify pass + crop: its cache now ends at crop_len
             kv.len.copy_(ctx[nxt])
         else:
-            M.kv_crop(kv, ctx[cur])
+            for km in kvs:
+                M.kv_crop(km, ctx[cur])
 
     for r in range(args.warmup):
         step(r)
@@ -232,7 +263,7 @@ def main():
             traffic = rec.get("bytes_per_launch")
 
     cpu = None
-    if args.cpu_seconds > 0 and not T:
+    if args.cpu_seconds > 0 and not T and MODS == 1:
         cpu = cpu_baseline(cfg, w, K, Vv, args.cpu_seconds)
 
     line = {
@@ -240,7 +271,8 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded random-init weights, KV prefix, hiddens and target-logit noise)",
-        "config": {"workload": cfg.name + (f"-sharedkv{T}" if T else ""), "batch": B, "draft_tokens": D,
+        "config": {"workload": cfg.name + (f"-sharedkv{T}" if T else "") + (f"-modules{MODS}" if MODS > 1 else ""),
+                   "batch": B, "draft_tokens": D, "mtp_modules": MODS,
                    "kv_context": cfg.ctx,
                    "head_kv": f"reads a {T}-layer main-model cache (layer l mod {T})" if T else "own cache",
                    "target_noise_std": cfg.noise_std,

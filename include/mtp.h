@@ -143,6 +143,26 @@ int mtp_draft_loop(const mtp_config* cfg, const mtp_weights* w, const mtp_kv* kv
                    int32_t rows_per_seq, const int32_t* tokens, const float* hidden_in, int32_t* drafts,
                    float* hiddens, float* draft_logits, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* The D-step draft loop over M MTP modules ([YL 二.3]: the predictor holds several MTP layers; a
+ * single module is reused for every step, chosen by the step index modulo the layer count, and
+ * multi-module MTP gives each draft position its own layer; [YL 五]: that form needs a re-prefill
+ * to repair the stale KV left by rejected tokens).  modules[m] and kvs[m] (HOST arrays of M) are
+ * module m's weights and its own cache (all caches with the same batch B and max_len; the
+ * embedding and lm_head may be the same tensors for every module).
+ *   Catch-up: every module appends the catch-up rows (tokens / hidden_in as in mtp_draft_loop);
+ *   module 0's last row gives draft 1.  Modules other than 0 skip the final norm and lm_head.
+ *   Step k >= 2: module (k-1) mod M first appends the rows of this round's chain it has not seen
+ *   (steps s+1 .. k-1 after the last step s it drafted, or after the catch-up), each row fed
+ *   (draft, output hidden) of the step before it and placed one position after it, then its own
+ *   row for step k; that row gives draft k.
+ * With M = 1 this is mtp_draft_loop.  Outputs as in mtp_draft_loop.  Each kvs[m].len grows by the
+ * rows module m appended; after verification the caller crops every module's cache to the same
+ * length (kv_crop) and the next catch-up re-prefills the settled rows.
+ * Workspace: mtp_draft_workspace_size(cfg, B, max(rows_per_seq, M > 1 ? D - 1 : 1), D, max_len). */
+int mtp_draft_loop_multi(const mtp_config* cfg, const mtp_weights* modules, int32_t M, const mtp_kv* kvs, int32_t D,
+                         int32_t rows_per_seq, const int32_t* tokens, const float* hidden_in, int32_t* drafts,
+                         float* hiddens, float* draft_logits, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* The D-step draft loop of a head that keeps no KV cache of its own and reads the main model's
  * keys and values ([DLM "MTP speculative decoding"] item 1: the drafter has no cache and reads the
  * model's keys and values directly; its input is the last token's embedding beside the model's

@@ -80,6 +80,8 @@ _sigs = {
                         _P, _P, _P, _SZ, _P], _I),
     "mtp_draft_loop": ([ctypes.POINTER(MtpConfig), ctypes.POINTER(MtpWeights), ctypes.POINTER(MtpKV), _I, _I, _P, _P,
                         _P, _P, _P, _P, _SZ, _P], _I),
+    "mtp_draft_loop_multi": ([ctypes.POINTER(MtpConfig), ctypes.POINTER(MtpWeights), _I, ctypes.POINTER(MtpKV), _I, _I,
+                              _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
     "mtp_draft_loop_shared_kv": ([ctypes.POINTER(MtpConfig), ctypes.POINTER(MtpWeights), ctypes.POINTER(MtpKV), _I,
                                   ctypes.POINTER(_I), _I, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
     "spec_verify_workspace_size": ([_I, _I, _I, ctypes.POINTER(MtpSampling), ctypes.POINTER(_SZ)], _I),
@@ -264,6 +266,23 @@ def mtp_draft_loop(cfg: Config, w: Weights, kv: KVCache, D: int, rows_per_seq: i
     R = B * rows_per_seq
     _check(_lib.mtp_draft_loop(
         ctypes.byref(cfg.c()), ctypes.byref(w.c), ctypes.byref(kv.c()), D, rows_per_seq,
+        _ptr(tokens, torch.int32, "tokens", R), _ptr(hidden_in, torch.float32, "hidden_in", R * H),
+        _ptr(drafts, torch.int32, "drafts", B * D), _ptr(hiddens, torch.float32, "hiddens", B * D * H),
+        _ptr(draft_logits, torch.float32, "draft_logits", B * D * cfg.vocab), _ptr(ws, None, "ws"), ws.numel(),
+        _stream(stream)))
+
+
+def mtp_draft_loop_multi(cfg: Config, modules: Sequence[Weights], kvs: Sequence[KVCache], D: int, rows_per_seq: int,
+                         tokens, hidden_in, drafts, hiddens, draft_logits, ws: torch.Tensor, stream=None) -> None:
+    M = len(modules)
+    if M < 1 or len(kvs) != M:
+        raise MTPError(-1, "one cache per module needed")
+    B, H = kvs[0].batch, cfg.hidden
+    R = B * rows_per_seq
+    ws_arr = (MtpWeights * M)(*[w.c for w in modules])
+    kv_arr = (MtpKV * M)(*[kv.c() for kv in kvs])
+    _check(_lib.mtp_draft_loop_multi(
+        ctypes.byref(cfg.c()), ws_arr, M, kv_arr, D, rows_per_seq,
         _ptr(tokens, torch.int32, "tokens", R), _ptr(hidden_in, torch.float32, "hidden_in", R * H),
         _ptr(drafts, torch.int32, "drafts", B * D), _ptr(hiddens, torch.float32, "hiddens", B * D * H),
         _ptr(draft_logits, torch.float32, "draft_logits", B * D * cfg.vocab), _ptr(ws, None, "ws"), ws.numel(),

@@ -210,6 +210,7 @@ StepArgs base_step(const mtp_config* cfg, const mtp_weights* w, const mtp_kv* kv
   s.shared = 0;
   s.pos_off = 0;
   s.kv_layer = nullptr;
+  s.no_head = 0;
   return s;
 }
 
@@ -388,6 +389,72 @@ int mtp_draft_loop_shared_kv(const mtp_config* cfg, const mtp_weights* w, const 
     timer_events(MTP_KERNEL_LM_HEAD, &s.ev_begin, &s.ev_end);
     const hipError_t e = run_step(s);
     if (e != hipSuccess) return hip_fail(e, "mtp_draft_loop_shared_kv launch");
+  }
+  return MTP_OK;
+}
+
+int mtp_draft_loop_multi(const mtp_config* cfg, const mtp_weights* modules, int32_t M, const mtp_kv* kvs, int32_t D,
+                         int32_t rows_per_seq, const int32_t* tokens, const float* hidden_in, int32_t* drafts,
+                         float* hiddens, float* draft_logits, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (M < 1 || !modules || !kvs) return fail(MTP_ERR_ARG, "M >= 1 modules and caches needed");
+  if (D < 1) return fail(MTP_ERR_ARG, "D must be >= 1");
+  int rc;
+  if ((rc = check_cfg(cfg))) return rc;
+  for (int m = 0; m < M; ++m) {
+    if ((rc = check_weights(cfg, &modules[m])) || (rc = check_kv(&kvs[m]))) return rc;
+    if (kvs[m].batch != kvs[0].batch || kvs[m].max_len != kvs[0].max_len)
+      return fail(MTP_ERR_ARG, "every module's cache needs the same batch and max_len");
+  }
+  if (rows_per_seq < 1) return fail(MTP_ERR_ARG, "rows_per_seq must be >= 1");
+  if (!tokens || !hidden_in || !aligned16(hidden_in)) return fail(MTP_ERR_ARG, "tokens / hidden_in NULL or misaligned");
+  if (!drafts) return fail(MTP_ERR_ARG, "drafts is NULL");
+  if ((hiddens && !aligned16(hiddens)) || (draft_logits && !aligned16(draft_logits)))
+    return fail(MTP_ERR_ARG, "hiddens / draft_logits misaligned");
+  if (!ws || !aligned16(ws)) return fail(MTP_ERR_ARG, "workspace NULL or misaligned");
+  const int rmax = M > 1 && D - 1 > rows_per_seq ? D - 1 : rows_per_seq;
+  const DraftLayout L = draft_layout(*cfg, kvs[0].batch, rmax, D, kvs[0].max_len);
+  if (ws_bytes < L.total) return fail(MTP_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, L.total);
+  const int H = cfg->hidden;
+  float* hbuf = hiddens ? hiddens : carve(ws, L).hid_fb;
+  std::vector<int> seen(M, 1);  // chain steps whose rows each module's cache holds
+  for (int m = 0; m < M; ++m) {  // catch-up: every module appends the settled rows
+    StepArgs s = base_step(cfg, &modules[m], &kvs[m], ws, L, stream);
+    s.rps = rows_per_seq;
+    s.tok = tokens;
+    s.tok_sb = rows_per_seq;
+    s.hin = hidden_in;
+    s.hin_sb = rows_per_seq;
+    s.no_head = m > 0;
+    s.hout = hbuf;
+    s.hout_sb = D;
+    s.hout_last = 1;
+    s.draft = drafts;
+    s.dr_sb = D;
+    s.logits = draft_logits;
+    s.lg_sb = (long)D * cfg->vocab;
+    if (m == 0) timer_events(MTP_KERNEL_LM_HEAD, &s.ev_begin, &s.ev_end);
+    const hipError_t e = run_step(s);
+    if (e != hipSuccess) return hip_fail(e, "mtp_draft_loop_multi launch");
+  }
+  for (int k = 2; k <= D; ++k) {  // step k: module (k-1) mod M over the chain rows it has not seen
+    const int m = (k - 1) % M, lo = seen[m];
+    StepArgs s = base_step(cfg, &modules[m], &kvs[m], ws, L, stream);
+    s.rps = k - lo;
+    s.tok = drafts + (lo - 1);
+    s.tok_sb = D;
+    s.hin = hbuf + (long)(lo - 1) * H;
+    s.hin_sb = D;
+    s.hout = hbuf + (long)(k - 1) * H;
+    s.hout_sb = D;
+    s.hout_last = 1;
+    s.draft = drafts + (k - 1);
+    s.dr_sb = D;
+    s.logits = draft_logits ? draft_logits + (long)(k - 1) * cfg->vocab : nullptr;
+    s.lg_sb = (long)D * cfg->vocab;
+    timer_events(MTP_KERNEL_LM_HEAD, &s.ev_begin, &s.ev_end);
+    const hipError_t e = run_step(s);
+    if (e != hipSuccess) return hip_fail(e, "mtp_draft_loop_multi launch");
+    seen[m] = k;
   }
   return MTP_OK;
 }

@@ -108,6 +108,7 @@ struct StepArgs {
   int shared;
   int pos_off;
   const int32_t* kv_layer;
+  int no_head;  // 1: append the rows' K/V and grow len only (no final norm, lm_head or outputs)
 };
 
 // Which GEMV layout, variant and grid serve nact activation rows of width K (VE elements per

@@ -681,6 +681,22 @@ hipError_t run_step_t(const StepArgs& s) {
     f.grow = !s.shared;
     return launch_finalize<W>(f, s.stream);
   }
+  if (s.no_head) {  // K/V appended: only the lengths (and device errors) remain
+    LmFinal f = {};
+    f.B = s.B;
+    f.tok = s.tok;
+    f.tok_sb = s.tok_sb;
+    f.rps = s.rps;
+    f.V = c.vocab;
+    f.len = s.kv_len;
+    f.max_len = s.max_len;
+    f.x = s.ws.x;
+    f.H = H;
+    f.status = s.ws.status;
+    f.rows = step_rows(s);
+    f.grow = 1;
+    return launch_finalize<W>(f, s.stream);
+  }
   {  // final norm + lm_head + argmax + finalisation
     PLmHead<W> p;
     fill_base<W>(p, s);
