@@ -434,9 +434,8 @@ bool use_mfma(const P& p, const MfmaBufs* mb) {
 // partials in split order and applies the policy's store.
 constexpr int kMfmaItems = 1024;  // (row group, K range) items a launch aims for: 4 per CU
 
-template <class P, int MG>
-hipError_t launch_mfma(P& p, hipStream_t st, int* grid_used, const MfmaBufs& mb) {
-  constexpr int NT = (P::kArgmax || P::kVocab) ? 2 : 1;  // 128 weight rows per workgroup for lm_head, else 64
+template <class P, int MG, int NT>
+hipError_t launch_mfma_nt(P& p, hipStream_t st, int* grid_used, const MfmaBufs& mb) {
   MfmaBufs m = mb;
   const int groups = (p.N + 4 * NT * 16 - 1) / (4 * NT * 16);
   // passes of MG activation tiles (at most: the valid rows are counted on the device); long
@@ -465,6 +464,21 @@ hipError_t launch_mfma(P& p, hipStream_t st, int* grid_used, const MfmaBufs& mb)
     hipLaunchKernelGGL((k_splitk_reduce<P>), dim3(rgrid), dim3(kWG), 0, st, p, m);
   }
   return hipGetLastError();
+}
+
+// 128 weight rows per workgroup (two 16-row tiles per wave) for lm_head, and for other wide
+// matrices at up to 64 activation rows: each activation chunk staged in LDS then serves twice the
+// weight rows; otherwise 64.
+template <class P, int MG>
+hipError_t launch_mfma(P& p, hipStream_t st, int* grid_used, const MfmaBufs& mb) {
+  if constexpr (P::kArgmax || P::kVocab) {
+    return launch_mfma_nt<P, MG, 2>(p, st, grid_used, mb);
+  } else {
+    if constexpr (MG <= 4) {
+      if (p.N >= 4096) return launch_mfma_nt<P, MG, 2>(p, st, grid_used, mb);
+    }
+    return launch_mfma_nt<P, MG, 1>(p, st, grid_used, mb);
+  }
 }
 
 template <class W, class P>
