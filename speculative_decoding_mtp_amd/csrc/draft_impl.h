@@ -49,11 +49,14 @@ struct PBase {
     }
     lds_len = s_len;
   }
+  // row is always a row of the call (0 for an index past the end): activation loads are issued
+  // for every row before validity masks them
   __device__ void act(int a, const int* s_n, int& row, bool& valid) const {
-    row = a;
+    row = 0;
     valid = false;
     if (a < B * rps) {
       const int b = a / rps, i = a - b * rps;
+      row = a;
       valid = i < s_n[b];
     }
   }
@@ -73,14 +76,17 @@ struct PEhProj : PBase<W> {
   int hin_sb, H;
   float* xout;
 
+  // Branch-free: both halves are read at in-bounds addresses (a padding row's token is clamped
+  // into the vocabulary; its values are masked by the caller) and the right one is kept.
   __device__ void load_x(int row, int k, float (&f)[W::VE]) const {
     const int b = row / this->rps, i = row - b * this->rps;
-    if (k < H) {
-      const int t = this->tok[(long)b * this->tok_sb + i];
-      W::cvt(ld16(embed + (long)t * H + k), f);
-    } else {
-      load_f32_vec<W::VE>(hin + ((long)b * hin_sb + i) * H + (k - H), f);
-    }
+    const int t = min(max(this->tok[(long)b * this->tok_sb + i], 0), this->V - 1);
+    const bool emb = k < H;
+    float e[W::VE], h[W::VE];
+    W::cvt(ld16(embed + (long)t * H + (emb ? k : 0)), e);
+    load_f32_vec<W::VE>(hin + ((long)b * hin_sb + i) * H + (emb ? 0 : k - H), h);
+#pragma unroll
+    for (int j = 0; j < W::VE; ++j) f[j] = emb ? e[j] : h[j];
   }
   __device__ uint4 gain_raw(int k) const { return ld16(k < H ? enorm + k : hnorm + (k - H)); }
   __device__ const T* wrow(int m) const { return w + (long)m * (2 * H); }

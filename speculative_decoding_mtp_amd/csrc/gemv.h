@@ -104,26 +104,29 @@ __device__ __forceinline__ void load_slice(const P& p, const int (&rows)[RB], co
 #pragma unroll
     for (int j = 0; j < NJ; ++j) graw[j] = p.gain_raw(min(cbase + j * cstride, Kc - 1) * VE);
   }
+  // every activation load is issued before any is used (in-bounds addresses: the row from act()
+  // and the column clamped), then masked: no branch around a load, one memory round trip
+#pragma unroll
+  for (int r = 0; r < RB; ++r)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) p.load_x(rows[r], min(cbase + j * cstride, Kc - 1) * VE, x[r][j]);
 #pragma unroll
   for (int r = 0; r < RB; ++r) {
     float s0 = 0.f, s1 = 0.f;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int c = cbase + j * cstride;
-      if (valid[r] && c < Kc) {
-        p.load_x(rows[r], c * VE, x[r][j]);
-        if constexpr (P::kNorm > 0) {
-          float s = 0.f;
+      const bool live = valid[r] && c < Kc;
 #pragma unroll
-          for (int e = 0; e < VE; ++e) s = fmaf(x[r][j][e], x[r][j][e], s);
-          if (P::kNorm == 2 && c * VE >= p.split)
-            s1 += s;
-          else
-            s0 += s;
-        }
-      } else {
+      for (int e = 0; e < VE; ++e) x[r][j][e] = live ? x[r][j][e] : 0.f;
+      if constexpr (P::kNorm > 0) {
+        float s = 0.f;
 #pragma unroll
-        for (int e = 0; e < VE; ++e) x[r][j][e] = 0.f;
+        for (int e = 0; e < VE; ++e) s = fmaf(x[r][j][e], x[r][j][e], s);
+        if (P::kNorm == 2 && c * VE >= p.split)
+          s1 += s;
+        else
+          s0 += s;
       }
     }
     if constexpr (P::kNorm > 0) {
