@@ -472,17 +472,16 @@ hipError_t launch_mfma_nt(P& p, hipStream_t st, int* grid_used, const MfmaBufs& 
   return hipGetLastError();
 }
 
-// 128 weight rows per workgroup (two 16-row tiles per wave) for lm_head, and for other wide
-// matrices at up to 64 activation rows: each activation chunk staged in LDS then serves twice the
-// weight rows; otherwise 64.
+// 128 weight rows per workgroup (two 16-row tiles per wave) for lm_head and for other matrices
+// with enough column groups (4096+ rows at up to 64 activation rows, 1024+ in 128-row passes, where
+// the passes add parallelism): each activation chunk staged in LDS then serves twice the weight
+// rows; otherwise 64.
 template <class P, int MG>
 hipError_t launch_mfma(P& p, hipStream_t st, int* grid_used, const MfmaBufs& mb) {
   if constexpr (P::kArgmax || P::kVocab) {
     return launch_mfma_nt<P, MG, 2>(p, st, grid_used, mb);
   } else {
-    if constexpr (MG <= 4) {
-      if (p.N >= 4096) return launch_mfma_nt<P, MG, 2>(p, st, grid_used, mb);
-    }
+    if (p.N >= (MG >= 8 ? 1024 : 4096)) return launch_mfma_nt<P, MG, 2>(p, st, grid_used, mb);
     return launch_mfma_nt<P, MG, 1>(p, st, grid_used, mb);
   }
 }
