@@ -253,8 +253,13 @@ def main():
     lm_avg_s = lm_ms / 1e3 / max(lm_n, 1)
     achieved = lm_bytes / lm_avg_s / 1e9
     traffic = None
+    workload = cfg.name + (f"-sharedkv{T}" if T else "") + (f"-modules{MODS}" if MODS > 1 else "")
     if args.traffic and os.path.exists(args.traffic):
         rec = json.load(open(args.traffic))
+    else:
+        rec = {}
+    # the counters were taken on one workload's lm_head, with the kernel sources of that time
+    if rec.get("workload") == workload:
         root = os.path.dirname(os.path.abspath(__file__))
         h = hashlib.sha256()
         for p in rec.get("source_files", []):
@@ -271,7 +276,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded random-init weights, KV prefix, hiddens and target-logit noise)",
-        "config": {"workload": cfg.name + (f"-sharedkv{T}" if T else "") + (f"-modules{MODS}" if MODS > 1 else ""),
+        "config": {"workload": workload,
                    "batch": B, "draft_tokens": D, "mtp_modules": MODS,
                    "kv_context": cfg.ctx,
                    "head_kv": f"reads a {T}-layer main-model cache (layer l mod {T})" if T else "own cache",
