@@ -275,19 +275,28 @@ static_assert((kTopCap & (kTopCap - 1)) == 0, "the candidate sort pads to a powe
 static_assert(kMaxTopK <= 128, "the decision keeps two candidates per lane");
 
 // Item e of tile `base` for thread t: ids base + 4 (t + kWG q) + r, e = 4 q + r.
-__device__ __forceinline__ void load_tile(const float* x, int V, int base, bool vec, float (&v)[16]) {
+// One tile: items base + 4 (tid + kWG q) + r, q, r < 4.  Every load is issued unconditionally (a
+// clamped in-bounds address, items past V masked to -inf), so the loads of one tile can be in
+// flight together with the next tile's.  VEC: float4 loads (the row is 16-byte aligned and V a
+// multiple of 4, so a group of four is either wholly inside the row or wholly past it).
+template <bool VEC>
+__device__ __forceinline__ void load_tile(const float* x, int V, int base, float (&v)[16]) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int k0 = base + 4 * (threadIdx.x + kWG * q);
-    if (vec && k0 + 3 < V) {
-      const float4 f = *reinterpret_cast<const float4*>(x + k0);
-      v[4 * q] = f.x;
-      v[4 * q + 1] = f.y;
-      v[4 * q + 2] = f.z;
-      v[4 * q + 3] = f.w;
+    if constexpr (VEC) {
+      const float4 f = *reinterpret_cast<const float4*>(x + min(k0, V - 4));
+      const bool in = k0 < V;
+      v[4 * q] = in ? f.x : -INFINITY;
+      v[4 * q + 1] = in ? f.y : -INFINITY;
+      v[4 * q + 2] = in ? f.z : -INFINITY;
+      v[4 * q + 3] = in ? f.w : -INFINITY;
     } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[4 * q + r] = k0 + r < V ? x[k0 + r] : -INFINITY;
+      for (int r = 0; r < 4; ++r) {
+        const float f = x[min(k0 + r, V - 1)];
+        v[4 * q + r] = k0 + r < V ? f : -INFINITY;
+      }
     }
   }
 }
@@ -305,14 +314,11 @@ __device__ int sort_candidates(TopkSmem& sm, int S, int keep) {
   return min(keep, S);
 }
 
-__global__ __launch_bounds__(kWG) void k_topk_stream(VerifyArgs a) {
-  __shared__ TopkSmem sm;
-  const int row = blockIdx.x, K = a.top_k, V = a.V;
-  const int tgt_rows = a.B * (a.D + 1);
-  const float* x = row < tgt_rows ? a.tl + (long)row * V : a.dl + (long)(row - tgt_rows) * V;
-  const bool vec = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
+template <bool VEC>
+__device__ __forceinline__ void topk_row(const VerifyArgs& a, TopkSmem& sm, int row, const float* x) {
+  const int K = a.top_k, V = a.V;
   float cur[16], nxt[16];
-  load_tile(x, V, 0, vec, cur);
+  load_tile<VEC>(x, V, 0, cur);
   float rmax = -INFINITY;  // this thread's running maximum
 #pragma unroll
   for (int e = 0; e < 16; ++e) rmax = fmaxf(rmax, cur[e]);
@@ -346,10 +352,12 @@ __global__ __launch_bounds__(kWG) void k_topk_stream(VerifyArgs a) {
     }
   };
   for (int base = 0; base < V; base += 2 * kTile) {
-    if (base + kTile < V) load_tile(x, V, base + kTile, vec, nxt);  // in flight meanwhile
+    // loads are unconditional (past the row they are clamped and masked): the compiler can then
+    // count them and keep the next tile in flight while this one is scanned
+    load_tile<VEC>(x, V, base + kTile, nxt);
     append(cur, base);
     if (base + kTile >= V) break;
-    if (base + 2 * kTile < V) load_tile(x, V, base + 2 * kTile, vec, cur);
+    load_tile<VEC>(x, V, base + 2 * kTile, cur);
     append(nxt, base + kTile);
     if (base == 2 * kTile && base + 2 * kTile < V) theta = fmaxf(theta, bound());
   }
@@ -361,7 +369,7 @@ __global__ __launch_bounds__(kWG) void k_topk_stream(VerifyArgs a) {
     if (threadIdx.x == 0) sm.cnt = 0;
     __syncthreads();
     for (int base = 0; base < V; base += kTile) {
-      load_tile(x, V, base, vec, cur);
+      load_tile<VEC>(x, V, base, cur);
 #pragma unroll
       for (int h = 0; h < 4; ++h) {  // a quarter tile (at most kTile / 4 appends) at a time
 #pragma unroll
@@ -435,6 +443,16 @@ __global__ __launch_bounds__(kWG) void k_topk_stream(VerifyArgs a) {
     oi[t] = -1;
   }
   if (threadIdx.x == 0) a.top_n[row] = n;
+}
+
+__global__ __launch_bounds__(kWG) void k_topk_stream(VerifyArgs a) {
+  __shared__ TopkSmem sm;
+  const int row = blockIdx.x, tgt_rows = a.B * (a.D + 1);
+  const float* x = row < tgt_rows ? a.tl + (long)row * a.V : a.dl + (long)(row - tgt_rows) * a.V;
+  if ((reinterpret_cast<uintptr_t>(x) & 15) == 0 && (a.V & 3) == 0)
+    topk_row<true>(a, sm, row, x);
+  else
+    topk_row<false>(a, sm, row, x);
 }
 
 // One wave per sequence: accept / reject / draw ([P2 "Speculative sampling"], [P3 rejection
