@@ -413,8 +413,9 @@ def bench_prefill(args, cfg, rows):
 def bench_target(args, cfg, layers, row_counts=(1, 2, 7)):
     """The target's verify pass (mtp_target_forward) on a dense stand-in with the head's
     dimensions and ``layers`` blocks over a KV context of cfg.ctx positions (B = cfg.batch):
-    time per call when it scores 1, 2 or 7 positions per sequence ([P2]: seven positions cost
-    about as much as one, because the pass is bound by streaming the weights)."""
+    time per call when it scores 1, 2 or 7 positions per sequence ([DLM "MTP speculative
+    decoding"]: seven positions cost little more than one, because the pass is bound by reading
+    the weights)."""
     import dataclasses
     import torch
     import speculative_decoding_mtp_amd as M

@@ -455,8 +455,8 @@ __global__ __launch_bounds__(kWG) void k_topk_stream(VerifyArgs a) {
     topk_row<false>(a, sm, row, x);
 }
 
-// One wave per sequence: accept / reject / draw ([P2 "Speculative sampling"], [P3 rejection
-// sampler]).  P_j = warp(target row j); Q_j = one-hot at the draft (q_mode 0) or warp(draft row
+// One wave per sequence: accept / reject / draw ([DLM "MTP speculative decoding"] item 3, [YL 三
+// stage 3]).  P_j = warp(target row j); Q_j = one-hot at the draft (q_mode 0) or warp(draft row
 // j) (q_mode 1).  Draft j is accepted iff P_j(d) > 0 and U_j <= P_j(d) / Q_j(d); at the first
 // rejection a token is drawn from normalize(max(0, P_j - Q_j)) (P_j if that is all zero), and
 // if every draft holds, from P_D.

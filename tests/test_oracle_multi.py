@@ -140,9 +140,9 @@ def test_each_module_holds_the_rows_of_the_chain_it_was_asked_about():
 
 
 def test_crop_and_catch_up_remove_the_rows_of_rejected_drafts():
-    # Round 1 drafts, the caches are cropped back to the settled length, round 2's catch-up
-    # appends the settled rows: every module then equals a module that only ever saw the settled
-    # rows, and round 2 drafts the same.
+    # A first speculative round drafts, the caches are cropped back to the settled length, the
+    # next round's catch-up appends the settled rows: every module then equals a module that only
+    # ever saw the settled rows, and the next round drafts the same.
     cfg = _cfg(D=3, batch=2)
     rng = np.random.default_rng(34)
     models = [O.OracleModel(cfg, _weights(cfg, rng)) for _ in range(3)]
