@@ -4,7 +4,7 @@ A step is one round of the whole path on synthetic inputs resident in HBM:
   mtp_draft_loop (catch-up rows + D-1 serial draft steps: dual RMSNorm + eh_proj, decoder
   block with RoPE over the head's KV cache, final norm, lm_head + argmax)
   -> synthetic target logits (draft logits + seeded noise, standing in for the main model)
-  -> mtp_state_snapshot (recurrent state of the target, p1's 19 MB per sequence)
+  -> mtp_state_snapshot (the main model's recurrent state, [HB14]'s 19 MB per sequence)
   -> spec_verify -> mtp_state_restore (where a draft was rejected) -> kv_crop.
 The workload is the single-layer bf16 head with H=2048, 16/4 heads of 128, FFN 6144, vocab
 151936, a 4096-position KV context, B=1, D=1, greedy verification over 2 positions with target
