@@ -160,7 +160,7 @@ __global__ __launch_bounds__(kWG, MG <= 4 ? 2 : 1) void k_gemm_mfma(P p, MfmaBuf
   constexpr int WR = NT * 16;          // weight rows per wave
   constexpr int WL = WR / 4;           // weight loads per lane and chunk (four rows per load)
   constexpr bool DB = MG <= 2;         // double-buffered activation staging
-  constexpr bool RP = MG == 4;         // single buffer, next chunk's activations held in registers
+  constexpr bool RP = MG >= 4;         // single buffer, next chunk's activations held in registers
   constexpr int NB = DB ? 2 : 1;
   constexpr int AV = 2 * MG * 16 * (kMfmaKC / 8);  // 16-byte activation vectors per chunk (hi + lo)
   constexpr int PER = (AV + kWG - 1) / kWG;
