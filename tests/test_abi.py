@@ -20,7 +20,8 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for n in ["mtp_draft_step", "mtp_draft_loop", "spec_verify", "kv_crop", "mtp_state_snapshot",
               "mtp_state_restore", "mtp_draft_workspace_size", "spec_verify_workspace_size", "mtp_check",
-              "mtp_last_error", "mtp_timer_start", "mtp_timer_read"]:
+              "mtp_last_error", "mtp_timer_start", "mtp_timer_read", "mtp_target_workspace_size",
+              "mtp_target_forward", "mtp_draft_loop_shared_kv", "mtp_draft_loop_multi"]:
         assert n in names, n
 
 
@@ -47,3 +48,25 @@ def test_host_side_checks_without_a_gpu():
     with pytest.raises(M.MTPError):
         M.spec_verify_workspace_size(4, 2, 1000, M.sampling(1.0, 500, 0.9))
     assert M.spec_verify_workspace_size(4, 2, 1000, M.sampling(1.0, 50, 0.9)) > 0
+
+
+def test_host_side_checks_of_the_widened_loops_without_a_gpu():
+    # NULL device pointers: every check below fails on the host, before any launch
+    M = pytest.importorskip("speculative_decoding_mtp_amd")
+    from synth import CONFIGS
+    from tests.gpu_util import config
+    c = config(CONFIGS["tiny"]).c()
+    lib = M._lib
+    rc = lib.mtp_draft_loop_multi(ctypes.byref(c), None, 0, None, 2, 1, None, None, None, None, None, None, 0, None)
+    assert rc == -1
+    assert b"M >= 1" in M._lib.mtp_last_error()
+    w = (M.MtpWeights * 1)()
+    kv = (M.MtpKV * 1)()
+    rc = lib.mtp_draft_loop_multi(ctypes.byref(c), w, 1, kv, 2, 1, None, None, None, None, None, None, 0, None)
+    assert rc == -1                                  # NULL weights
+    layers = (ctypes.c_int32 * 1)(0)
+    rc = lib.mtp_draft_loop_shared_kv(ctypes.byref(c), None, None, 1, layers, 2, None, None, None, None, None,
+                                      None, 0, None)
+    assert rc == -1
+    rc = lib.mtp_target_forward(ctypes.byref(c), None, None, 1, None, None, None, None, 0, None)
+    assert rc == -1
