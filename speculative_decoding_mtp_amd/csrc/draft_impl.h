@@ -449,7 +449,7 @@ hipError_t launch_mfma_nt(P& p, hipStream_t st, int* grid_used, const MfmaBufs& 
   const int npass = P::kArgmax ? 1 : (p.nact + MG * 16 - 1) / (MG * 16);
   const int par = npass > 2 ? npass * groups : groups;
   int ks = 1;
-  if (!P::kArgmax && par < kMfmaItems && m.part) {
+  if (!P::kArgmax && par < (npass > 2 ? kMfmaItems / 2 : kMfmaItems) && m.part) {
     ks = (kMfmaItems + par - 1) / par;
     const int kc = p.K / kMfmaKC;
     if (ks > kc) ks = kc;
@@ -473,15 +473,16 @@ hipError_t launch_mfma_nt(P& p, hipStream_t st, int* grid_used, const MfmaBufs& 
 }
 
 // 128 weight rows per workgroup (two 16-row tiles per wave) for lm_head and for other matrices
-// with enough column groups (4096+ rows at up to 64 activation rows, 1024+ in 128-row passes, where
-// the passes add parallelism): each activation chunk staged in LDS then serves twice the weight
+// with enough column groups (4096+ rows, or 1024+ when four or more activation passes add
+// parallelism, as in a prefill): each activation chunk staged in LDS then serves twice the weight
 // rows; otherwise 64.
 template <class P, int MG>
 hipError_t launch_mfma(P& p, hipStream_t st, int* grid_used, const MfmaBufs& mb) {
   if constexpr (P::kArgmax || P::kVocab) {
     return launch_mfma_nt<P, MG, 2>(p, st, grid_used, mb);
   } else {
-    if (p.N >= (MG >= 8 ? 1024 : 4096)) return launch_mfma_nt<P, MG, 2>(p, st, grid_used, mb);
+    const int npass = (p.nact + MG * 16 - 1) / (MG * 16);
+    if (p.N >= 4096 || (npass >= 4 && p.N >= 1024)) return launch_mfma_nt<P, MG, 2>(p, st, grid_used, mb);
     return launch_mfma_nt<P, MG, 1>(p, st, grid_used, mb);
   }
 }
@@ -491,12 +492,12 @@ hipError_t launch_gemv(P& p, hipStream_t st, int* grid_used = nullptr, const Mfm
   if constexpr (std::is_same<W, BF16>::value) {
     if (use_mfma<W>(p, mb)) {
       hipLaunchKernelGGL((k_prep<W, P>), dim3(p.nact), dim3(kWG), 0, st, p, *mb);
-      // activation tiles per pass from the activation count (an upper bound of the valid rows)
-      // (up to 128 rows take 64-row passes: a catch-up's valid rows are usually far fewer
-      // than its padded count)
+      // activation tiles per pass from the activation count (an upper bound of the valid rows):
+      // 32-row passes for a batch of serial steps, 64-row passes above (long calls too: at two
+      // waves per SIMD they beat 128-row passes at one, despite streaming the weights twice as
+      // often)
       if (p.nact <= 32) return launch_mfma<P, 2>(p, st, grid_used, *mb);
-      if (p.nact <= 128) return launch_mfma<P, 4>(p, st, grid_used, *mb);
-      return launch_mfma<P, 8>(p, st, grid_used, *mb);
+      return launch_mfma<P, 4>(p, st, grid_used, *mb);
     }
   }
   const GemvPlan pl = plan_gemv(p.nact, p.K, W::VE, p.N);
