@@ -112,8 +112,9 @@ struct StepArgs {
 };
 
 // Which GEMV layout, variant and grid serve nact activation rows of width K (VE elements per
-// 16-byte vector) over N output rows.  kind 0: k_gemv_w with nj = NJ; kind 1: k_gemv_s with
-// nj = NXM.  The same plan sizes the lm_head partial buffer and launches the kernel.
+// 16-byte vector) over N output rows.  kind 0: k_gemv_w with nj = NJ, rw rows per wave; kind 1:
+// k_gemv_s with nj = NXM, rw rows per workgroup.  The same plan sizes the lm_head partial buffer
+// and launches the kernel.
 struct GemvPlan {
   int kind, nj, rb, rw, grid;
 };

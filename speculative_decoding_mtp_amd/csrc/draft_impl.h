@@ -515,15 +515,16 @@ hipError_t launch_gemv(P& p, hipStream_t st, int* grid_used = nullptr, const Mfm
     MTP_W(4, 1, 2) MTP_W(4, 2, 2)  // short matrices: more waves across the compute units
 #undef MTP_W
   } else {
-#define MTP_S(NX_, RB_)                                                                    \
-  if (pl.nj == NX_ && pl.rb == RB_) {                                                      \
-    static int cap = 0;                                                                    \
-    const int grid = min(pl.grid, resident_cap(k_gemv_s<W, RB_, NX_, 8, P>, &cap));        \
-    if (grid_used) *grid_used = grid;                                                      \
-    hipLaunchKernelGGL((k_gemv_s<W, RB_, NX_, 8, P>), dim3(grid), dim3(kWG), 0, st, p);    \
-    return hipGetLastError();                                                              \
+#define MTP_S(NX_, RB_, RW_)                                                                 \
+  if (pl.nj == NX_ && pl.rb == RB_ && pl.rw == RW_) {                                          \
+    static int cap = 0;                                                                      \
+    const int grid = min(pl.grid, resident_cap(k_gemv_s<W, RB_, NX_, RW_, P>, &cap));        \
+    if (grid_used) *grid_used = grid;                                                        \
+    hipLaunchKernelGGL((k_gemv_s<W, RB_, NX_, RW_, P>), dim3(grid), dim3(kWG), 0, st, p);    \
+    return hipGetLastError();                                                                \
   }
-    MTP_S(4, 1) MTP_S(4, 2) MTP_S(4, 4) MTP_S(8, 1) MTP_S(8, 2) MTP_S(16, 1)
+    MTP_S(4, 1, 8) MTP_S(4, 2, 8) MTP_S(4, 4, 8) MTP_S(8, 1, 8) MTP_S(8, 2, 8) MTP_S(16, 1, 8)
+    MTP_S(4, 1, 4) MTP_S(4, 2, 4) MTP_S(4, 4, 4) MTP_S(8, 1, 4) MTP_S(8, 2, 4) MTP_S(16, 1, 4)
 #undef MTP_S
   }
   return hipErrorInvalidValue;
