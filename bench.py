@@ -285,6 +285,7 @@ def main():
                    f"sampling T={sp.temperature} top_k={sp.top_k} top_p={sp.top_p} q_mode={sp.q_mode}",
                    "recurrent_state_bytes_per_seq": state_bytes},
         "steps_per_s": round(args.steps / wall, 2),
+        "accepted_drafts_per_s": round(float(acc.sum()) * (args.steps / max(len(acc), 1)) / wall, 2),
         "acceptance": round(float(acc.mean()) / D, 4),
         "gpu_event_ms_per_step": round(gpu_ms / args.steps, 4),
         "roofline": {"bound": "hbm", "kernel": "lm_head GEMV + argmax", "achieved": round(achieved, 1),
@@ -479,36 +480,48 @@ def bench_target(args, cfg, layers, row_counts=(1, 2, 7)):
 
 
 def cpu_baseline(cfg, w, K, Vv, budget_s):
-    """The float64 oracle on the same workload, rounds until the time budget is spent."""
+    """The float64 oracle on the same workload, rounds until the time budget is spent: two thirds
+    of the budget with NumPy's BLAS threads as configured (all host cores by default), one third
+    with a single thread (reported as single_thread_value)."""
     import oracle as O
     from synth import make_first_round, make_round_hiddens, make_round_noise, make_round_uniforms
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        threads = os.cpu_count()
+        threads, threadpool_limits = os.cpu_count(), None
     model = O.OracleModel(cfg, w)
     B, D = cfg.batch, cfg.D
-    cache = O.KVCache(cfg, B, cfg.ctx + 256)
-    cache.load_prefix(K, Vv, cfg.ctx)
-    toks, hid = make_first_round(cfg)
-    tokens_out = rounds = 0
-    t0 = time.perf_counter()
-    while rounds < 2 or time.perf_counter() - t0 < budget_s:
-        drafts, _, logits, _ = O.draft_loop(model, cache, toks, hid, D)
-        ctx = cache.len.copy() - (D - 1)
-        tl = np.concatenate([logits, logits[:, D - 1:D]], axis=1).astype(np.float32) + make_round_noise(cfg, rounds)
-        ua, us = make_round_uniforms(cfg.index, B, D, rounds)
-        res = O.spec_verify(tl, drafts, ctx, cfg.sampling, None, ua, us)
-        O.kv_crop(cache, ctx)
-        tokens_out += int((res.n_accept + 1).sum())
-        toks, hid = res.out_tokens, make_round_hiddens(cfg, rounds)
-        rounds += 1
-        if cache.len.max() + D + 2 >= cache.max_len:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": round(tokens_out / dt, 4), "unit": "accepted tokens/s", "cores": threads, "kind": "oracle",
+
+    def run(budget):
+        cache = O.KVCache(cfg, B, cfg.ctx + 256)
+        cache.load_prefix(K, Vv, cfg.ctx)
+        toks, hid = make_first_round(cfg)
+        tokens_out = rounds = 0
+        t0 = time.perf_counter()
+        while rounds < 2 or time.perf_counter() - t0 < budget:
+            drafts, _, logits, _ = O.draft_loop(model, cache, toks, hid, D)
+            ctx = cache.len.copy() - (D - 1)
+            tl = np.concatenate([logits, logits[:, D - 1:D]], axis=1).astype(np.float32) + make_round_noise(cfg, rounds)
+            ua, us = make_round_uniforms(cfg.index, B, D, rounds)
+            res = O.spec_verify(tl, drafts, ctx, cfg.sampling, None, ua, us)
+            O.kv_crop(cache, ctx)
+            tokens_out += int((res.n_accept + 1).sum())
+            toks, hid = res.out_tokens, make_round_hiddens(cfg, rounds)
+            rounds += 1
+            if cache.len.max() + D + 2 >= cache.max_len:
+                break
+        return tokens_out, rounds, time.perf_counter() - t0
+
+    tok, rounds, dt = run(budget_s * 2 / 3)
+    line = {"value": round(tok / dt, 4), "unit": "accepted tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{rounds} rounds of the same workload (float64 NumPy, row by row), {dt:.1f} s"}
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            tok1, rounds1, dt1 = run(budget_s / 3)
+        line["single_thread_value"] = round(tok1 / dt1, 4)
+        line["single_thread_sample"] = f"{rounds1} rounds, {dt1:.1f} s"
+    return line
 
 
 if __name__ == "__main__":
