@@ -115,31 +115,53 @@ __device__ __forceinline__ void wg_sum(float (&v)[N], float* red) {
 
 // Number of valid rows of a sequence: the prefix of non-negative tokens that are inside the
 // vocabulary and still fit in the cache.  Also returns the flags that stopped the prefix.
-// Tokens are read eight at a time so that short rows cost one memory round trip.
+// count_tokens8 judges the first min(rps, 8) tokens already in registers (t[e] for e < 8; the
+// caller resolves rps > 8 with count_rows); count_rows reads eight tokens at a time, every load
+// of a group issued unconditionally (clamped to the row) so that short rows cost one memory
+// round trip.
+__device__ __forceinline__ int count_tokens8(const int (&t)[8], int rps, int V, int len, int max_len, int* flags) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if (e >= rps || t[e] < 0) {
+      if (flags) *flags = 0;
+      return e < rps ? e : rps;
+    }
+    if (t[e] >= V) {
+      if (flags) *flags = kFlagToken;
+      return e;
+    }
+    if (len + e >= max_len) {
+      if (flags) *flags = kFlagCapacity;
+      return e;
+    }
+  }
+  if (flags) *flags = 0;
+  return 8;
+}
+
 __device__ __forceinline__ int count_rows(const int32_t* tok, int rps, int V, int len, int max_len, int* flags) {
-  int f = 0;
   for (int i0 = 0; i0 < rps; i0 += 8) {
     int t[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) t[e] = (i0 + e < rps) ? tok[i0 + e] : -1;
+    for (int e = 0; e < 8; ++e) t[e] = tok[min(i0 + e, rps - 1)];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int n = i0 + e;
       if (n >= rps || t[e] < 0) {
-        if (flags) *flags = f;
+        if (flags) *flags = 0;
         return n < rps ? n : rps;
       }
       if (t[e] >= V) {
-        if (flags) *flags = f | kFlagToken;
+        if (flags) *flags = kFlagToken;
         return n;
       }
       if (len + n >= max_len) {
-        if (flags) *flags = f | kFlagCapacity;
+        if (flags) *flags = kFlagCapacity;
         return n;
       }
     }
   }
-  if (flags) *flags = f;
+  if (flags) *flags = 0;
   return rps;
 }
 

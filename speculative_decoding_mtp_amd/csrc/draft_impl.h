@@ -41,14 +41,39 @@ struct PBase {
   const int* rows;      // NULL, or valid rows counted once for the step
   const int* lds_len;  // cache lengths in LDS, set by setup()
 
-  __device__ void setup(int* s_n, int* s_len) {
-    for (int b = threadIdx.x; b < B; b += kWG) {
-      const int l = len[b];
-      s_len[b] = l;
-      s_n[b] = rows ? rows[b] : count_rows(tok + (long)b * tok_sb, rps, V, l, max_len, nullptr);
+  // Per-sequence row counts and cache lengths into LDS, in two halves so that a kernel can put
+  // its weight loads between them: setup_load issues thread b's loads (sequence b = thread;
+  // B <= kMaxBatch == kWG; clamped, so every lane loads in bounds), setup_store counts and
+  // writes.  setup() does both.
+  struct SeqPre {
+    int len, r;
+    int t[8];
+  };
+  __device__ SeqPre setup_load() const {
+    SeqPre q;
+    const int b = min((int)threadIdx.x, B - 1);
+    q.len = len[b];
+    q.r = (rows ? rows : len)[b];
+    const int32_t* tb = tok + (long)b * tok_sb;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q.t[e] = tb[min(e, rps - 1)];
+    return q;
+  }
+  __device__ void setup_store(const SeqPre& q, int* s_n, int* s_len) {
+    const int b = threadIdx.x;
+    if (b < B) {
+      s_len[b] = q.len;
+      s_n[b] = rows ? q.r
+                    : (rps <= 8 ? count_tokens8(q.t, rps, V, q.len, max_len, nullptr)
+                                : count_rows(tok + (long)b * tok_sb, rps, V, q.len, max_len, nullptr));
     }
     lds_len = s_len;
   }
+  __device__ void setup(int* s_n, int* s_len) { setup_store(setup_load(), s_n, s_len); }
+  // activation rows are known before the counts (row = activation index): a kernel may issue
+  // the first block's activation loads before setup
+  static constexpr bool kEarlyRows = true;
+  __device__ int row_of(int a) const { return a < B * rps ? a : 0; }
   // row is always a row of the call (0 for an index past the end): activation loads are issued
   // for every row before validity masks them
   __device__ void act(int a, const int* s_n, int& row, bool& valid) const {
@@ -111,13 +136,14 @@ struct PQKV : PBase<W> {
 
   // Per-sequence rows and cache lengths, and the rotation frequencies (exp in double once per
   // workgroup instead of once per output pair).
-  __device__ void setup(int* s_n, int* s_len) {
-    PBase<W>::setup(s_n, s_len);
+  __device__ void setup_store(const typename PBase<W>::SeqPre& q, int* s_n, int* s_len) {
+    PBase<W>::setup_store(q, s_n, s_len);
     __shared__ double s_inv_freq[64];  // head_dim <= 128
     for (int u = threadIdx.x; u < (hd >> 1); u += kWG)
       s_inv_freq[u] = exp(-2.0 * double(u) / double(hd) * log_theta);
     inv_freq = s_inv_freq;
   }
+  __device__ void setup(int* s_n, int* s_len) { setup_store(this->setup_load(), s_n, s_len); }
 
   __device__ void load_x(int row, int k, float (&f)[W::VE]) const { load_f32_vec<W::VE>(xin + (long)row * H + k, f); }
   __device__ uint4 gain_raw(int k) const { return ld16(g + k); }
@@ -201,6 +227,7 @@ struct PLmHead : PBase<W> {
   using T = typename W::T;
   static constexpr int kNorm = 1;
   static constexpr bool kArgmax = true;
+  static constexpr bool kEarlyRows = false;  // the row of sequence b is its last valid one
   const T *g, *w;
   const float* xin;
   int H;

@@ -24,6 +24,7 @@
 namespace mtp {
 
 constexpr int kMaxBatch = 256;  // sequences per drafter call (per-sequence row counts live in LDS)
+static_assert(kMaxBatch == kWG, "one sequence per thread in the policies' setup");
 
 template <int VE>
 __device__ __forceinline__ void load_f32_vec(const float* p, float (&f)[VE]) {
@@ -80,7 +81,9 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
 //   static constexpr bool kArgmax;  track the argmax over logical rows of every activation row
 //   static constexpr bool kVocab;   output rows are a vocabulary (wider MFMA row groups)
 //   void setup(int* s_n, int* s_len) per-sequence row counts and cache lengths into LDS (the
-//                                   kernel then syncs)
+//                                   kernel then syncs); also in halves: SeqPre setup_load() issues
+//                                   the loads, setup_store(pre, s_n, s_len) counts and writes
+//   static constexpr bool kEarlyRows; row_of(a) gives activation a's row before the counts exist
 //   void act(int a, const int* s_n, int& row, bool& valid)
 //   void load_x(int row, int k, float (&f)[VE])     raw activations k..k+VE-1 of a row
 //   uint4 gain_raw(int k)                            16 bytes of norm gains from column k (kNorm > 0)
@@ -92,24 +95,28 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
 
 // Register slice of RB activation rows: x[r][j] holds the VE activations of chunk
 // c = cbase + j * cstride (zero outside the row and for invalid rows), RMS-normalised when the
-// policy asks.  `reduce(s0, s1)` turns per-thread sums of squares into row totals.
-template <class W, int RB, int NJ, class P, class Reduce>
-__device__ __forceinline__ void load_slice(const P& p, const int (&rows)[RB], const bool (&valid)[RB], int cbase,
-                                           int cstride, int Kc, float (&x)[RB][NJ][W::VE], Reduce reduce) {
+// policy asks.  issue_slice starts the loads -- every one at an in-bounds address (the row from
+// row_of()/act() and the column clamped), none behind a branch, the norm gains of the thread's
+// columns with them -- and norm_slice masks and normalises once the rows' validity is known;
+// `reduce(s0, s1)` turns per-thread sums of squares into row totals.
+template <class W, int RB, int NJ, class P>
+__device__ __forceinline__ void issue_slice(const P& p, const int (&rows)[RB], int cbase, int cstride, int Kc,
+                                            float (&x)[RB][NJ][W::VE], uint4 (&graw)[NJ]) {
   constexpr int VE = W::VE;
-  // the norm gains of this thread's columns are fetched with the activations (one memory round
-  // trip before the reduction, not a second one after it)
-  uint4 graw[NJ];
   if constexpr (P::kNorm > 0) {
 #pragma unroll
     for (int j = 0; j < NJ; ++j) graw[j] = p.gain_raw(min(cbase + j * cstride, Kc - 1) * VE);
   }
-  // every activation load is issued before any is used (in-bounds addresses: the row from act()
-  // and the column clamped), then masked: no branch around a load, one memory round trip
 #pragma unroll
   for (int r = 0; r < RB; ++r)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) p.load_x(rows[r], min(cbase + j * cstride, Kc - 1) * VE, x[r][j]);
+}
+
+template <class W, int RB, int NJ, class P, class Reduce>
+__device__ __forceinline__ void norm_slice(const P& p, const bool (&valid)[RB], int cbase, int cstride, int Kc,
+                                           float (&x)[RB][NJ][W::VE], const uint4 (&graw)[NJ], Reduce reduce) {
+  constexpr int VE = W::VE;
 #pragma unroll
   for (int r = 0; r < RB; ++r) {
     float s0 = 0.f, s1 = 0.f;
@@ -225,13 +232,24 @@ __global__ __launch_bounds__(kWG) void k_gemv_w(P p) {
       for (int j = 0; j < NJ; ++j) wv[q][j] = ld_stream(wp + (long)min(lane + j * kWave, Kc - 1) * VE);
     }
   };
-  p.setup(s_n, s_len);                   // issues the token / length loads first
-  if (wave < ngroups) load_group(wave);  // the first weights are in flight during the prologue
+  // Issue order: the per-sequence count inputs, the first activation block (when its rows are
+  // known without the counts), then this wave's first weights; the counts are written to LDS
+  // once their own loads are back, with the later loads still in flight.
+  const auto pre = p.setup_load();
+  int rows[RB];
+  bool valid[RB];
+  float x[RB][NJ][VE];
+  uint4 graw[NJ];
+  if constexpr (P::kEarlyRows) {
+#pragma unroll
+    for (int r = 0; r < RB; ++r) rows[r] = p.row_of(r);
+    issue_slice<W, RB, NJ>(p, rows, lane, kWave, Kc, x, graw);
+  }
+  if (wave < ngroups) load_group(wave);
+  p.setup_store(pre, s_n, s_len);
   __syncthreads();
 
   for (int a0 = 0; a0 < p.nact; a0 += RB) {
-    int rows[RB];
-    bool valid[RB];
     bool any = false;
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
@@ -239,8 +257,8 @@ __global__ __launch_bounds__(kWG) void k_gemv_w(P p) {
       any |= valid[r];
     }
     if (!any) continue;  // uniform across the workgroup; the prefetched group is the next block's first
-    float x[RB][NJ][VE];
-    load_slice<W, RB, NJ>(p, rows, valid, lane, kWave, Kc, x, [](float& s0, float& s1) {
+    if (!P::kEarlyRows || a0 > 0) issue_slice<W, RB, NJ>(p, rows, lane, kWave, Kc, x, graw);
+    norm_slice<W, RB, NJ>(p, valid, lane, kWave, Kc, x, graw, [](float& s0, float& s1) {
       s0 = wave_sum_dpp(s0);
       s1 = wave_sum_dpp(s1);
     });
@@ -304,23 +322,45 @@ __global__ __launch_bounds__(kWG) void k_gemv_s(P p) {
   __shared__ float s_bv[4 * RB];
   __shared__ int s_bi[4 * RB];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  p.setup(s_n, s_len);
-  __syncthreads();
   const int Kc = p.K / VE;
   const int ngroups = (p.N + ROWS - 1) / ROWS;
+  uint4 wv[NXM][ROWS];
+  // chunk c = tid + j * kWG of rows m0 .. m0 + ROWS - 1; lanes past the row end read a clamped
+  // chunk (multiplied by x = 0)
+  auto load_group = [&](int g) {
+    const int m0 = g * ROWS;
+#pragma unroll
+    for (int j = 0; j < NXM; ++j)
+      if (j * kWG < Kc)  // uniform
+#pragma unroll
+        for (int q = 0; q < ROWS; ++q)
+          wv[j][q] = ld_stream(p.wrow(min(m0 + q, p.N - 1)) + (long)min(tid + j * kWG, Kc - 1) * VE);
+  };
+  // issue order as in k_gemv_w: count inputs, first activation block, first weights
+  const auto pre = p.setup_load();
+  int rows[RB];
+  bool valid[RB];
+  float x[RB][NXM][VE];
+  uint4 graw[NXM];
+  if constexpr (P::kEarlyRows) {
+#pragma unroll
+    for (int r = 0; r < RB; ++r) rows[r] = p.row_of(r);
+    issue_slice<W, RB, NXM>(p, rows, tid, kWG, Kc, x, graw);
+  }
+  if ((int)blockIdx.x < ngroups) load_group(blockIdx.x);
+  p.setup_store(pre, s_n, s_len);
+  __syncthreads();
 
   for (int a0 = 0; a0 < p.nact; a0 += RB) {
-    int rows[RB];
-    bool valid[RB];
     bool any = false;
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
       p.act(a0 + r, s_n, rows[r], valid[r]);
       any |= valid[r];
     }
-    if (!any) continue;
-    float x[RB][NXM][VE];
-    load_slice<W, RB, NXM>(p, rows, valid, tid, kWG, Kc, x, [&](float& s0, float& s1) {
+    if (!any) continue;  // uniform; the prefetched group is the next block's first
+    if (!P::kEarlyRows || a0 > 0) issue_slice<W, RB, NXM>(p, rows, tid, kWG, Kc, x, graw);
+    norm_slice<W, RB, NXM>(p, valid, tid, kWG, Kc, x, graw, [&](float& s0, float& s1) {
       s0 = wave_sum_dpp(s0);
       s1 = wave_sum_dpp(s1);
       if (lane == 0) {
@@ -348,16 +388,11 @@ __global__ __launch_bounds__(kWG) void k_gemv_s(P p) {
         for (int r = 0; r < RB; ++r) acc[q][r] = 0.f;
 #pragma unroll
       for (int j = 0; j < NXM; ++j) {
-        const int c = tid + j * kWG;
-        if (j * kWG < Kc) {  // uniform; lanes past the row end read a clamped chunk against x = 0
-          uint4 wv[ROWS];
-#pragma unroll
-          for (int q = 0; q < ROWS; ++q)
-            wv[q] = ld_stream(p.wrow(min(m0 + q, p.N - 1)) + (long)min(c, Kc - 1) * VE);
+        if (j * kWG < Kc) {  // uniform
 #pragma unroll
           for (int q = 0; q < ROWS; ++q) {
             float wf[VE];
-            W::cvt(wv[q], wf);
+            W::cvt(wv[j][q], wf);
 #pragma unroll
             for (int r = 0; r < RB; ++r)
 #pragma unroll
@@ -365,6 +400,10 @@ __global__ __launch_bounds__(kWG) void k_gemv_s(P p) {
           }
         }
       }
+      // the next group's weights (this block's next, or the next block's first) in flight
+      // while this group is reduced and stored
+      const int gn = g + (int)gridDim.x < ngroups ? g + (int)gridDim.x : (a0 + RB < p.nact ? (int)blockIdx.x : -1);
+      if (gn >= 0) load_group(gn);
 #pragma unroll
       for (int q = 0; q < ROWS; ++q)
 #pragma unroll
