@@ -58,7 +58,11 @@ GemvPlan plan_gemv(int nact, int K, int VE, int N) {
   const int nj = (Kc + 63) / 64;
   GemvPlan pl;
   pl.rw = 0;
-  if (nj <= 8) {  // whole rows per wave: RW = 16 / NJ rows per pass keep 16 loads in flight
+  // Whole rows per wave while a row is at most 4 loads per lane (K <= 2048 bf16): RW = 16 / NJ
+  // rows per pass keep 16 loads in flight.  Wider rows are split over the workgroup: with whole
+  // rows, every wave would hold (and normalise) the full activation slice -- 8 loads per lane
+  // and row put the wave at one per SIMD, with nothing to overlap its prologue.
+  if (nj <= 4) {
     pl.kind = 0;
     pl.nj = pow2_at_least(nj);
     const int rbmax = pl.nj <= 2 ? 4 : 2;
@@ -74,7 +78,7 @@ GemvPlan plan_gemv(int nact, int K, int VE, int N) {
   } else {  // rows split over the workgroup
     pl.kind = 1;
     pl.nj = pow2_at_least((Kc + kWG - 1) / kWG);
-    const int rbmax = 16 / pl.nj;
+    const int rbmax = pl.nj <= 4 ? 4 : 16 / pl.nj;
     pl.rb = pow2_at_most(nact < rbmax ? (nact < 1 ? 1 : nact) : rbmax);
     // four rows per workgroup when eight would leave fewer than 512 workgroups
     pl.rw = (N + 7) / 8 < 512 ? 4 : 8;

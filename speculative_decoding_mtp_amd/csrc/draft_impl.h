@@ -538,7 +538,7 @@ hipError_t launch_gemv(P& p, hipStream_t st, int* grid_used = nullptr, const Mfm
     return hipGetLastError();                                                                \
   }
     MTP_W(1, 1, 16) MTP_W(1, 2, 16) MTP_W(1, 4, 16) MTP_W(2, 1, 8) MTP_W(2, 2, 8) MTP_W(2, 4, 8)
-    MTP_W(4, 1, 4) MTP_W(4, 2, 4) MTP_W(8, 1, 2) MTP_W(8, 2, 2)
+    MTP_W(4, 1, 4) MTP_W(4, 2, 4)
     MTP_W(4, 1, 2) MTP_W(4, 2, 2)  // short matrices: more waves across the compute units
 #undef MTP_W
   } else {
@@ -550,6 +550,7 @@ hipError_t launch_gemv(P& p, hipStream_t st, int* grid_used = nullptr, const Mfm
     hipLaunchKernelGGL((k_gemv_s<W, RB_, NX_, RW_, P>), dim3(grid), dim3(kWG), 0, st, p);    \
     return hipGetLastError();                                                                \
   }
+    MTP_S(2, 1, 8) MTP_S(2, 2, 8) MTP_S(2, 4, 8) MTP_S(2, 1, 4) MTP_S(2, 2, 4) MTP_S(2, 4, 4)
     MTP_S(4, 1, 8) MTP_S(4, 2, 8) MTP_S(4, 4, 8) MTP_S(8, 1, 8) MTP_S(8, 2, 8) MTP_S(16, 1, 8)
     MTP_S(4, 1, 4) MTP_S(4, 2, 4) MTP_S(4, 4, 4) MTP_S(8, 1, 4) MTP_S(8, 2, 4) MTP_S(16, 1, 4)
 #undef MTP_S
