@@ -519,6 +519,18 @@ hipError_t launch_gemv(P& p, hipStream_t st, int* grid_used = nullptr, const Mfm
   if constexpr (std::is_same<W, BF16>::value) {
     if (use_mfma<W>(p, mb)) {
       hipLaunchKernelGGL((k_prep<W, P>), dim3(p.nact), dim3(kWG), 0, st, p, *mb);
+      if constexpr (!P::kArgmax) {
+        // hundreds of rows (a prefill): 128 x 128 output tiles, when there are enough of them
+        // (by the activation count, an upper bound of the valid rows) to fill the GPU
+        static int cap = 0;
+        const long items = (long)((p.nact + kTileM - 1) / kTileM) * ((p.N + kTileN - 1) / kTileN);
+        if (p.nact >= kTileRows && items >= resident_cap(k_gemm_tile<P>, &cap)) {
+          const int grid = resident_cap(k_gemm_tile<P>, &cap);
+          if (grid_used) *grid_used = grid;
+          hipLaunchKernelGGL((k_gemm_tile<P>), dim3(grid), dim3(kWG), 0, st, p, *mb);
+          return hipGetLastError();
+        }
+      }
       // activation tiles per pass from the activation count (an upper bound of the valid rows):
       // 32-row passes for a batch of serial steps, 64-row passes above (long calls too: at two
       // waves per SIMD they beat 128-row passes at one, despite streaming the weights twice as

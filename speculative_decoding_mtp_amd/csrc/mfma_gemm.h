@@ -23,6 +23,8 @@
 // D[4 (l / 16) + r][l % 16].
 #pragma once
 
+#include <type_traits>
+
 #include "gemv.h"
 
 namespace mtp {
@@ -382,6 +384,150 @@ __global__ __launch_bounds__(kWG, MG <= 4 ? 2 : 1) void k_gemm_mfma(P p, MfmaBuf
       }
       __syncthreads();
     }
+  }
+  p.finish(s_n);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Large tiles for calls with hundreds of activation rows (a prefill).  The skinny kernel above
+// streams the whole weight matrix once per 64-row pass; here each workgroup owns a 128
+// (compact activation rows) x 128 (weight rows) output tile and walks K in 32-column chunks
+// with both operands staged in LDS (double-buffered, one barrier per chunk, two chunks in
+// flight from memory), so the weights of
+// a column group are read once per 128 rows and every staged element feeds four MFMA tiles.
+// The four waves split the tile 2 x 2 (64 x 64 each: 4 x 4 MFMA tiles, hi and lo activation
+// products into the same accumulators).  Global loads are row-contiguous (four threads x 16 B
+// = one row's 64-byte chunk slice), issued two chunks ahead of the one multiplied, every
+// one unconditional: rows past the count or the matrix re-read the last valid row, and their
+// outputs are never stored.  LDS rows are padded to 40 bf16 (20 dwords): the sixteen rows a
+// quarter-wave reads for one operand fall on distinct banks.  K must be a multiple of 64.
+constexpr int kTileM = 128, kTileN = 128, kTileK = 32, kTileLd = kTileK + 8;
+constexpr int kTileRows = 256;  // activation rows from which the large tiles are used
+
+template <class P>
+__global__ __launch_bounds__(kWG, 2) void k_gemm_tile(P p, MfmaBufs mb) {
+  __shared__ __align__(16) uint16_t sA[2][2][kTileM * kTileLd];  // [buffer][hi/lo][row][k]
+  __shared__ __align__(16) uint16_t sB[2][kTileN * kTileLd];     // [buffer][weight row][k]
+  __shared__ int s_n[kMaxBatch];
+  __shared__ int s_len[kMaxBatch];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int jl = lane & 15, hq = lane >> 4;
+  const int wm = wid & 1, wn = wid >> 1;  // this wave's 64 x 64 quarter of the tile
+  p.setup(s_n, s_len);
+  const int count = *mb.count;
+  __syncthreads();
+  const int nrt = (count + kTileM - 1) / kTileM;
+  const int nct = (p.N + kTileN - 1) / kTileN;
+  const int nk = p.K / kTileK;
+  // staging map: thread t moves 16 bytes of row (t / 4) + 64 h at column 8 (t % 4) of a chunk
+  const int lr = tid >> 2, lc = 8 * (tid & 3);
+  for (int it = blockIdx.x; it < nrt * nct; it += gridDim.x) {
+    const int i = it % nrt, j = it / nrt;  // consecutive items share the weight column group
+    const uint16_t* arow_hi[2];
+    const uint16_t* arow_lo[2];
+    const uint16_t* brow[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int cr = min(i * kTileM + lr + 64 * h, count - 1);
+      arow_hi[h] = mb.xhi + (long)cr * p.K + lc;
+      arow_lo[h] = mb.xlo + (long)cr * p.K + lc;
+      brow[h] = reinterpret_cast<const uint16_t*>(p.wrow(min(j * kTileN + lr + 64 * h, p.N - 1))) + lc;
+    }
+    // two chunks in flight: register slot S holds chunk kc while kc is staged, then receives
+    // kc + 2 (the K loop is unrolled by two so that slots are compile-time; K / 32 is even)
+    uint4 ga[2][2][2], gb[2][2];  // [slot][hi/lo][half], [slot][half]
+    auto gload = [&](int kc, uint4 (&a)[2][2], uint4 (&b)[2]) {
+      const int k0 = kc * kTileK;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        b[h] = ld_stream(brow[h] + k0);
+        a[0][h] = ld16(arow_hi[h] + k0);
+        a[1][h] = ld16(arow_lo[h] + k0);
+      }
+    };
+    auto sstore = [&](int buf, const uint4 (&a)[2][2], const uint4 (&b)[2]) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = lr + 64 * h;
+        *reinterpret_cast<uint4*>(&sB[buf][r * kTileLd + lc]) = b[h];
+        *reinterpret_cast<uint4*>(&sA[buf][0][r * kTileLd + lc]) = a[0][h];
+        *reinterpret_cast<uint4*>(&sA[buf][1][r * kTileLd + lc]) = a[1][h];
+      }
+    };
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int n = 0; n < 4; ++n) acc[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // the padded row and activation index of this lane's 16 output rows, fetched up front (the
+    // epilogue would otherwise wait for each pair of loads in turn)
+    int orow[4][4], oact[4][4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int cr = min(i * kTileM + wm * 64 + m * 16 + 4 * hq + r, count - 1);
+        orow[m][r] = mb.rowmap[cr];
+        oact[m][r] = mb.amap[cr];
+      }
+    __syncthreads();  // the previous item's readers are done with both buffers
+    gload(0, ga[0], gb[0]);
+    gload(1, ga[1], gb[1]);
+    sstore(0, ga[0], gb[0]);
+    __syncthreads();
+    auto chunk = [&](auto slot, int kc) {
+      constexpr int S = decltype(slot)::value;  // == kc & 1, also the LDS buffer of chunk kc
+      // chunk kc + 2 into the slot chunk kc came in (the last chunk again near the end: every
+      // load unconditional, so the compiler waits for one chunk's loads, not all)
+      gload(min(kc + 2, nk - 1), ga[S], gb[S]);
+#pragma unroll
+      for (int s = 0; s < kTileK / 32; ++s) {
+        const int kk = 32 * s + 8 * hq;
+        bf16x8_t bw[4];
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+          bw[n] = *reinterpret_cast<const bf16x8_t*>(&sB[S][(wn * 64 + n * 16 + jl) * kTileLd + kk]);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int ra = (wm * 64 + m * 16 + jl) * kTileLd + kk;
+          const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(&sA[S][0][ra]);
+          const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(&sA[S][1][ra]);
+#pragma unroll
+          for (int n = 0; n < 4; ++n) {
+            acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bw[n], acc[m][n], 0, 0, 0);
+            acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bw[n], acc[m][n], 0, 0, 0);
+          }
+        }
+      }
+      // chunk kc + 1 (requested an iteration ago) into the other buffer, last read before the
+      // previous barrier
+      if (kc + 1 < nk) sstore(S ^ 1, ga[S ^ 1], gb[S ^ 1]);
+      __syncthreads();
+    };
+    for (int kc = 0; kc < nk; kc += 2) {
+      chunk(std::integral_constant<int, 0>{}, kc);
+      chunk(std::integral_constant<int, 1>{}, kc + 1);
+    }
+    // epilogue: lane holds compact rows 4 hq + r of each 16-row tile, column jl of each weight tile
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const int col = j * kTileN + wn * 64 + n * 16 + jl;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int cr = i * kTileM + wm * 64 + m * 16 + 4 * hq + r;
+          const float v = acc[m][n][r];
+          const float partner = __shfl_xor(v, 1, kWave);
+          if (cr < count && col < p.N) {
+            if constexpr (P::kPair) {
+              if ((jl & 1) == 0) p.store_pair(col, oact[m][r], orow[m][r], v, partner);
+            } else {
+              p.store(col, oact[m][r], orow[m][r], v);
+            }
+          }
+        }
+      }
   }
   p.finish(s_n);
 }
