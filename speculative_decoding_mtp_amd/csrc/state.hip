@@ -18,8 +18,10 @@ __global__ void k_kv_crop(int32_t* len, const int32_t* new_len, int B) {
   }
 }
 
-// dst[b] = src[b] for the sequences selected by mask (all when n_accept is NULL), 16 bytes per
-// thread and iteration; grid.y = sequence.
+// dst[b] = src[b] for the sequences selected by mask (all when n_accept is NULL); grid.y =
+// sequence, grid.x sized so that four strides of the grid cover a sequence: each thread has its
+// four 16-byte loads in flight at once (unconditional, from clamped addresses), then stores the
+// ones inside the sequence.
 __global__ __launch_bounds__(kWG) void k_copy_states(uint4* __restrict__ dst, const uint4* __restrict__ src,
                                                      long vec_per_seq, const int32_t* n_accept, int D) {
   const int b = blockIdx.y;
@@ -27,17 +29,14 @@ __global__ __launch_bounds__(kWG) void k_copy_states(uint4* __restrict__ dst, co
   const uint4* s = src + (long)b * vec_per_seq;
   uint4* d = dst + (long)b * vec_per_seq;
   const long stride = (long)gridDim.x * kWG;
-  long i = (long)blockIdx.x * kWG + threadIdx.x;
-  // four independent 16-byte loads in flight per thread
-  for (; i + 3 * stride < vec_per_seq; i += 4 * stride) {
-    const uint4 a0 = ld_stream(s + i), a1 = ld_stream(s + i + stride);
-    const uint4 a2 = ld_stream(s + i + 2 * stride), a3 = ld_stream(s + i + 3 * stride);
-    __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(&a0), reinterpret_cast<u32x4*>(d + i));
-    __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(&a1), reinterpret_cast<u32x4*>(d + i + stride));
-    __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(&a2), reinterpret_cast<u32x4*>(d + i + 2 * stride));
-    __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(&a3), reinterpret_cast<u32x4*>(d + i + 3 * stride));
-  }
-  for (; i < vec_per_seq; i += stride) d[i] = ld_stream(s + i);
+  const long i = (long)blockIdx.x * kWG + threadIdx.x;
+  uint4 a[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) a[k] = ld_stream(s + min(i + k * stride, vec_per_seq - 1));
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (i + k * stride < vec_per_seq)
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(&a[k]), reinterpret_cast<u32x4*>(d + i + k * stride));
 }
 
 hipError_t run_kv_crop(int32_t* len, const int32_t* new_len, int B, hipStream_t st) {
@@ -48,11 +47,9 @@ hipError_t run_kv_crop(int32_t* len, const int32_t* new_len, int B, hipStream_t 
 hipError_t run_copy_states(void* dst, const void* src, size_t bytes_per_seq, int B, const int32_t* n_accept, int D,
                            hipStream_t st) {
   const long vec = (long)(bytes_per_seq / 16);
-  // about 2048 workgroups in total, at most one per 16 KB of a sequence
-  long per_seq = (2048 + B - 1) / B;
-  const long cap = (vec + 4 * kWG - 1) / (4 * kWG);
-  if (per_seq > cap) per_seq = cap;
-  if (per_seq < 1) per_seq = 1;
+  // 16 KB of a sequence per workgroup (four 16-byte vectors per thread)
+  const long per_seq = (vec + 4 * kWG - 1) / (4 * kWG);
+  if (per_seq > 0x7fffffffL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_copy_states, dim3((unsigned)per_seq, B), dim3(kWG), 0, st, reinterpret_cast<uint4*>(dst),
                      reinterpret_cast<const uint4*>(src), vec, n_accept, D);
   return hipGetLastError();
