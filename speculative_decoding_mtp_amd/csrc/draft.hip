@@ -58,8 +58,8 @@ GemvPlan plan_gemv(int nact, int K, int VE, int N) {
   const int nj = (Kc + 63) / 64;
   GemvPlan pl;
   pl.rw = 0;
-  // Whole rows per wave while a row is at most 4 loads per lane (K <= 2048 bf16): RW = 16 / NJ
-  // rows per pass keep 16 loads in flight.  Wider rows are split over the workgroup: with whole
+  // Whole rows per wave while a row is at most 4 loads per lane (K <= 2048 bf16), RW rows per
+  // wave and pass with about 8-16 loads in flight.  Wider rows are split over the workgroup: with whole
   // rows, every wave would hold (and normalise) the full activation slice -- 8 loads per lane
   // and row put the wave at one per SIMD, with nothing to overlap its prologue.
   if (nj <= 4) {
@@ -67,11 +67,10 @@ GemvPlan plan_gemv(int nact, int K, int VE, int N) {
     pl.nj = pow2_at_least(nj);
     const int rbmax = pl.nj <= 2 ? 4 : 2;
     pl.rb = pow2_at_most(nact < rbmax ? (nact < 1 ? 1 : nact) : rbmax);
-    int rw = 16 / pl.nj;
-    // a short matrix with 4 loads per row (fewer than 512 four-wave row groups) takes two rows
-    // per wave instead of four
-    if (pl.nj == 4 && (N + 4 * rw - 1) / (4 * rw) < 512) rw /= 2;
-    pl.rw = rw;
+    // rows of 4 loads per lane take two rows per wave (8 loads in flight, twice the waves): as
+    // fast for the vocabulary-sized lm_head as four, faster for the 2048-column layer matrices
+    pl.rw = pl.nj == 4 ? 2 : 16 / pl.nj;
+    const int rw = pl.rw;
     const int groups = (N + rw - 1) / rw;
     const int wgs = (groups + 3) / 4;
     pl.grid = wgs < kMaxGemvGrid ? wgs : kMaxGemvGrid;

@@ -5,14 +5,15 @@
 //
 // Two layouts of the same computation:
 //
-// * k_gemv_w ("wave rows", rows of up to 64*8 16-byte chunks): every wave owns whole weight
+// * k_gemv_w ("wave rows", rows of up to 64*4 16-byte chunks): every wave owns whole weight
 //   rows.  Lane l reads chunks c = l + 64 j of a row, so one load instruction covers 1 KB of a
 //   row and a wave keeps RW*NJ loads (about 16) in flight.  The lane's slice of RB activation
 //   rows stays in registers for the whole kernel.  Row sums are wave reductions through DPP
 //   moves and lane reads: no LDS traffic and no barrier in the streaming loop; the waves of a
 //   workgroup are independent.
 // * k_gemv_s ("split K", wider rows): the 256 threads of a workgroup share each row (chunk
-//   c = tid + 256 j); partial sums meet in LDS once per ROWS rows.
+//   c = tid + 256 j); partial sums meet in LDS once per ROWS rows, the next rows' weights in
+//   flight meanwhile.
 //
 // Activation rows beyond RB are handled in further passes over the weights.  A policy class
 // supplies the activation prologue (raw loads, RMSNorm), the logical-row -> weight-row map and
