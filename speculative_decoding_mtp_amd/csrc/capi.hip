@@ -218,7 +218,11 @@ StepArgs base_step(const mtp_config* cfg, const mtp_weights* w, const mtp_kv* kv
 
 namespace mtp {
 int attn_nsplit(int B, int nkv, int max_len, int qrows) {
-  int n = (512 + B * nkv - 1) / (B * nkv);  // about two resident workgroups per compute unit
+  // about one workgroup per compute unit: a single decode row per sequence then gets chunks of
+  // 128+ positions (every wave of a workgroup has a 32-position slice; two splits per unit left
+  // half the waves idle), and a batch of 32 sequences x 8 kv heads runs unsplit, with no
+  // combine launch
+  int n = (256 + B * nkv - 1) / (B * nkv);
   if (n > kMaxSplit) n = kMaxSplit;
   // many queries per kv head (a long prefill): bound the partials to 8192 query rows per head
   const int qcap = 8192 / (qrows < 1 ? 1 : qrows);
