@@ -1,0 +1,60 @@
+"""GPU parity of the large-tile MFMA GEMM (128 x 128 output tiles, both operands staged in LDS),
+which a head call takes for a matrix when it has 256+ activation rows and enough tiles to fill the
+GPU: here the gate/up projection of a head with a 4096-wide FFN (8192 interleaved output rows) over
+a 1152-row prefill (9 x 64 tiles) and over a ragged batch of two sequences (640 and 517 valid rows
+of 640: 1157 compact rows, the last tile partly empty, padding rows excluded from the compaction).
+
+Compared with the oracle's draft_step ([HB14] "14. MTP: speculative decoding with the built-in
+draft head", section "The draft head"): every valid row's post-norm hidden and appended K/V, the
+last row's logits and the draft (where the oracle's top-2 gap is at least 1e-4); cache lengths
+exact.  bf16 weights: max relative error 2e-2 per row; the bf16 K/V within one bf16 ulp."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from synth import CONFIGS, make_weights
+
+pytestmark = pytest.mark.gpu
+
+M = pytest.importorskip("speculative_decoding_mtp_amd")
+from tests.gpu_util import MARGIN, config, f32, i32, max_rel, upload_weights  # noqa: E402
+
+
+@pytest.mark.parametrize("B, rows, valid", [(1, 1152, [1152]), (2, 640, [640, 517])], ids=["1152rows", "ragged"])
+def test_large_tile_gemm_rows_match_oracle(B, rows, valid):
+    cfg = CONFIGS["tiny"].replace(index=91 + B, wdtype="bf16", n_layers=1, n_heads=4, n_kv_heads=2, head_dim=128,
+                                  hidden=256, ffn=4096, vocab=2000, embed_std=1.0, batch=B, D=1, ctx=0,
+                                  prefill_rows=0)
+    H, V = cfg.hidden, cfg.vocab
+    w = make_weights(cfg)
+    model = O.OracleModel(cfg, w)
+    c, gw = config(cfg), upload_weights(cfg, w)
+    rng = np.random.default_rng(cfg.index)
+    toks = rng.integers(0, V, size=(B, rows)).astype(np.int32)
+    for b, n in enumerate(valid):
+        toks[b, n:] = -1
+    hid = rng.standard_normal((B, rows, H)).astype(np.float32)
+    max_len = M.round_max_len(rows + 8)
+    kv = M.KVCache(c, B, max_len)
+    ws = M.new_workspace(M.mtp_draft_workspace_size(c, B, rows, 1, max_len))
+    hout = torch.zeros(B, rows, H, device="cuda")
+    draft = torch.zeros(B, dtype=torch.int32, device="cuda")
+    logits = torch.zeros(B, V, device="cuda")
+    M.mtp_draft_step(c, gw, kv, rows, i32(toks), f32(hid), hout, draft, logits, ws)
+    M.mtp_check(ws)
+    cache = O.KVCache(cfg, B, max_len)
+    h_o, d_o, l_o, m_o = O.draft_step(model, cache, toks, hid)
+    assert kv.len.cpu().tolist() == valid == cache.len.tolist()
+    hg, lg = hout.cpu().numpy(), logits.cpu().numpy()
+    kg = kv.k.float().cpu().numpy()
+    vg = kv.v.transpose(-1, -2).float().cpu().numpy()
+    ulp = 2.0 ** -7
+    for b, n in enumerate(valid):
+        for i in range(n):
+            assert max_rel(hg[b, i], h_o[b, i]) < 2e-2, (b, i)
+        assert max_rel(kg[:, b, :, :n], cache.K[:, b, :, :n]) < ulp, b
+        assert max_rel(vg[:, b, :, :n], cache.V[:, b, :, :n]) < ulp, b
+        assert max_rel(lg[b], l_o[b]) < 2e-2, b
+        if m_o[b] >= MARGIN:
+            assert int(draft[b]) == d_o[b], b
