@@ -1,8 +1,10 @@
-// Skinny GEMM on bf16 MFMA for draft steps with many activation rows (a batch of sequences).
+// GEMMs on bf16 MFMA for draft steps with many activation rows (a batch of sequences, a
+// prefill).
 //
 //   y[row][m] = sum_k W[m][k] * x[row][k],   W bf16 [N][K], x fp32 (after the policy's norm)
 //
-// Two kernels:
+// k_prep and the skinny k_gemm_mfma below (k_gemm_tile, further down, takes calls with hundreds
+// of rows):
 // * k_prep: one workgroup per activation row; the policy's prologue (raw loads, RMSNorm, gains)
 //   gives the fp32 row, which is written as two bf16 rows hi = bf16(x), lo = bf16(x - hi)
 //   (x = hi + lo to about 2^-17 relative), compacted over the valid rows.  rowmap / amap record
