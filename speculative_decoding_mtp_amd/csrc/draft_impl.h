@@ -518,7 +518,10 @@ template <class W, class P>
 hipError_t launch_gemv(P& p, hipStream_t st, int* grid_used = nullptr, const MfmaBufs* mb = nullptr) {
   if constexpr (std::is_same<W, BF16>::value) {
     if (use_mfma<W>(p, mb)) {
-      hipLaunchKernelGGL((k_prep<W, P>), dim3(p.nact), dim3(kWG), 0, st, p, *mb);
+      if (p.K > 4 * kWG * W::VE)  // rows wider than 8192: the whole row in registers
+        hipLaunchKernelGGL((k_prep<W, P, 12>), dim3(p.nact), dim3(kWG), 0, st, p, *mb);
+      else
+        hipLaunchKernelGGL((k_prep<W, P, 4>), dim3(p.nact), dim3(kWG), 0, st, p, *mb);
       if constexpr (!P::kArgmax) {
         // hundreds of rows (a prefill): 128 x 128 output tiles, when there are enough of them
         // (by the activation count, an upper bound of the valid rows) to fill the GPU

@@ -44,15 +44,34 @@ struct MfmaBufs {
   long part_cap;        // floats available at part
 };
 
-// One workgroup per activation index a (grid = nact).
-template <class W, class P>
+// One workgroup per activation index a (grid = nact).  The first KEEP chunks of each thread
+// stay in registers, with their gains, across the norm reduction (KEEP = 12 holds rows of up to
+// 24576 columns, chosen for rows wider than 8192; 4 otherwise); their loads are issued
+// unconditionally from clamped columns -- before the row counts are in LDS when the row is
+// known without them -- so the row arrives in one memory round trip.  The hi / lo rows are
+// written 16 bytes at a time.
+template <class W, class P, int KEEP>
 __global__ __launch_bounds__(kWG) void k_prep(P p, MfmaBufs mb) {
   constexpr int VE = W::VE;
+  static_assert(VE == 8, "bf16 weights");
   __shared__ int s_n[kMaxBatch];
   __shared__ int s_len[kMaxBatch];
   __shared__ float red[8];
   const int a = blockIdx.x, tid = threadIdx.x;
-  p.setup(s_n, s_len);
+  const int Kc = p.K / VE;
+  float keep[KEEP][VE];
+  uint4 gk[KEEP];
+  auto issue = [&](int row) {
+#pragma unroll
+    for (int i = 0; i < KEEP; ++i) {
+      const int ch = min(tid + i * kWG, Kc - 1);
+      p.load_x(row, ch * VE, keep[i]);
+      if constexpr (P::kNorm > 0) gk[i] = p.gain_raw(ch * VE);
+    }
+  };
+  const auto pre = p.setup_load();
+  if constexpr (P::kEarlyRows) issue(p.row_of(a));
+  p.setup_store(pre, s_n, s_len);
   __syncthreads();
   int row;
   bool valid;
@@ -75,12 +94,7 @@ __global__ __launch_bounds__(kWG) void k_prep(P p, MfmaBufs mb) {
   }
   if (a == 0 && tid == 0) *mb.count = total;
   if (!valid) return;
-  const int Kc = p.K / VE;
-  // The first KEEP chunks of each thread (K <= KEEP * kWG * VE: every width here but the widest
-  // FFN) stay in registers, with their gains, across the norm reduction: one memory round trip.
-  constexpr int KEEP = 4;
-  float keep[KEEP][VE];
-  uint4 gk[KEEP];
+  if constexpr (!P::kEarlyRows) issue(row);
   float ss[2] = {0.f, 0.f};
   auto sumsq = [&](const float (&f)[VE], int ch) {
     float s = 0.f;
@@ -91,14 +105,6 @@ __global__ __launch_bounds__(kWG) void k_prep(P p, MfmaBufs mb) {
     else
       ss[0] += s;
   };
-#pragma unroll
-  for (int i = 0; i < KEEP; ++i) {
-    const int ch = tid + i * kWG;
-    if (ch < Kc) {
-      p.load_x(row, ch * VE, keep[i]);
-      if constexpr (P::kNorm > 0) gk[i] = p.gain_raw(ch * VE);
-    }
-  }
   if constexpr (P::kNorm > 0) {
 #pragma unroll
     for (int i = 0; i < KEEP; ++i)
@@ -128,18 +134,18 @@ __global__ __launch_bounds__(kWG) void k_prep(P p, MfmaBufs mb) {
       for (int e = 0; e < VE; ++e) g[e] = 1.f;
     }
     const float sc = (P::kNorm == 2 && ch * VE >= p.split) ? sc1 : sc0;
-    uint16_t h16[VE], l16[VE];
+    uint32_t h2[VE / 2], l2[VE / 2];
 #pragma unroll
-    for (int e = 0; e < VE; ++e) {
-      const float x = P::kNorm > 0 ? f[e] * sc * g[e] : f[e];
-      h16[e] = bf16_rne(x);
-      l16[e] = bf16_rne(x - __uint_as_float(uint32_t(h16[e]) << 16));
+    for (int e = 0; e < VE; e += 2) {
+      const float x0 = P::kNorm > 0 ? f[e] * sc * g[e] : f[e];
+      const float x1 = P::kNorm > 0 ? f[e + 1] * sc * g[e + 1] : f[e + 1];
+      const uint32_t a0 = bf16_rne(x0), a1 = bf16_rne(x1);
+      const uint32_t b0 = bf16_rne(x0 - __uint_as_float(a0 << 16)), b1 = bf16_rne(x1 - __uint_as_float(a1 << 16));
+      h2[e / 2] = a0 | (a1 << 16);
+      l2[e / 2] = b0 | (b1 << 16);
     }
-#pragma unroll
-    for (int e = 0; e < VE; ++e) {
-      hi[ch * VE + e] = h16[e];
-      lo[ch * VE + e] = l16[e];
-    }
+    *reinterpret_cast<uint4*>(hi + ch * VE) = make_uint4(h2[0], h2[1], h2[2], h2[3]);
+    *reinterpret_cast<uint4*>(lo + ch * VE) = make_uint4(l2[0], l2[1], l2[2], l2[3]);
   };
 #pragma unroll
   for (int i = 0; i < KEEP; ++i)
