@@ -79,8 +79,9 @@ GemvPlan plan_gemv(int nact, int K, int VE, int N) {
     pl.nj = pow2_at_least((Kc + kWG - 1) / kWG);
     const int rbmax = pl.nj <= 4 ? 4 : 16 / pl.nj;
     pl.rb = pow2_at_most(nact < rbmax ? (nact < 1 ? 1 : nact) : rbmax);
-    // four rows per workgroup when eight would leave fewer than 512 workgroups
-    pl.rw = (N + 7) / 8 < 512 ? 4 : 8;
+    // rows per workgroup: two for matrices under 4096 rows (1024+ workgroups), else four when
+    // eight would leave fewer than 512 workgroups
+    pl.rw = (N + 3) / 4 < 1024 ? 2 : ((N + 7) / 8 < 512 ? 4 : 8);
     const int groups = (N + pl.rw - 1) / pl.rw;
     pl.grid = groups < kMaxGemvGrid ? groups : kMaxGemvGrid;
   }

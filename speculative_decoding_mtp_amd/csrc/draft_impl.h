@@ -565,6 +565,8 @@ hipError_t launch_gemv(P& p, hipStream_t st, int* grid_used = nullptr, const Mfm
     return hipGetLastError();                                                                \
   }
     MTP_S(2, 1, 8) MTP_S(2, 2, 8) MTP_S(2, 4, 8) MTP_S(2, 1, 4) MTP_S(2, 2, 4) MTP_S(2, 4, 4)
+    MTP_S(2, 1, 2) MTP_S(2, 2, 2) MTP_S(2, 4, 2) MTP_S(4, 1, 2) MTP_S(4, 2, 2) MTP_S(4, 4, 2)
+    MTP_S(8, 1, 2) MTP_S(8, 2, 2) MTP_S(16, 1, 2)
     MTP_S(4, 1, 8) MTP_S(4, 2, 8) MTP_S(4, 4, 8) MTP_S(8, 1, 8) MTP_S(8, 2, 8) MTP_S(16, 1, 8)
     MTP_S(4, 1, 4) MTP_S(4, 2, 4) MTP_S(4, 4, 4) MTP_S(8, 1, 4) MTP_S(8, 2, 4) MTP_S(16, 1, 4)
 #undef MTP_S
