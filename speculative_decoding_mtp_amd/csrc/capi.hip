@@ -477,6 +477,9 @@ int spec_verify_workspace_size(int32_t B, int32_t D, int32_t V, const mtp_sampli
     const int K = sp->top_k;
     if (K < 1 || K > kMaxTopK) return fail(MTP_ERR_ARG, "top_k must be in [1, %d]", kMaxTopK);
     t += 2 * up256(rows * K * 4) + up256(rows * 4);
+    int nch = 1, chunk = V;
+    topk_split((int)rows, V, &nch, &chunk);
+    if (nch > 1) t += 2 * up256(rows * nch * K * 4);  // per-chunk candidates
   }
   *bytes = t;
   return MTP_OK;
@@ -536,6 +539,15 @@ int spec_verify(int32_t B, int32_t D, int32_t V, const float* target_logits, con
     o += up256((size_t)rows * K * 4);
     a.top_n = reinterpret_cast<int*>(base + o);
     o += up256((size_t)rows * 4);
+    topk_split(rows, V, &a.tk_nchunk, &a.tk_chunk);
+    a.cand_v = nullptr;
+    a.cand_i = nullptr;
+    if (a.tk_nchunk > 1) {
+      a.cand_v = reinterpret_cast<float*>(base + o);
+      o += up256((size_t)rows * a.tk_nchunk * K * 4);
+      a.cand_i = reinterpret_cast<int*>(base + o);
+      o += up256((size_t)rows * a.tk_nchunk * K * 4);
+    }
   }
   hipEvent_t eb, ee;
   timer_events(MTP_KERNEL_VERIFY, &eb, &ee);

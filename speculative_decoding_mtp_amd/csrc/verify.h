@@ -29,7 +29,25 @@ struct VerifyArgs {
   float* top_v;  // [rows][top_k]
   int* top_i;
   int* top_n;  // [rows]
+  // few rows: each row in tk_nchunk chunks of tk_chunk items, every chunk's own top-k first
+  int tk_nchunk, tk_chunk;
+  float* cand_v;  // [rows][tk_nchunk][top_k]
+  int* cand_i;
 };
+
+// Chunks of the sampling top-k pass: calls with fewer than 128 rows split each row into chunks
+// of at least 4096 items (16-byte aligned starts) so that about 512 workgroups stream the logits.
+inline void topk_split(int rows, int V, int* nchunk, int* chunk) {
+  int n = 1;
+  if (rows < 128 && V >= 2 * 4096) {
+    n = (512 + rows - 1) / rows;
+    if (n > V / 4096) n = V / 4096;
+  }
+  int c = (V + n - 1) / n;
+  c = (c + 3) & ~3;
+  *chunk = c;
+  *nchunk = (V + c - 1) / c;
+}
 
 hipError_t run_verify(const VerifyArgs& a, hipStream_t st);
 

@@ -314,9 +314,13 @@ __device__ int sort_candidates(TopkSmem& sm, int S, int keep) {
   return min(keep, S);
 }
 
+// The top K of the V items at x (value desc, position asc) into ov / oi, the count into *on (when
+// not NULL).  An output id is the item's position plus id_base, or id_map[position].
 template <bool VEC>
-__device__ __forceinline__ void topk_row(const VerifyArgs& a, TopkSmem& sm, int row, const float* x) {
-  const int K = a.top_k, V = a.V;
+__device__ __forceinline__ void topk_row(const VerifyArgs& a, TopkSmem& sm, const float* x, int V, float* ov,
+                                         int* oi, int* on, int id_base, const int* id_map) {
+  const int K = a.top_k;
+  auto out_id = [&](int pos) { return id_map ? id_map[pos] : pos + id_base; };
   float cur[16], nxt[16];
   load_tile<VEC>(x, V, 0, cur);
   float rmax = -INFINITY;  // this thread's running maximum
@@ -399,8 +403,6 @@ __device__ __forceinline__ void topk_row(const VerifyArgs& a, TopkSmem& sm, int 
   // (rank = candidates ranked before it, value desc, id asc) straight into their output slots.
   // If too many remain (ties), the whole buffer is sorted instead.
   const int S = sm.cnt;
-  float* ov = a.top_v + (long)row * K;
-  int* oi = a.top_i + (long)row * K;
   float tmax = -INFINITY;
   for (int c = threadIdx.x; c < S; c += kWG) tmax = fmaxf(tmax, sm.v[c]);
   sm.tm[threadIdx.x] = tmax;
@@ -428,31 +430,73 @@ __device__ __forceinline__ void topk_row(const VerifyArgs& a, TopkSmem& sm, int 
       for (int d = 0; d < S2; ++d) r += better(sm.v2[d], sm.i2[d], cv, ci) ? 1 : 0;
       if (r < K) {
         ov[r] = cv;
-        oi[r] = ci;
+        oi[r] = out_id(ci);
       }
     }
   } else {
     n = sort_candidates(sm, S, K);
     for (int t = threadIdx.x; t < n; t += kWG) {
       ov[t] = sm.v[t];
-      oi[t] = sm.i[t];
+      oi[t] = out_id(sm.i[t]);
     }
   }
   for (int t = n + threadIdx.x; t < K; t += kWG) {
     ov[t] = -INFINITY;
     oi[t] = -1;
   }
-  if (threadIdx.x == 0) a.top_n[row] = n;
+  if (on && threadIdx.x == 0) *on = n;
 }
 
+__device__ __forceinline__ const float* topk_src(const VerifyArgs& a, int row) {
+  const int tgt_rows = a.B * (a.D + 1);
+  return row < tgt_rows ? a.tl + (long)row * a.V : a.dl + (long)(row - tgt_rows) * a.V;
+}
+
+__device__ __forceinline__ bool vec_ok(const float* x, int n) {
+  return (reinterpret_cast<uintptr_t>(x) & 15) == 0 && (n & 3) == 0;
+}
+
+// One workgroup per row.
 __global__ __launch_bounds__(kWG) void k_topk_stream(VerifyArgs a) {
   __shared__ TopkSmem sm;
-  const int row = blockIdx.x, tgt_rows = a.B * (a.D + 1);
-  const float* x = row < tgt_rows ? a.tl + (long)row * a.V : a.dl + (long)(row - tgt_rows) * a.V;
-  if ((reinterpret_cast<uintptr_t>(x) & 15) == 0 && (a.V & 3) == 0)
-    topk_row<true>(a, sm, row, x);
+  const int row = blockIdx.x, K = a.top_k;
+  const float* x = topk_src(a, row);
+  float* ov = a.top_v + (long)row * K;
+  int* oi = a.top_i + (long)row * K;
+  if (vec_ok(x, a.V))
+    topk_row<true>(a, sm, x, a.V, ov, oi, a.top_n + row, 0, nullptr);
   else
-    topk_row<false>(a, sm, row, x);
+    topk_row<false>(a, sm, x, a.V, ov, oi, a.top_n + row, 0, nullptr);
+}
+
+// Few rows: workgroup (c, row) takes the top K of items [c chunk, (c + 1) chunk) of the row ...
+__global__ __launch_bounds__(kWG) void k_topk_chunks(VerifyArgs a) {
+  __shared__ TopkSmem sm;
+  const int c = blockIdx.x, row = blockIdx.y, K = a.top_k;
+  const int c0 = c * a.tk_chunk, n = min(a.tk_chunk, a.V - c0);
+  const float* x = topk_src(a, row) + c0;
+  const long slot = ((long)row * a.tk_nchunk + c) * K;
+  if (vec_ok(x, n))
+    topk_row<true>(a, sm, x, n, a.cand_v + slot, a.cand_i + slot, nullptr, c0, nullptr);
+  else
+    topk_row<false>(a, sm, x, n, a.cand_v + slot, a.cand_i + slot, nullptr, c0, nullptr);
+}
+
+// ... and one workgroup per row then takes the top K of the row's chunk candidates.  Candidates
+// sit in chunk order (ascending ids) and, inside a chunk, best first with ascending ids among
+// equal values, so ordering them by (value desc, position asc) is ordering them by (value desc,
+// id asc): the result equals the one-pass selection over the whole row.
+__global__ __launch_bounds__(kWG) void k_topk_merge(VerifyArgs a) {
+  __shared__ TopkSmem sm;
+  const int row = blockIdx.x, K = a.top_k, n = a.tk_nchunk * K;
+  const float* x = a.cand_v + (long)row * n;
+  const int* ids = a.cand_i + (long)row * n;
+  float* ov = a.top_v + (long)row * K;
+  int* oi = a.top_i + (long)row * K;
+  if (vec_ok(x, n))
+    topk_row<true>(a, sm, x, n, ov, oi, a.top_n + row, 0, ids);
+  else
+    topk_row<false>(a, sm, x, n, ov, oi, a.top_n + row, 0, ids);
 }
 
 // One wave per sequence: accept / reject / draw ([DLM "MTP speculative decoding"] item 3, [YL 三
@@ -541,7 +585,12 @@ hipError_t run_verify(const VerifyArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(k_verify_greedy_final, dim3(a.B), dim3(kWG), 0, st, a);
   } else {
     const int rows = a.B * (a.D + 1) + (a.q_mode == 1 ? a.B * a.D : 0);
-    hipLaunchKernelGGL(k_topk_stream, dim3(rows), dim3(kWG), 0, st, a);
+    if (a.tk_nchunk > 1) {
+      hipLaunchKernelGGL(k_topk_chunks, dim3(a.tk_nchunk, rows), dim3(kWG), 0, st, a);
+      hipLaunchKernelGGL(k_topk_merge, dim3(rows), dim3(kWG), 0, st, a);
+    } else {
+      hipLaunchKernelGGL(k_topk_stream, dim3(rows), dim3(kWG), 0, st, a);
+    }
     hipLaunchKernelGGL(k_sample_decide, dim3(a.B), dim3(64), 0, st, a);
   }
   return hipGetLastError();
