@@ -69,8 +69,10 @@ GemvPlan plan_gemv(int nact, int K, int VE, int N) {
     pl.rb = pow2_at_most(nact < rbmax ? (nact < 1 ? 1 : nact) : rbmax);
     // rows of 4 loads per lane take two rows per wave (8 loads in flight, twice the waves): as
     // fast for the vocabulary-sized lm_head as four, faster for the 2048-column layer matrices
-    pl.rw = pl.nj == 4 ? 2 : 16 / pl.nj;
-    const int rw = pl.rw;
+    int rw = pl.nj == 4 ? 2 : 16 / pl.nj;
+    // short matrices: fewer rows per wave (down to two) until there are 256+ workgroups
+    while (rw > 2 && ((N + rw - 1) / rw + 3) / 4 < 256) rw /= 2;
+    pl.rw = rw;
     const int groups = (N + rw - 1) / rw;
     const int wgs = (groups + 3) / 4;
     pl.grid = wgs < kMaxGemvGrid ? wgs : kMaxGemvGrid;

@@ -553,6 +553,9 @@ hipError_t launch_gemv(P& p, hipStream_t st, int* grid_used = nullptr, const Mfm
     return hipGetLastError();                                                                \
   }
     MTP_W(1, 1, 16) MTP_W(1, 2, 16) MTP_W(1, 4, 16) MTP_W(2, 1, 8) MTP_W(2, 2, 8) MTP_W(2, 4, 8)
+    MTP_W(1, 1, 8) MTP_W(1, 2, 8) MTP_W(1, 4, 8) MTP_W(1, 1, 4) MTP_W(1, 2, 4) MTP_W(1, 4, 4)
+    MTP_W(1, 1, 2) MTP_W(1, 2, 2) MTP_W(1, 4, 2) MTP_W(2, 1, 4) MTP_W(2, 2, 4) MTP_W(2, 4, 4)
+    MTP_W(2, 1, 2) MTP_W(2, 2, 2) MTP_W(2, 4, 2)
     MTP_W(4, 1, 2) MTP_W(4, 2, 2)
 #undef MTP_W
   } else {
