@@ -4,17 +4,19 @@ A step is one round of the whole path on synthetic inputs resident in HBM:
   mtp_draft_loop (catch-up rows + D-1 serial draft steps: dual RMSNorm + eh_proj, decoder
   block with RoPE over the head's KV cache, final norm, lm_head + argmax)
   -> synthetic target logits (draft logits + seeded noise, standing in for the main model)
-  -> mtp_state_snapshot (the main model's recurrent state, [HB14]'s 19 MB per sequence)
-  -> spec_verify -> mtp_state_restore (where a draft was rejected) -> kv_crop.
-The workload is the single-layer bf16 head with H=2048, 16/4 heads of 128, FFN 6144, vocab
-151936, a 4096-position KV context, B=1, D=1, greedy verification over 2 positions with target
-logits = draft logits + N(0, 0.5).
+  -> [mtp_state_snapshot of a recurrent state, for workloads that carry one]
+  -> spec_verify -> [mtp_state_restore where a draft was rejected] -> kv_crop.
+The default workload is the largest single-GPU one: the DeepSeek-V3-scale single-module head
+(H 7168, eh_proj 14336 -> 7168, 56/8 heads of 128, FFN 18432, vocab 129280, bf16), the same
+layer reused for D = 3 serial drafts, B = 32 sequences at an 8192-position KV context, greedy
+verification over 4 positions with target logits = draft logits + N(0, 0.7).
 
 Prints one JSON line: accepted tokens/s (sum over rounds and sequences of accepted drafts + 1,
 divided by the timed wall time), the lm_head kernel's HBM roofline and the CPU oracle timed on
-a bounded sample of the same workload.  --config names another head workload (drafter4: the
-4-layer 1024-hidden drafter with sampling verification; dsv3: the 7168-hidden head at batch 32)
-or, with --config stress, the verifier alone (B=256, D=4, vocab 151936, sampling).
+a bounded sample of the same workload.  --config names another head workload (qwen: the
+single-layer 2048-hidden head at B 1, D 1; drafter4: the 4-layer 1024-hidden drafter with
+sampling verification) or, with --config stress, the verifier alone (B=256, D=4, vocab 151936,
+sampling).
 --target-layers L times the target's verify pass instead: a dense stand-in with the head's
 dimensions and L blocks, scoring 1, 2 or 7 positions per call.  --prefill-rows N times one MTP
 prefill call over N prompt rows.  --shared-kv T runs the same rounds with a head that keeps no
@@ -41,7 +43,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="qwen")
+    ap.add_argument("--config", default="dsv3")
     ap.add_argument("--state-bytes", type=int, default=None, help="recurrent state bytes per sequence")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle baseline sample budget (0: skip)")
     ap.add_argument("--traffic", default=os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
@@ -249,7 +251,9 @@ def main():
     value = tokens_out / wall
     ms_per_step = wall * 1e3 / args.steps
 
-    lm_bytes = V * H * cfg.wbytes + B * H * 4 + B * V * 4      # weights + activations in + logits out
+    # the lm_head kernel's algorithmic bytes per launch: the weights once, each sequence's
+    # (normalised, fp32-equivalent) activation row in, its logits row out
+    lm_bytes = V * H * cfg.wbytes + B * H * 4 + B * V * 4
     lm_avg_s = lm_ms / 1e3 / max(lm_n, 1)
     achieved = lm_bytes / lm_avg_s / 1e9
     traffic = None
@@ -288,7 +292,8 @@ def main():
         "accepted_drafts_per_s": round(float(acc.sum()) * (args.steps / max(len(acc), 1)) / wall, 2),
         "acceptance": round(float(acc.mean()) / D, 4),
         "gpu_event_ms_per_step": round(gpu_ms / args.steps, 4),
-        "roofline": {"bound": "hbm", "kernel": "lm_head GEMV + argmax", "achieved": round(achieved, 1),
+        "roofline": {"bound": "hbm", "kernel": M.mtp_timer_kernel_name(M.MTP_KERNEL_LM_HEAD),
+                     "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "bytes_per_launch": lm_bytes,
                      "avg_launch_us": round(lm_avg_s * 1e6, 2), "launches": lm_n},
@@ -479,48 +484,85 @@ def bench_target(args, cfg, layers, row_counts=(1, 2, 7)):
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(cfg, w, K, Vv, budget_s):
-    """The float64 oracle on the same workload, rounds until the time budget is spent: two thirds
-    of the budget with NumPy's BLAS threads as configured (all host cores by default), one third
-    with a single thread (reported as single_thread_value)."""
-    import oracle as O
-    from synth import make_first_round, make_round_hiddens, make_round_noise, make_round_uniforms
+def host_cores():
+    """Host cores this process may run on, and the BLAS thread pool size NumPy uses."""
+    cores = len(os.sched_getaffinity(0))
     try:
-        from threadpoolctl import threadpool_info, threadpool_limits
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        threads, threadpool_limits = os.cpu_count(), None
-    model = O.OracleModel(cfg, w)
-    B, D = cfg.batch, cfg.D
+        blas = cores
+    return cores, blas
 
-    def run(budget):
-        cache = O.KVCache(cfg, B, cfg.ctx + 256)
-        cache.load_prefix(K, Vv, cfg.ctx)
-        toks, hid = make_first_round(cfg)
-        tokens_out = rounds = 0
-        t0 = time.perf_counter()
-        while rounds < 2 or time.perf_counter() - t0 < budget:
-            drafts, _, logits, _ = O.draft_loop(model, cache, toks, hid, D)
-            ctx = cache.len.copy() - (D - 1)
-            tl = np.concatenate([logits, logits[:, D - 1:D]], axis=1).astype(np.float32) + make_round_noise(cfg, rounds)
-            ua, us = make_round_uniforms(cfg.index, B, D, rounds)
-            res = O.spec_verify(tl, drafts, ctx, cfg.sampling, None, ua, us)
-            O.kv_crop(cache, ctx)
-            tokens_out += int((res.n_accept + 1).sum())
-            toks, hid = res.out_tokens, make_round_hiddens(cfg, rounds)
-            rounds += 1
-            if cache.len.max() + D + 2 >= cache.max_len:
-                break
-        return tokens_out, rounds, time.perf_counter() - t0
 
-    tok, rounds, dt = run(budget_s * 2 / 3)
-    line = {"value": round(tok / dt, 4), "unit": "accepted tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{rounds} rounds of the same workload (float64 NumPy, row by row), {dt:.1f} s"}
+def _timed_split(run, budget_s):
+    """run(budget) -> (units, seconds, sample text); two thirds of the budget with NumPy's BLAS
+    threads as configured, one third single-threaded (reported as single_thread_value)."""
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+    cores, blas = host_cores()
+    units, dt, what = run(budget_s * 2 / 3)
+    line = {"value": round(units / dt, 4), "cores": cores, "blas_threads": blas, "kind": "oracle",
+            "sample": f"{what}; {dt:.1f} s"}
     if threadpool_limits is not None:
         with threadpool_limits(limits=1):
-            tok1, rounds1, dt1 = run(budget_s / 3)
-        line["single_thread_value"] = round(tok1 / dt1, 4)
-        line["single_thread_sample"] = f"{rounds1} rounds, {dt1:.1f} s"
+            u1, dt1, what1 = run(budget_s / 3)
+        line["single_thread_value"] = round(u1 / dt1, 4)
+        line["single_thread_sample"] = f"{what1}; {dt1:.1f} s"
+    return line
+
+
+def cpu_baseline(cfg, w, K, Vv, budget_s):
+    """The float64 oracle as it stands, on a bounded sample of the same workload and inputs.
+
+    The oracle runs one row of one sequence at a time, so a sequence's round costs it the same
+    inside or outside the batch: the sample is round 0 of sequences 0, 1, 2, ... (batched
+    workloads) or rounds 0, 1, 2, ... of the one sequence (B = 1), each with the same catch-up
+    rows, draft steps, target-logit recipe and verification as the device rounds, until the time
+    budget is spent.  Building the float64 weights and loading each sequence's KV prefix are
+    set-up, outside the timed part."""
+    import oracle as O
+    from synth import make_first_round, make_round_hiddens, make_round_noise, make_round_uniforms
+    model = O.OracleModel(cfg, w)
+    B, D = cfg.batch, cfg.D
+    toks0, hid0 = make_first_round(cfg)
+    noise0 = make_round_noise(cfg, 0)
+    sp = cfg.sampling
+
+    def run(budget):
+        tokens_out = units = 0
+        spent = 0.0
+        b = r = 0
+        cache = None
+        toks = hid = None
+        while units < 1 or spent < budget:
+            if cache is None:   # a fresh sequence: its KV prefix and first catch-up row
+                cache = O.KVCache(cfg, 1, cfg.ctx + 64 * (D + 1))
+                cache.load_prefix(K[:, b:b + 1], Vv[:, b:b + 1], cfg.ctx)
+                toks, hid = toks0[b:b + 1], hid0[b:b + 1]
+            noise = noise0[b:b + 1] if r == 0 else make_round_noise(cfg, r)[b:b + 1]
+            ua, us = make_round_uniforms(cfg.index, B, D, r)
+            t0 = time.perf_counter()
+            drafts, _, logits, _ = O.draft_loop(model, cache, toks, hid, D)
+            ctx = cache.len.copy() - (D - 1)
+            tl = np.concatenate([logits, logits[:, D - 1:D]], axis=1).astype(np.float32) + noise
+            res = O.spec_verify(tl, drafts, ctx, sp, None, ua[b:b + 1], us[b:b + 1])
+            O.kv_crop(cache, ctx)
+            spent += time.perf_counter() - t0
+            tokens_out += int(res.n_accept[0]) + 1
+            units += 1
+            if B > 1 or r + 1 >= 64:   # batched: the next sequence's round 0
+                b, r, cache = (b + 1) % B, 0, None
+            else:                      # one sequence: its next round
+                r += 1
+                toks, hid = res.out_tokens, make_round_hiddens(cfg, r)[:1]
+        what = (f"round 0 of {units} of the {B} sequences" if B > 1 else f"{units} rounds of the one sequence")
+        return tokens_out, spent, what + " (float64 NumPy, row by row)"
+
+    line = _timed_split(run, budget_s)
+    line["unit"] = "accepted tokens/s"
     return line
 
 

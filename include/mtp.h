@@ -223,13 +223,17 @@ int mtp_state_restore(void* state, const void* snap, size_t bytes_per_seq, int32
  * workspace: MTP_OK, MTP_ERR_CAPACITY or MTP_ERR_TOKEN. */
 int mtp_check(void* ws, hipStream_t stream);
 
-/* Per-kernel timing with HIP events recorded around every launch of one kernel.
- * kernel: MTP_KERNEL_LM_HEAD (the lm_head GEMV + argmax) or MTP_KERNEL_VERIFY.
- * mtp_timer_start arms recording for up to max_launches launches; mtp_timer_read
- * synchronises on the last event and returns the summed milliseconds and the launch count. */
+/* Per-kernel timing with HIP events recorded around every launch of one kernel (a measurement
+ * aid, not part of the method).  kernel: MTP_KERNEL_LM_HEAD (the lm_head's main kernel: the
+ * GEMV or the MFMA GEMM with its per-workgroup argmax, without its activation preparation) or
+ * MTP_KERNEL_VERIFY (the whole spec_verify call).  mtp_timer_start arms recording for up to
+ * max_launches launches; mtp_timer_read synchronises on the last event and returns the summed
+ * milliseconds and the launch count; mtp_timer_kernel_name names the kernel last timed (a
+ * static string, "" before any). */
 enum { MTP_KERNEL_LM_HEAD = 1, MTP_KERNEL_VERIFY = 2 };
 int mtp_timer_start(int32_t kernel, int32_t max_launches);
 int mtp_timer_read(int32_t kernel, float* total_ms, int32_t* launches);
+const char* mtp_timer_kernel_name(int32_t kernel);
 
 /* ---- The target's verify forward (a dense stand-in main model) ----
  * [HB14 "The draft head"]: the main model scores the settled token and the D drafts in one pass,

@@ -551,6 +551,16 @@ class VerifyResult:
     out_tokens: np.ndarray      # [B][D+1], -1 after the emitted tokens
     crop_len: np.ndarray        # [B] = ctx_len + 1 + n_accept
     margins: List[List[float]]  # per sequence, the margins of every decision taken, in order
+    margin_pos: List[List[int]] = None  # per sequence, the output position j each margin decides
+
+    def trusted_prefix(self, b: int, margin: float) -> int:
+        """How many of sequence b's emitted tokens follow only from decisions whose margin is at
+        least ``margin`` (all a+1 of them when every margin is): the tokens before the first
+        position holding a closer decision."""
+        for m, j in zip(self.margins[b], self.margin_pos[b]):
+            if m < margin:
+                return j
+        return int(self.n_accept[b]) + 1
 
 
 def greedy_verify(target_logits, drafts, ctx_len) -> VerifyResult:
@@ -569,13 +579,14 @@ def greedy_verify(target_logits, drafts, ctx_len) -> VerifyResult:
     n_acc = np.zeros(B, dtype=np.int64)
     out = np.full((B, D + 1), -1, dtype=np.int64)
     crop = np.zeros(B, dtype=np.int64)
-    margins = []
+    margins, mpos = [], []
     for b in range(B):
-        ms = []
+        ms, mp = [], []
         a = 0
         while True:
             t, m = argmax_lowest(target_logits[b, a])
             ms.append(m)
+            mp.append(a)
             if a < D and t == drafts[b, a]:
                 out[b, a] = t
                 a += 1
@@ -585,7 +596,8 @@ def greedy_verify(target_logits, drafts, ctx_len) -> VerifyResult:
         n_acc[b] = a
         crop[b] = int(ctx_len[b]) + 1 + a
         margins.append(ms)
-    return VerifyResult(n_acc, out, crop, margins)
+        mpos.append(mp)
+    return VerifyResult(n_acc, out, crop, margins, mpos)
 
 
 # --------------------------------------------------------------------------------------------
@@ -691,9 +703,10 @@ def sampling_verify(target_logits, drafts, draft_logits, temperature: float, top
     n_acc = np.zeros(B, dtype=np.int64)
     out = np.full((B, D + 1), -1, dtype=np.int64)
     crop = np.zeros(B, dtype=np.int64)
-    margins = []
+    margins, mpos = [], []
     for b in range(B):
         ms = []
+        pos = []                             # the output position each margin belongs to
         a = 0
         tok = None
         while a < D:
@@ -710,6 +723,7 @@ def sampling_verify(target_logits, drafts, draft_logits, temperature: float, top
             u = float(u_accept[b, a])
             if np.isfinite(ratio):
                 ms.append(abs(ratio - u))
+            pos += [a] * (len(ms) - len(pos))
             if P[d] > 0.0 and u <= ratio:
                 out[b, a] = d
                 a += 1
@@ -722,11 +736,13 @@ def sampling_verify(target_logits, drafts, draft_logits, temperature: float, top
             ms += mp
             tok, m = sample(P, float(u_sample[b]))
             ms.append(m)
+        pos += [a] * (len(ms) - len(pos))
         out[b, a] = tok
         n_acc[b] = a
         crop[b] = int(ctx_len[b]) + 1 + a
         margins.append(ms)
-    return VerifyResult(n_acc, out, crop, margins)
+        mpos.append(pos)
+    return VerifyResult(n_acc, out, crop, margins, mpos)
 
 
 def spec_verify(target_logits, drafts, ctx_len, sampling=None, draft_logits=None,

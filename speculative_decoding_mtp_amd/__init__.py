@@ -95,6 +95,7 @@ _sigs = {
                             _P, _P, _P, _P, _SZ, _P], _I),
     "mtp_timer_start": ([_I, _I], _I),
     "mtp_timer_read": ([_I, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(_I)], _I),
+    "mtp_timer_kernel_name": ([_I], ctypes.c_char_p),
 }
 for _name, (_args, _res) in _sigs.items():
     _f = getattr(_lib, _name)
@@ -348,3 +349,7 @@ def mtp_timer_read(kernel: int):
     n = _I()
     _check(_lib.mtp_timer_read(kernel, ctypes.byref(ms), ctypes.byref(n)))
     return ms.value, n.value
+
+
+def mtp_timer_kernel_name(kernel: int) -> str:
+    return _lib.mtp_timer_kernel_name(kernel).decode()

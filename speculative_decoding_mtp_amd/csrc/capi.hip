@@ -43,6 +43,7 @@ struct Timer {
   bool armed = false;
 };
 Timer g_timers[3];
+const char* g_timer_name[3] = {"", "", ""};
 
 void timer_events(int kernel, hipEvent_t* b, hipEvent_t* e) {
   *b = nullptr;
@@ -207,6 +208,7 @@ StepArgs base_step(const mtp_config* cfg, const mtp_weights* w, const mtp_kv* kv
   s.logits = nullptr;
   s.lg_sb = 0;
   s.ev_begin = s.ev_end = nullptr;
+  s.ev_name = &g_timer_name[MTP_KERNEL_LM_HEAD];
   s.shared = 0;
   s.pos_off = 0;
   s.kv_layer = nullptr;
@@ -551,7 +553,11 @@ int spec_verify(int32_t B, int32_t D, int32_t V, const float* target_logits, con
   }
   hipEvent_t eb, ee;
   timer_events(MTP_KERNEL_VERIFY, &eb, &ee);
-  if (eb) (void)hipEventRecord(eb, stream);
+  if (eb) {
+    (void)hipEventRecord(eb, stream);
+    g_timer_name[MTP_KERNEL_VERIFY] = a.greedy ? "spec_verify (greedy: chunk argmax + prefix match)"
+                                               : "spec_verify (top-k scan, merge, decide)";
+  }
   const hipError_t e = run_verify(a, stream);
   if (ee) (void)hipEventRecord(ee, stream);
   return e == hipSuccess ? MTP_OK : hip_fail(e, "spec_verify launch");
@@ -611,6 +617,11 @@ int mtp_timer_start(int32_t kernel, int32_t max_launches) {
   t.count = 0;
   t.armed = true;
   return MTP_OK;
+}
+
+const char* mtp_timer_kernel_name(int32_t kernel) {
+  if (kernel != MTP_KERNEL_LM_HEAD && kernel != MTP_KERNEL_VERIFY) return "";
+  return g_timer_name[kernel];
 }
 
 int mtp_timer_read(int32_t kernel, float* total_ms, int32_t* launches) {

@@ -102,7 +102,8 @@ struct StepArgs {
   long lg_sb;
   DraftWs ws;
   hipStream_t stream;
-  hipEvent_t ev_begin, ev_end;  // optional, around the lm_head launch
+  hipEvent_t ev_begin, ev_end;  // optional, around the lm_head's main kernel launch
+  const char** ev_name;         // set to that kernel's name when the events are recorded
   // A head without a cache of its own: kc/vc/kv_len are the main model's cache, read only; head
   // layer l reads its layer kv_layer[l] (host array); rows sit at kv_len[b] + i + pos_off.
   int shared;

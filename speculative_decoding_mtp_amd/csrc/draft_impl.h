@@ -462,13 +462,27 @@ bool use_mfma(const P& p, const MfmaBufs* mb) {
   return p.nact >= 16 || p.nact > plan_gemv(p.nact, p.K, W::VE, p.N).rb;
 }
 
+// Optional HIP events recorded around a GEMV/GEMM's main kernel (not its preparation or
+// reduction launches), with that kernel's name.
+struct KTimer {
+  hipEvent_t b = nullptr, e = nullptr;
+  const char** name = nullptr;
+  void begin(hipStream_t st, const char* n) const {
+    if (b) (void)hipEventRecord(b, st);
+    if (b && name) *name = n;
+  }
+  void end(hipStream_t st) const {
+    if (e) (void)hipEventRecord(e, st);
+  }
+};
+
 // MFMA GEMM with MG activation tiles per pass.  Few weight-row groups (N < 256 x 128): K is
 // split over workgroups so every compute unit streams weights, and a second kernel sums the
 // partials in split order and applies the policy's store.
 constexpr int kMfmaItems = 1024;  // (row group, K range) items a launch aims for: 4 per CU
 
 template <class P, int MG, int NT>
-hipError_t launch_mfma_nt(P& p, hipStream_t st, int* grid_used, const MfmaBufs& mb) {
+hipError_t launch_mfma_nt(P& p, hipStream_t st, int* grid_used, const MfmaBufs& mb, const KTimer& tm) {
   MfmaBufs m = mb;
   const int groups = (p.N + 4 * NT * 16 - 1) / (4 * NT * 16);
   // passes of MG activation tiles (at most: the valid rows are counted on the device); long
@@ -490,7 +504,10 @@ hipError_t launch_mfma_nt(P& p, hipStream_t st, int* grid_used, const MfmaBufs& 
   int grid = min(npass * groups * ks, resident_cap(k_gemm_mfma<P, NT, MG>, &cap));
   grid = min(grid, kMaxGemvGrid);
   if (grid_used) *grid_used = grid;
+  tm.begin(st, NT == 2 ? (MG == 2 ? "k_gemm_mfma<NT=2,MG=2>" : "k_gemm_mfma<NT=2,MG=4>")
+                       : (MG == 2 ? "k_gemm_mfma<NT=1,MG=2>" : "k_gemm_mfma<NT=1,MG=4>"));
   hipLaunchKernelGGL((k_gemm_mfma<P, NT, MG>), dim3(grid), dim3(kWG), 0, st, p, m);
+  tm.end(st);
   if (m.part) {
     const long items = (long)m.cap * (p.N / (P::kPair ? 2 : 1));
     const int rgrid = (int)std::min<long>((items + kWG - 1) / kWG, 4096);
@@ -504,18 +521,19 @@ hipError_t launch_mfma_nt(P& p, hipStream_t st, int* grid_used, const MfmaBufs& 
 // parallelism, as in a prefill): each activation chunk staged in LDS then serves twice the weight
 // rows; otherwise 64.
 template <class P, int MG>
-hipError_t launch_mfma(P& p, hipStream_t st, int* grid_used, const MfmaBufs& mb) {
+hipError_t launch_mfma(P& p, hipStream_t st, int* grid_used, const MfmaBufs& mb, const KTimer& tm) {
   if constexpr (P::kArgmax || P::kVocab) {
-    return launch_mfma_nt<P, MG, 2>(p, st, grid_used, mb);
+    return launch_mfma_nt<P, MG, 2>(p, st, grid_used, mb, tm);
   } else {
     const int npass = (p.nact + MG * 16 - 1) / (MG * 16);
-    if (p.N >= 4096 || (npass >= 4 && p.N >= 1024)) return launch_mfma_nt<P, MG, 2>(p, st, grid_used, mb);
-    return launch_mfma_nt<P, MG, 1>(p, st, grid_used, mb);
+    if (p.N >= 4096 || (npass >= 4 && p.N >= 1024)) return launch_mfma_nt<P, MG, 2>(p, st, grid_used, mb, tm);
+    return launch_mfma_nt<P, MG, 1>(p, st, grid_used, mb, tm);
   }
 }
 
 template <class W, class P>
-hipError_t launch_gemv(P& p, hipStream_t st, int* grid_used = nullptr, const MfmaBufs* mb = nullptr) {
+hipError_t launch_gemv(P& p, hipStream_t st, int* grid_used = nullptr, const MfmaBufs* mb = nullptr,
+                       const KTimer& tm = KTimer()) {
   if constexpr (std::is_same<W, BF16>::value) {
     if (use_mfma<W>(p, mb)) {
       if (p.K > 4 * kWG * W::VE)  // rows wider than 8192: the whole row in registers
@@ -530,7 +548,9 @@ hipError_t launch_gemv(P& p, hipStream_t st, int* grid_used = nullptr, const Mfm
         if (p.nact >= kTileRows && items >= resident_cap(k_gemm_tile<P>, &cap)) {
           const int grid = resident_cap(k_gemm_tile<P>, &cap);
           if (grid_used) *grid_used = grid;
+          tm.begin(st, "k_gemm_tile");
           hipLaunchKernelGGL((k_gemm_tile<P>), dim3(grid), dim3(kWG), 0, st, p, *mb);
+          tm.end(st);
           return hipGetLastError();
         }
       }
@@ -538,8 +558,8 @@ hipError_t launch_gemv(P& p, hipStream_t st, int* grid_used = nullptr, const Mfm
       // 32-row passes for a batch of serial steps, 64-row passes above (long calls too: at two
       // waves per SIMD they beat 128-row passes at one, despite streaming the weights twice as
       // often)
-      if (p.nact <= 32) return launch_mfma<P, 2>(p, st, grid_used, *mb);
-      return launch_mfma<P, 4>(p, st, grid_used, *mb);
+      if (p.nact <= 32) return launch_mfma<P, 2>(p, st, grid_used, *mb, tm);
+      return launch_mfma<P, 4>(p, st, grid_used, *mb, tm);
     }
   }
   const GemvPlan pl = plan_gemv(p.nact, p.K, W::VE, p.N);
@@ -549,7 +569,9 @@ hipError_t launch_gemv(P& p, hipStream_t st, int* grid_used = nullptr, const Mfm
     static int cap = 0;                                                                      \
     const int grid = min(pl.grid, resident_cap(k_gemv_w<W, RB_, NJ_, RW_, P>, &cap));       \
     if (grid_used) *grid_used = grid;                                                        \
+    tm.begin(st, "k_gemv_w (VALU GEMV, whole rows per wave)");                                \
     hipLaunchKernelGGL((k_gemv_w<W, RB_, NJ_, RW_, P>), dim3(grid), dim3(kWG), 0, st, p);    \
+    tm.end(st);                                                                              \
     return hipGetLastError();                                                                \
   }
     MTP_W(1, 1, 16) MTP_W(1, 2, 16) MTP_W(1, 4, 16) MTP_W(2, 1, 8) MTP_W(2, 2, 8) MTP_W(2, 4, 8)
@@ -564,7 +586,9 @@ hipError_t launch_gemv(P& p, hipStream_t st, int* grid_used = nullptr, const Mfm
     static int cap = 0;                                                                      \
     const int grid = min(pl.grid, resident_cap(k_gemv_s<W, RB_, NX_, RW_, P>, &cap));        \
     if (grid_used) *grid_used = grid;                                                        \
+    tm.begin(st, "k_gemv_s (VALU GEMV, rows split over the workgroup)");                      \
     hipLaunchKernelGGL((k_gemv_s<W, RB_, NX_, RW_, P>), dim3(grid), dim3(kWG), 0, st, p);    \
+    tm.end(st);                                                                              \
     return hipGetLastError();                                                                \
   }
     MTP_S(2, 1, 8) MTP_S(2, 2, 8) MTP_S(2, 4, 8) MTP_S(2, 1, 4) MTP_S(2, 2, 4) MTP_S(2, 4, 4)
@@ -779,10 +803,12 @@ hipError_t run_step_t(const StepArgs& s) {
     p.lg_sb = s.lg_sb;
     p.part_v = s.ws.lm_part_v;
     p.part_i = s.ws.lm_part_i;
-    if (s.ev_begin) (void)hipEventRecord(s.ev_begin, s.stream);
     int grid = 0;
-    e = launch_gemv<W>(p, s.stream, &grid, mb);
-    if (s.ev_end) (void)hipEventRecord(s.ev_end, s.stream);
+    KTimer tm;
+    tm.b = s.ev_begin;
+    tm.e = s.ev_end;
+    tm.name = s.ev_name;
+    e = launch_gemv<W>(p, s.stream, &grid, mb, tm);
     if (e != hipSuccess) return e;
     LmFinal f;
     f.B = s.B;

@@ -17,6 +17,7 @@ bit patterns.  RMSNorm gains are 1.
 from __future__ import annotations
 
 import dataclasses
+import os
 from dataclasses import dataclass
 from typing import Dict, Optional, Tuple
 
@@ -112,9 +113,41 @@ VERIFY_CONFIGS: Dict[str, VerifyConfig] = {
 }
 
 
-def gen(cfg_index: int, stream: int, sub: int = 0) -> np.random.Generator:
-    """The PCG64 stream for (config, stream, sub-key)."""
-    return np.random.Generator(np.random.PCG64([1000 * cfg_index + stream, sub]))
+def gen(cfg_index: int, stream: int, sub: int = 0, block: Optional[int] = None) -> np.random.Generator:
+    """The PCG64 stream for (config, stream, sub-key[, block])."""
+    key = [1000 * cfg_index + stream, sub] if block is None else [1000 * cfg_index + stream, sub, block]
+    return np.random.Generator(np.random.PCG64(key))
+
+
+_BLOCK = 1 << 22          # elements per independently seeded block of a large tensor
+_WORKERS = min(16, os.cpu_count() or 1)
+
+
+def _normal_blocks(cfg_index: int, stream: int, sub: int, shape, std: float, wdtype: str) -> np.ndarray:
+    """N(0, std) float32 of ``shape`` in the config's dtype, drawn in blocks of whole leading-axis
+    rows (about 2^22 elements each), block i from its own stream (config, stream, sub, i), the
+    blocks filled in parallel threads (NumPy's generators release the GIL while filling)."""
+    out = np.empty(shape, dtype=np.float32)
+    flat = out.reshape(shape[0], -1)
+    row = flat.shape[1]
+    rows_per = max(1, _BLOCK // max(row, 1))
+    starts = list(range(0, shape[0], rows_per))
+
+    def fill(i):
+        lo, hi = starts[i], min(starts[i] + rows_per, shape[0])
+        gen(cfg_index, stream, sub, i).standard_normal((hi - lo, row), dtype=np.float32, out=flat[lo:hi])
+        if std != 1.0:
+            flat[lo:hi] *= np.float32(std)
+        if wdtype != "f32":
+            flat[lo:hi] = bf16_bits_to_f32(to_bf16_bits(flat[lo:hi]))
+
+    if len(starts) == 1:
+        fill(0)
+    else:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(_WORKERS) as ex:
+            list(ex.map(fill, range(len(starts))))
+    return out
 
 
 def to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -126,12 +159,6 @@ def to_bf16_bits(a: np.ndarray) -> np.ndarray:
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
-
-
-def _as_wdtype(a: np.ndarray, wdtype: str) -> np.ndarray:
-    if wdtype == "f32":
-        return np.ascontiguousarray(a, dtype=np.float32)
-    return bf16_bits_to_f32(to_bf16_bits(a))
 
 
 def _normal(g: np.random.Generator, shape, std: float) -> np.ndarray:
@@ -167,9 +194,12 @@ class Weights:
 
 
 def make_weights(cfg: MTPConfig, std: float = 0.02) -> Weights:
-    g = gen(cfg.index, S_WEIGHTS)
+    """The head's matrices N(0, std) in the config's dtype, each tensor from its own sub-key of the
+    weights stream (in the order eh_proj, then per layer q, k, v, o, gate, up, down, then lm_head);
+    the embedding N(0, embed_std) from the embedding stream; gains 1."""
     H, F = cfg.hidden, cfg.ffn
-    w = lambda *shape: _as_wdtype(_normal(g, shape, std), cfg.wdtype)
+    key = iter(range(1 << 20))
+    w = lambda *shape: _normal_blocks(cfg.index, S_WEIGHTS, next(key), shape, std, cfg.wdtype)
     ones = lambda n: np.ones(n, dtype=np.float32)
     eh = w(H, 2 * H)
     layers = []
@@ -177,8 +207,7 @@ def make_weights(cfg: MTPConfig, std: float = 0.02) -> Weights:
         layers.append(LayerWeights(ones(H), w(cfg.q_dim, H), w(cfg.kv_dim, H), w(cfg.kv_dim, H),
                                    w(H, cfg.q_dim), ones(H), w(F, H), w(F, H), w(H, F)))
     lm = w(cfg.vocab, H)
-    ge = gen(cfg.index, S_EMBED)
-    embed = _as_wdtype(_normal(ge, (cfg.vocab, H), cfg.embed_std), cfg.wdtype)
+    embed = _normal_blocks(cfg.index, S_EMBED, 0, (cfg.vocab, H), cfg.embed_std, cfg.wdtype)
     return Weights(embed, ones(H), ones(H), eh, layers, ones(H), lm)
 
 
@@ -195,9 +224,9 @@ class TargetWeights:
 def make_target_weights(cfg: MTPConfig, n_layers: int, head: Weights, std: float = 0.02) -> TargetWeights:
     """n_layers target blocks with the head's dimensions, matrices N(0, std) in the config's
     dtype, gains 1; embedding and lm_head taken from ``head``."""
-    g = gen(cfg.index, S_TARGET)
     H, F = cfg.hidden, cfg.ffn
-    w = lambda *shape: _as_wdtype(_normal(g, shape, std), cfg.wdtype)
+    key = iter(range(1 << 20))
+    w = lambda *shape: _normal_blocks(cfg.index, S_TARGET, next(key), shape, std, cfg.wdtype)
     ones = lambda n: np.ones(n, dtype=np.float32)
     layers = [LayerWeights(ones(H), w(cfg.q_dim, H), w(cfg.kv_dim, H), w(cfg.kv_dim, H), w(H, cfg.q_dim), ones(H),
                            w(F, H), w(F, H), w(H, F)) for _ in range(n_layers)]
@@ -209,10 +238,10 @@ def make_kv_prefix(cfg: MTPConfig, length: Optional[int] = None):
 
     Returns float32 arrays K, V of shape [L][B][nkv][length][hd]."""
     T = cfg.ctx if length is None else length
-    g = gen(cfg.index, S_KV)
-    shape = (cfg.n_layers, cfg.batch, cfg.n_kv_heads, T, cfg.head_dim)
-    K = _as_wdtype(_normal(g, shape, 1.0), cfg.wdtype)
-    V = _as_wdtype(_normal(g, shape, 1.0), cfg.wdtype)
+    shape = (cfg.n_layers * cfg.batch * cfg.n_kv_heads, T, cfg.head_dim)
+    full = (cfg.n_layers, cfg.batch, cfg.n_kv_heads, T, cfg.head_dim)
+    K = _normal_blocks(cfg.index, S_KV, 0, shape, 1.0, cfg.wdtype).reshape(full)
+    V = _normal_blocks(cfg.index, S_KV, 1, shape, 1.0, cfg.wdtype).reshape(full)
     return K, V
 
 
@@ -245,8 +274,8 @@ def make_round_hiddens(cfg: MTPConfig, rnd: int) -> np.ndarray:
 
 def make_round_noise(cfg: MTPConfig, rnd: int, std: Optional[float] = None) -> np.ndarray:
     """Target-logit noise of round ``rnd``: N(0, noise_std), [B][D+1][V] float32."""
-    g = gen(cfg.index, S_NOISE, rnd)
-    return _normal(g, (cfg.batch, cfg.D + 1, cfg.vocab), cfg.noise_std if std is None else std)
+    return _normal_blocks(cfg.index, S_NOISE, rnd, (cfg.batch * (cfg.D + 1), cfg.vocab),
+                          cfg.noise_std if std is None else std, "f32").reshape(cfg.batch, cfg.D + 1, cfg.vocab)
 
 
 def make_round_uniforms(cfg_index: int, B: int, D: int, rnd: int):

@@ -1,115 +1,146 @@
-"""Full-size parity of the draft head and verifier, in the launch configuration bench.py uses
-(the same entry points, workspace sizing and kernels), on sampled outputs the oracle can
-compute one by one.
+"""Full-size parity of the draft head and the verifier, chained over rounds, in the launch
+configuration bench.py uses (the same entry points, workspace sizing and kernels).
+
+Every sequence of the batch also runs through the float64 oracle.  A round is: the draft loop
+(GPU and oracle on the same catch-up rows), target logits = the ORACLE's draft logits + seeded
+noise, the oracle's drafts verified on both sides, then both caches cropped to the settled length
+and the next catch-up taken from the oracle's emitted tokens (teacher forcing: no input of either
+side ever comes from the device path).
 
 Workloads: the single-layer bf16 head (H 2048, 16/4 heads, FFN 6144, vocab 151936, 4096-position
-context), the 4-layer bf16 drafter (H 1024, 8/2 heads, FFN 4096, vocab 262144, D 6, sampling
-verify), and the large single-module head (H 7168, 56/8 heads, FFN 18432, vocab 129280, B 32,
-D 3, 8192-position context) on three sampled sequences.  Bar: drafts exact except where the
-oracle's top-2 gap is below 1e-4, hiddens and logits within max relative error 2e-2."""
+context, B 1, D 1, greedy), the 4-layer bf16 drafter (H 1024, 8/2 heads, FFN 4096, vocab 262144,
+D 6, sampling T 1 / top-k 64 / top-p 0.95), and the large single-module head (H 7168, 56/8 heads,
+FFN 18432, vocab 129280, B 32, D 3, 8192-position context, greedy over all 32 sequences).
+
+Bars: hiddens and logits within max relative error 2e-2 (bf16 weights, fp32 accumulation) and
+within the tighter 2e-3 that the arithmetic gives (identical bf16 weights and bf16-rounded K/V on
+both sides; fp32 against float64 sums, activations carried as bf16 hi + lo pairs); the appended
+K/V within one bf16 ulp; drafts and every verification decision exact unless the oracle's margin
+is below 1e-4 (then the sequence is compared up to that decision).  Each test asserts how many
+decisions it compared, so a near tie cannot leave a workload unchecked."""
 import numpy as np
 import pytest
 import torch
 
 import oracle as O
-from synth import CONFIGS, gen, make_first_round, make_kv_prefix, make_round_noise, make_weights
+from synth import CONFIGS, make_first_round, make_kv_prefix, make_round_hiddens, make_round_noise, \
+    make_round_uniforms, make_weights
 
 pytestmark = [pytest.mark.gpu]
 
 M = pytest.importorskip("speculative_decoding_mtp_amd")
 from tests.gpu_util import MARGIN, config, f32, i32, kv_from_numpy, max_rel, upload_weights  # noqa: E402
 
-TOL = 2e-2
+TOL_ARITH = 2e-3  # below the stated 2e-2: what fp32-vs-float64 arithmetic on identical bf16 operands gives
+KV_ULP = 2.0 ** -7
 
 
-def _round(cfg, seqs, rounds=1):
-    """Run `rounds` rounds on the GPU for the whole batch; check sequences `seqs` with the oracle."""
+def _chain(cfg, rounds):
+    """Run `rounds` chained rounds; yield per-round statistics after checking them."""
     w = make_weights(cfg)
     c, gw = config(cfg), upload_weights(cfg, w)
     B, D, H, V = cfg.batch, cfg.D, cfg.hidden, cfg.vocab
+    sp = cfg.sampling
     max_len = M.round_max_len(cfg.ctx + rounds * (D + 1) + 8)
     K, Vv = make_kv_prefix(cfg)
     kv = kv_from_numpy(cfg, K, Vv, cfg.ctx, max_len)
     model = O.OracleModel(cfg, w)
-    cache = O.KVCache(cfg, len(seqs), max_len)
-    cache.load_prefix(K[:, seqs], Vv[:, seqs], cfg.ctx)
+    del w
+    cache = O.KVCache(cfg, B, max_len)
+    cache.load_prefix(K, Vv, cfg.ctx)
     del K, Vv
-    toks, hid = make_first_round(cfg)
+    first_t, first_h = make_first_round(cfg)
+    toks = np.full((B, D + 1), -1, np.int32)
+    toks[:, :1] = first_t
+    hid = np.zeros((B, D + 1, H), np.float32)
+    hid[:, :1] = first_h
     ws = M.new_workspace(M.mtp_draft_workspace_size(c, B, D + 1, D, max_len))
+    csp = None if sp is None else M.sampling(sp.temperature, sp.top_k, sp.top_p, sp.q_mode)
+    vws = M.new_workspace(M.spec_verify_workspace_size(B, D, V, csp))
     drafts = torch.zeros(B, D, dtype=torch.int32, device="cuda")
     hids = torch.zeros(B, D, H, device="cuda")
     dlog = torch.zeros(B, D, V, device="cuda")
-    excluded = 0
+    n_acc = torch.zeros(B, dtype=torch.int32, device="cuda")
+    out = torch.zeros(B, D + 1, dtype=torch.int32, device="cuda")
+    crop = torch.zeros(B, dtype=torch.int32, device="cuda")
     for r in range(rounds):
-        M.mtp_draft_loop(c, gw, kv, D, toks.shape[1], i32(toks), f32(hid), drafts, hids, dlog, ws)
+        len0 = cache.len.copy()
+        M.mtp_draft_loop(c, gw, kv, D, D + 1, i32(toks), f32(hid), drafts, hids, dlog, ws)
         M.mtp_check(ws)
-        d_o, h_o, l_o, m_o = O.draft_loop(model, cache, toks[seqs], hid[seqs], D)
-        dg, hg, lg = drafts.cpu().numpy()[seqs], hids.cpu().numpy()[seqs], dlog.cpu().numpy()[seqs]
-        assert np.array_equal(kv.len.cpu().numpy()[seqs], cache.len)
-        for j in range(len(seqs)):
+        d_o, h_o, l_o, m_o = O.draft_loop(model, cache, toks, hid, D)
+        assert np.array_equal(kv.len.cpu().numpy(), cache.len), r
+        dg, hg, lg = drafts.cpu().numpy(), hids.cpu().numpy(), dlog.cpu().numpy()
+        st = dict(r=r, drafts_compared=0, drafts_excluded=0, err_hidden=0.0, err_logits=0.0, err_kv=0.0,
+                  decisions_compared=0, tokens_compared=0)
+        for b in range(B):
+            n_rows = int((toks[b] >= 0).sum())
+            steps_ok = D
             for k in range(D):
-                assert max_rel(hg[j, k], h_o[j, k]) < TOL, (r, j, k)
-                assert max_rel(lg[j, k], l_o[j, k]) < TOL, (r, j, k)
-                if m_o[j, k] < MARGIN:
-                    excluded += 1
+                eh, el = max_rel(hg[b, k], h_o[b, k]), max_rel(lg[b, k], l_o[b, k])
+                st["err_hidden"], st["err_logits"] = max(st["err_hidden"], eh), max(st["err_logits"], el)
+                assert eh < TOL_ARITH and el < TOL_ARITH, (r, b, k, eh, el)
+                if m_o[b, k] < MARGIN:      # a near tie: the GPU may pick the other token
+                    st["drafts_excluded"] += 1
+                    steps_ok = k + 1
                     break
-                assert dg[j, k] == d_o[j, k], (r, j, k)
-        yield dict(d_o=d_o, l_o=l_o, kv=kv, cache=cache, drafts=drafts, dlog=dlog, c=c, r=r)
-        # next round: a forced two-row catch-up (one accepted draft) on every sequence
-        ctx = cache.len - (D - 1)
+                assert dg[b, k] == d_o[b, k], (r, b, k)
+                st["drafts_compared"] += 1
+            # K/V appended by the catch-up rows and by every serial step fed a compared draft
+            p0, p1 = int(len0[b]), int(len0[b]) + n_rows + min(steps_ok, D - 1)
+            kg = kv.k[0, b, :, p0:p1].float().cpu().numpy()
+            vg = kv.v[0, b, :, :, p0:p1].transpose(-1, -2).float().cpu().numpy()
+            for p in range(p1 - p0):
+                ek = max_rel(kg[:, p], cache.K[0, b, :, p0 + p])
+                ev = max_rel(vg[:, p], cache.V[0, b, :, p0 + p])
+                st["err_kv"] = max(st["err_kv"], ek, ev)
+                assert ek < KV_ULP and ev < KV_ULP, (r, b, p0 + p, ek, ev)
+        # verification of the oracle's drafts against target logits built from the oracle's logits
+        ctx = (cache.len - (D - 1)).astype(np.int32)
+        tl = np.concatenate([l_o, l_o[:, D - 1:D]], axis=1).astype(np.float32) + make_round_noise(cfg, r)
+        ua, us = make_round_uniforms(cfg.index, B, D, r)
+        M.spec_verify(B, D, V, f32(tl), i32(d_o), None, csp, None if sp is None else f32(ua),
+                      None if sp is None else f32(us), i32(ctx), n_acc, out, crop, vws)
+        res = O.spec_verify(tl, d_o, ctx, sp, None, ua, us)
+        og, ng, cg = out.cpu().numpy(), n_acc.cpu().numpy(), crop.cpu().numpy()
+        for b in range(B):
+            j = res.trusted_prefix(b, MARGIN)
+            st["tokens_compared"] += j
+            full = j == int(res.n_accept[b]) + 1
+            st["decisions_compared"] += len(res.margins[b]) if full else sum(1 for p in res.margin_pos[b] if p < j)
+            assert np.array_equal(og[b, :j], res.out_tokens[b, :j]), (r, b, og[b], res.out_tokens[b])
+            if full:
+                assert ng[b] == res.n_accept[b] and cg[b] == res.crop_len[b], (r, b)
+                assert np.all(og[b, j:] == -1), (r, b)
+            else:
+                assert ng[b] >= j, (r, b)
+        yield st
+        # next round: both caches cut to the settled length, the oracle's emitted tokens caught up
         O.kv_crop(cache, ctx)
-        full_ctx = kv.len.cpu().numpy() - (D - 1)
-        M.kv_crop(kv, i32(full_ctx))
-        toks = np.full((B, D + 1), -1, np.int32)
-        toks[:, 0] = dg[0, 0] if len(dg) else 0
-        toks[:, 1] = np.arange(B) % V
-        g = gen(cfg.index, 2, 500 + r)
-        hid = g.standard_normal((B, D + 1, H), dtype=np.float32)
-    assert excluded <= len(seqs) * rounds
+        M.kv_crop(kv, i32(ctx))
+        toks = res.out_tokens.astype(np.int32)
+        hid = make_round_hiddens(cfg, r)
 
 
-def test_qwen_head_full_size():
-    cfg = CONFIGS["qwen"]
-    for st in _round(cfg, [0], rounds=2):
-        # greedy verify of the round against target logits = oracle logits + noise
-        D, V = cfg.D, cfg.vocab
-        l_o = st["l_o"]
-        tl = np.concatenate([l_o, l_o[:, D - 1:D]], axis=1).astype(np.float32) + make_round_noise(cfg, st["r"])
-        ctx = (st["cache"].len - (D - 1)).astype(np.int32)
-        vws = M.new_workspace(M.spec_verify_workspace_size(1, D, V, None))
-        n = torch.zeros(1, dtype=torch.int32, device="cuda")
-        out = torch.zeros(1, D + 1, dtype=torch.int32, device="cuda")
-        crop = torch.zeros(1, dtype=torch.int32, device="cuda")
-        M.spec_verify(1, D, V, f32(tl), i32(st["d_o"]), None, None, None, None, i32(ctx), n, out, crop, vws)
-        r = O.greedy_verify(tl, st["d_o"], ctx)
-        assert np.array_equal(out.cpu().numpy(), r.out_tokens)
-        assert np.array_equal(crop.cpu().numpy(), r.crop_len)
+def _run(name, rounds):
+    stats = list(_chain(CONFIGS[name], rounds))
+    for st in stats:
+        print(name, st, flush=True)
+        assert st["drafts_compared"] >= 1 and st["tokens_compared"] >= 1, st
+    return stats
 
 
-def test_four_layer_drafter_full_size_with_sampling_verify():
-    cfg = CONFIGS["drafter4"]
-    sp = cfg.sampling
-    for st in _round(cfg, [0], rounds=1):
-        D, V = cfg.D, cfg.vocab
-        l_o = st["l_o"]
-        tl = np.concatenate([l_o, l_o[:, D - 1:D]], axis=1).astype(np.float32) + make_round_noise(cfg, 0)
-        ctx = (st["cache"].len - (D - 1)).astype(np.int32)
-        g = gen(cfg.index, 6, 0)
-        ua, us = g.random((1, D), dtype=np.float32), g.random(1, dtype=np.float32)
-        csp = M.sampling(sp.temperature, sp.top_k, sp.top_p, sp.q_mode)
-        vws = M.new_workspace(M.spec_verify_workspace_size(1, D, V, csp))
-        n = torch.zeros(1, dtype=torch.int32, device="cuda")
-        out = torch.zeros(1, D + 1, dtype=torch.int32, device="cuda")
-        crop = torch.zeros(1, dtype=torch.int32, device="cuda")
-        M.spec_verify(1, D, V, f32(tl), i32(st["d_o"]), None, csp, f32(ua), f32(us), i32(ctx), n, out, crop, vws)
-        r = O.sampling_verify(tl, st["d_o"], None, sp.temperature, sp.top_k, sp.top_p, sp.q_mode, ua, us, ctx)
-        if min(r.margins[0]) >= MARGIN:
-            assert np.array_equal(out.cpu().numpy(), r.out_tokens)
-            assert np.array_equal(crop.cpu().numpy(), r.crop_len)
+def test_qwen_head_full_size_chained_greedy():
+    _run("qwen", rounds=3)
 
 
-@pytest.mark.timeout(600)
-def test_large_single_module_head_batch32_sampled():
-    cfg = CONFIGS["dsv3"]
-    for st in _round(cfg, [0, 17, 31], rounds=1):
-        pass
+def test_four_layer_drafter_full_size_chained_sampling_verify():
+    stats = _run("drafter4", rounds=3)
+    assert all(st["decisions_compared"] >= 1 for st in stats)
+
+
+@pytest.mark.timeout(900)
+def test_large_single_module_head_batch32_chained_greedy_verify():
+    """All 32 sequences through the oracle, two rounds: the second round's catch-up has the a+1
+    rows each sequence's verification settled."""
+    stats = _run("dsv3", rounds=2)
+    assert sum(st["tokens_compared"] for st in stats) >= 2 * 32

@@ -46,6 +46,30 @@ def test_emitted_count_is_one_to_d_plus_one():
         assert np.all(r.out_tokens[0, k:] == -1)
 
 
+def test_trusted_prefix_stops_at_the_first_close_decision():
+    # greedy, D = 3: target rows 0 and 1 agree with the drafts by clear gaps, row 2 has a tie
+    # (margin 0) between the draft and a lower id, so only the first two tokens are trusted
+    tl = np.array([[[0.0, 5.0, 0.0, 0.0], [0.0, 0.0, 5.0, 0.0], [0.0, 4.0, 0.0, 4.0], [9.0, 0.0, 0.0, 0.0]]])
+    r = O.greedy_verify(tl, np.array([[1, 2, 3]]), [10])
+    assert r.n_accept[0] == 2 and list(r.out_tokens[0]) == [1, 2, 1, -1]
+    assert r.margin_pos[0] == [0, 1, 2]
+    assert r.trusted_prefix(0, 1e-4) == 2
+    assert r.trusted_prefix(0, 0.0) == 3            # every margin >= 0: all a + 1 tokens
+    # sampling: every margin is tagged with the output position it decides, in order
+    rng = np.random.default_rng(3)
+    for _ in range(50):
+        D = int(rng.integers(1, 5))
+        tl = rng.normal(size=(1, D + 1, 7))
+        dr = rng.integers(0, 7, size=(1, D))
+        rs = O.sampling_verify(tl, dr, None, 0.9, 4, 0.8, 0, rng.random((1, D)), rng.random(1), [0])
+        pos = rs.margin_pos[0]
+        assert len(pos) == len(rs.margins[0]) and pos == sorted(pos)
+        assert pos[-1] == rs.n_accept[0] and pos[0] == 0
+        j = rs.trusted_prefix(0, 1e-4)
+        assert 0 <= j <= rs.n_accept[0] + 1
+        assert all(m >= 1e-4 for m, p in zip(rs.margins[0], pos) if p < j)
+
+
 # ---------------------------------------------------------------- warp
 def _warp_by_counting(l, T, k, p):
     """Independent definitions: a token survives top-k when fewer than k tokens rank
