@@ -19,6 +19,7 @@
 #include "draft.h"
 #include "gemv.h"
 #include "mfma_gemm.h"
+#include "stream_gemm.h"
 
 namespace mtp {
 
@@ -458,7 +459,7 @@ int resident_cap(K kernel, int* cache) {
 // VALU GEMV would have to stream the weights more than once (more rows than it holds per pass).
 template <class W, class P>
 bool use_mfma(const P& p, const MfmaBufs* mb) {
-  if (!mb || !std::is_same<W, BF16>::value || p.K % kMfmaKC != 0) return false;
+  if (!mb || !std::is_same<W, BF16>::value || p.K % kMfmaKC != 0) return false;  // K: whole 128-wide chunks
   return p.nact >= 16 || p.nact > plan_gemv(p.nact, p.K, W::VE, p.N).rb;
 }
 
@@ -476,37 +477,75 @@ struct KTimer {
   }
 };
 
-// MFMA GEMM with MG activation tiles per pass.  Few weight-row groups (N < 256 x 128): K is
-// split over workgroups so every compute unit streams weights, and a second kernel sums the
-// partials in split order and applies the policy's store.
-constexpr int kMfmaItems = 1024;  // (row group, K range) items a launch aims for: 4 per CU
-
-template <class P, int MG, int NT>
-hipError_t launch_mfma_nt(P& p, hipStream_t st, int* grid_used, const MfmaBufs& mb, const KTimer& tm) {
-  MfmaBufs m = mb;
-  const int groups = (p.N + 4 * NT * 16 - 1) / (4 * NT * 16);
-  // passes of MG activation tiles (at most: the valid rows are counted on the device); long
-  // prefills spread their passes over the grid instead of splitting K
-  const int npass = P::kArgmax ? 1 : (p.nact + MG * 16 - 1) / (MG * 16);
-  const int par = npass > 2 ? npass * groups : groups;
-  int ks = 1;
-  if (!P::kArgmax && par < (npass > 2 ? kMfmaItems / 2 : kMfmaItems) && m.part) {
-    ks = (kMfmaItems + par - 1) / par;
-    const int kc = p.K / kMfmaKC;
-    if (ks > kc) ks = kc;
-    if (ks > kMaxKSplit) ks = kMaxKSplit;
-    const long fit = m.part_cap / ((long)m.cap * p.N);
-    if (ks > fit) ks = (int)fit;
+// Compute units of the current device, cached.
+inline int device_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (cus < 1) cus = 1;
   }
-  if (ks <= 1) m.part = nullptr;
-  m.ksplit = ks;
-  static int cap = 0;
-  int grid = min(npass * groups * ks, resident_cap(k_gemm_mfma<P, NT, MG>, &cap));
-  grid = min(grid, kMaxGemvGrid);
+  return cus;
+}
+
+// Work decomposition of k_gemm_stream for an N x K matrix and up to nact activation rows: waves
+// per workgroup, tiles per wave and K parts chosen to minimise the estimated time of the weight
+// stream -- (rounds of workgroups over the compute units) x (bytes one workgroup streams) -- plus
+// the split-K partial sums written and read back.  One workgroup runs per compute unit (LDS).
+struct SgChoice {
+  SgPlan pl;
+  int nt, mt, items;
+};
+inline SgChoice plan_stream(int N, int K, int nact, bool whole_rows, long part_room, int cap) {
+  const int cus = device_cus();
+  SgChoice best{};
+  best.mt = nact <= 32 ? 2 : 4;
+  const int rows = 16 * best.mt;
+  const int npass = (nact + rows - 1) / rows;
+  const int nk = K / kSgKC, tiles = (N + 15) / 16;
+  const int rc = best.mt <= 2 ? SgShape<2>::RC : SgShape<4>::RC;
+  double best_t = 1e300;
+  const int ks_opts[7] = {1, 2, 3, 4, 6, 8, 12};
+  for (int nw = 7; nw <= kSgMaxWaves; ++nw)
+    for (int nt = 1; nt <= 2; ++nt)
+      for (int ks : ks_opts) {
+        if (whole_rows && ks > 1) continue;
+        if (ks > 1 && (nk / ks < 2 * rc || (long)ks * cap * N > part_room)) continue;
+        const int sets = (tiles + nw * nt - 1) / (nw * nt);
+        const long items = (long)npass * sets * ks;
+        const long rounds = (items + cus - 1) / cus;
+        const double per_item = (double)nw * nt * 16 * ((double)K / ks) * 2;
+        double t = rounds * per_item * cus;                           // bytes-equivalent of the stream
+        if (ks > 1) t += 2.0 * ks * nact * (double)N * 4 + 4.0e7;     // partials + the reduce launch
+        if (nt == 1 && best.mt == 4) t *= 1.5;                        // 64-row passes: operand reads
+        if (t < best_t * 0.999) {
+          best_t = t;
+          best.pl.nw = nw;
+          best.nt = nt;
+          best.pl.ks = ks;
+          best.pl.sets = sets;
+          best.pl.kper = (nk + ks - 1) / ks;
+          best.items = (int)items;
+        }
+      }
+  return best;
+}
+
+template <class P, int NT, int MT, int KPT>
+hipError_t launch_stream_t(P& p, hipStream_t st, int* grid_used, const MfmaBufs& mb, const KTimer& tm,
+                           const SgChoice& ch) {
+  if (KPT * 64 * ch.pl.nw < SgShape<MT>::SLICE || ch.pl.nw > kSgMaxWaves) return hipErrorInvalidConfiguration;
+  MfmaBufs m = mb;
+  if (ch.pl.ks <= 1) m.part = nullptr;
+  m.ksplit = ch.pl.ks;
+  int grid = min(ch.items, device_cus());
+  grid = max(1, min(grid, kMaxGemvGrid));
   if (grid_used) *grid_used = grid;
-  tm.begin(st, NT == 2 ? (MG == 2 ? "k_gemm_mfma<NT=2,MG=2>" : "k_gemm_mfma<NT=2,MG=4>")
-                       : (MG == 2 ? "k_gemm_mfma<NT=1,MG=2>" : "k_gemm_mfma<NT=1,MG=4>"));
-  hipLaunchKernelGGL((k_gemm_mfma<P, NT, MG>), dim3(grid), dim3(kWG), 0, st, p, m);
+  static const char* name = NT == 2 ? (MT == 2 ? "k_gemm_stream<NT=2,MT=2>" : "k_gemm_stream<NT=2,MT=4>")
+                                    : (MT == 2 ? "k_gemm_stream<NT=1,MT=2>" : "k_gemm_stream<NT=1,MT=4>");
+  tm.begin(st, name);
+  hipLaunchKernelGGL((k_gemm_stream<P, NT, MT, KPT>), dim3(grid), dim3(64 * ch.pl.nw), 0, st, p, m, ch.pl);
   tm.end(st);
   if (m.part) {
     const long items = (long)m.cap * (p.N / (P::kPair ? 2 : 1));
@@ -516,18 +555,43 @@ hipError_t launch_mfma_nt(P& p, hipStream_t st, int* grid_used, const MfmaBufs& 
   return hipGetLastError();
 }
 
-// 128 weight rows per workgroup (two 16-row tiles per wave) for lm_head and for other matrices
-// with enough column groups (4096+ rows, or 1024+ when four or more activation passes add
-// parallelism, as in a prefill): each activation chunk staged in LDS then serves twice the weight
-// rows; otherwise 64.
-template <class P, int MG>
-hipError_t launch_mfma(P& p, hipStream_t st, int* grid_used, const MfmaBufs& mb, const KTimer& tm) {
-  if constexpr (P::kArgmax || P::kVocab) {
-    return launch_mfma_nt<P, MG, 2>(p, st, grid_used, mb, tm);
+// The skinny MFMA GEMM: lm_head (argmax) and the target's lm_head keep whole rows (no split K)
+// with two tiles per wave; the other matrices take the planned decomposition.
+template <class P>
+hipError_t launch_stream(P& p, hipStream_t st, int* grid_used, const MfmaBufs& mb, const KTimer& tm) {
+  const bool whole = P::kArgmax || P::kVocab;
+  SgChoice ch;
+  if (whole) {
+    ch.mt = p.nact <= 32 ? 2 : 4;
+    ch.nt = 2;
+    ch.pl.nw = 8;
+    ch.pl.ks = 1;
+    ch.pl.kper = p.K / kSgKC;
+    ch.pl.sets = (p.N + 8 * 2 * 16 - 1) / (8 * 2 * 16);
+    const int npass = P::kArgmax ? 1 : (p.nact + 16 * ch.mt - 1) / (16 * ch.mt);
+    ch.items = npass * ch.pl.sets;
   } else {
-    const int npass = (p.nact + MG * 16 - 1) / (MG * 16);
-    if (p.N >= 4096 || (npass >= 4 && p.N >= 1024)) return launch_mfma_nt<P, MG, 2>(p, st, grid_used, mb, tm);
-    return launch_mfma_nt<P, MG, 1>(p, st, grid_used, mb, tm);
+    ch = plan_stream(p.N, p.K, p.nact, false, mb.part ? mb.part_cap : 0, mb.cap);
+  }
+  // activation pieces per thread and chunk: ceil(SLICE / threads); 512 pieces (32-row passes):
+  // 2 with 7 waves, 1 with 8 or 9; 1024 pieces (64-row passes): 3 with 7 waves, 2 with 8 or 9
+  const bool seven = ch.pl.nw == 7;
+  if constexpr (P::kArgmax || P::kVocab) {  // 8 waves, two tiles each
+    if (ch.mt == 2) return launch_stream_t<P, 2, 2, 1>(p, st, grid_used, mb, tm, ch);
+    return launch_stream_t<P, 2, 4, 2>(p, st, grid_used, mb, tm, ch);
+  } else {
+    if (ch.mt == 2) {
+      if (ch.nt == 2)
+        return seven ? launch_stream_t<P, 2, 2, 2>(p, st, grid_used, mb, tm, ch)
+                     : launch_stream_t<P, 2, 2, 1>(p, st, grid_used, mb, tm, ch);
+      return seven ? launch_stream_t<P, 1, 2, 2>(p, st, grid_used, mb, tm, ch)
+                   : launch_stream_t<P, 1, 2, 1>(p, st, grid_used, mb, tm, ch);
+    }
+    if (ch.nt == 2)
+      return seven ? launch_stream_t<P, 2, 4, 3>(p, st, grid_used, mb, tm, ch)
+                   : launch_stream_t<P, 2, 4, 2>(p, st, grid_used, mb, tm, ch);
+    return seven ? launch_stream_t<P, 1, 4, 3>(p, st, grid_used, mb, tm, ch)
+                 : launch_stream_t<P, 1, 4, 2>(p, st, grid_used, mb, tm, ch);
   }
 }
 
@@ -554,12 +618,9 @@ hipError_t launch_gemv(P& p, hipStream_t st, int* grid_used = nullptr, const Mfm
           return hipGetLastError();
         }
       }
-      // activation tiles per pass from the activation count (an upper bound of the valid rows):
-      // 32-row passes for a batch of serial steps, 64-row passes above (long calls too: at two
-      // waves per SIMD they beat 128-row passes at one, despite streaming the weights twice as
-      // often)
-      if (p.nact <= 32) return launch_mfma<P, 2>(p, st, grid_used, *mb, tm);
-      return launch_mfma<P, 4>(p, st, grid_used, *mb, tm);
+      // 32-row passes for a batch of serial steps, 64-row passes above (by the activation count,
+      // an upper bound of the valid rows)
+      return launch_stream(p, st, grid_used, *mb, tm);
     }
   }
   const GemvPlan pl = plan_gemv(p.nact, p.K, W::VE, p.N);
