@@ -215,7 +215,9 @@ int kv_crop(const mtp_kv* kv, const int32_t* new_len, hipStream_t stream);
  * windows are copied because they cannot be truncated).  bytes_per_seq multiple of 16. */
 int mtp_state_snapshot(const void* state, void* snap, size_t bytes_per_seq, int32_t B, hipStream_t stream);
 
-/* Copy snap back into state for every sequence b with n_accept[b] < D (a rejected draft). */
+/* Copy snap back into state for every sequence b with n_accept[b] < D (a rejected draft): [HB14],
+ * the paragraph after the loop -- on a miss the recurrent layers' memory tables and conv windows
+ * are put back from the copy taken before verification, while attention caches are only cut. */
 int mtp_state_restore(void* state, const void* snap, size_t bytes_per_seq, int32_t B, const int32_t* n_accept,
                       int32_t D, hipStream_t stream);
 
