@@ -206,6 +206,23 @@ int spec_verify(int32_t B, int32_t D, int32_t V, const float* target_logits, con
                 const int32_t* ctx_len, int32_t* n_accept, int32_t* out_tokens, int32_t* crop_len, void* ws,
                 size_t ws_bytes, hipStream_t stream);
 
+/* spec_verify for callers that cannot allocate device memory or bring a workspace: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments (without
+ * ws / ws_bytes), checks and results as spec_verify.  Its scratch (the greedy chunk partials or
+ * the sampling top-k buffers) is a device array inside the library of MTP_VERIFY_SCRATCH_BYTES,
+ * one per GPU the library runs on, held until the process ends; the call allocates and frees
+ * nothing.  A call that would need more scratch than that (greedy: 8 bytes per target row and
+ * logits chunk; sampling: 8 * top_k bytes per row, plus per-chunk candidates when there are fewer
+ * than 128 rows) returns MTP_ERR_WORKSPACE and launches nothing.  Every call on a GPU uses the
+ * same array, which keeps the last call's contents (nothing in it needs to start at zero): calls
+ * that overlap in time on one GPU, from other streams or threads, race on it and must be
+ * serialised by the caller. */
+#define MTP_VERIFY_SCRATCH_BYTES (4u << 20)
+int spec_verify_noalloc(int32_t B, int32_t D, int32_t V, const float* target_logits, const int32_t* drafts,
+                        const float* draft_logits, const mtp_sampling* sp, const float* u_accept,
+                        const float* u_sample, const int32_t* ctx_len, int32_t* n_accept, int32_t* out_tokens,
+                        int32_t* crop_len, hipStream_t stream);
+
 /* Truncate each sequence's cache: len[b] = min(len[b], max(new_len[b], 0)) ([HB14] rollback
  * keeps the first n positions; [DLM] item 2 crop()). new_len: device int32[batch]. */
 int kv_crop(const mtp_kv* kv, const int32_t* new_len, hipStream_t stream);

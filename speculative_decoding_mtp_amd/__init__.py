@@ -86,6 +86,7 @@ _sigs = {
                                   ctypes.POINTER(_I), _I, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
     "spec_verify_workspace_size": ([_I, _I, _I, ctypes.POINTER(MtpSampling), ctypes.POINTER(_SZ)], _I),
     "spec_verify": ([_I, _I, _I, _P, _P, _P, ctypes.POINTER(MtpSampling), _P, _P, _P, _P, _P, _P, _P, _SZ, _P], _I),
+    "spec_verify_noalloc": ([_I, _I, _I, _P, _P, _P, ctypes.POINTER(MtpSampling), _P, _P, _P, _P, _P, _P, _P], _I),
     "kv_crop": ([ctypes.POINTER(MtpKV), _P, _P], _I),
     "mtp_state_snapshot": ([_P, _P, _SZ, _I, _P], _I),
     "mtp_state_restore": ([_P, _P, _SZ, _I, _P, _I, _P], _I),
@@ -319,6 +320,18 @@ def spec_verify(B: int, D: int, V: int, target_logits, drafts, draft_logits, sp:
         _ptr(u_sample, torch.float32, "u_sample", B), _ptr(ctx_len, torch.int32, "ctx_len", B),
         _ptr(n_accept, torch.int32, "n_accept", B), _ptr(out_tokens, torch.int32, "out_tokens", B * (D + 1)),
         _ptr(crop_len, torch.int32, "crop_len", B), _ptr(ws, None, "ws"), ws.numel(), _stream(stream)))
+
+
+def spec_verify_noalloc(B: int, D: int, V: int, target_logits, drafts, draft_logits, sp: Optional[MtpSampling],
+                        u_accept, u_sample, ctx_len, n_accept, out_tokens, crop_len, stream=None) -> None:
+    """spec_verify with the library's own per-GPU scratch array instead of a workspace."""
+    _check(_lib.spec_verify_noalloc(
+        B, D, V, _ptr(target_logits, torch.float32, "target_logits", B * (D + 1) * V),
+        _ptr(drafts, torch.int32, "drafts", B * D), _ptr(draft_logits, torch.float32, "draft_logits", B * D * V),
+        ctypes.byref(sp) if sp is not None else None, _ptr(u_accept, torch.float32, "u_accept", B * D),
+        _ptr(u_sample, torch.float32, "u_sample", B), _ptr(ctx_len, torch.int32, "ctx_len", B),
+        _ptr(n_accept, torch.int32, "n_accept", B), _ptr(out_tokens, torch.int32, "out_tokens", B * (D + 1)),
+        _ptr(crop_len, torch.int32, "crop_len", B), _stream(stream)))
 
 
 def kv_crop(kv: KVCache, new_len, stream=None) -> None:

@@ -3,6 +3,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -214,6 +215,115 @@ StepArgs base_step(const mtp_config* cfg, const mtp_weights* w, const mtp_kv* kv
   s.kv_layer = nullptr;
   s.no_head = 0;
   return s;
+}
+
+// Checks spec_verify's arguments and lays its scratch out from `base` (a workspace, or the
+// library's own array): the greedy chunk argmax partials, or the sampling top-k buffers.  *used
+// is the number of bytes this call needs from base (exact, unlike the workspace-size bound).
+int verify_setup(int32_t B, int32_t D, int32_t V, const float* target_logits, const int32_t* drafts,
+                 const float* draft_logits, const mtp_sampling* sp, const float* u_accept, const float* u_sample,
+                 const int32_t* ctx_len, int32_t* n_accept, int32_t* out_tokens, int32_t* crop_len, char* base,
+                 VerifyArgs* out, size_t* used) {
+  if (B < 1 || D < 1 || V < 1) return fail(MTP_ERR_ARG, "B, D, V must be positive");
+  if (D > kMaxDraft) return fail(MTP_ERR_ARG, "D must be <= %d", kMaxDraft);
+  if (!target_logits || !drafts || !ctx_len || !n_accept || !out_tokens || !crop_len)
+    return fail(MTP_ERR_ARG, "a required pointer is NULL");
+  if (!aligned16(target_logits)) return fail(MTP_ERR_ARG, "target_logits misaligned");
+  VerifyArgs a = {};
+  a.B = B;
+  a.D = D;
+  a.V = V;
+  a.greedy = !sp || !(sp->temperature > 0.f);
+  a.tl = target_logits;
+  a.drafts = drafts;
+  a.ctx_len = ctx_len;
+  a.n_accept = n_accept;
+  a.out = out_tokens;
+  a.crop = crop_len;
+  size_t o = 256;
+  const int rows = B * (D + 1) + (!a.greedy && sp->q_mode == 1 ? B * D : 0);
+  if (a.greedy) {
+    int target = (1024 + rows - 1) / rows;
+    int chunk = (V + target - 1) / target;
+    chunk = (chunk + 1023) & ~1023;
+    a.chunk = chunk;
+    a.nchunk = (V + chunk - 1) / chunk;
+    a.part_v = reinterpret_cast<float*>(base + o);
+    o += up256((size_t)rows * a.nchunk * 4);
+    a.part_i = reinterpret_cast<int*>(base + o);
+    o += up256((size_t)rows * a.nchunk * 4);
+  } else {
+    if (sp->q_mode != 0 && sp->q_mode != 1) return fail(MTP_ERR_ARG, "q_mode must be 0 or 1");
+    if (sp->top_k < 1 || sp->top_k > kMaxTopK) return fail(MTP_ERR_ARG, "top_k must be in [1, %d]", kMaxTopK);
+    if (sp->q_mode == 1 && (!draft_logits || !aligned16(draft_logits)))
+      return fail(MTP_ERR_ARG, "q_mode 1 needs draft_logits");
+    if (!u_accept || !u_sample) return fail(MTP_ERR_ARG, "sampling needs u_accept and u_sample");
+    const int K = sp->top_k;
+    a.q_mode = sp->q_mode;
+    a.top_k = K;
+    a.temperature = sp->temperature;
+    a.top_p = sp->top_p;
+    a.dl = draft_logits;
+    a.u_accept = u_accept;
+    a.u_sample = u_sample;
+    a.top_v = reinterpret_cast<float*>(base + o);
+    o += up256((size_t)rows * K * 4);
+    a.top_i = reinterpret_cast<int*>(base + o);
+    o += up256((size_t)rows * K * 4);
+    a.top_n = reinterpret_cast<int*>(base + o);
+    o += up256((size_t)rows * 4);
+    topk_split(rows, V, &a.tk_nchunk, &a.tk_chunk);
+    a.cand_v = nullptr;
+    a.cand_i = nullptr;
+    if (a.tk_nchunk > 1) {
+      a.cand_v = reinterpret_cast<float*>(base + o);
+      o += up256((size_t)rows * a.tk_nchunk * K * 4);
+      a.cand_i = reinterpret_cast<int*>(base + o);
+      o += up256((size_t)rows * a.tk_nchunk * K * 4);
+    }
+  }
+  *out = a;
+  *used = o;
+  return MTP_OK;
+}
+
+int verify_launch(const VerifyArgs& a, hipStream_t stream) {
+  hipEvent_t eb, ee;
+  timer_events(MTP_KERNEL_VERIFY, &eb, &ee);
+  if (eb) {
+    (void)hipEventRecord(eb, stream);
+    g_timer_name[MTP_KERNEL_VERIFY] = a.greedy ? "spec_verify (greedy: chunk argmax + prefix match)"
+                                               : "spec_verify (top-k scan, merge, decide)";
+  }
+  const hipError_t e = run_verify(a, stream);
+  if (ee) (void)hipEventRecord(ee, stream);
+  return e == hipSuccess ? MTP_OK : hip_fail(e, "spec_verify launch");
+}
+
+// ------------------------------------------------------------------ scratch of spec_verify_noalloc
+// A file-scope device array, one copy per GPU for the life of the process.  Host code must not use
+// the symbol's name as a device address: its address on each device comes from
+// hipGetSymbolAddress, taken once per device (with that device current) and kept here.
+__device__ __align__(256) char scratch[MTP_VERIFY_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_for_current_device(char** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MTP_ERR_ARG, "device index %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hip_fail(e == hipSuccess ? hipErrorInvalidSymbol : e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = static_cast<char*>(g_scratch_ptr[dev]);
+  return MTP_OK;
 }
 
 }  // namespace
@@ -494,73 +604,32 @@ int spec_verify(int32_t B, int32_t D, int32_t V, const float* target_logits, con
   size_t need;
   int rc = spec_verify_workspace_size(B, D, V, sp, &need);
   if (rc) return rc;
-  if (!target_logits || !drafts || !ctx_len || !n_accept || !out_tokens || !crop_len)
-    return fail(MTP_ERR_ARG, "a required pointer is NULL");
-  if (!aligned16(target_logits) || !ws || !aligned16(ws)) return fail(MTP_ERR_ARG, "target_logits / ws misaligned");
+  if (!ws || !aligned16(ws)) return fail(MTP_ERR_ARG, "workspace NULL or misaligned");
   if (ws_bytes < need) return fail(MTP_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, need);
-  VerifyArgs a = {};
-  a.B = B;
-  a.D = D;
-  a.V = V;
-  a.greedy = !sp || !(sp->temperature > 0.f);
-  a.tl = target_logits;
-  a.drafts = drafts;
-  a.ctx_len = ctx_len;
-  a.n_accept = n_accept;
-  a.out = out_tokens;
-  a.crop = crop_len;
-  char* base = static_cast<char*>(ws);
-  size_t o = 256;
-  const int rows = B * (D + 1) + (!a.greedy && sp->q_mode == 1 ? B * D : 0);
-  if (a.greedy) {
-    int target = (1024 + rows - 1) / rows;
-    int chunk = (V + target - 1) / target;
-    chunk = (chunk + 1023) & ~1023;
-    a.chunk = chunk;
-    a.nchunk = (V + chunk - 1) / chunk;
-    a.part_v = reinterpret_cast<float*>(base + o);
-    o += up256((size_t)rows * 1024 * 4);
-    a.part_i = reinterpret_cast<int*>(base + o);
-    o += up256((size_t)rows * 1024 * 4);
-  } else {
-    if (sp->q_mode != 0 && sp->q_mode != 1) return fail(MTP_ERR_ARG, "q_mode must be 0 or 1");
-    if (sp->q_mode == 1 && (!draft_logits || !aligned16(draft_logits)))
-      return fail(MTP_ERR_ARG, "q_mode 1 needs draft_logits");
-    if (!u_accept || !u_sample) return fail(MTP_ERR_ARG, "sampling needs u_accept and u_sample");
-    const int K = sp->top_k;
-    a.q_mode = sp->q_mode;
-    a.top_k = K;
-    a.temperature = sp->temperature;
-    a.top_p = sp->top_p;
-    a.dl = draft_logits;
-    a.u_accept = u_accept;
-    a.u_sample = u_sample;
-    a.top_v = reinterpret_cast<float*>(base + o);
-    o += up256((size_t)rows * K * 4);
-    a.top_i = reinterpret_cast<int*>(base + o);
-    o += up256((size_t)rows * K * 4);
-    a.top_n = reinterpret_cast<int*>(base + o);
-    o += up256((size_t)rows * 4);
-    topk_split(rows, V, &a.tk_nchunk, &a.tk_chunk);
-    a.cand_v = nullptr;
-    a.cand_i = nullptr;
-    if (a.tk_nchunk > 1) {
-      a.cand_v = reinterpret_cast<float*>(base + o);
-      o += up256((size_t)rows * a.tk_nchunk * K * 4);
-      a.cand_i = reinterpret_cast<int*>(base + o);
-      o += up256((size_t)rows * a.tk_nchunk * K * 4);
-    }
-  }
-  hipEvent_t eb, ee;
-  timer_events(MTP_KERNEL_VERIFY, &eb, &ee);
-  if (eb) {
-    (void)hipEventRecord(eb, stream);
-    g_timer_name[MTP_KERNEL_VERIFY] = a.greedy ? "spec_verify (greedy: chunk argmax + prefix match)"
-                                               : "spec_verify (top-k scan, merge, decide)";
-  }
-  const hipError_t e = run_verify(a, stream);
-  if (ee) (void)hipEventRecord(ee, stream);
-  return e == hipSuccess ? MTP_OK : hip_fail(e, "spec_verify launch");
+  VerifyArgs a;
+  size_t used;
+  if ((rc = verify_setup(B, D, V, target_logits, drafts, draft_logits, sp, u_accept, u_sample, ctx_len, n_accept,
+                         out_tokens, crop_len, static_cast<char*>(ws), &a, &used)))
+    return rc;
+  return verify_launch(a, stream);
+}
+
+int spec_verify_noalloc(int32_t B, int32_t D, int32_t V, const float* target_logits, const int32_t* drafts,
+                        const float* draft_logits, const mtp_sampling* sp, const float* u_accept,
+                        const float* u_sample, const int32_t* ctx_len, int32_t* n_accept, int32_t* out_tokens,
+                        int32_t* crop_len, hipStream_t stream) {
+  char* base = nullptr;
+  int rc = scratch_for_current_device(&base);
+  if (rc) return rc;
+  VerifyArgs a;
+  size_t used;
+  if ((rc = verify_setup(B, D, V, target_logits, drafts, draft_logits, sp, u_accept, u_sample, ctx_len, n_accept,
+                         out_tokens, crop_len, base, &a, &used)))
+    return rc;
+  if (used > MTP_VERIFY_SCRATCH_BYTES)
+    return fail(MTP_ERR_WORKSPACE, "this call needs %zu bytes of scratch; the library's array holds %u", used,
+                (unsigned)MTP_VERIFY_SCRATCH_BYTES);
+  return verify_launch(a, stream);
 }
 
 int kv_crop(const mtp_kv* kv, const int32_t* new_len, hipStream_t stream) {
