@@ -445,6 +445,278 @@ __global__ __launch_bounds__(kWG) void k_attn_mfma(AttnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// bf16 heads with a batch of sequences (B x kv heads fill the GPU): the same MFMA attention with
+// the keys and values staged through LDS.  Reading K and V^T straight in the operand layout
+// fetches 64 bytes of each of 16 rows per load instruction, a pattern that streams well below
+// the read ceiling; here each wave fetches 64-position superslices row-contiguously -- keys as
+// four 256-byte rows per load, values as eight 128-byte channel rows -- into a private LDS tile
+// (XOR-swizzled in 16-byte units) and reads the operands from there.  The next superslice is in
+// flight in registers while one is used (at one wave per SIMD the registers are free); the tile
+// is the wave's own, so the streaming loop has no barrier.  Per 32-position half the products
+// are those of k_attn_mfma.
+template <int NQT>
+__global__ __launch_bounds__(kWG) void k_attn_lds(AttnArgs a) {
+  constexpr int HD = 128;
+  constexpr int NS = HD / 32;   // q.k steps
+  constexpr int ND = HD / 16;   // 16-channel tiles of the output
+  constexpr int QB = 16 * NQT;  // queries per pass
+  constexpr int OP = HD + 4;    // padded LDS row of the merged output
+  constexpr int QP = HD + 8;    // padded LDS row of the split queries (bf16)
+  constexpr int SP = 64;        // positions per superslice
+  constexpr int KT = SP * HD * 2;   // bytes of a key tile: 64 rows x 256 B (16 units)
+  constexpr int VT = HD * SP * 2;   // bytes of a value tile: 128 channel rows x 128 B (8 units)
+  __shared__ float sm[4][QB], sl[4][QB];
+  __shared__ __align__(16) __bf16 sQ[2 * QB * QP];  // [hi/lo][query][channel]
+  __shared__ __align__(16) char sKV[4][KT + VT];     // each wave's tiles
+  __shared__ int s_n;
+  // the merged output reuses the tiles: it is written after every wave has left the streaming
+  // loop (behind a barrier) and read before the next pass stores tiles again (another barrier)
+  float* sO = reinterpret_cast<float*>(&sKV[0][0]);
+  static_assert(QB * OP * 4 <= 4 * (KT + VT), "merged output fits in the tiles");
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, j = lane & 15, hq = lane >> 4;
+  const int s = blockIdx.x, kvh = blockIdx.y % a.nkv, b = blockIdx.z;
+  const int qgrp = blockIdx.y / a.nkv, nqgrp = gridDim.y / a.nkv;
+  const int G = a.nq / a.nkv;
+  const int L0 = a.len[b];
+  if (tid == 0) s_n = a.rows ? a.rows[b] : count_rows(a.tok + (long)b * a.tok_sb, a.rps, a.V, L0, a.max_len, nullptr);
+  __syncthreads();
+  const int n = s_n;
+  if (n == 0) return;
+  const int Tn = L0 + (a.shared ? 0 : n);
+  const int chunk = attn_chunk(Tn, a.nsplit);
+  const int p_beg = s * chunk;
+  if (p_beg >= Tn) return;
+  const int p_end = min(Tn, p_beg + chunk);
+  const int NQ = n * G;
+  const uint16_t* Kb = reinterpret_cast<const uint16_t*>(a.kc) + ((long)b * a.nkv + kvh) * a.max_len * HD;
+  const uint16_t* Vt = reinterpret_cast<const uint16_t*>(a.vc) + ((long)b * a.nkv + kvh) * a.max_len * HD;
+  const float scale = 1.0f / sqrtf(float(HD));
+  const int krow = 8 * (j >> 2) + (j & 3);  // this lane's K row in sub-tile 0 (+4 in sub-tile 1)
+  char* tK = sKV[wid];
+  char* tV = sKV[wid] + KT;
+  auto vswz = [](int r) { return (r & 7) ^ ((r >> 3) & 1); };
+
+  for (int q0 = qgrp * QB; q0 < NQ; q0 += QB * nqgrp) {
+    const int p_stop = min(p_end, L0 + (min(NQ, q0 + QB) - 1) / G + 1);
+    for (int idx = tid; idx < QB * (HD / 8); idx += kWG) {
+      const int q = idx / (HD / 8), c = idx - q * (HD / 8), qi = q0 + q;
+      float f[8];
+      if (qi < NQ) {
+        const int i = qi / G, g = qi - i * G;
+        const float* qp = a.q + (((long)b * a.rps + i) * a.nq + kvh * G + g) * HD + 8 * c;
+        const float4 x0 = *reinterpret_cast<const float4*>(qp);
+        const float4 x1 = *reinterpret_cast<const float4*>(qp + 4);
+        f[0] = x0.x; f[1] = x0.y; f[2] = x0.z; f[3] = x0.w;
+        f[4] = x1.x; f[5] = x1.y; f[6] = x1.z; f[7] = x1.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = 0.f;
+      }
+      bf16x8_t h, l;
+      split_bf16x8(f, h, l);
+      *reinterpret_cast<bf16x8_t*>(sQ + q * QP + 8 * c) = h;
+      *reinterpret_cast<bf16x8_t*>(sQ + (QB + q) * QP + 8 * c) = l;
+    }
+    int lim[NQT];
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) {
+      const int qi = q0 + 16 * qt + j;
+      lim[qt] = qi < NQ ? L0 + qi / G : -1;
+    }
+    __syncthreads();
+    float m_run[NQT], l_run[NQT];
+    f32x4_t acc[ND][NQT];
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) {
+      m_run[qt] = -INFINITY;
+      l_run[qt] = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) acc[dt][qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    // this pass's queries as B operands, held in registers for the whole pass
+    bf16x8_t qH[NQT][NS], qL[NQT][NS];
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        qH[qt][st] = *reinterpret_cast<const bf16x8_t*>(sQ + (16 * qt + j) * QP + 32 * st + 8 * hq);
+        qL[qt][st] = *reinterpret_cast<const bf16x8_t*>(sQ + (QB + 16 * qt + j) * QP + 32 * st + 8 * hq);
+      }
+    // superslice loads, unconditional from clamped in-range addresses: key row 4 i + lane / 16
+    // (unit lane % 16); value channel row 8 i + lane / 8 (unit lane % 8 = 8 positions).  The next
+    // superslice is in flight in registers while one is multiplied.
+    uint4 rk[1][16], rv[1][16];
+    auto load = [&](int buf, int pw) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int p = min(pw + 4 * i + (lane >> 4), p_end - 1);
+        rk[buf][i] = ld16(Kb + (long)p * HD + 8 * (lane & 15));
+        const int d = 8 * i + (lane >> 3);
+        const int pv = min(pw + 8 * (lane & 7), (p_end - 1) & ~7);
+        rv[buf][i] = ld16(Vt + (long)d * a.max_len + pv);
+      }
+    };
+    // a buffer into the wave's tiles; value positions past the range become zero
+    auto store = [&](int buf, int pw) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = 4 * i + (lane >> 4), u = lane & 15;
+        *reinterpret_cast<uint4*>(tK + r * 256 + ((u ^ (r & 15)) << 4)) = rk[buf][i];
+        const int d = 8 * i + (lane >> 3), uv = lane & 7;
+        const int keep = p_end - (pw + 8 * uv);
+        uint4 v = rv[buf][i];
+        if (keep < 8) {
+          uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (e >= keep) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+          v = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+        *reinterpret_cast<uint4*>(tV + d * 128 + ((uv ^ vswz(d)) << 4)) = v;
+      }
+    };
+    auto compute = [&](int pw) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {  // 32-position halves
+        const int ph = pw + 32 * hh;
+        if (ph >= p_stop) break;
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt) {
+          f32x4_t sc[2];
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            sc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            const int r = 32 * hh + krow + 4 * t;
+#pragma unroll
+            for (int st = 0; st < NS; ++st) {
+              const int u = 4 * st + hq;
+              const bf16x8_t kop = *reinterpret_cast<const bf16x8_t*>(tK + r * 256 + ((u ^ (r & 15)) << 4));
+              sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qH[qt][st], sc[t], 0, 0, 0);
+              sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qL[qt][st], sc[t], 0, 0, 0);
+            }
+          }
+          float pe[8];
+          float mx = -INFINITY;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int p = ph + 8 * hq + e;
+            const float v = (p < p_end && p <= lim[qt]) ? sc[e >> 2][e & 3] * scale : -INFINITY;
+            pe[e] = v;
+            mx = fmaxf(mx, v);
+          }
+          mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+          mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+          const float m_new = fmaxf(m_run[qt], mx);
+          float alpha = 1.f, rs = 0.f;
+          if (m_new != -INFINITY) {
+            alpha = m_run[qt] == -INFINITY ? 0.f : expf(m_run[qt] - m_new);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              pe[e] = pe[e] == -INFINITY ? 0.f : expf(pe[e] - m_new);
+              rs += pe[e];
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pe[e] = 0.f;
+          }
+          rs += __shfl_xor(rs, 16, kWave);
+          rs += __shfl_xor(rs, 32, kWave);
+          l_run[qt] = l_run[qt] * alpha + rs;
+          m_run[qt] = m_new;
+          bf16x8_t pH, pL;
+          split_bf16x8(pe, pH, pL);
+#pragma unroll
+          for (int dt = 0; dt < ND; ++dt) {
+            acc[dt][qt] *= alpha;
+            const int d = 16 * dt + j, u = 4 * hh + hq;
+            const bf16x8_t vop = *reinterpret_cast<const bf16x8_t*>(tV + d * 128 + ((u ^ vswz(d)) << 4));
+            acc[dt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pH, acc[dt][qt], 0, 0, 0);
+            acc[dt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pL, acc[dt][qt], 0, 0, 0);
+          }
+        }
+      }
+    };
+    // wave w takes superslices w, w + 4, ... ; the load past the end re-reads the clamped last
+    // position (cached) and is not used, so every iteration issues the same loads
+    const int pw0 = p_beg + SP * wid;
+    load(0, pw0);
+    for (int pw = pw0; pw < p_stop; pw += 4 * SP) {
+      store(0, pw);
+      load(0, pw + 4 * SP);
+      compute(pw);
+    }
+    // merge the four waves: o = sum_w o_w e^{m_w - M}, l = sum_w l_w e^{m_w - M}
+    if (hq == 0) {
+#pragma unroll
+      for (int qt = 0; qt < NQT; ++qt) {
+        sm[wid][16 * qt + j] = m_run[qt];
+        sl[wid][16 * qt + j] = l_run[qt];
+      }
+    }
+    __syncthreads();
+    float cw[NQT];
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) {
+      const int q = 16 * qt + j;
+      const float M = fmaxf(fmaxf(sm[0][q], sm[1][q]), fmaxf(sm[2][q], sm[3][q]));
+      cw[qt] = m_run[qt] == -INFINITY ? 0.f : expf(m_run[qt] - M);
+    }
+    for (int w = 0; w < 4; ++w) {
+      if (wid == w) {
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+          for (int dt = 0; dt < ND; ++dt) {
+            float4* op = reinterpret_cast<float4*>(sO + (16 * qt + j) * OP + 16 * dt + 4 * hq);
+            const f32x4_t v = acc[dt][qt] * cw[qt];
+            if (w == 0) {
+              *op = make_float4(v[0], v[1], v[2], v[3]);
+            } else {
+              const float4 o = *op;
+              *op = make_float4(o.x + v[0], o.y + v[1], o.z + v[2], o.w + v[3]);
+            }
+          }
+      }
+      __syncthreads();
+    }
+    if (a.out) {  // the only split: normalise here and write the output rows (no combine pass)
+      for (int q = tid; q < QB; q += kWG) {
+        const float M = fmaxf(fmaxf(sm[0][q], sm[1][q]), fmaxf(sm[2][q], sm[3][q]));
+        float L = 0.f;
+        for (int w = 0; w < 4; ++w)
+          if (sm[w][q] != -INFINITY) L += sl[w][q] * expf(sm[w][q] - M);
+        sl[0][q] = L;
+      }
+      __syncthreads();
+      for (int idx = tid; idx < QB * HD; idx += kWG) {
+        const int q = idx / HD, d = idx - q * HD, qi = q0 + q;
+        if (qi < NQ) {
+          const int i = qi / G, g = qi - i * G;
+          a.out[(((long)b * a.rps + i) * a.nq + kvh * G + g) * HD + d] = sO[q * OP + d] / sl[0][q];
+        }
+      }
+    } else {
+      float* P = a.part + (((long)b * a.nkv + kvh) * a.nsplit + s) * (long)a.qstride * (HD + 2);
+      for (int idx = tid; idx < QB * HD; idx += kWG) {
+        const int q = idx / HD, d = idx - q * HD;
+        if (q0 + q < NQ) P[(long)(q0 + q) * (HD + 2) + d] = sO[q * OP + d];
+      }
+      for (int q = tid; q < QB; q += kWG) {
+        if (q0 + q < NQ) {
+          const float M = fmaxf(fmaxf(sm[0][q], sm[1][q]), fmaxf(sm[2][q], sm[3][q]));
+          float L = 0.f;
+          for (int w = 0; w < 4; ++w)
+            if (sm[w][q] != -INFINITY) L += sl[w][q] * expf(sm[w][q] - M);
+          P[(long)(q0 + q) * (HD + 2) + HD] = M;
+          P[(long)(q0 + q) * (HD + 2) + HD + 1] = L;
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // Merge the split partials of one (row, query head): o = sum_s o_s e^{m_s - M} / sum_s l_s e^{m_s - M}.
 // kWG / HD thread groups take every (kWG / HD)-th split, summed in LDS at the end.
 template <int HD>
@@ -514,6 +786,17 @@ void launch_attention(AttnArgs a, int wdtype, float* out, hipStream_t st) {
   if (wdtype == MTP_BF16) {
     if (a.nsplit == 1) a.out = out;
     const double kv_bytes = 4.0 * a.B * a.nkv * (double)a.max_len * HD;
+    if constexpr (HD == 128) {
+      // a batch whose (sequence, kv head) pairs fill the GPU on their own, over a long cache:
+      // the LDS-staged kernel (one wave per SIMD, registers free for the prefetch)
+      // (one 16-query tile per pass: with two the kernel's registers overflow)
+      if (a.B * a.nkv >= 128 && a.max_len >= 1024 && a.qstride <= 16) {
+        dim3 grid(a.nsplit, a.nkv * attn_qgroups(a, 16), a.B);
+        hipLaunchKernelGGL((k_attn_lds<1>), grid, dim3(kWG), 0, st, a);
+        if (!a.out) hipLaunchKernelGGL((k_attn_combine<HD>), dim3(a.B * a.rps * a.nq), dim3(kWG), 0, st, a, out);
+        return;
+      }
+    }
     if (a.qstride <= 16 || kv_bytes < 64.0 * 1024 * 1024) {
       dim3 grid(a.nsplit, a.nkv * attn_qgroups(a, 16), a.B);
       hipLaunchKernelGGL((k_attn_mfma<HD, 1>), grid, dim3(kWG), 0, st, a);
