@@ -96,7 +96,9 @@ typedef struct {
 
 /* Verification settings.  temperature <= 0 selects greedy verification.  Otherwise
  * temperature, top-k and top-p are applied in that order ([DLM "Why a hand-written decoding
- * loop"]); top_k must be in [1, 128] on this device path; top_p >= 1 disables top-p.
+ * loop"]); top_k <= 0 (or >= vocab) disables top-k, top_p >= 1 disables top-p.  top_k in
+ * [1, 128] runs on a per-row candidate buffer; top-k off or larger runs over the whole
+ * vocabulary (a radix search of each row's kept set: slower, for settings without a small k).
  * q_mode 0: the drafts are greedy, so the draft distribution is one-hot at the draft;
  * q_mode 1: the draft distribution is the same warp of draft_logits and the drafts were
  * sampled from it. */

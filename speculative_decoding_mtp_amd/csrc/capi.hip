@@ -243,7 +243,15 @@ int verify_setup(int32_t B, int32_t D, int32_t V, const float* target_logits, co
   size_t o = 256;
   const int rows = B * (D + 1) + (!a.greedy && sp->q_mode == 1 ? B * D : 0);
   if (a.greedy) {
-    int target = (1024 + rows - 1) / rows;
+    // Early exit: when the logits run to hundreds of MB the scan is bound by bytes, and each
+    // workgroup walks its chunk of a sequence's rows in order, stopping where the sequence must
+    // (about 1024 workgroups over the sequences); below that, latency decides, and every row is
+    // scanned at once (about 1024 workgroups over the rows).  Chunks of at least 1024 logits, at
+    // most 1024 chunks.
+    a.walk = (double)rows * V * 4.0 >= 256.0 * 1024 * 1024;
+    const int over = a.walk ? B : rows;
+    int target = (1024 + over - 1) / over;
+    if (target > 1024) target = 1024;
     int chunk = (V + target - 1) / target;
     chunk = (chunk + 1023) & ~1023;
     a.chunk = chunk;
@@ -254,7 +262,6 @@ int verify_setup(int32_t B, int32_t D, int32_t V, const float* target_logits, co
     o += up256((size_t)rows * a.nchunk * 4);
   } else {
     if (sp->q_mode != 0 && sp->q_mode != 1) return fail(MTP_ERR_ARG, "q_mode must be 0 or 1");
-    if (sp->top_k < 1 || sp->top_k > kMaxTopK) return fail(MTP_ERR_ARG, "top_k must be in [1, %d]", kMaxTopK);
     if (sp->q_mode == 1 && (!draft_logits || !aligned16(draft_logits)))
       return fail(MTP_ERR_ARG, "q_mode 1 needs draft_logits");
     if (!u_accept || !u_sample) return fail(MTP_ERR_ARG, "sampling needs u_accept and u_sample");
@@ -266,6 +273,14 @@ int verify_setup(int32_t B, int32_t D, int32_t V, const float* target_logits, co
     a.dl = draft_logits;
     a.u_accept = u_accept;
     a.u_sample = u_sample;
+    a.full = K < 1 || K > kMaxTopK;
+    if (a.full) {  // top-k off, or more than the candidate buffer holds: the whole vocabulary
+      a.rowinfo = reinterpret_cast<FullRow*>(base + o);
+      o += up256((size_t)rows * sizeof(FullRow));
+      *out = a;
+      *used = o;
+      return MTP_OK;
+    }
     a.top_v = reinterpret_cast<float*>(base + o);
     o += up256((size_t)rows * K * 4);
     a.top_i = reinterpret_cast<int*>(base + o);
@@ -585,9 +600,10 @@ int spec_verify_workspace_size(int32_t B, int32_t D, int32_t V, const mtp_sampli
   if (greedy) {
     const size_t nchunk = 1024;  // upper bound of the chunk count chosen at launch
     t += 2 * up256(rows * nchunk * 4);
+  } else if (sp->top_k < 1 || sp->top_k > kMaxTopK) {  // the whole vocabulary
+    t += up256(rows * sizeof(FullRow));
   } else {
     const int K = sp->top_k;
-    if (K < 1 || K > kMaxTopK) return fail(MTP_ERR_ARG, "top_k must be in [1, %d]", kMaxTopK);
     t += 2 * up256(rows * K * 4) + up256(rows * 4);
     int nch = 1, chunk = V;
     topk_split((int)rows, V, &nch, &chunk);

@@ -1,25 +1,15 @@
-// GEMMs on bf16 MFMA for draft steps with many activation rows (a batch of sequences, a
-// prefill).
+// MFMA GEMMs for draft steps with many activation rows (a batch of sequences, a prefill):
 //
 //   y[row][m] = sum_k W[m][k] * x[row][k],   W bf16 [N][K], x fp32 (after the policy's norm)
 //
-// k_prep and the skinny k_gemm_mfma below (k_gemm_tile, further down, takes calls with hundreds
-// of rows):
 // * k_prep: one workgroup per activation row; the policy's prologue (raw loads, RMSNorm, gains)
 //   gives the fp32 row, which is written as two bf16 rows hi = bf16(x), lo = bf16(x - hi)
 //   (x = hi + lo to about 2^-17 relative), compacted over the valid rows.  rowmap / amap record
 //   each compact row's padded row and activation index; `count` the number of compact rows.
-// * k_gemm_mfma: each workgroup owns 4 waves x NT tiles of 16 weight rows and a range of K
-//   (the whole of K, or one of `ksplit` ranges when there are few row groups), walked in
-//   chunks of 128.  Per chunk the workgroup stages the compact activations (hi and lo, up to MG
-//   tiles of 16 rows) in LDS, and every wave streams its weight rows once from HBM, the next
-//   chunk's weights in flight while this one is multiplied.  In step s of a chunk, lane l holds
-//   columns 32 s + 8 (l / 16) .. +7 of row l % 16, so the four lanes of a row read 64
-//   contiguous bytes per load.  v_mfma_f32_16x16x32_bf16 consumes the chunk in four steps; the
-//   activations are read with the same column order, so the dot products are unchanged.  Two
-//   MFMAs (hi, lo) per step keep fp32-like accuracy.  Rows beyond MG tiles are handled in
-//   further passes.  With K split, raw partial sums go to a buffer and k_splitk_reduce adds
-//   them in range order and applies the policy's store.
+//   Those compact rows feed the weight-streaming GEMM (stream_gemm.h) and, for calls with
+//   hundreds of rows, k_gemm_tile below.
+// * k_gemm_tile: 128 x 128 output tiles with both operands staged in LDS (a prefill).
+// * k_splitk_reduce: sums split-K partials in range order and applies the policy's store.
 // Operand layout of v_mfma_f32_16x16x32_bf16 (checked on the device): lane l supplies
 // A[l % 16][8 (l / 16) + e] and B[8 (l / 16) + e][l % 16], e < 8; result r of lane l is
 // D[4 (l / 16) + r][l % 16].
@@ -31,8 +21,7 @@
 
 namespace mtp {
 
-constexpr int kMfmaKC = 128;          // K per LDS chunk
-constexpr int kMfmaLdr = kMfmaKC + 8; // padded LDS row (bf16 elements)
+constexpr int kMfmaKC = 128;  // MFMA paths take K in whole 128-column chunks
 
 struct MfmaBufs {
   uint16_t *xhi, *xlo;  // [cap][K] compact split activations
@@ -163,242 +152,9 @@ __global__ __launch_bounds__(kWG) void k_prep(P p, MfmaBufs mb) {
   }
 }
 
-// NT weight-row tiles (16 rows each) per wave, MG activation tiles (16 compact rows) per pass.
-template <class P, int NT, int MG>
-__global__ __launch_bounds__(kWG, MG <= 4 ? 2 : 1) void k_gemm_mfma(P p, MfmaBufs mb) {
-  using T = uint16_t;
-  constexpr int WR = NT * 16;          // weight rows per wave
-  constexpr int WL = WR / 4;           // weight loads per lane and chunk (four rows per load)
-  constexpr bool DB = MG <= 2;         // double-buffered activation staging
-  constexpr bool RP = MG >= 4;         // single buffer, next chunk's activations held in registers
-  constexpr int NB = DB ? 2 : 1;
-  constexpr int AV = 2 * MG * 16 * (kMfmaKC / 8);  // 16-byte activation vectors per chunk (hi + lo)
-  constexpr int PER = (AV + kWG - 1) / kWG;
-  __shared__ __align__(16) uint16_t sA[NB][2][MG * 16 * kMfmaLdr];  // [buffer][hi/lo][row][k]
-  __shared__ __align__(16) uint16_t sW[4][WR * kMfmaLdr];            // each wave's weight tile
-  __shared__ int s_n[kMaxBatch];
-  __shared__ int s_len[kMaxBatch];
-  __shared__ float s_bv[4 * MG * 16];
-  __shared__ int s_bi[4 * MG * 16];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int jl = lane & 15, hq = lane >> 4;  // column of the tile, quarter of the wave
-  uint16_t* myW = sW[wid];
-  p.setup(s_n, s_len);
-  const int count = *mb.count;
-  __syncthreads();
-  const int Kc = p.K / kMfmaKC;  // K is a multiple of 128 on this path
-  const int rows_per_wg = 4 * WR;
-  const int ngroups = (p.N + rows_per_wg - 1) / rows_per_wg;
-  const int ks = mb.part ? mb.ksplit : 1;           // K ranges per row group
-  const int kper = (Kc + ks - 1) / ks;
-
-  const int npass = (count + MG * 16 - 1) / (MG * 16);  // passes of MG activation tiles
-  const int per_pass = ngroups * ks;
-  // lm_head (argmax) walks the passes in order (each workgroup's running bests are flushed per
-  // pass); the other policies spread their (pass, row group, K range) items over the grid
-  const int outer = P::kArgmax ? npass : (npass > 0 ? 1 : 0);
-  for (int op = 0; op < outer; ++op) {
-   const int n_items = P::kArgmax ? per_pass : npass * per_pass;
-   for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
-    const int pass = P::kArgmax ? op : it / per_pass;
-    const int gk = P::kArgmax ? it : it - pass * per_pass;
-    const int mg0 = pass * MG * 16;
-    const int mrows = min(MG * 16, count - mg0);
-    const int mt = (mrows + 15) / 16;
-    const int srows = mt * 16;                        // staged rows (zero past mrows)
-    const int nav = 2 * srows * (kMfmaKC / 8);        // staged vectors per chunk
-    uint4 st[PER];
-    // the pass's activations of chunk kc: vector idx -> (hi/lo, row, 8-column group)
-    auto aload = [&](int kc) {
-#pragma unroll
-      for (int v = 0; v < PER; ++v) {
-        const int idx = tid + kWG * v;
-        const int half = idx / (srows * (kMfmaKC / 8)), rem = idx - half * (srows * (kMfmaKC / 8));
-        const int r = rem / (kMfmaKC / 8), cv = rem - r * (kMfmaKC / 8);
-        st[v] = (idx < nav && r < mrows)
-                    ? ld16((half ? mb.xlo : mb.xhi) + (long)(mg0 + r) * p.K + kc * kMfmaKC + cv * 8)
-                    : make_uint4(0, 0, 0, 0);
-      }
-    };
-    auto astore = [&](int buf) {
-#pragma unroll
-      for (int v = 0; v < PER; ++v) {
-        const int idx = tid + kWG * v;
-        const int half = idx / (srows * (kMfmaKC / 8)), rem = idx - half * (srows * (kMfmaKC / 8));
-        const int r = rem / (kMfmaKC / 8), cv = rem - r * (kMfmaKC / 8);
-        if (idx < nav) *reinterpret_cast<uint4*>(&sA[buf][half][r * kMfmaLdr + cv * 8]) = st[v];
-      }
-    };
-    {
-      const int g = gk / ks, kpart = gk - g * ks;
-      const int kc_beg = kpart * kper, kc_end = min(Kc, kc_beg + kper);
-      const int n0 = g * rows_per_wg + wid * WR;
-      f32x4_t acc[MG][NT];
-#pragma unroll
-      for (int m = 0; m < MG; ++m)
-#pragma unroll
-        for (int t = 0; t < NT; ++t) acc[m][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      // Weights are read row-contiguous: load i of a lane takes 16 bytes at column 8 (l % 16) of
-      // the wave's row 4 i + l / 16, so sixteen lanes read 256 contiguous bytes of one row.  The
-      // wave moves them through its own LDS tile into the MFMA operand layout.
-      const T* wrow[WL];
-#pragma unroll
-      for (int i = 0; i < WL; ++i) wrow[i] = p.wrow(min(n0 + 4 * i + hq, p.N - 1)) + 8 * jl;
-      uint4 wn[WL];
-      auto wload = [&](int kc) {
-#pragma unroll
-        for (int i = 0; i < WL; ++i) wn[i] = ld_stream(wrow[i] + kc * kMfmaKC);
-      };
-      if (kc_beg < kc_end) {
-        __syncthreads();  // the previous item's readers are done with the staging buffers
-        wload(kc_beg);
-        aload(kc_beg);
-        astore(0);
-        __syncthreads();
-      }
-      for (int kc = kc_beg; kc < kc_end; ++kc) {
-        const int buf = DB ? ((kc - kc_beg) & 1) : 0;
-#pragma unroll
-        for (int i = 0; i < WL; ++i)  // this chunk's weights into the wave's tile
-          *reinterpret_cast<uint4*>(&myW[(4 * i + hq) * kMfmaLdr + 8 * jl]) = wn[i];
-        if (!DB && !RP && kc > kc_beg) {  // single buffer: stage this chunk now
-          __syncthreads();
-          aload(kc);
-          astore(0);
-          __syncthreads();
-        }
-        if (kc + 1 < kc_end) {  // the next chunk in flight while this one is multiplied
-          wload(kc + 1);
-          if (DB || RP) aload(kc + 1);
-        }
-#pragma unroll
-        for (int m = 0; m < MG; ++m) {
-          if (m < mt) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-              const int kk = 32 * s + 8 * hq;
-              const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(&sA[buf][0][(m * 16 + jl) * kMfmaLdr + kk]);
-              const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(&sA[buf][1][(m * 16 + jl) * kMfmaLdr + kk]);
-#pragma unroll
-              for (int t = 0; t < NT; ++t) {
-                const bf16x8_t bw = *reinterpret_cast<const bf16x8_t*>(&myW[(t * 16 + jl) * kMfmaLdr + kk]);
-                acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bw, acc[m][t], 0, 0, 0);
-                acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bw, acc[m][t], 0, 0, 0);
-              }
-            }
-          }
-        }
-        if (DB) {
-          if (kc + 1 < kc_end) astore(buf ^ 1);
-          __syncthreads();
-        } else if (RP && kc + 1 < kc_end) {
-          __syncthreads();  // every wave is done with this chunk's activations
-          astore(0);
-          __syncthreads();
-        }
-      }
-      if (mb.part) {  // split-K: raw partial sums, reduced and stored by k_splitk_reduce
-#pragma unroll
-        for (int m = 0; m < MG; ++m) {
-          if (m >= mt) continue;
-#pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            const int col = n0 + t * 16 + jl;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int cr = mg0 + m * 16 + 4 * hq + r;
-              if (cr < count && col < p.N) mb.part[((long)kpart * mb.cap + cr) * p.N + col] = acc[m][t][r];
-            }
-          }
-        }
-        continue;
-      }
-      // epilogue: lane holds rows 4 hq + r of each activation tile, column jl of each weight tile
-#pragma unroll
-      for (int m = 0; m < MG; ++m) {
-        if (m >= mt) continue;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const int col = n0 + t * 16 + jl;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int cr = mg0 + m * 16 + 4 * hq + r;
-            const float v = acc[m][t][r];
-            const float partner = __shfl_xor(v, 1, kWave);
-            if (cr < count && col < p.N) {
-              const int row = mb.rowmap[cr], a = mb.amap[cr];
-              if constexpr (P::kPair) {
-                if ((jl & 1) == 0) p.store_pair(col, a, row, v, partner);
-              } else {
-                p.store(col, a, row, v);
-              }
-            }
-          }
-        }
-      }
-      if constexpr (P::kArgmax) {
-        // running best per compact row over this group's columns, lowest id on ties
-#pragma unroll
-        for (int m = 0; m < MG; ++m) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float bv = -INFINITY;
-            int bi = 0x7fffffff;
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-              const int col = n0 + t * 16 + jl;
-              if (m < mt && col < p.N && better(acc[m][t][r], col, bv, bi)) {
-                bv = acc[m][t][r];
-                bi = col;
-              }
-            }
-#pragma unroll
-            for (int o = 8; o > 0; o >>= 1) {  // over the 16 lanes of this quarter
-              const float ov = __shfl_xor(bv, o, kWave);
-              const int oi = __shfl_xor(bi, o, kWave);
-              if (better(ov, oi, bv, bi)) {
-                bv = ov;
-                bi = oi;
-              }
-            }
-            const int k = m * 16 + 4 * hq + r;
-            if (jl == 0) {
-              if (gk == (int)blockIdx.x) {
-                s_bv[wid * MG * 16 + k] = bv;
-                s_bi[wid * MG * 16 + k] = bi;
-              } else if (better(bv, bi, s_bv[wid * MG * 16 + k], s_bi[wid * MG * 16 + k])) {
-                s_bv[wid * MG * 16 + k] = bv;
-                s_bi[wid * MG * 16 + k] = bi;
-              }
-            }
-          }
-        }
-      }
-    }
-   }
-    if constexpr (P::kArgmax) {
-      const int mg0 = op * MG * 16, mrows = min(MG * 16, count - mg0);
-      __syncthreads();
-      for (int k = tid; k < mrows; k += kWG) {
-        float v = -INFINITY;
-        int i = 0x7fffffff;
-        if ((int)blockIdx.x < ngroups * ks)
-          for (int w = 0; w < 4; ++w)
-            if (better(s_bv[w * MG * 16 + k], s_bi[w * MG * 16 + k], v, i)) {
-              v = s_bv[w * MG * 16 + k];
-              i = s_bi[w * MG * 16 + k];
-            }
-        p.partial(mb.amap[mg0 + k], v, i);
-      }
-      __syncthreads();
-    }
-  }
-  p.finish(s_n);
-}
-
 // ---------------------------------------------------------------------------------------------
-// Large tiles for calls with hundreds of activation rows (a prefill).  The skinny kernel above
-// streams the whole weight matrix once per 64-row pass; here each workgroup owns a 128
+// Large tiles for calls with hundreds of activation rows (a prefill).  The streaming kernel
+// (stream_gemm.h) reads the whole weight matrix once per 64-row pass; here each workgroup owns a 128
 // (compact activation rows) x 128 (weight rows) output tile and walks K in 32-column chunks
 // with both operands staged in LDS (double-buffered, one barrier per chunk, two chunks in
 // flight from memory), so the weights of

@@ -22,6 +22,7 @@ struct VerifyArgs {
   const int32_t* ctx_len;
   int32_t *n_accept, *out, *crop;
   int nchunk, chunk;
+  int walk;  // greedy: 1 = each workgroup walks its chunk of a sequence's rows in order (early exit)
   // greedy scratch
   float* part_v;
   int* part_i;
@@ -33,6 +34,21 @@ struct VerifyArgs {
   int tk_nchunk, tk_chunk;
   float* cand_v;  // [rows][tk_nchunk][top_k]
   int* cand_i;
+  // the whole vocabulary (top-k off, or larger than the candidate buffer): each row's kept set
+  int full;
+  struct FullRow* rowinfo;  // [rows]
+};
+
+// The kept set of one row under the whole-vocabulary warp: tokens ranked by (logit desc, id asc)
+// up to and including the boundary (key, id), where key is the order-preserving bit pattern of
+// the logit; weights are exp((l - lmax) / T) in fixed point (2^-40), zk their sum over the set.
+struct FullRow {
+  float lmax;
+  uint32_t key;
+  int id;
+  int pad;
+  unsigned long long zk;
+  unsigned long long pad2;
 };
 
 // Chunks of the sampling top-k pass: calls with fewer than 128 rows split each row into chunks

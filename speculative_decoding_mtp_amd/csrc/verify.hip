@@ -41,45 +41,97 @@ __device__ __forceinline__ void wg_argmax(float& v, int& i, float* sv, int* si) 
 // ---------------------------------------------------------------------------------------------
 // greedy
 // ---------------------------------------------------------------------------------------------
+// One workgroup per (chunk, sequence) takes the chunk's argmax of the sequence's rows 0, 1, ... in
+// order.  Greedy verification stops at the first row whose argmax is not the draft it judges
+// ([YL 三 stage 3]), so no row after that one is needed: once this chunk holds an element ranked
+// above row j's draft (value desc, id asc), the draft cannot be row j's argmax, the sequence stops
+// at row j or before, and the workgroup skips the later rows.  Every row the decision needs (each
+// row up to the first mismatch) is therefore scanned by every chunk.
+// Each draft's own target logit is loaded up front, and while row j is reduced the next row's
+// slice is already in flight (slices of at most 4096 logits, up to four float4 per thread), so a
+// row costs one memory latency only when its predecessor was needed.
+__device__ __forceinline__ void chunk_best4(const uint4 u, int k, int end, float& bv, int& bi) {
+  const float f[4] = {__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w)};
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (k + e < end && better(f[e], k + e, bv, bi)) {
+      bv = f[e];
+      bi = k + e;
+    }
+}
+
 __global__ __launch_bounds__(kWG) void k_verify_greedy(VerifyArgs a) {
   __shared__ float sv[4];
   __shared__ int si[4];
-  const int c = blockIdx.x, row = blockIdx.y;
-  const float* x = a.tl + (long)row * a.V;
+  __shared__ float s_vd[kMaxDraft];
+  __shared__ int s_d[kMaxDraft];
+  const int c = blockIdx.x, R = a.D + 1;
   const int beg = c * a.chunk, end = min(a.V, beg + a.chunk);
-  float bv = -INFINITY;
-  int bi = 0x7fffffff;
-  if ((a.V & 3) == 0) {
-    for (int k = beg + 4 * threadIdx.x; k < end; k += 4 * kWG) {
-      const uint4 u = ld_stream(x + k);
-      const float f[4] = {__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w)};
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (better(f[e], k + e, bv, bi)) {
-          bv = f[e];
-          bi = k + e;
-        }
-    }
-  } else {
-    for (int k = beg + threadIdx.x; k < end; k += kWG)
-      if (better(x[k], k, bv, bi)) {
-        bv = x[k];
-        bi = k;
-      }
+  // without the walk (small calls, where latency rather than bytes decides) every workgroup
+  // takes one row, blockIdx.y = b * (D + 1) + j, and no row is skipped
+  const int b = a.walk ? blockIdx.y : blockIdx.y / R;
+  const int j0 = a.walk ? 0 : blockIdx.y - b * R, j1 = a.walk ? R : j0 + 1;
+  for (int t = threadIdx.x; t < a.D && a.walk; t += kWG) {
+    const int d = a.drafts[(long)b * a.D + t];
+    const bool ok = d >= 0 && d < a.V;
+    s_d[t] = ok ? d : -1;
+    s_vd[t] = ok ? a.tl[((long)b * R + t) * a.V + d] : 0.f;
   }
-  wg_argmax(bv, bi, sv, si);
-  if (threadIdx.x == 0) {
-    a.part_v[(long)row * a.nchunk + c] = bv;
-    a.part_i[(long)row * a.nchunk + c] = bi;
+  // slices of up to 4096 logits: up to four float4 per thread, the next row's held in registers
+  const bool pipelined = (a.V & 3) == 0 && end - beg <= 16 * kWG;
+  const int nsw = (end - beg + 4 * kWG - 1) / (4 * kWG);
+  const int k4 = beg + 4 * threadIdx.x;
+  uint4 cur[4], nxt[4];
+  auto load_row = [&](long row, uint4 (&r)[4]) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      if (s < nsw) r[s] = ld_stream(a.tl + row * a.V + min(k4 + 4 * kWG * s, (end - 1) & ~3));
+  };
+  if (pipelined) load_row((long)b * R + j0, cur);
+  __syncthreads();
+  for (int j = j0; j < j1; ++j) {
+    const long row = (long)b * R + j;
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    if (pipelined) {
+      if (j + 1 < j1) load_row(row + 1, nxt);  // the next row in flight
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        if (s < nsw) chunk_best4(cur[s], k4 + 4 * kWG * s, end, bv, bi);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) cur[s] = nxt[s];
+    } else {
+      const float* x = a.tl + row * a.V;
+      if ((a.V & 3) == 0) {
+        for (int k = k4; k < end; k += 4 * kWG) chunk_best4(ld_stream(x + k), k, end, bv, bi);
+      } else {
+        for (int k = beg + threadIdx.x; k < end; k += kWG)
+          if (better(x[k], k, bv, bi)) {
+            bv = x[k];
+            bi = k;
+          }
+      }
+    }
+    wg_argmax(bv, bi, sv, si);  // every thread holds the chunk's argmax
+    if (threadIdx.x == 0) {
+      a.part_v[row * a.nchunk + c] = bv;
+      a.part_i[row * a.nchunk + c] = bi;
+    }
+    if (!a.walk || j == a.D) break;
+    const int d = s_d[j];
+    if (d < 0) break;                           // no valid draft: the sequence stops here
+    if (better(bv, bi, s_vd[j], d)) break;      // ranked above the draft: row j rejects it
   }
 }
 
-// one workgroup per sequence: argmax of each of its D+1 rows, then the prefix match
+// one workgroup per sequence: the argmax of rows 0, 1, ... from the chunk partials, up to the
+// first row whose argmax differs from its draft; then the emitted tokens and lengths
 __global__ __launch_bounds__(kWG) void k_verify_greedy_final(VerifyArgs a) {
   __shared__ float sv[4];
   __shared__ int si[4];
-  __shared__ int st[kMaxDraft + 1];
   const int b = blockIdx.x, rows_per_seq = a.D + 1;
+  const int* d = a.drafts + (long)b * a.D;
+  int n = 0, last = 0;
   for (int j = 0; j < rows_per_seq; ++j) {
     const long row = (long)b * rows_per_seq + j;
     float bv = -INFINITY;
@@ -92,16 +144,15 @@ __global__ __launch_bounds__(kWG) void k_verify_greedy_final(VerifyArgs a) {
         bi = i;
       }
     }
-    wg_argmax(bv, bi, sv, si);
-    if (threadIdx.x == 0) st[j] = bi;
+    wg_argmax(bv, bi, sv, si);  // uniform
+    last = bi;
+    if (j == a.D || bi != d[j]) break;
+    n = j + 1;
   }
   if (threadIdx.x == 0) {
-    const int* d = a.drafts + (long)b * a.D;
-    int n = 0;
-    while (n < a.D && st[n] == d[n]) ++n;
     int32_t* out = a.out + (long)b * rows_per_seq;
     for (int j = 0; j < n; ++j) out[j] = d[j];
-    out[n] = st[n];
+    out[n] = last;
     for (int j = n + 1; j < rows_per_seq; ++j) out[j] = -1;
     a.n_accept[b] = n;
     a.crop[b] = a.ctx_len[b] + 1 + n;
@@ -579,10 +630,327 @@ __global__ __launch_bounds__(64) void k_sample_decide(VerifyArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// sampling over the whole vocabulary: top-k off (or above the candidate buffer), top-p on the rest
+// ---------------------------------------------------------------------------------------------
+// [DLM "Why a hand-written decoding loop"]: temperature, then top-k, then top-p, in that order.
+// The kept set of a row is a prefix of the tokens ranked by (logit desc, id asc) -- the same
+// ranking as scaled logits, since T > 0 -- so it is described by its last member.  One workgroup
+// per row finds it by radix selection over order-preserving 32-bit keys of the logits, 8 bits per
+// pass: by count for the k-th token, by weight for the token whose inclusive mass first reaches
+// p times the mass of the top-k set (the token that crosses p is kept).  Equal keys are taken in
+// ascending id order with a scan over the row.  Weights exp((l - lmax) / T) are summed as 2^-40
+// fixed-point integers, so every sum (and every decision) is the same from run to run.
+constexpr double kFix = 1099511627776.0;  // 2^40
+
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f == 0.f ? 0.f : f);  // -0 ranks with +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ unsigned long long fix_weight(float l, float lmax, float T) {
+  return (unsigned long long)((double)expf((l - lmax) / T) * kFix + 0.5);
+}
+// rank order: token i is ranked at or before the boundary (key, id)
+__device__ __forceinline__ bool kept_by(uint32_t k, int i, uint32_t bk, int bi) {
+  return k > bk || (k == bk && i <= bi);
+}
+
+// Block-wide exclusive scan of one 64-bit value per thread (256 threads); returns the thread's
+// exclusive prefix, *total the sum.  s64: __shared__ unsigned long long[kWG].
+__device__ unsigned long long scan_u64(unsigned long long v, unsigned long long* s64, unsigned long long* total) {
+  const int tid = threadIdx.x;
+  s64[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < kWG; off <<= 1) {
+    const unsigned long long add = tid >= off ? s64[tid - off] : 0ull;
+    __syncthreads();
+    s64[tid] += add;
+    __syncthreads();
+  }
+  const unsigned long long incl = s64[tid];
+  *total = s64[kWG - 1];
+  __syncthreads();
+  return incl - v;
+}
+
+struct FullSmem {
+  unsigned long long hist[256];
+  unsigned long long s64[kWG];
+  float red[4];
+  int pick, pick_id;
+  unsigned long long pick_above;
+};
+
+// The row's search.  Each thread walks a contiguous id segment [seg0, seg1) wherever the order of
+// ids matters (the tie scans), and strided elements elsewhere.
+__global__ __launch_bounds__(kWG) void k_full_select(VerifyArgs a) {
+  __shared__ FullSmem sm;
+  const int row = blockIdx.x, tid = threadIdx.x, V = a.V;
+  const float T = a.temperature;
+  const int tgt_rows = a.B * (a.D + 1);
+  const float* x = row < tgt_rows ? a.tl + (long)row * V : a.dl + (long)(row - tgt_rows) * V;
+  const int seg = (V + kWG - 1) / kWG, seg0 = min(V, tid * seg), seg1 = min(V, seg0 + seg);
+  // the row maximum
+  float mx = -INFINITY;
+  for (int i = tid; i < V; i += kWG) mx = fmaxf(mx, x[i]);
+  mx = wave_max(mx);
+  if ((tid & 63) == 0) sm.red[tid >> 6] = mx;
+  __syncthreads();
+  const float lmax = fmaxf(fmaxf(sm.red[0], sm.red[1]), fmaxf(sm.red[2], sm.red[3]));
+  __syncthreads();
+  // top-k boundary: the k-th token in rank order (none when top-k is off)
+  uint32_t tk = 0;
+  int ik = 0x7fffffff;
+  const bool use_k = a.top_k > 0 && a.top_k < V;
+  if (use_k) {
+    uint32_t prefix = 0, mask = 0;
+    unsigned long long need = (unsigned long long)a.top_k;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      sm.hist[tid] = 0;
+      __syncthreads();
+      for (int i = tid; i < V; i += kWG) {
+        const uint32_t k = order_key(x[i]);
+        if ((k & mask) == prefix) atomicAdd(&sm.hist[(k >> shift) & 255], 1ull);
+      }
+      __syncthreads();
+      if (tid == 0) {
+        unsigned long long cum = 0;
+        int d = 255;
+        for (; d > 0; --d) {
+          if (cum + sm.hist[d] >= need) break;
+          cum += sm.hist[d];
+        }
+        sm.pick = d;
+        sm.pick_above = cum;
+      }
+      __syncthreads();
+      need -= sm.pick_above;
+      prefix |= (uint32_t)sm.pick << shift;
+      mask |= 255u << shift;
+      __syncthreads();
+    }
+    tk = prefix;
+    // the need-th lowest id among the tokens whose key is tk
+    unsigned long long c = 0;
+    for (int i = seg0; i < seg1; ++i) c += order_key(x[i]) == tk ? 1ull : 0ull;
+    unsigned long long tot;
+    const unsigned long long before = scan_u64(c, sm.s64, &tot);
+    if (before < need && need <= before + c) {
+      unsigned long long cnt = before;
+      for (int i = seg0; i < seg1; ++i)
+        if (order_key(x[i]) == tk && ++cnt == need) {
+          sm.pick_id = i;
+          break;
+        }
+    }
+    __syncthreads();
+    ik = sm.pick_id;
+    __syncthreads();
+  }
+  // the top-k set's weight
+  unsigned long long z = 0;
+  for (int i = tid; i < V; i += kWG)
+    if (!use_k || kept_by(order_key(x[i]), i, tk, ik)) z += fix_weight(x[i], lmax, T);
+  unsigned long long zk;
+  (void)scan_u64(z, sm.s64, &zk);
+  uint32_t bk = tk;
+  int bi = ik;
+  unsigned long long zkept = zk;
+  if (a.top_p < 1.f) {
+    // top-p boundary inside the top-k set: the token whose inclusive mass first reaches p * zk
+    const double target = (double)a.top_p * (double)zk;
+    uint32_t prefix = 0, mask = 0;
+    unsigned long long above = 0;
+    bool crossed = true;
+    for (int shift = 24; shift >= 0 && crossed; shift -= 8) {
+      sm.hist[tid] = 0;
+      __syncthreads();
+      for (int i = tid; i < V; i += kWG) {
+        const uint32_t k = order_key(x[i]);
+        if ((k & mask) == prefix && (!use_k || kept_by(k, i, tk, ik)))
+          atomicAdd(&sm.hist[(k >> shift) & 255], fix_weight(x[i], lmax, T));
+      }
+      __syncthreads();
+      if (tid == 0) {
+        unsigned long long cum = above;
+        int d = 255;
+        for (; d >= 0; --d) {
+          if ((double)(cum + sm.hist[d]) >= target) break;
+          cum += sm.hist[d];
+        }
+        sm.pick = d;
+        sm.pick_above = cum;
+      }
+      __syncthreads();
+      if (sm.pick < 0) {
+        crossed = false;  // rounding left the whole set below p: keep all of it
+      } else {
+        above = sm.pick_above;
+        prefix |= (uint32_t)sm.pick << shift;
+        mask |= 255u << shift;
+      }
+      __syncthreads();
+    }
+    if (crossed) {
+      // among the tokens with key == prefix (inside the top-k set), ascending ids until the
+      // inclusive mass reaches the target
+      unsigned long long c = 0;
+      for (int i = seg0; i < seg1; ++i) {
+        const uint32_t k = order_key(x[i]);
+        if (k == prefix && (!use_k || kept_by(k, i, tk, ik))) c += fix_weight(x[i], lmax, T);
+      }
+      unsigned long long tot;
+      const unsigned long long before = scan_u64(c, sm.s64, &tot);
+      if ((double)(above + before) < target && (double)(above + before + c) >= target) {
+        unsigned long long cum = above + before;
+        for (int i = seg0; i < seg1; ++i) {
+          const uint32_t k = order_key(x[i]);
+          if (k == prefix && (!use_k || kept_by(k, i, tk, ik))) {
+            cum += fix_weight(x[i], lmax, T);
+            if ((double)cum >= target) {
+              sm.pick_id = i;
+              sm.pick_above = cum;
+              break;
+            }
+          }
+        }
+      }
+      __syncthreads();
+      bk = prefix;
+      bi = sm.pick_id;
+      zkept = sm.pick_above;
+    }
+  }
+  if (tid == 0) {
+    FullRow f;
+    f.lmax = lmax;
+    f.key = bk;
+    f.id = bi;
+    f.pad = 0;
+    f.zk = zkept;
+    f.pad2 = 0;
+    a.rowinfo[row] = f;
+  }
+}
+
+// One workgroup per sequence: the decisions of k_sample_decide with the whole-vocabulary kept
+// sets.  P_j(i) = w_i / zk for kept i; the draw takes the smallest id whose inclusive cumulative
+// fixed-point weight exceeds u times the total, over the row in ascending id order.
+__global__ __launch_bounds__(kWG) void k_full_decide(VerifyArgs a) {
+  __shared__ unsigned long long s64[kWG];
+  __shared__ int s_tok;
+  const int b = blockIdx.x, tid = threadIdx.x, V = a.V;
+  const float T = a.temperature;
+  const int tgt_rows = a.B * (a.D + 1);
+  const int seg = (V + kWG - 1) / kWG, seg0 = min(V, tid * seg), seg1 = min(V, seg0 + seg);
+  auto prob = [&](int row, int i) -> double {  // P of token i under row's warp
+    const FullRow f = a.rowinfo[row];
+    const float* x = row < tgt_rows ? a.tl + (long)row * V : a.dl + (long)(row - tgt_rows) * V;
+    const float l = x[i];
+    if (!kept_by(order_key(l), i, f.key, f.id)) return 0.0;
+    return (double)fix_weight(l, f.lmax, T) / (double)f.zk;
+  };
+  // inverse-CDF draw over the row's residual (qrow >= 0: max(0, P - Q) against that row; qrow ==
+  // -1: P without the one-hot draft d; qrow == -2: P itself); falls back to P when all zero
+  auto draw = [&](int prow, int qrow, int d, float u) -> int {
+    const FullRow fp = a.rowinfo[prow];
+    const float* xp = a.tl + (long)prow * V;
+    FullRow fq = fp;
+    const float* xq = xp;
+    if (qrow >= 0) {
+      fq = a.rowinfo[qrow];
+      xq = a.dl + (long)(qrow - tgt_rows) * V;
+    }
+    auto weight = [&](int i, bool resid) -> unsigned long long {
+      const float l = xp[i];
+      if (!kept_by(order_key(l), i, fp.key, fp.id)) return 0ull;
+      const unsigned long long wp = fix_weight(l, fp.lmax, T);
+      if (!resid || qrow == -2) return wp;
+      if (qrow == -1) return i == d ? 0ull : wp;
+      const double P = (double)wp / (double)fp.zk;
+      const float lq = xq[i];
+      const double Q = kept_by(order_key(lq), i, fq.key, fq.id) ? (double)fix_weight(lq, fq.lmax, T) / (double)fq.zk : 0.0;
+      return P > Q ? (unsigned long long)((P - Q) * kFix + 0.5) : 0ull;
+    };
+    bool resid = qrow != -2;
+    for (int attempt = 0; attempt < 2; ++attempt) {
+      unsigned long long c = 0;
+      for (int i = seg0; i < seg1; ++i) c += weight(i, resid);
+      unsigned long long S;
+      const unsigned long long before = scan_u64(c, s64, &S);
+      if (S == 0ull) {
+        resid = false;  // max(0, P - Q) is all zero: draw from P
+        continue;
+      }
+      const double t = (double)u * (double)S;
+      if (tid == 0) s_tok = -1;
+      __syncthreads();
+      if ((double)before <= t && (double)(before + c) > t) {
+        unsigned long long cum = before;
+        for (int i = seg0; i < seg1; ++i) {
+          cum += weight(i, resid);
+          if ((double)cum > t) {
+            s_tok = i;
+            break;
+          }
+        }
+      }
+      __syncthreads();
+      int tok = s_tok;
+      if (tok < 0) {  // u * S rounded onto S: the last id with weight
+        for (int i = V - 1 - tid; i >= 0 && tok < 0; i -= kWG)
+          if (weight(i, resid) > 0ull) tok = i;
+        s64[tid] = (unsigned long long)(tok < 0 ? -1 : tok);
+        __syncthreads();
+        if (tid == 0) {
+          long long best = -1;
+          for (int k = 0; k < kWG; ++k) best = max(best, (long long)s64[k]);
+          s_tok = (int)best;
+        }
+        __syncthreads();
+        tok = s_tok;
+      }
+      __syncthreads();
+      return tok;
+    }
+    return -1;
+  };
+  int n_acc = 0, tok = -1;
+  for (int j = 0; j < a.D && tok < 0; ++j) {
+    const int prow = b * (a.D + 1) + j, d = a.drafts[(long)b * a.D + j];
+    const int qrow = a.q_mode == 1 ? tgt_rows + b * a.D + j : -1;
+    double Pd = 0.0, Qd = 1.0;
+    if (d >= 0 && d < V) {
+      Pd = prob(prow, d);
+      if (qrow >= 0) Qd = prob(qrow, d);
+    }
+    const float u = a.u_accept[(long)b * a.D + j];
+    if (Pd > 0.0 && (Qd == 0.0 || (double)u <= Pd / Qd)) {
+      if (tid == 0) a.out[(long)b * (a.D + 1) + j] = d;
+      ++n_acc;
+      continue;
+    }
+    tok = draw(prow, qrow, d, a.u_sample[b]);
+    if (tok < 0) tok = -2;
+  }
+  if (tok == -1) tok = draw(b * (a.D + 1) + a.D, -2, -1, a.u_sample[b]);
+  if (tid == 0) {
+    int32_t* out = a.out + (long)b * (a.D + 1);
+    out[n_acc] = tok < 0 ? -1 : tok;
+    for (int j = n_acc + 1; j <= a.D; ++j) out[j] = -1;
+    a.n_accept[b] = n_acc;
+    a.crop[b] = a.ctx_len[b] + 1 + n_acc;
+  }
+}
+
 hipError_t run_verify(const VerifyArgs& a, hipStream_t st) {
   if (a.greedy) {
-    hipLaunchKernelGGL(k_verify_greedy, dim3(a.nchunk, a.B * (a.D + 1)), dim3(kWG), 0, st, a);
+    hipLaunchKernelGGL(k_verify_greedy, dim3(a.nchunk, a.walk ? a.B : a.B * (a.D + 1)), dim3(kWG), 0, st, a);
     hipLaunchKernelGGL(k_verify_greedy_final, dim3(a.B), dim3(kWG), 0, st, a);
+  } else if (a.full) {
+    const int rows = a.B * (a.D + 1) + (a.q_mode == 1 ? a.B * a.D : 0);
+    hipLaunchKernelGGL(k_full_select, dim3(rows), dim3(kWG), 0, st, a);
+    hipLaunchKernelGGL(k_full_decide, dim3(a.B), dim3(kWG), 0, st, a);
   } else {
     const int rows = a.B * (a.D + 1) + (a.q_mode == 1 ? a.B * a.D : 0);
     if (a.tk_nchunk > 1) {

@@ -45,9 +45,12 @@ def test_host_side_checks_without_a_gpu():
     with pytest.raises(M.MTPError) as e:
         M.mtp_draft_workspace_size(c, 0, 2, 1, 16)
     assert e.value.code == -1
-    with pytest.raises(M.MTPError):
-        M.spec_verify_workspace_size(4, 2, 1000, M.sampling(1.0, 500, 0.9))
+    # top-k off or above the candidate buffer takes the whole-vocabulary path
+    assert M.spec_verify_workspace_size(4, 2, 1000, M.sampling(1.0, 500, 0.9)) > 0
+    assert M.spec_verify_workspace_size(4, 2, 1000, M.sampling(1.0, 0, 0.9)) > 0
     assert M.spec_verify_workspace_size(4, 2, 1000, M.sampling(1.0, 50, 0.9)) > 0
+    with pytest.raises(M.MTPError):
+        M.spec_verify_workspace_size(4, 0, 1000, M.sampling(1.0, 50, 0.9))
 
 
 def test_host_side_checks_of_the_widened_loops_without_a_gpu():

@@ -94,4 +94,4 @@ def test_host_side_errors_launch_nothing():
     assert e.value.code == -2
     assert kv.len.cpu().tolist() == [0, 0]
     with pytest.raises(M.MTPError):
-        M.spec_verify_workspace_size(2, 2, 100, M.sampling(1.0, 0, 0.9))
+        M.spec_verify_workspace_size(2, 0, 100, M.sampling(1.0, 0, 0.9))  # D must be positive

@@ -92,6 +92,56 @@ def test_verify_small_matches_oracle(V, si):
     assert excl <= B // 4
 
 
+# top-k off (0) or above the 128-entry candidate buffer: the whole-vocabulary path
+FULL_SETTINGS = [
+    Sampling(0.5, 0, 0.8, 0),      # top-p alone
+    Sampling(0.5, 0, 0.8, 1),
+    Sampling(1.0, 256, 0.95, 0),   # a large top-k, then top-p
+    Sampling(0.7, 300, 1.0, 1),    # a large top-k alone
+    Sampling(1.0, 0, 1.0, 0),      # temperature alone
+]
+
+
+@pytest.mark.parametrize("V", [3000, 4093, 20000])
+@pytest.mark.parametrize("si", range(len(FULL_SETTINGS)))
+def test_verify_whole_vocabulary_matches_oracle(V, si):
+    sp = FULL_SETTINGS[si]
+    B, D = 16, 3
+    tl, dl, ua, us, ctx = _inputs(B, D, V, 1.0, seed=100 + V + si)
+    if sp.q_mode == 1:
+        drafts = _sample_drafts(dl, sp, V + si)
+    else:
+        drafts = np.argmax(dl, axis=-1).astype(np.int32)
+        drafts[::3, 0] = np.argmax(tl[::3, 0], -1)
+    excl, n = _compare(tl, drafts, dl if sp.q_mode == 1 else None, sp, ua, us, ctx)
+    assert excl <= B // 2, excl
+
+
+def test_verify_whole_vocabulary_ties_at_the_boundary():
+    """Equal logits straddle both boundaries: rows of one value at 150 ids, the rest far below.
+    top-k 130 cuts inside the block of equal values (the lowest ids are kept); top-p 0.503 over
+    150 equal tokens keeps the lowest-id 76 (the 76th is the one that crosses p).  Uniforms sit
+    away from every cumulative boundary."""
+    B, D, V = 4, 2, 5000
+    g = gen(62, 7, 0)
+    tl = np.full((B, D + 1, V), -30.0, np.float32)
+    for b in range(B):
+        for j in range(D + 1):
+            ids = g.choice(V, 150, replace=False)
+            tl[b, j, ids] = 2.0
+    drafts = np.array([[int(np.nonzero(tl[b, j] == 2.0)[0][k]) for j, k in enumerate((0, 140))]
+                       for b in range(B)], np.int32)
+    ctx = np.full(B, 10, np.int32)
+    for sp in (Sampling(1.0, 130, 1.0, 0), Sampling(1.0, 0, 0.503, 0), Sampling(1.0, 200, 0.503, 0)):
+        for ua0, us0 in ((0.0, 0.2137), (0.001, 0.5813), (0.004, 0.0371)):
+            ua = np.full((B, D), ua0, np.float32)
+            us = np.full(B, us0, np.float32)
+            n, out, crop = _gpu_verify(tl, drafts, None, sp, ua, us, ctx)
+            r = O.spec_verify(tl, drafts, ctx, sp, None, ua, us)
+            assert np.array_equal(n, r.n_accept), (sp, us0)
+            assert np.array_equal(out, r.out_tokens), (sp, us0, out, r.out_tokens)
+
+
 def test_verify_all_accept_gives_the_bonus_row():
     B, D, V = 8, 3, 3000
     tl, dl, ua, us, ctx = _inputs(B, D, V, 0.0, seed=5)
