@@ -493,6 +493,8 @@ inline int device_cus() {
 // per workgroup, tiles per wave and K parts chosen to minimise the estimated time of the weight
 // stream -- (rounds of workgroups over the compute units) x (bytes one workgroup streams) -- plus
 // the split-K partial sums written and read back.  One workgroup runs per compute unit (LDS).
+// How many rows are valid is known only on the device, so the plan fills the GPU with the items
+// of one pass of 16 MT rows; a call with more valid rows takes one more round per extra pass.
 struct SgChoice {
   SgPlan pl;
   int nt, mt, items;
@@ -501,8 +503,6 @@ inline SgChoice plan_stream(int N, int K, int nact, bool whole_rows, long part_r
   const int cus = device_cus();
   SgChoice best{};
   best.mt = nact <= 32 ? 2 : 4;
-  const int rows = 16 * best.mt;
-  const int npass = (nact + rows - 1) / rows;
   const int nk = K / kSgKC, tiles = (N + 15) / 16;
   const int rc = best.mt <= 2 ? SgShape<2>::RC : SgShape<4>::RC;
   double best_t = 1e300;
@@ -511,9 +511,12 @@ inline SgChoice plan_stream(int N, int K, int nact, bool whole_rows, long part_r
     for (int nt = 1; nt <= 2; ++nt)
       for (int ks : ks_opts) {
         if (whole_rows && ks > 1) continue;
-        if (ks > 1 && (nk / ks < 2 * rc || (long)ks * cap * N > part_room)) continue;
+        // every K part holds at least two ranges (and so is never empty)
+        if (ks > 1 && (nk / ks < 2 * rc || (long)(ks - 1) * ((nk + ks - 1) / ks) >= nk ||
+                       (long)ks * cap * N > part_room))
+          continue;
         const int sets = (tiles + nw * nt - 1) / (nw * nt);
-        const long items = (long)npass * sets * ks;
+        const long items = (long)sets * ks;
         const long rounds = (items + cus - 1) / cus;
         const double per_item = (double)nw * nt * 16 * ((double)K / ks) * 2;
         double t = rounds * per_item * cus;                           // bytes-equivalent of the stream
@@ -532,20 +535,22 @@ inline SgChoice plan_stream(int N, int K, int nact, bool whole_rows, long part_r
   return best;
 }
 
-template <class P, int NT, int MT, int KPT>
+template <class P, int NT, int MT, int KPT, int AC = (MT <= 2 ? 256 : 128)>
 hipError_t launch_stream_t(P& p, hipStream_t st, int* grid_used, const MfmaBufs& mb, const KTimer& tm,
                            const SgChoice& ch) {
-  if (KPT * 64 * ch.pl.nw < SgShape<MT>::SLICE || ch.pl.nw > kSgMaxWaves) return hipErrorInvalidConfiguration;
+  if (KPT * 64 * ch.pl.nw < SgShape<MT, AC>::SLICE || ch.pl.nw > sg_max_waves(NT, MT))
+    return hipErrorInvalidConfiguration;
   MfmaBufs m = mb;
   if (ch.pl.ks <= 1) m.part = nullptr;
   m.ksplit = ch.pl.ks;
   int grid = min(ch.items, device_cus());
   grid = max(1, min(grid, kMaxGemvGrid));
   if (grid_used) *grid_used = grid;
-  static const char* name = NT == 2 ? (MT == 2 ? "k_gemm_stream<NT=2,MT=2>" : "k_gemm_stream<NT=2,MT=4>")
+  static const char* name = NT == 4 ? (MT == 2 ? "k_gemm_stream<NT=4,MT=2>" : "k_gemm_stream<NT=4,MT=4>")
+                          : NT == 2 ? (MT == 2 ? "k_gemm_stream<NT=2,MT=2>" : "k_gemm_stream<NT=2,MT=4>")
                                     : (MT == 2 ? "k_gemm_stream<NT=1,MT=2>" : "k_gemm_stream<NT=1,MT=4>");
   tm.begin(st, name);
-  hipLaunchKernelGGL((k_gemm_stream<P, NT, MT, KPT>), dim3(grid), dim3(64 * ch.pl.nw), 0, st, p, m, ch.pl);
+  hipLaunchKernelGGL((k_gemm_stream<P, NT, MT, KPT, AC>), dim3(grid), dim3(64 * ch.pl.nw), 0, st, p, m, ch.pl);
   tm.end(st);
   if (m.part) {
     const long items = (long)m.cap * (p.N / (P::kPair ? 2 : 1));
@@ -563,11 +568,11 @@ hipError_t launch_stream(P& p, hipStream_t st, int* grid_used, const MfmaBufs& m
   SgChoice ch;
   if (whole) {
     ch.mt = p.nact <= 32 ? 2 : 4;
-    ch.nt = 2;
+    ch.nt = ch.mt == 2 ? 4 : 2;
     ch.pl.nw = 8;
     ch.pl.ks = 1;
     ch.pl.kper = p.K / kSgKC;
-    ch.pl.sets = (p.N + 8 * 2 * 16 - 1) / (8 * 2 * 16);
+    ch.pl.sets = (p.N + 8 * ch.nt * 16 - 1) / (8 * ch.nt * 16);
     const int npass = P::kArgmax ? 1 : (p.nact + 16 * ch.mt - 1) / (16 * ch.mt);
     ch.items = npass * ch.pl.sets;
   } else {
@@ -576,8 +581,9 @@ hipError_t launch_stream(P& p, hipStream_t st, int* grid_used, const MfmaBufs& m
   // activation pieces per thread and chunk: ceil(SLICE / threads); 512 pieces (32-row passes):
   // 2 with 7 waves, 1 with 8 or 9; 1024 pieces (64-row passes): 3 with 7 waves, 2 with 8 or 9
   const bool seven = ch.pl.nw == 7;
-  if constexpr (P::kArgmax || P::kVocab) {  // 8 waves, two tiles each
-    if (ch.mt == 2) return launch_stream_t<P, 2, 2, 1>(p, st, grid_used, mb, tm, ch);
+  if constexpr (P::kArgmax || P::kVocab) {  // 8 waves; 32-row passes: four tiles each and
+    // 128-column activation ranges (halving the activation operand reads per weight byte)
+    if (ch.mt == 2) return launch_stream_t<P, 4, 2, 1, 128>(p, st, grid_used, mb, tm, ch);
     return launch_stream_t<P, 2, 4, 2>(p, st, grid_used, mb, tm, ch);
   } else {
     if (ch.mt == 2) {

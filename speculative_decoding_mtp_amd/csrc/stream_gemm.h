@@ -37,12 +37,15 @@ namespace mtp {
 
 constexpr int kSgKC = 64;        // K per chunk (128 bytes of a weight row)
 constexpr int kSgMaxWaves = 9;   // waves per workgroup at most
-constexpr int kSgThreads = 64 * kSgMaxWaves;
 
-template <int MT>
+// Waves a workgroup may have with NT tiles per wave and 16 MT-row passes: bounded by the LDS of
+// the weight tiles next to the activation ranges (and, through the launch bound, the registers).
+constexpr int sg_max_waves(int NT, int MT) { return NT * MT >= 16 ? 6 : NT >= 3 ? 8 : kSgMaxWaves; }
+
+template <int MT, int AC = (MT <= 2 ? 256 : 128)>
 struct SgShape {
   static constexpr int ROWS = 16 * MT;                 // activation rows per pass
-  static constexpr int ACOLS = MT <= 2 ? 256 : 128;    // activation columns per staged range
+  static constexpr int ACOLS = AC;                     // activation columns per staged range
   static constexpr int RC = ACOLS / kSgKC;             // chunks per range
   static constexpr int D = RC < 3 ? RC : 3;            // weight chunks in flight per wave
   static constexpr int UNITS = ACOLS / 8;              // 16-byte units per staged activation row
@@ -65,18 +68,19 @@ __device__ __forceinline__ int sg_wswz(int r) { return (r & 7) ^ ((r >> 3) & 1);
 
 // KPT: activation pieces each thread loads per chunk (ceil(SLICE / threads)); the same count in
 // every thread keeps the loads per iteration fixed.
-template <class P, int NT, int MT, int KPT>
-__global__ __launch_bounds__(kSgThreads) void k_gemm_stream(P p, MfmaBufs mb, SgPlan pl) {
-  using S = SgShape<MT>;
+template <class P, int NT, int MT, int KPT, int AC = (MT <= 2 ? 256 : 128)>
+__global__ __launch_bounds__(64 * sg_max_waves(NT, MT)) void k_gemm_stream(P p, MfmaBufs mb, SgPlan pl) {
+  using S = SgShape<MT, AC>;
   constexpr int D = S::D, RC = S::RC;
+  constexpr int WMAX = sg_max_waves(NT, MT);
   constexpr int WL = 2 * NT;              // weight loads per lane and chunk
   constexpr int WT = NT * 16 * 128;       // bytes of a wave's weight tile
   __shared__ __align__(16) char s_act[3][S::BUF];
-  __shared__ __align__(16) char s_w[kSgMaxWaves][WT];
+  __shared__ __align__(16) char s_w[WMAX][WT];
   __shared__ int s_n[kMaxBatch];
   __shared__ int s_len[kMaxBatch];
-  __shared__ float s_bv[kSgMaxWaves * S::ROWS];
-  __shared__ int s_bi[kSgMaxWaves * S::ROWS];
+  __shared__ float s_bv[(P::kArgmax ? WMAX * S::ROWS : 1)];
+  __shared__ int s_bi[(P::kArgmax ? WMAX * S::ROWS : 1)];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int jl = lane & 15, hq = lane >> 4;
   const int nw = pl.nw, nthreads = 64 * nw;
