@@ -58,6 +58,8 @@ def parse():
                     help="draft with this many MTP modules, step k by module (k-1) mod M (mtp_draft_loop_multi)")
     ap.add_argument("--shared-kv", type=int, default=0,
                     help="the head keeps no cache and reads a main-model cache of this many layers instead")
+    ap.add_argument("--sigma", type=float, default=1.0,
+                    help="verifier-only workloads: std of the target-logit noise around the draft logits")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB first (counter calibration)")
     return ap.parse_args()
@@ -76,7 +78,7 @@ def main():
 
     from synth import VERIFY_CONFIGS
     if args.config in VERIFY_CONFIGS:
-        return bench_verify(args, VERIFY_CONFIGS[args.config])
+        return bench_verify(args, VERIFY_CONFIGS[args.config], args.sigma)
     cfg = CONFIGS[args.config]
     if args.target_layers > 0:
         return bench_target(args, cfg, args.target_layers)
@@ -339,6 +341,11 @@ def bench_verify(args, vc, sigma=1.0):
     wall = time.perf_counter() - t0
     v_ms, v_n = M.mtp_timer_read(M.MTP_KERNEL_VERIFY)
     logits_bytes = B * (D + 1) * V * 4
+    cpu = None
+    if args.cpu_seconds > 0:
+        tl_h, ctx_h, d_h = tl.cpu().numpy(), ctx.cpu().numpy(), drafts.cpu().numpy()
+        ua_h, us_h = ua.cpu().numpy(), us.cpu().numpy()
+        cpu = cpu_baseline_verify(tl_h, d_h, ctx_h, sp, ua_h, us_h, args.cpu_seconds)
     achieved = logits_bytes / (v_ms / v_n * 1e-3) / 1e9
     line = {
         "metric": "spec_verify sequences/s; target-logits scan HBM GB/s vs MI355X peak",
@@ -355,7 +362,7 @@ def bench_verify(args, vc, sigma=1.0):
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "bytes_per_launch": logits_bytes, "avg_launch_us": round(v_ms / v_n * 1e3, 2),
                      "launches": v_n},
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 
@@ -511,6 +518,27 @@ def _timed_split(run, budget_s):
             u1, dt1, what1 = run(budget_s / 3)
         line["single_thread_value"] = round(u1 / dt1, 4)
         line["single_thread_sample"] = f"{what1}; {dt1:.1f} s"
+    return line
+
+
+def cpu_baseline_verify(tl, drafts, ctx, sp, ua, us, budget_s):
+    """The oracle's verification on the same resident inputs, one sequence at a time (sequences
+    0, 1, 2, ... until the time budget is spent): verified sequences/s."""
+    import oracle as O
+    B = tl.shape[0]
+
+    def run(budget):
+        n, spent = 0, 0.0
+        while n < 1 or spent < budget:
+            b = n % B
+            t0 = time.perf_counter()
+            O.spec_verify(tl[b:b + 1], drafts[b:b + 1], ctx[b:b + 1], sp, None, ua[b:b + 1], us[b:b + 1])
+            spent += time.perf_counter() - t0
+            n += 1
+        return n, spent, f"{n} sequences of the same batch (the oracle verifies one at a time)"
+
+    line = _timed_split(run, budget_s)
+    line["unit"] = "verified sequences/s"
     return line
 
 
