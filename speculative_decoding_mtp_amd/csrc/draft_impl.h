@@ -453,14 +453,20 @@ int resident_cap(K kernel, int* cache) {
 
 // Launch the planned variant with a grid of at most one resident wave of workgroups (the
 // kernels loop over row groups), so no partial second wave of workgroups trails the first.
-// The bf16 MFMA path (K a multiple of the 128-wide chunk) serves every activation count the
-// VALU GEMVs cannot take in one pass over the weights.
-// bf16 weights take the MFMA path for 16 or more activation rows, and also for fewer when the
-// VALU GEMV would have to stream the weights more than once (more rows than it holds per pass).
+// The bf16 MFMA path (K a multiple of the 128-wide chunk) takes 16 or more activation rows, and
+// fewer when the VALU GEMV would stream a large matrix more than once (more rows than it holds
+// per pass).  A matrix of at most 32 MB stays on the GEMV for up to four passes: the passes after
+// the first re-read it from the last-level cache, blocks of rows with no valid row are skipped
+// (a catch-up call usually has one or two of its rows valid), and the MFMA path's preparation,
+// split-K reduction and few workgroups (a small matrix has few weight tiles) cost more.
 template <class W, class P>
 bool use_mfma(const P& p, const MfmaBufs* mb) {
   if (!mb || !std::is_same<W, BF16>::value || p.K % kMfmaKC != 0) return false;  // K: whole 128-wide chunks
-  return p.nact >= 16 || p.nact > plan_gemv(p.nact, p.K, W::VE, p.N).rb;
+  if (p.nact >= 16) return true;
+  const int rb = plan_gemv(p.nact, p.K, W::VE, p.N).rb;
+  if (p.nact <= rb) return false;
+  const long bytes = (long)p.N * p.K * (long)sizeof(typename W::T);
+  return bytes > (32l << 20) || (p.nact + rb - 1) / rb > 4;
 }
 
 // Optional HIP events recorded around a GEMV/GEMM's main kernel (not its preparation or
