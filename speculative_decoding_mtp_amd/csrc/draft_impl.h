@@ -552,9 +552,13 @@ hipError_t launch_stream_t(P& p, hipStream_t st, int* grid_used, const MfmaBufs&
   int grid = min(ch.items, device_cus());
   grid = max(1, min(grid, kMaxGemvGrid));
   if (grid_used) *grid_used = grid;
-  static const char* name = NT == 4 ? (MT == 2 ? "k_gemm_stream<NT=4,MT=2>" : "k_gemm_stream<NT=4,MT=4>")
-                          : NT == 2 ? (MT == 2 ? "k_gemm_stream<NT=2,MT=2>" : "k_gemm_stream<NT=2,MT=4>")
-                                    : (MT == 2 ? "k_gemm_stream<NT=1,MT=2>" : "k_gemm_stream<NT=1,MT=4>");
+  static const char* const names[2][7] = {
+      {"", "k_gemm_stream<NT=1,MT=2>", "k_gemm_stream<NT=2,MT=2>", "k_gemm_stream<NT=3,MT=2>",
+       "k_gemm_stream<NT=4,MT=2>", "k_gemm_stream<NT=5,MT=2>", "k_gemm_stream<NT=6,MT=2>"},
+      {"", "k_gemm_stream<NT=1,MT=4>", "k_gemm_stream<NT=2,MT=4>", "k_gemm_stream<NT=3,MT=4>",
+       "k_gemm_stream<NT=4,MT=4>", "k_gemm_stream<NT=5,MT=4>", "k_gemm_stream<NT=6,MT=4>"}};
+  static_assert(NT >= 1 && NT <= 6 && (MT == 2 || MT == 4), "kernel name table");
+  const char* name = names[MT == 4][NT];
   tm.begin(st, name);
   hipLaunchKernelGGL((k_gemm_stream<P, NT, MT, KPT, AC>), dim3(grid), dim3(64 * ch.pl.nw), 0, st, p, m, ch.pl);
   tm.end(st);
@@ -574,7 +578,23 @@ hipError_t launch_stream(P& p, hipStream_t st, int* grid_used, const MfmaBufs& m
   SgChoice ch;
   if (whole) {
     ch.mt = p.nact <= 32 ? 2 : 4;
-    ch.nt = ch.mt == 2 ? 4 : 2;
+    ch.nt = 2;
+    if (ch.mt == 2) {
+      // tiles per wave (8 waves): the fewest rounds of workgroups over the compute units, each
+      // round weighted by the tiles one workgroup streams over its measured share of the HBM
+      // peak (two tiles 0.76, three 0.80, four or five 0.82); 151936 rows take five tiles (238
+      // sets in one round) where four would need 297 sets, two rounds
+      const int tiles = (p.N + 15) / 16, cus = device_cus();
+      double best = 1e300;
+      for (int nt = 2; nt <= 5; ++nt) {
+        const int sets = (tiles + 8 * nt - 1) / (8 * nt);
+        const double t = (double)((sets + cus - 1) / cus) * nt / (nt == 2 ? 0.76 : nt == 3 ? 0.80 : 0.82);
+        if (t < best * 0.999) {
+          best = t;
+          ch.nt = nt;
+        }
+      }
+    }
     ch.pl.nw = 8;
     ch.pl.ks = 1;
     ch.pl.kper = p.K / kSgKC;
@@ -587,9 +607,16 @@ hipError_t launch_stream(P& p, hipStream_t st, int* grid_used, const MfmaBufs& m
   // activation pieces per thread and chunk: ceil(SLICE / threads); 512 pieces (32-row passes):
   // 2 with 7 waves, 1 with 8 or 9; 1024 pieces (64-row passes): 3 with 7 waves, 2 with 8 or 9
   const bool seven = ch.pl.nw == 7;
-  if constexpr (P::kArgmax || P::kVocab) {  // 8 waves; 32-row passes: four tiles each and
-    // 128-column activation ranges (halving the activation operand reads per weight byte)
-    if (ch.mt == 2) return launch_stream_t<P, 4, 2, 1, 128>(p, st, grid_used, mb, tm, ch);
+  if constexpr (P::kArgmax || P::kVocab) {  // 8 waves; 32-row passes with three or more tiles
+    // take 128-column activation ranges (fewer activation operand reads per weight byte)
+    if (ch.mt == 2) {
+      switch (ch.nt) {
+        case 3: return launch_stream_t<P, 3, 2, 1, 128>(p, st, grid_used, mb, tm, ch);
+        case 4: return launch_stream_t<P, 4, 2, 1, 128>(p, st, grid_used, mb, tm, ch);
+        case 5: return launch_stream_t<P, 5, 2, 1, 128>(p, st, grid_used, mb, tm, ch);
+        default: return launch_stream_t<P, 2, 2, 1>(p, st, grid_used, mb, tm, ch);
+      }
+    }
     return launch_stream_t<P, 2, 4, 2>(p, st, grid_used, mb, tm, ch);
   } else {
     if (ch.mt == 2) {
