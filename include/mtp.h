@@ -86,7 +86,9 @@ typedef struct {
  * v: [n_layers][batch][n_kv_heads][head_dim][max_len] in cfg->wdtype: values are stored
  * transposed (each channel's positions contiguous), the layout the attention's value
  * contraction over positions reads.  max_len: a positive multiple of 8 (MTP_ERR_ARG
- * otherwise).  len: device int32[batch], the number of valid positions per sequence;
+ * otherwise); a multiple of 64 puts every 64-position segment of a bf16 value row on one
+ * 128-byte line, which the batched attention streams fastest (the binding rounds to 64).
+ * len: device int32[batch], the number of valid positions per sequence;
  * position p lives in slot p.  Slots at or past len may hold anything. */
 typedef struct {
   void *k, *v;

@@ -195,8 +195,9 @@ class TargetWeights:
 
 
 def round_max_len(n: int) -> int:
-    """The smallest cache capacity >= n that the library accepts (a multiple of 8)."""
-    return -(-int(n) // 8) * 8
+    """The smallest cache capacity >= n that is a multiple of 64 (the library accepts multiples
+    of 8; with 64 every 64-position segment of a bf16 value row sits on one 128-byte line)."""
+    return -(-int(n) // 64) * 64
 
 
 class KVCache:

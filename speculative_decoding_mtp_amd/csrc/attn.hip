@@ -449,31 +449,42 @@ __global__ __launch_bounds__(kWG) void k_attn_mfma(AttnArgs a) {
 // bf16 heads with a batch of sequences (B x kv heads fill the GPU): the same MFMA attention with
 // the keys and values staged through LDS.  Reading K and V^T straight in the operand layout
 // fetches 64 bytes of each of 16 rows per load instruction, a pattern that streams well below
-// the read ceiling; here each wave fetches 64-position superslices row-contiguously -- keys as
-// four 256-byte rows per load, values as eight 128-byte channel rows -- into a private LDS tile
-// (XOR-swizzled in 16-byte units) and reads the operands from there.  The next superslice is in
-// flight in registers while one is used (at one wave per SIMD the registers are free); the tile
-// is the wave's own, so the streaming loop has no barrier.  Per 32-position half the products
-// are those of k_attn_mfma.
-template <int NQT>
-__global__ __launch_bounds__(kWG) void k_attn_lds(AttnArgs a) {
+// the read ceiling; here each wave fetches SP-position superslices row-contiguously -- keys as
+// four 256-byte rows per load, values as 64 / (SP / 8) channel rows of 2 SP bytes -- into a
+// private LDS tile (XOR-swizzled in 16-byte units) and reads the operands from there.  NB
+// superslices per wave are in flight in registers while one is used; the tile is the wave's own,
+// so the streaming loop has no barrier.  Per 32-position half the products are those of
+// k_attn_mfma.  NWV waves per workgroup (NWV x tile bytes of LDS) share the position range
+// round-robin and merge at the end.
+// The cache is read once per step and is larger than the caches, so keys are loaded
+// nontemporally; values too when every 2 SP-byte segment of a value row is a whole 128-byte line
+// (max_len a multiple of 64).  Otherwise each segment straddles two lines and cached loads let
+// L2 serve the shared line once.  Measured at 32 sequences x 8 kv heads x 8192 positions:
+// 187 -> 167 us (0.67 -> 0.75 of the HBM peak) with line-aligned rows.
+template <int NQT, int NWV, int SP, int NB, bool VNT>
+__global__ __launch_bounds__(64 * NWV) void k_attn_lds(AttnArgs a) {
   constexpr int HD = 128;
+  constexpr int NT = 64 * NWV;  // threads
   constexpr int NS = HD / 32;   // q.k steps
   constexpr int ND = HD / 16;   // 16-channel tiles of the output
   constexpr int QB = 16 * NQT;  // queries per pass
   constexpr int OP = HD + 4;    // padded LDS row of the merged output
   constexpr int QP = HD + 8;    // padded LDS row of the split queries (bf16)
-  constexpr int SP = 64;        // positions per superslice
-  constexpr int KT = SP * HD * 2;   // bytes of a key tile: 64 rows x 256 B (16 units)
-  constexpr int VT = HD * SP * 2;   // bytes of a value tile: 128 channel rows x 128 B (8 units)
-  __shared__ float sm[4][QB], sl[4][QB];
+  constexpr int KT = SP * HD * 2;   // bytes of a key tile: SP rows x 256 B (16 units)
+  constexpr int VU = SP / 8;        // 16-byte units of a value channel row
+  constexpr int VT = HD * SP * 2;   // bytes of a value tile: 128 channel rows x 2 SP bytes
+  constexpr int LK = SP / 4;        // key loads per lane and superslice (4 rows each)
+  constexpr int VR = 64 / VU;       // value channel rows per load
+  constexpr int LV = HD / VR;       // value loads per lane and superslice
+  static_assert(SP == 32 || SP == 64, "superslices of one or two 32-position halves");
+  __shared__ float sm[NWV][QB], sl[NWV][QB];
   __shared__ __align__(16) __bf16 sQ[2 * QB * QP];  // [hi/lo][query][channel]
-  __shared__ __align__(16) char sKV[4][KT + VT];     // each wave's tiles
+  __shared__ __align__(16) char sKV[NWV][KT + VT];   // each wave's tiles
   __shared__ int s_n;
   // the merged output reuses the tiles: it is written after every wave has left the streaming
   // loop (behind a barrier) and read before the next pass stores tiles again (another barrier)
   float* sO = reinterpret_cast<float*>(&sKV[0][0]);
-  static_assert(QB * OP * 4 <= 4 * (KT + VT), "merged output fits in the tiles");
+  static_assert(QB * OP * 4 <= NWV * (KT + VT), "merged output fits in the tiles");
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, j = lane & 15, hq = lane >> 4;
   const int s = blockIdx.x, kvh = blockIdx.y % a.nkv, b = blockIdx.z;
   const int qgrp = blockIdx.y / a.nkv, nqgrp = gridDim.y / a.nkv;
@@ -495,11 +506,12 @@ __global__ __launch_bounds__(kWG) void k_attn_lds(AttnArgs a) {
   const int krow = 8 * (j >> 2) + (j & 3);  // this lane's K row in sub-tile 0 (+4 in sub-tile 1)
   char* tK = sKV[wid];
   char* tV = sKV[wid] + KT;
-  auto vswz = [](int r) { return (r & 7) ^ ((r >> 3) & 1); };
+  // value rows: 16 distinct banks for the 16 rows a quarter wave reads at one unit
+  auto vswz = [](int r) { return SP == 64 ? (r & 7) ^ ((r >> 3) & 1) : (r >> 2) & 3; };
 
   for (int q0 = qgrp * QB; q0 < NQ; q0 += QB * nqgrp) {
     const int p_stop = min(p_end, L0 + (min(NQ, q0 + QB) - 1) / G + 1);
-    for (int idx = tid; idx < QB * (HD / 8); idx += kWG) {
+    for (int idx = tid; idx < QB * (HD / 8); idx += NT) {
       const int q = idx / (HD / 8), c = idx - q * (HD / 8), qi = q0 + q;
       float f[8];
       if (qi < NQ) {
@@ -534,51 +546,64 @@ __global__ __launch_bounds__(kWG) void k_attn_lds(AttnArgs a) {
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt) acc[dt][qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    // this pass's queries as B operands, held in registers for the whole pass
-    bf16x8_t qH[NQT][NS], qL[NQT][NS];
+    // this pass's queries as B operands: one 16-query tile is held in registers for the whole
+    // pass, two are read from LDS at each use (registers for the second tile's accumulators)
+    constexpr bool QREG = NQT == 1;
+    bf16x8_t qH[QREG ? NQT : 1][NS], qL[QREG ? NQT : 1][NS];
+    if constexpr (QREG) {
 #pragma unroll
-    for (int qt = 0; qt < NQT; ++qt)
+      for (int qt = 0; qt < NQT; ++qt)
 #pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        qH[qt][st] = *reinterpret_cast<const bf16x8_t*>(sQ + (16 * qt + j) * QP + 32 * st + 8 * hq);
-        qL[qt][st] = *reinterpret_cast<const bf16x8_t*>(sQ + (QB + 16 * qt + j) * QP + 32 * st + 8 * hq);
-      }
+        for (int st = 0; st < NS; ++st) {
+          qH[qt][st] = *reinterpret_cast<const bf16x8_t*>(sQ + (16 * qt + j) * QP + 32 * st + 8 * hq);
+          qL[qt][st] = *reinterpret_cast<const bf16x8_t*>(sQ + (QB + 16 * qt + j) * QP + 32 * st + 8 * hq);
+        }
+    }
+    auto qop = [&](int qt, int st, int lo) {
+      if constexpr (QREG) return lo ? qL[qt][st] : qH[qt][st];
+      return *reinterpret_cast<const bf16x8_t*>(sQ + (lo * QB + 16 * qt + j) * QP + 32 * st + 8 * hq);
+    };
     // superslice loads, unconditional from clamped in-range addresses: key row 4 i + lane / 16
-    // (unit lane % 16); value channel row 8 i + lane / 8 (unit lane % 8 = 8 positions).  The next
-    // superslice is in flight in registers while one is multiplied.
-    uint4 rk[1][16], rv[1][16];
-    auto load = [&](int buf, int pw) {
+    // (unit lane % 16); value channel row VR i + lane / VU (unit lane % VU = 8 positions)
+    uint4 rk[NB][LK], rv[NB][LV];
+    auto load = [&](uint4 (&k)[LK], uint4 (&v)[LV], int pw) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
+      for (int i = 0; i < LK; ++i) {
         const int p = min(pw + 4 * i + (lane >> 4), p_end - 1);
-        rk[buf][i] = ld16(Kb + (long)p * HD + 8 * (lane & 15));
-        const int d = 8 * i + (lane >> 3);
-        const int pv = min(pw + 8 * (lane & 7), (p_end - 1) & ~7);
-        rv[buf][i] = ld16(Vt + (long)d * a.max_len + pv);
+        k[i] = ld_stream(Kb + (long)p * HD + 8 * (lane & 15));
+      }
+#pragma unroll
+      for (int i = 0; i < LV; ++i) {
+        const int d = VR * i + lane / VU;
+        const int pv = min(pw + 8 * (lane % VU), (p_end - 1) & ~7);
+        v[i] = VNT ? ld_stream(Vt + (long)d * a.max_len + pv) : ld16(Vt + (long)d * a.max_len + pv);
       }
     };
     // a buffer into the wave's tiles; value positions past the range become zero
-    auto store = [&](int buf, int pw) {
+    auto store = [&](const uint4 (&k)[LK], const uint4 (&v)[LV], int pw) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
+      for (int i = 0; i < LK; ++i) {
         const int r = 4 * i + (lane >> 4), u = lane & 15;
-        *reinterpret_cast<uint4*>(tK + r * 256 + ((u ^ (r & 15)) << 4)) = rk[buf][i];
-        const int d = 8 * i + (lane >> 3), uv = lane & 7;
+        *reinterpret_cast<uint4*>(tK + r * 256 + ((u ^ (r & 15)) << 4)) = k[i];
+      }
+#pragma unroll
+      for (int i = 0; i < LV; ++i) {
+        const int d = VR * i + lane / VU, uv = lane % VU;
         const int keep = p_end - (pw + 8 * uv);
-        uint4 v = rv[buf][i];
+        uint4 x = v[i];
         if (keep < 8) {
-          uint32_t w[4] = {v.x, v.y, v.z, v.w};
+          uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
           for (int e = 0; e < 8; ++e)
             if (e >= keep) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-          v = make_uint4(w[0], w[1], w[2], w[3]);
+          x = make_uint4(w[0], w[1], w[2], w[3]);
         }
-        *reinterpret_cast<uint4*>(tV + d * 128 + ((uv ^ vswz(d)) << 4)) = v;
+        *reinterpret_cast<uint4*>(tV + d * (2 * SP) + ((uv ^ vswz(d)) << 4)) = x;
       }
     };
     auto compute = [&](int pw) {
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {  // 32-position halves
+      for (int hh = 0; hh < SP / 32; ++hh) {  // 32-position halves
         const int ph = pw + 32 * hh;
         if (ph >= p_stop) break;
 #pragma unroll
@@ -592,8 +617,8 @@ __global__ __launch_bounds__(kWG) void k_attn_lds(AttnArgs a) {
             for (int st = 0; st < NS; ++st) {
               const int u = 4 * st + hq;
               const bf16x8_t kop = *reinterpret_cast<const bf16x8_t*>(tK + r * 256 + ((u ^ (r & 15)) << 4));
-              sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qH[qt][st], sc[t], 0, 0, 0);
-              sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qL[qt][st], sc[t], 0, 0, 0);
+              sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop(qt, st, 0), sc[t], 0, 0, 0);
+              sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop(qt, st, 1), sc[t], 0, 0, 0);
             }
           }
           float pe[8];
@@ -630,23 +655,29 @@ __global__ __launch_bounds__(kWG) void k_attn_lds(AttnArgs a) {
           for (int dt = 0; dt < ND; ++dt) {
             acc[dt][qt] *= alpha;
             const int d = 16 * dt + j, u = 4 * hh + hq;
-            const bf16x8_t vop = *reinterpret_cast<const bf16x8_t*>(tV + d * 128 + ((u ^ vswz(d)) << 4));
+            const bf16x8_t vop = *reinterpret_cast<const bf16x8_t*>(tV + d * (2 * SP) + ((u ^ vswz(d)) << 4));
             acc[dt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pH, acc[dt][qt], 0, 0, 0);
             acc[dt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pL, acc[dt][qt], 0, 0, 0);
           }
         }
       }
     };
-    // wave w takes superslices w, w + 4, ... ; the load past the end re-reads the clamped last
-    // position (cached) and is not used, so every iteration issues the same loads
+    // wave w takes superslices w, w + NWV, ... ; loads past the end re-read the clamped last
+    // position (cached) and are not used, so every iteration issues the same loads
+    constexpr int STEP = NWV * SP;
     const int pw0 = p_beg + SP * wid;
-    load(0, pw0);
-    for (int pw = pw0; pw < p_stop; pw += 4 * SP) {
-      store(0, pw);
-      load(0, pw + 4 * SP);
-      compute(pw);
+#pragma unroll
+    for (int c = 0; c < NB; ++c) load(rk[c], rv[c], pw0 + c * STEP);
+    for (int pw = pw0; pw < p_stop; pw += NB * STEP) {
+#pragma unroll
+      for (int c = 0; c < NB; ++c) {
+        const int pc = pw + c * STEP;
+        if (c == 0 || pc < p_stop) store(rk[c], rv[c], pc);
+        load(rk[c], rv[c], pc + NB * STEP);
+        if (c == 0 || pc < p_stop) compute(pc);
+      }
     }
-    // merge the four waves: o = sum_w o_w e^{m_w - M}, l = sum_w l_w e^{m_w - M}
+    // merge the waves: o = sum_w o_w e^{m_w - M}, l = sum_w l_w e^{m_w - M}
     if (hq == 0) {
 #pragma unroll
       for (int qt = 0; qt < NQT; ++qt) {
@@ -655,14 +686,19 @@ __global__ __launch_bounds__(kWG) void k_attn_lds(AttnArgs a) {
       }
     }
     __syncthreads();
+    auto row_max = [&](int q) {
+      float M = sm[0][q];
+#pragma unroll
+      for (int w = 1; w < NWV; ++w) M = fmaxf(M, sm[w][q]);
+      return M;
+    };
     float cw[NQT];
 #pragma unroll
     for (int qt = 0; qt < NQT; ++qt) {
-      const int q = 16 * qt + j;
-      const float M = fmaxf(fmaxf(sm[0][q], sm[1][q]), fmaxf(sm[2][q], sm[3][q]));
+      const float M = row_max(16 * qt + j);
       cw[qt] = m_run[qt] == -INFINITY ? 0.f : expf(m_run[qt] - M);
     }
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NWV; ++w) {
       if (wid == w) {
 #pragma unroll
         for (int qt = 0; qt < NQT; ++qt)
@@ -680,16 +716,16 @@ __global__ __launch_bounds__(kWG) void k_attn_lds(AttnArgs a) {
       }
       __syncthreads();
     }
+    auto row_sum = [&](int q, float M) {
+      float L = 0.f;
+      for (int w = 0; w < NWV; ++w)
+        if (sm[w][q] != -INFINITY) L += sl[w][q] * expf(sm[w][q] - M);
+      return L;
+    };
     if (a.out) {  // the only split: normalise here and write the output rows (no combine pass)
-      for (int q = tid; q < QB; q += kWG) {
-        const float M = fmaxf(fmaxf(sm[0][q], sm[1][q]), fmaxf(sm[2][q], sm[3][q]));
-        float L = 0.f;
-        for (int w = 0; w < 4; ++w)
-          if (sm[w][q] != -INFINITY) L += sl[w][q] * expf(sm[w][q] - M);
-        sl[0][q] = L;
-      }
+      for (int q = tid; q < QB; q += NT) sl[0][q] = row_sum(q, row_max(q));
       __syncthreads();
-      for (int idx = tid; idx < QB * HD; idx += kWG) {
+      for (int idx = tid; idx < QB * HD; idx += NT) {
         const int q = idx / HD, d = idx - q * HD, qi = q0 + q;
         if (qi < NQ) {
           const int i = qi / G, g = qi - i * G;
@@ -698,22 +734,19 @@ __global__ __launch_bounds__(kWG) void k_attn_lds(AttnArgs a) {
       }
     } else {
       float* P = a.part + (((long)b * a.nkv + kvh) * a.nsplit + s) * (long)a.qstride * (HD + 2);
-      for (int idx = tid; idx < QB * HD; idx += kWG) {
+      for (int idx = tid; idx < QB * HD; idx += NT) {
         const int q = idx / HD, d = idx - q * HD;
         if (q0 + q < NQ) P[(long)(q0 + q) * (HD + 2) + d] = sO[q * OP + d];
       }
-      for (int q = tid; q < QB; q += kWG) {
+      for (int q = tid; q < QB; q += NT) {
         if (q0 + q < NQ) {
-          const float M = fmaxf(fmaxf(sm[0][q], sm[1][q]), fmaxf(sm[2][q], sm[3][q]));
-          float L = 0.f;
-          for (int w = 0; w < 4; ++w)
-            if (sm[w][q] != -INFINITY) L += sl[w][q] * expf(sm[w][q] - M);
+          const float M = row_max(q);
           P[(long)(q0 + q) * (HD + 2) + HD] = M;
-          P[(long)(q0 + q) * (HD + 2) + HD + 1] = L;
+          P[(long)(q0 + q) * (HD + 2) + HD + 1] = row_sum(q, M);
         }
       }
     }
-    __syncthreads();
+    __syncthreads();  // sm, sl, sO are reused by the next pass
   }
 }
 
@@ -788,11 +821,15 @@ void launch_attention(AttnArgs a, int wdtype, float* out, hipStream_t st) {
     const double kv_bytes = 4.0 * a.B * a.nkv * (double)a.max_len * HD;
     if constexpr (HD == 128) {
       // a batch whose (sequence, kv head) pairs fill the GPU on their own, over a long cache:
-      // the LDS-staged kernel (one wave per SIMD, registers free for the prefetch)
-      // (one 16-query tile per pass: with two the kernel's registers overflow)
+      // the LDS-staged kernel (one wave per SIMD, registers free for the prefetch);
+      // (up to 16 queries per kv head, one tile held in registers: a catch-up of several rows
+      // per sequence measured no faster here than k_attn_mfma's two-tile kernel)
       if (a.B * a.nkv >= 128 && a.max_len >= 1024 && a.qstride <= 16) {
         dim3 grid(a.nsplit, a.nkv * attn_qgroups(a, 16), a.B);
-        hipLaunchKernelGGL((k_attn_lds<1>), grid, dim3(kWG), 0, st, a);
+        if (a.max_len % 64 == 0)
+          hipLaunchKernelGGL((k_attn_lds<1, 4, 64, 1, true>), grid, dim3(kWG), 0, st, a);
+        else
+          hipLaunchKernelGGL((k_attn_lds<1, 4, 64, 1, false>), grid, dim3(kWG), 0, st, a);
         if (!a.out) hipLaunchKernelGGL((k_attn_combine<HD>), dim3(a.B * a.rps * a.nq), dim3(kWG), 0, st, a, out);
         return;
       }

@@ -2,8 +2,10 @@
 caches of 1000+ positions, which takes the LDS-staged decode attention -- against the oracle.
 
 Ragged per-sequence cache lengths (not multiples of the 64-position superslice), catch-up calls
-of one to four rows per sequence (some sequences without rows), and query groups of 2 and 8 per
-kv head (one and two 16-query tiles per pass).  Every sequence's hiddens, logits and draft of
+of one to four rows per sequence (some sequences without rows), query groups of 2 and 8 per kv
+head (the LDS-staged kernel takes up to 16 queries per kv head, the catch-up of 4 rows x 8 the
+two-tile MFMA kernel), and capacities of 1280 and 1288 positions (value rows on whole 128-byte
+lines, read nontemporally, or straddling lines, read through the cache).  Every sequence's hiddens, logits and draft of
 each step and the appended K/V are compared.  Bar: 2e-3 max relative error on hiddens and logits
 (bf16 weights and K/V on both sides, fp32 against float64 arithmetic), K/V within one bf16 ulp,
 drafts exact unless the oracle's top-2 gap is below 1e-4."""
@@ -23,8 +25,9 @@ TOL = 2e-3
 KV_ULP = 2.0 ** -7
 
 
+@pytest.mark.parametrize("max_len", [1280, 1288])
 @pytest.mark.parametrize("nq", [8, 32])
-def test_batched_head_with_ragged_caches_matches_oracle(nq):
+def test_batched_head_with_ragged_caches_matches_oracle(nq, max_len):
     nkv, B, D = 4, 32, 2
     cfg = CONFIGS["tiny"].replace(index=61, wdtype="bf16", hidden=256, n_heads=nq, n_kv_heads=nkv, head_dim=128,
                                   ffn=512, vocab=2000, embed_std=1.0, batch=B, D=D)
@@ -32,7 +35,6 @@ def test_batched_head_with_ragged_caches_matches_oracle(nq):
     model = O.OracleModel(cfg, w)
     c, gw = config(cfg), upload_weights(cfg, w)
     g = gen(61, 3, nq)
-    max_len = 1280
     lens = g.integers(1, 1200, size=B)
     lens[:3] = [1, 63, 1151]
     K = (g.standard_normal((1, B, nkv, max_len, 128), dtype=np.float32))
