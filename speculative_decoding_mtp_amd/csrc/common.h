@@ -70,6 +70,10 @@ __device__ __forceinline__ uint4 ld_stream(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ float4 ld_stream_f4(const float* p) {
+  const uint4 v = ld_stream(p);
+  return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+}
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -335,8 +335,8 @@ __device__ __forceinline__ void load_tile(const float* x, int V, int base, float
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int k0 = base + 4 * (threadIdx.x + kWG * q);
-    if constexpr (VEC) {
-      const float4 f = *reinterpret_cast<const float4*>(x + min(k0, V - 4));
+    if constexpr (VEC) {  // each logit is read once: streamed past L2
+      const float4 f = ld_stream_f4(x + min(k0, V - 4));
       const bool in = k0 < V;
       v[4 * q] = in ? f.x : -INFINITY;
       v[4 * q + 1] = in ? f.y : -INFINITY;
