@@ -14,6 +14,7 @@
 // draft head"; [YL] "MTP 原理详解" sections 二.1-二.3 and 三 stages 1-2.
 #pragma once
 
+#include <functional>
 #include <type_traits>
 
 #include "draft.h"
@@ -117,6 +118,11 @@ struct PEhProj : PBase<W> {
   __device__ uint4 gain_raw(int k) const { return ld16(k < H ? enorm + k : hnorm + (k - H)); }
   __device__ const T* wrow(int m) const { return w + (long)m * (2 * H); }
   __device__ void store(int m, int, int row, float v) { xout[(long)row * H + m] = v; }
+  // store, returning the residual-stream value written
+  __device__ float reduce_store(int m, int, int row, float v) {
+    xout[(long)row * H + m] = v;
+    return v;
+  }
 };
 
 // Q/K/V projection of rms(x) with RoPE on q and k and the K/V append.  Logical rows are
@@ -201,6 +207,12 @@ struct PResidual : PBase<W> {
   }
   __device__ const T* wrow(int m) const { return w + (long)m * this->K; }
   __device__ void store(int m, int, int row, float v) { xres[(long)row * this->N + m] += v; }
+  // store, returning the residual-stream value written
+  __device__ float reduce_store(int m, int, int row, float v) {
+    const float x = xres[(long)row * this->N + m] + v;
+    xres[(long)row * this->N + m] = x;
+    return x;
+  }
 };
 
 // gate/up of rms(x), interleaved as (gate f, up f); stores silu(gate) * up
@@ -541,9 +553,17 @@ inline SgChoice plan_stream(int N, int K, int nact, bool whole_rows, long part_r
   return best;
 }
 
+// Replaces the split-K reduction after a stream GEMM (k_reduce_prep: the reduction fused with the
+// next GEMM's activation split); `used` is set when it ran, so the next GEMM skips its own split.
+using ReduceHook = std::function<hipError_t(const MfmaBufs&)>;
+struct ReduceCtx {
+  const ReduceHook* hook = nullptr;
+  bool* used = nullptr;
+};
+
 template <class P, int NT, int MT, int KPT, int AC = (MT <= 2 ? 256 : 128)>
 hipError_t launch_stream_t(P& p, hipStream_t st, int* grid_used, const MfmaBufs& mb, const KTimer& tm,
-                           const SgChoice& ch) {
+                           const SgChoice& ch, const ReduceCtx& rc) {
   if (KPT * 64 * ch.pl.nw < SgShape<MT, AC>::SLICE || ch.pl.nw > sg_max_waves(NT, MT))
     return hipErrorInvalidConfiguration;
   MfmaBufs m = mb;
@@ -562,6 +582,11 @@ hipError_t launch_stream_t(P& p, hipStream_t st, int* grid_used, const MfmaBufs&
   tm.begin(st, name);
   hipLaunchKernelGGL((k_gemm_stream<P, NT, MT, KPT, AC>), dim3(grid), dim3(64 * ch.pl.nw), 0, st, p, m, ch.pl);
   tm.end(st);
+  if (m.part && rc.hook) {
+    const hipError_t e = (*rc.hook)(m);
+    if (rc.used) *rc.used = e == hipSuccess;
+    return e;
+  }
   if (m.part) {
     const long items = (long)m.cap * (p.N / (P::kPair ? 2 : 1));
     const int rgrid = (int)std::min<long>((items + kWG - 1) / kWG, 4096);
@@ -573,7 +598,8 @@ hipError_t launch_stream_t(P& p, hipStream_t st, int* grid_used, const MfmaBufs&
 // The skinny MFMA GEMM: lm_head (argmax) and the target's lm_head keep whole rows (no split K)
 // with two tiles per wave; the other matrices take the planned decomposition.
 template <class P>
-hipError_t launch_stream(P& p, hipStream_t st, int* grid_used, const MfmaBufs& mb, const KTimer& tm) {
+hipError_t launch_stream(P& p, hipStream_t st, int* grid_used, const MfmaBufs& mb, const KTimer& tm,
+                         const ReduceCtx& rc) {
   const bool whole = P::kArgmax || P::kVocab;
   SgChoice ch;
   if (whole) {
@@ -611,38 +637,42 @@ hipError_t launch_stream(P& p, hipStream_t st, int* grid_used, const MfmaBufs& m
     // take 128-column activation ranges (fewer activation operand reads per weight byte)
     if (ch.mt == 2) {
       switch (ch.nt) {
-        case 3: return launch_stream_t<P, 3, 2, 1, 128>(p, st, grid_used, mb, tm, ch);
-        case 4: return launch_stream_t<P, 4, 2, 1, 128>(p, st, grid_used, mb, tm, ch);
-        case 5: return launch_stream_t<P, 5, 2, 1, 128>(p, st, grid_used, mb, tm, ch);
-        default: return launch_stream_t<P, 2, 2, 1>(p, st, grid_used, mb, tm, ch);
+        case 3: return launch_stream_t<P, 3, 2, 1, 128>(p, st, grid_used, mb, tm, ch, rc);
+        case 4: return launch_stream_t<P, 4, 2, 1, 128>(p, st, grid_used, mb, tm, ch, rc);
+        case 5: return launch_stream_t<P, 5, 2, 1, 128>(p, st, grid_used, mb, tm, ch, rc);
+        default: return launch_stream_t<P, 2, 2, 1>(p, st, grid_used, mb, tm, ch, rc);
       }
     }
-    return launch_stream_t<P, 2, 4, 2>(p, st, grid_used, mb, tm, ch);
+    return launch_stream_t<P, 2, 4, 2>(p, st, grid_used, mb, tm, ch, rc);
   } else {
     if (ch.mt == 2) {
       if (ch.nt == 2)
-        return seven ? launch_stream_t<P, 2, 2, 2>(p, st, grid_used, mb, tm, ch)
-                     : launch_stream_t<P, 2, 2, 1>(p, st, grid_used, mb, tm, ch);
-      return seven ? launch_stream_t<P, 1, 2, 2>(p, st, grid_used, mb, tm, ch)
-                   : launch_stream_t<P, 1, 2, 1>(p, st, grid_used, mb, tm, ch);
+        return seven ? launch_stream_t<P, 2, 2, 2>(p, st, grid_used, mb, tm, ch, rc)
+                     : launch_stream_t<P, 2, 2, 1>(p, st, grid_used, mb, tm, ch, rc);
+      return seven ? launch_stream_t<P, 1, 2, 2>(p, st, grid_used, mb, tm, ch, rc)
+                   : launch_stream_t<P, 1, 2, 1>(p, st, grid_used, mb, tm, ch, rc);
     }
     if (ch.nt == 2)
-      return seven ? launch_stream_t<P, 2, 4, 3>(p, st, grid_used, mb, tm, ch)
-                   : launch_stream_t<P, 2, 4, 2>(p, st, grid_used, mb, tm, ch);
-    return seven ? launch_stream_t<P, 1, 4, 3>(p, st, grid_used, mb, tm, ch)
-                 : launch_stream_t<P, 1, 4, 2>(p, st, grid_used, mb, tm, ch);
+      return seven ? launch_stream_t<P, 2, 4, 3>(p, st, grid_used, mb, tm, ch, rc)
+                   : launch_stream_t<P, 2, 4, 2>(p, st, grid_used, mb, tm, ch, rc);
+    return seven ? launch_stream_t<P, 1, 4, 3>(p, st, grid_used, mb, tm, ch, rc)
+                 : launch_stream_t<P, 1, 4, 2>(p, st, grid_used, mb, tm, ch, rc);
   }
 }
 
+// rc: a split-K stream GEMM's reduction may be replaced (the fused reduction + next split);
+// prepped: the split activations were already written by the previous GEMM's fused reduction.
 template <class W, class P>
 hipError_t launch_gemv(P& p, hipStream_t st, int* grid_used = nullptr, const MfmaBufs* mb = nullptr,
-                       const KTimer& tm = KTimer()) {
+                       const KTimer& tm = KTimer(), const ReduceCtx& rc = ReduceCtx(), bool prepped = false) {
   if constexpr (std::is_same<W, BF16>::value) {
     if (use_mfma<W>(p, mb)) {
-      if (p.K > 4 * kWG * W::VE)  // rows wider than 8192: the whole row in registers
+      if (prepped) {
+      } else if (p.K > 4 * kWG * W::VE) {  // rows wider than 8192: the whole row in registers
         hipLaunchKernelGGL((k_prep<W, P, 12>), dim3(p.nact), dim3(kWG), 0, st, p, *mb);
-      else
+      } else {
         hipLaunchKernelGGL((k_prep<W, P, 4>), dim3(p.nact), dim3(kWG), 0, st, p, *mb);
+      }
       if constexpr (!P::kArgmax) {
         // hundreds of rows (a prefill): 128 x 128 output tiles, when there are enough of them
         // (by the activation count, an upper bound of the valid rows) to fill the GPU
@@ -659,7 +689,7 @@ hipError_t launch_gemv(P& p, hipStream_t st, int* grid_used = nullptr, const Mfm
       }
       // 32-row passes for a batch of serial steps, 64-row passes above (by the activation count,
       // an upper bound of the valid rows)
-      return launch_stream(p, st, grid_used, *mb, tm);
+      return launch_stream(p, st, grid_used, *mb, tm, rc);
     }
   }
   const GemvPlan pl = plan_gemv(p.nact, p.K, W::VE, p.N);
@@ -718,6 +748,52 @@ void fill_base(P& p, const StepArgs& s) {
   p.rows = step_rows(s);
 }
 
+// Policy pairs whose split-K reduction and next activation split run as one k_reduce_prep: a
+// GEMM writing the residual stream followed by one that normalises it.
+template <class P, class Pn>
+struct CanFuse : std::false_type {};
+template <class W>
+struct CanFuse<PEhProj<W>, PQKV<W>> : std::true_type {};
+template <class W>
+struct CanFuse<PResidual<W>, PGateUp<W>> : std::true_type {};
+template <class W>
+struct CanFuse<PResidual<W>, PQKV<W>> : std::true_type {};
+template <class W>
+struct CanFuse<PResidual<W>, PLmHead<W>> : std::true_type {};
+
+template <class W, class P, class Pn>
+hipError_t launch_reduce_prep(const P& p, const Pn& pn, const MfmaBufs& m, hipStream_t st) {
+  if (p.N <= 4 * kWG * 8)
+    hipLaunchKernelGGL((k_reduce_prep<W, P, Pn, 4>), dim3(p.nact), dim3(kWG), 0, st, p, pn, m);
+  else
+    hipLaunchKernelGGL((k_reduce_prep<W, P, Pn, 12>), dim3(p.nact), dim3(kWG), 0, st, p, pn, m);
+  return hipGetLastError();
+}
+
+// Launch one GEMM of the step.  With a following GEMM `next` that can take the fused reduction
+// (both on the MFMA path, the row width within the fused kernel's registers), the hook replaces
+// this GEMM's split-K reduction; `prepped` carries whether it ran into the next launch.
+template <class W, class P, class Pn>
+hipError_t step_gemm(P& p, const Pn* next, const MfmaBufs* mb, hipStream_t st, bool& prepped, int* grid_used = nullptr,
+                     const KTimer& tm = KTimer()) {
+  const bool skip = prepped;
+  prepped = false;
+  ReduceHook hook;
+  ReduceCtx rc;
+  bool used = false;
+  if constexpr (std::is_same<W, BF16>::value && CanFuse<P, Pn>::value) {
+    if (next && mb && p.N == next->K && p.N % 8 == 0 && p.N <= 12 * kWG * 8 && use_mfma<W>(p, mb) &&
+        use_mfma<W>(*next, mb)) {
+      hook = [&p, next, st](const MfmaBufs& m) { return launch_reduce_prep<W>(p, *next, m, st); };
+      rc.hook = &hook;
+      rc.used = &used;
+    }
+  }
+  const hipError_t e = launch_gemv<W>(p, st, grid_used, mb, tm, rc, skip);
+  prepped = used;
+  return e;
+}
+
 template <class W>
 hipError_t run_step_t(const StepArgs& s) {
   using T = typename W::T;
@@ -730,6 +806,53 @@ hipError_t run_step_t(const StepArgs& s) {
   const MfmaBufs* mb = s.ws.xhi ? &mbuf : nullptr;
 
   if (step_rows(s) && (e = count_step_rows(s)) != hipSuccess) return e;
+  const mtp_layer_weights* layers = s.target ? s.tw->layers : s.w->layers;
+  // the step's GEMM policies, built ahead so that each launch knows the GEMM after it
+  auto layer_off = [&](int l) { return (long)(s.kv_layer ? s.kv_layer[l] : l) * s.B * nkv * s.max_len * hd; };
+  auto make_qkv = [&](int l) {  // q/k/v + RoPE + append
+    const mtp_layer_weights& lw = layers[l];
+    PQKV<W> p;
+    fill_base<W>(p, s);
+    p.K = H;
+    p.N = (nq + (s.shared ? 0 : 2 * nkv)) * hd;  // a head reading another cache projects q only
+    p.nact = R;
+    p.g = (const T*)lw.in_norm;
+    p.wq = (const T*)lw.wq;
+    p.wk = (const T*)lw.wk;
+    p.wv = (const T*)lw.wv;
+    p.xin = s.ws.x;
+    p.H = H;
+    p.nq = nq;
+    p.nkv = nkv;
+    p.hd = hd;
+    p.log_theta = log((double)c.rope_theta);
+    p.qout = s.ws.q;
+    p.kc = (T*)s.kc + layer_off(l);
+    p.vc = (T*)s.vc + layer_off(l);
+    p.pos_off = s.pos_off;
+    return p;
+  };
+  auto make_lm = [&]() {  // final norm + lm_head + argmax
+    PLmHead<W> p;
+    fill_base<W>(p, s);
+    p.K = H;
+    p.N = c.vocab;
+    p.nact = s.B;
+    p.g = (const T*)s.w->final_norm;
+    p.w = (const T*)s.w->lm_head;
+    p.xin = s.ws.x;
+    p.H = H;
+    p.logits = s.logits;
+    p.lg_sb = s.lg_sb;
+    p.part_v = s.ws.lm_part_v;
+    p.part_i = s.ws.lm_part_i;
+    return p;
+  };
+  const bool head = !s.target && !s.no_head;
+  PLmHead<W> plm;
+  if (head) plm = make_lm();
+  bool prepped = false;  // the next GEMM's split activations were written by a fused reduction
+  PQKV<W> pqkv = make_qkv(0);
   if (s.target) {  // the target's input: token embeddings
     hipLaunchKernelGGL((k_embed_rows<W>), dim3(R), dim3(kWG), 0, s.stream, s.tw->embed, s.tok, s.tok_sb, s.rps,
                        c.vocab, s.kv_len, s.max_len, H, s.ws.x, step_rows(s));
@@ -749,39 +872,16 @@ hipError_t run_step_t(const StepArgs& s) {
     p.hin_sb = s.hin_sb;
     p.H = H;
     p.xout = s.ws.x;
-    if ((e = launch_gemv<W>(p, s.stream, nullptr, mb)) != hipSuccess) return e;
+    if ((e = step_gemm<W>(p, &pqkv, mb, s.stream, prepped)) != hipSuccess) return e;
   }
-  const mtp_layer_weights* layers = s.target ? s.tw->layers : s.w->layers;
   for (int l = 0; l < c.n_layers; ++l) {
     const mtp_layer_weights& lw = layers[l];
-    const long layer_off = (long)(s.kv_layer ? s.kv_layer[l] : l) * s.B * nkv * s.max_len * hd;
-    {  // q/k/v + RoPE + append
-      PQKV<W> p;
-      fill_base<W>(p, s);
-      p.K = H;
-      p.N = (nq + (s.shared ? 0 : 2 * nkv)) * hd;  // a head reading another cache projects q only
-      p.nact = R;
-      p.g = (const T*)lw.in_norm;
-      p.wq = (const T*)lw.wq;
-      p.wk = (const T*)lw.wk;
-      p.wv = (const T*)lw.wv;
-      p.xin = s.ws.x;
-      p.H = H;
-      p.nq = nq;
-      p.nkv = nkv;
-      p.hd = hd;
-      p.log_theta = log((double)c.rope_theta);
-      p.qout = s.ws.q;
-      p.kc = (T*)s.kc + layer_off;
-      p.vc = (T*)s.vc + layer_off;
-      p.pos_off = s.pos_off;
-      if ((e = launch_gemv<W>(p, s.stream, nullptr, mb)) != hipSuccess) return e;
-    }
+    if ((e = step_gemm<W>(pqkv, (const PQKV<W>*)nullptr, mb, s.stream, prepped)) != hipSuccess) return e;
     {  // attention
       AttnArgs a;
       a.q = s.ws.q;
-      a.kc = (const T*)s.kc + layer_off;
-      a.vc = (const T*)s.vc + layer_off;
+      a.kc = (const T*)s.kc + layer_off(l);
+      a.vc = (const T*)s.vc + layer_off(l);
       a.tok = s.tok;
       a.tok_sb = s.tok_sb;
       a.len = s.kv_len;
@@ -798,6 +898,18 @@ hipError_t run_step_t(const StepArgs& s) {
       a.shared = s.shared;
       if ((e = run_attention(a, hd, c.wdtype, s.ws.attn_out, s.stream)) != hipSuccess) return e;
     }
+    PGateUp<W> pgu;  // gate/up + SwiGLU
+    fill_base<W>(pgu, s);
+    pgu.K = H;
+    pgu.N = 2 * F;
+    pgu.nact = R;
+    pgu.g = (const T*)lw.post_norm;
+    pgu.wg = (const T*)lw.wgate;
+    pgu.wu = (const T*)lw.wup;
+    pgu.xin = s.ws.x;
+    pgu.H = H;
+    pgu.F = F;
+    pgu.aout = s.ws.act;
     {  // o_proj + residual
       PResidual<W> p;
       fill_base<W>(p, s);
@@ -807,24 +919,10 @@ hipError_t run_step_t(const StepArgs& s) {
       p.w = (const T*)lw.wo;
       p.ain = s.ws.attn_out;
       p.xres = s.ws.x;
-      if ((e = launch_gemv<W>(p, s.stream, nullptr, mb)) != hipSuccess) return e;
+      if ((e = step_gemm<W>(p, &pgu, mb, s.stream, prepped)) != hipSuccess) return e;
     }
-    {  // gate/up + SwiGLU
-      PGateUp<W> p;
-      fill_base<W>(p, s);
-      p.K = H;
-      p.N = 2 * F;
-      p.nact = R;
-      p.g = (const T*)lw.post_norm;
-      p.wg = (const T*)lw.wgate;
-      p.wu = (const T*)lw.wup;
-      p.xin = s.ws.x;
-      p.H = H;
-      p.F = F;
-      p.aout = s.ws.act;
-      if ((e = launch_gemv<W>(p, s.stream, nullptr, mb)) != hipSuccess) return e;
-    }
-    {  // down + residual
+    if ((e = step_gemm<W>(pgu, (const PQKV<W>*)nullptr, mb, s.stream, prepped)) != hipSuccess) return e;
+    {  // down + residual, then the next layer's q/k/v or the lm_head
       PResidual<W> p;
       fill_base<W>(p, s);
       p.K = F;
@@ -833,7 +931,13 @@ hipError_t run_step_t(const StepArgs& s) {
       p.w = (const T*)lw.wdown;
       p.ain = s.ws.act;
       p.xres = s.ws.x;
-      if ((e = launch_gemv<W>(p, s.stream, nullptr, mb)) != hipSuccess) return e;
+      if (l + 1 < c.n_layers) {
+        pqkv = make_qkv(l + 1);
+        e = step_gemm<W>(p, &pqkv, mb, s.stream, prepped);
+      } else {
+        e = step_gemm<W>(p, head ? &plm : nullptr, mb, s.stream, prepped);
+      }
+      if (e != hipSuccess) return e;
     }
   }
   if (s.target) {  // final norm + lm_head over every valid row, hiddens, len
@@ -890,25 +994,12 @@ hipError_t run_step_t(const StepArgs& s) {
     return launch_finalize<W>(f, s.stream);
   }
   {  // final norm + lm_head + argmax + finalisation
-    PLmHead<W> p;
-    fill_base<W>(p, s);
-    p.K = H;
-    p.N = c.vocab;
-    p.nact = s.B;
-    p.g = (const T*)s.w->final_norm;
-    p.w = (const T*)s.w->lm_head;
-    p.xin = s.ws.x;
-    p.H = H;
-    p.logits = s.logits;
-    p.lg_sb = s.lg_sb;
-    p.part_v = s.ws.lm_part_v;
-    p.part_i = s.ws.lm_part_i;
     int grid = 0;
     KTimer tm;
     tm.b = s.ev_begin;
     tm.e = s.ev_end;
     tm.name = s.ev_name;
-    e = launch_gemv<W>(p, s.stream, &grid, mb, tm);
+    e = step_gemm<W>(plm, (const PQKV<W>*)nullptr, mb, s.stream, prepped, &grid, tm);
     if (e != hipSuccess) return e;
     LmFinal f;
     f.B = s.B;

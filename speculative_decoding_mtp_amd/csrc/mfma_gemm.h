@@ -152,6 +152,124 @@ __global__ __launch_bounds__(kWG) void k_prep(P p, MfmaBufs mb) {
   }
 }
 
+// A split-K GEMM whose outputs are the residual stream (eh_proj, o_proj, down_proj) followed by a
+// GEMM that normalises that stream (QKV, gate/up, lm_head): one workgroup per row sums the
+// row's partials in split order and stores it through P (as k_splitk_reduce does), keeps it in
+// registers and prepares Pn's split activations from it (as k_prep does: the same chunks per
+// thread, the same sums, so the activations are bit-identical) -- one launch instead of two.
+// Rows are P's activation rows; with an argmax Pn (one row per sequence) only each sequence's
+// last valid row is prepared, at the sequence's compact index.  Requires P::N == Pn::K and
+// N <= KEEP * kWG * 8.  The compact maps and count written are Pn's.
+template <class W, class P, class Pn, int KEEP>
+__global__ __launch_bounds__(kWG) void k_reduce_prep(P p, Pn pn, MfmaBufs mb) {
+  constexpr int VE = 8;
+  static_assert(!P::kPair && Pn::kNorm == 1, "a residual-stream reduction feeding one RMSNorm");
+  __shared__ int s_n[kMaxBatch];
+  __shared__ int s_len[kMaxBatch];
+  __shared__ float red[8];
+  const int a = blockIdx.x, tid = threadIdx.x;
+  const int N = p.N, Kc = N / VE;
+  p.setup(s_n, s_len);
+  __syncthreads();
+  int row;
+  bool valid;
+  p.act(a, s_n, row, valid);
+  const int b = a / p.rps, i = a - b * p.rps;
+  int c = 0, total = 0, cs = 0, nseq = 0;  // compact index (P's rows, and Pn's for argmax)
+  for (int bb = 0; bb < p.B; ++bb) {
+    const int nb = s_n[bb];
+    if (bb < b) {
+      c += nb;
+      cs += nb > 0 ? 1 : 0;
+    }
+    total += nb;
+    nseq += nb > 0 ? 1 : 0;
+  }
+  c += i;
+  if (a == 0 && tid == 0) *mb.count = Pn::kArgmax ? nseq : total;
+  if (!valid) return;
+  // partial sums in split order; the loads of QS splits of every chunk are issued together
+  // (chunk columns clamped, so every load is in bounds and unconditional)
+  constexpr int QS = KEEP <= 4 ? 4 : 1;
+  float v[KEEP][VE];
+#pragma unroll
+  for (int k = 0; k < KEEP; ++k)
+#pragma unroll
+    for (int e = 0; e < VE; ++e) v[k][e] = 0.f;
+  const float* pc = mb.part + (long)c * N;
+  const long sstride = (long)mb.cap * N;
+  for (int sp = 0; sp < mb.ksplit; sp += QS) {
+    float4 u[QS][KEEP][2];
+#pragma unroll
+    for (int q = 0; q < QS; ++q)
+#pragma unroll
+      for (int k = 0; k < KEEP; ++k) {
+        const float* pp = pc + (long)min(sp + q, mb.ksplit - 1) * sstride + min(tid + k * kWG, Kc - 1) * VE;
+        u[q][k][0] = *reinterpret_cast<const float4*>(pp);
+        u[q][k][1] = *reinterpret_cast<const float4*>(pp + 4);
+      }
+#pragma unroll
+    for (int q = 0; q < QS; ++q)
+      if (sp + q < mb.ksplit) {
+#pragma unroll
+        for (int k = 0; k < KEEP; ++k) {
+          v[k][0] += u[q][k][0].x; v[k][1] += u[q][k][0].y; v[k][2] += u[q][k][0].z; v[k][3] += u[q][k][0].w;
+          v[k][4] += u[q][k][1].x; v[k][5] += u[q][k][1].y; v[k][6] += u[q][k][1].z; v[k][7] += u[q][k][1].w;
+        }
+      }
+  }
+  float x[KEEP][VE];
+#pragma unroll
+  for (int k = 0; k < KEEP; ++k) {
+    const int ch = tid + k * kWG;
+    if (ch < Kc) {
+#pragma unroll
+      for (int e = 0; e < VE; ++e) x[k][e] = p.reduce_store(ch * VE + e, a, row, v[k][e]);
+    }
+  }
+  int cn = c;
+  if constexpr (Pn::kArgmax) {  // the sequence's last valid row only (uniform per workgroup)
+    if (i != s_n[b] - 1) return;
+    cn = cs;
+  }
+  float ss[2] = {0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < KEEP; ++k)
+    if (tid + k * kWG < Kc) {
+      float sq = 0.f;
+#pragma unroll
+      for (int e = 0; e < VE; ++e) sq = fmaf(x[k][e], x[k][e], sq);
+      ss[0] += sq;
+    }
+  wg_sum<2>(ss, red);
+  const float sc = 1.0f / sqrtf(ss[0] / float(pn.K) + pn.eps);
+  uint16_t* hi = mb.xhi + (long)cn * pn.K;
+  uint16_t* lo = mb.xlo + (long)cn * pn.K;
+#pragma unroll
+  for (int k = 0; k < KEEP; ++k) {
+    const int ch = tid + k * kWG;
+    if (ch < Kc) {
+      float g[VE];
+      W::cvt(pn.gain_raw(ch * VE), g);
+      uint32_t h2[VE / 2], l2[VE / 2];
+#pragma unroll
+      for (int e = 0; e < VE; e += 2) {
+        const float x0 = x[k][e] * sc * g[e], x1 = x[k][e + 1] * sc * g[e + 1];
+        const uint32_t a0 = bf16_rne(x0), a1 = bf16_rne(x1);
+        const uint32_t b0 = bf16_rne(x0 - __uint_as_float(a0 << 16)), b1 = bf16_rne(x1 - __uint_as_float(a1 << 16));
+        h2[e / 2] = a0 | (a1 << 16);
+        l2[e / 2] = b0 | (b1 << 16);
+      }
+      *reinterpret_cast<uint4*>(hi + ch * VE) = make_uint4(h2[0], h2[1], h2[2], h2[3]);
+      *reinterpret_cast<uint4*>(lo + ch * VE) = make_uint4(l2[0], l2[1], l2[2], l2[3]);
+    }
+  }
+  if (tid == 0) {
+    mb.rowmap[cn] = row;
+    mb.amap[cn] = Pn::kArgmax ? b : a;
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // Large tiles for calls with hundreds of activation rows (a prefill).  The streaming kernel
 // (stream_gemm.h) reads the whole weight matrix once per 64-row pass; here each workgroup owns a 128
