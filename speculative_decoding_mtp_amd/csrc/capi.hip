@@ -114,7 +114,7 @@ int check_kv(const mtp_kv* kv) {
 
 // ------------------------------------------------------------------ drafter workspace
 struct DraftLayout {
-  size_t off[15];
+  size_t off[17];
   size_t total;
   int nsplit;  // attention splits the partial buffer is laid out for
 };
@@ -127,7 +127,7 @@ DraftLayout draft_layout(const mtp_config& c, int B, int rps, int D, int max_len
   if ((size_t)c.ffn > kmax) kmax = c.ffn;
   if ((size_t)c.n_heads * c.head_dim > kmax) kmax = (size_t)c.n_heads * c.head_dim;
   const bool mfma = c.wdtype == MTP_BF16 && R >= 3;  // more rows than one VALU GEMV pass may hold
-  const size_t sizes[15] = {
+  const size_t sizes[17] = {
       256 + (size_t)B * 8,                                                   // status word, row counts
       R * c.hidden * 4,                                                      // x
       R * c.n_heads * c.head_dim * 4,                                        // q
@@ -142,10 +142,12 @@ DraftLayout draft_layout(const mtp_config& c, int B, int rps, int D, int max_len
       mfma ? R * 4 : 0,                                                      // compact row map
       mfma ? R * 4 : 0,                                                      // compact activation map
       mfma ? (size_t)4 : (size_t)0,                                          // compact count
-      mfma ? R * kPartCols * 4 : 0};                                         // split-K partials
+      mfma ? R * c.ffn * 2 : 0,                                              // SwiGLU output split, hi
+      mfma ? R * c.ffn * 2 : 0,                                              // SwiGLU output split, lo
+      mfma ? R * kPartCols * 4 : 0};                                         // split-K partials (last)
   DraftLayout L;
   size_t o = 0;
-  for (int i = 0; i < 15; ++i) {
+  for (int i = 0; i < 17; ++i) {
     L.off[i] = o;
     o += up256(sizes[i]);
   }
@@ -173,8 +175,10 @@ DraftWs carve(void* ws, const DraftLayout& L) {
   w.rowmap = mfma ? reinterpret_cast<int*>(base + L.off[11]) : nullptr;
   w.amap = mfma ? reinterpret_cast<int*>(base + L.off[12]) : nullptr;
   w.mcount = mfma ? reinterpret_cast<int*>(base + L.off[13]) : nullptr;
-  w.kpart = mfma ? reinterpret_cast<float*>(base + L.off[14]) : nullptr;
-  w.kpart_cap = mfma ? (long)((L.total - L.off[14]) / 4) : 0;
+  w.shi = mfma ? reinterpret_cast<uint16_t*>(base + L.off[14]) : nullptr;
+  w.slo = mfma ? reinterpret_cast<uint16_t*>(base + L.off[15]) : nullptr;
+  w.kpart = mfma ? reinterpret_cast<float*>(base + L.off[16]) : nullptr;
+  w.kpart_cap = mfma ? (long)((L.total - L.off[16]) / 4) : 0;
   return w;
 }
 

@@ -78,6 +78,7 @@ struct DraftWs {
   uint16_t *xhi, *xlo;  // [R][Kmax]
   int *rowmap, *amap;   // [R]
   int* mcount;
+  uint16_t *shi, *slo;  // [R][F] the SwiGLU output split by the gate/up GEMM for down_proj
   float* kpart;    // [kPartCols][R] split-K partial sums
   long kpart_cap;  // floats in kpart
 };

@@ -33,6 +33,7 @@ struct PBase {
   static constexpr bool kPair = false;
   static constexpr bool kArgmax = false;
   static constexpr bool kVocab = false;  // output rows are a vocabulary (MFMA: 128 rows per workgroup)
+  static constexpr bool kSplitOut = false;  // can also write its outputs split for the next GEMM
   const int32_t* tok;
   int tok_sb;
   int B, rps;
@@ -231,6 +232,16 @@ struct PGateUp : PBase<W> {
   __device__ const T* wrow(int m) const { return ((m & 1) ? wu : wg) + (long)(m >> 1) * H; }
   __device__ void store_pair(int m, int, int row, float gt, float up) {
     aout[(long)row * F + (m >> 1)] = gt / (1.0f + expf(-gt)) * up;
+  }
+  // the same, and the value split into bf16 hi + lo at compact row cr of down_proj's activations
+  // (the split k_prep would make of it: the down projection takes it without a preparation)
+  static constexpr bool kSplitOut = true;
+  __device__ void store_pair_split(int m, int, int row, int cr, float gt, float up, uint16_t* shi, uint16_t* slo) {
+    const float y = gt / (1.0f + expf(-gt)) * up;
+    aout[(long)row * F + (m >> 1)] = y;
+    const uint32_t h = bf16_rne(y);
+    shi[(long)cr * F + (m >> 1)] = (uint16_t)h;
+    slo[(long)cr * F + (m >> 1)] = (uint16_t)bf16_rne(y - __uint_as_float(h << 16));
   }
 };
 
@@ -556,8 +567,10 @@ inline SgChoice plan_stream(int N, int K, int nact, bool whole_rows, long part_r
 // Replaces the split-K reduction after a stream GEMM (k_reduce_prep: the reduction fused with the
 // next GEMM's activation split); `used` is set when it ran, so the next GEMM skips its own split.
 using ReduceHook = std::function<hipError_t(const MfmaBufs&)>;
+// split: a kSplitOut GEMM also writes its outputs split for the next GEMM (into mb.shi / slo).
 struct ReduceCtx {
   const ReduceHook* hook = nullptr;
+  bool split = false;
   bool* used = nullptr;
 };
 
@@ -569,6 +582,8 @@ hipError_t launch_stream_t(P& p, hipStream_t st, int* grid_used, const MfmaBufs&
   MfmaBufs m = mb;
   if (ch.pl.ks <= 1) m.part = nullptr;
   m.ksplit = ch.pl.ks;
+  if (!rc.split) m.shi = m.slo = nullptr;
+  if (rc.split && rc.used) *rc.used = true;  // the epilogue or the reduction below writes them
   int grid = min(ch.items, device_cus());
   grid = max(1, min(grid, kMaxGemvGrid));
   if (grid_used) *grid_used = grid;
@@ -770,27 +785,58 @@ hipError_t launch_reduce_prep(const P& p, const Pn& pn, const MfmaBufs& m, hipSt
   return hipGetLastError();
 }
 
-// Launch one GEMM of the step.  With a following GEMM `next` that can take the fused reduction
-// (both on the MFMA path, the row width within the fused kernel's registers), the hook replaces
-// this GEMM's split-K reduction; `prepped` carries whether it ran into the next launch.
+// Where the next GEMM of a step finds its split activations already written: nowhere (it runs
+// its own k_prep), in the primary buffers (a fused reduction), or in the SwiGLU split buffers
+// (written by the gate/up GEMM for down_proj).
+enum class Prepped { kNo, kPrimary, kSwiglu };
+
+template <class P, class Pn>
+struct SplitsFor : std::false_type {};
+template <class W>
+struct SplitsFor<PGateUp<W>, PResidual<W>> : std::true_type {};
+
+// Launch one GEMM of the step.  With a following GEMM `next` that can take its outputs already
+// prepared (both on the MFMA path, the row width within the fused kernel's registers), either
+// the split-K reduction is replaced by k_reduce_prep or the GEMM writes the split itself;
+// `prepped` carries what ran into the next launch.
 template <class W, class P, class Pn>
-hipError_t step_gemm(P& p, const Pn* next, const MfmaBufs* mb, hipStream_t st, bool& prepped, int* grid_used = nullptr,
-                     const KTimer& tm = KTimer()) {
-  const bool skip = prepped;
-  prepped = false;
+hipError_t step_gemm(P& p, const Pn* next, const MfmaBufs* mb, hipStream_t st, Prepped& prepped,
+                     int* grid_used = nullptr, const KTimer& tm = KTimer()) {
+  const Prepped have = prepped;
+  prepped = Prepped::kNo;
+  MfmaBufs alt;
+  const MfmaBufs* use = mb;
+  if (mb && have == Prepped::kSwiglu) {
+    alt = *mb;
+    alt.xhi = mb->shi;
+    alt.xlo = mb->slo;
+    use = &alt;
+  }
   ReduceHook hook;
   ReduceCtx rc;
-  bool used = false;
+  bool used = false, split = false;
   if constexpr (std::is_same<W, BF16>::value && CanFuse<P, Pn>::value) {
     if (next && mb && p.N == next->K && p.N % 8 == 0 && p.N <= 12 * kWG * 8 && use_mfma<W>(p, mb) &&
         use_mfma<W>(*next, mb)) {
-      hook = [&p, next, st](const MfmaBufs& m) { return launch_reduce_prep<W>(p, *next, m, st); };
+      // the next GEMM's activations go to the primary buffers (this GEMM has finished with them)
+      hook = [&p, next, st, mb](const MfmaBufs& m) {
+        MfmaBufs m2 = m;
+        m2.xhi = mb->xhi;
+        m2.xlo = mb->xlo;
+        return launch_reduce_prep<W>(p, *next, m2, st);
+      };
       rc.hook = &hook;
       rc.used = &used;
     }
   }
-  const hipError_t e = launch_gemv<W>(p, st, grid_used, mb, tm, rc, skip);
-  prepped = used;
+  if constexpr (std::is_same<W, BF16>::value && SplitsFor<P, Pn>::value) {
+    if (next && mb && mb->shi && 2 * next->K == p.N && use_mfma<W>(p, mb) && use_mfma<W>(*next, mb)) {
+      rc.split = split = true;
+      rc.used = &used;
+    }
+  }
+  const hipError_t e = launch_gemv<W>(p, st, grid_used, use, tm, rc, have != Prepped::kNo);
+  if (used) prepped = split ? Prepped::kSwiglu : Prepped::kPrimary;
   return e;
 }
 
@@ -802,7 +848,7 @@ hipError_t run_step_t(const StepArgs& s) {
   const int R = s.B * s.rps;
   hipError_t e;
   const MfmaBufs mbuf = {s.ws.xhi, s.ws.xlo, s.ws.rowmap, s.ws.amap, s.ws.mcount, s.ws.kpart, 1, s.B * s.rps,
-                         s.ws.kpart_cap};
+                         s.ws.kpart_cap, s.ws.shi, s.ws.slo};
   const MfmaBufs* mb = s.ws.xhi ? &mbuf : nullptr;
 
   if (step_rows(s) && (e = count_step_rows(s)) != hipSuccess) return e;
@@ -851,7 +897,7 @@ hipError_t run_step_t(const StepArgs& s) {
   const bool head = !s.target && !s.no_head;
   PLmHead<W> plm;
   if (head) plm = make_lm();
-  bool prepped = false;  // the next GEMM's split activations were written by a fused reduction
+  Prepped prepped = Prepped::kNo;  // where the next GEMM's split activations already are
   PQKV<W> pqkv = make_qkv(0);
   if (s.target) {  // the target's input: token embeddings
     hipLaunchKernelGGL((k_embed_rows<W>), dim3(R), dim3(kWG), 0, s.stream, s.tw->embed, s.tok, s.tok_sb, s.rps,
@@ -921,16 +967,17 @@ hipError_t run_step_t(const StepArgs& s) {
       p.xres = s.ws.x;
       if ((e = step_gemm<W>(p, &pgu, mb, s.stream, prepped)) != hipSuccess) return e;
     }
-    if ((e = step_gemm<W>(pgu, (const PQKV<W>*)nullptr, mb, s.stream, prepped)) != hipSuccess) return e;
-    {  // down + residual, then the next layer's q/k/v or the lm_head
-      PResidual<W> p;
-      fill_base<W>(p, s);
-      p.K = F;
-      p.N = H;
-      p.nact = R;
-      p.w = (const T*)lw.wdown;
-      p.ain = s.ws.act;
-      p.xres = s.ws.x;
+    PResidual<W> pdn;  // down + residual
+    fill_base<W>(pdn, s);
+    pdn.K = F;
+    pdn.N = H;
+    pdn.nact = R;
+    pdn.w = (const T*)lw.wdown;
+    pdn.ain = s.ws.act;
+    pdn.xres = s.ws.x;
+    if ((e = step_gemm<W>(pgu, &pdn, mb, s.stream, prepped)) != hipSuccess) return e;
+    {  // then the next layer's q/k/v or the lm_head
+      PResidual<W>& p = pdn;
       if (l + 1 < c.n_layers) {
         pqkv = make_qkv(l + 1);
         e = step_gemm<W>(p, &pqkv, mb, s.stream, prepped);

@@ -31,6 +31,8 @@ struct MfmaBufs {
   float* part;          // split-K partial sums [ksplit][cap][N] (NULL: no split)
   int ksplit, cap;      // K ranges; activation rows the partial buffer is laid out for
   long part_cap;        // floats available at part
+  uint16_t *shi, *slo;  // NULL, or where a policy with kSplitOut also writes its outputs split
+                        // hi / lo (compact rows of width N / 2) for the next GEMM
 };
 
 // One workgroup per activation index a (grid = nact).  The first KEEP chunks of each thread
@@ -435,10 +437,18 @@ __global__ __launch_bounds__(kWG) void k_splitk_reduce(P p, MfmaBufs mb) {
       if (P::kPair) v1 += pp[1];
     }
     const int row = mb.rowmap[cr], a = mb.amap[cr];
-    if constexpr (P::kPair)
-      p.store_pair(col, a, row, v0, v1);
-    else
+    if constexpr (P::kPair) {
+      if constexpr (P::kSplitOut) {
+        if (mb.shi)
+          p.store_pair_split(col, a, row, cr, v0, v1, mb.shi, mb.slo);
+        else
+          p.store_pair(col, a, row, v0, v1);
+      } else {
+        p.store_pair(col, a, row, v0, v1);
+      }
+    } else {
       p.store(col, a, row, v0);
+    }
   }
 }
 

@@ -251,7 +251,16 @@ __global__ __launch_bounds__(64 * sg_max_waves(NT, MT)) void k_gemm_stream(P p, 
             if (cr < count && col < p.N) {
               const int row = mb.rowmap[cr], a = mb.amap[cr];
               if constexpr (P::kPair) {
-                if ((jl & 1) == 0) p.store_pair(col, a, row, v, partner);
+                if ((jl & 1) == 0) {
+                  if constexpr (P::kSplitOut) {
+                    if (mb.shi)
+                      p.store_pair_split(col, a, row, cr, v, partner, mb.shi, mb.slo);
+                    else
+                      p.store_pair(col, a, row, v, partner);
+                  } else {
+                    p.store_pair(col, a, row, v, partner);
+                  }
+                }
               } else {
                 p.store(col, a, row, v);
               }
