@@ -10,6 +10,28 @@
 
 namespace mtp {
 
+// The compact row of row 0 of sequence b: the valid rows of the sequences before it (the row
+// order of the MFMA GEMMs' split activations).  Thread t < B counts sequence t into s_cnt; call
+// with the whole workgroup (it contains a barrier).
+__device__ int attn_compact_base(const AttnArgs& a, int b, int* s_cnt) {
+  for (int t = threadIdx.x; t < a.B; t += blockDim.x)
+    s_cnt[t] = a.rows ? a.rows[t] : count_rows(a.tok + (long)t * a.tok_sb, a.rps, a.V, a.len[t], a.max_len, nullptr);
+  __syncthreads();
+  int c = 0;
+  for (int t = 0; t < b; ++t) c += s_cnt[t];
+  return c;
+}
+
+// One output value: at `o` of out, and split into bf16 hi + lo at `c` of a.shi / a.slo (when set).
+__device__ __forceinline__ void attn_store(const AttnArgs& a, float* out, long o, long c, float v) {
+  out[o] = v;
+  if (a.shi) {
+    const uint32_t h = bf16_rne(v);
+    a.shi[c] = (uint16_t)h;
+    a.slo[c] = (uint16_t)bf16_rne(v - __uint_as_float(h << 16));
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // decode attention, split over the cached positions (fp32 caches: VALU kernel)
 // ---------------------------------------------------------------------------------------------
@@ -246,6 +268,8 @@ __global__ __launch_bounds__(kWG) void k_attn_mfma(AttnArgs a) {
   if (p_beg >= Tn) return;
   const int p_end = min(Tn, p_beg + chunk);
   const int NQ = n * G;
+  __shared__ int s_cnt[kMaxBatch];
+  const int cbase = a.shi ? attn_compact_base(a, b, s_cnt) : 0;
   const uint16_t* Kb = reinterpret_cast<const uint16_t*>(a.kc) + ((long)b * a.nkv + kvh) * a.max_len * HD;
   const uint16_t* Vt = reinterpret_cast<const uint16_t*>(a.vc) + ((long)b * a.nkv + kvh) * a.max_len * HD;
   const float scale = 1.0f / sqrtf(float(HD));
@@ -421,7 +445,8 @@ __global__ __launch_bounds__(kWG) void k_attn_mfma(AttnArgs a) {
         const int q = idx / HD, d = idx - q * HD, qi = q0 + q;
         if (qi < NQ) {
           const int i = qi / G, g = qi - i * G;
-          a.out[(((long)b * a.rps + i) * a.nq + kvh * G + g) * HD + d] = sO[q * OP + d] / sl[0][q];
+          attn_store(a, a.out, (((long)b * a.rps + i) * a.nq + kvh * G + g) * HD + d,
+                     (long)(cbase + i) * a.nq * HD + (kvh * G + g) * HD + d, sO[q * OP + d] / sl[0][q]);
         }
       }
     } else {
@@ -500,6 +525,8 @@ __global__ __launch_bounds__(64 * NWV) void k_attn_lds(AttnArgs a) {
   if (p_beg >= Tn) return;
   const int p_end = min(Tn, p_beg + chunk);
   const int NQ = n * G;
+  __shared__ int s_cnt[kMaxBatch];
+  const int cbase = a.shi ? attn_compact_base(a, b, s_cnt) : 0;
   const uint16_t* Kb = reinterpret_cast<const uint16_t*>(a.kc) + ((long)b * a.nkv + kvh) * a.max_len * HD;
   const uint16_t* Vt = reinterpret_cast<const uint16_t*>(a.vc) + ((long)b * a.nkv + kvh) * a.max_len * HD;
   const float scale = 1.0f / sqrtf(float(HD));
@@ -729,7 +756,8 @@ __global__ __launch_bounds__(64 * NWV) void k_attn_lds(AttnArgs a) {
         const int q = idx / HD, d = idx - q * HD, qi = q0 + q;
         if (qi < NQ) {
           const int i = qi / G, g = qi - i * G;
-          a.out[(((long)b * a.rps + i) * a.nq + kvh * G + g) * HD + d] = sO[q * OP + d] / sl[0][q];
+          attn_store(a, a.out, (((long)b * a.rps + i) * a.nq + kvh * G + g) * HD + d,
+                     (long)(cbase + i) * a.nq * HD + (kvh * G + g) * HD + d, sO[q * OP + d] / sl[0][q]);
         }
       }
     } else {
@@ -764,6 +792,8 @@ __global__ __launch_bounds__(kWG) void k_attn_combine(AttnArgs a, float* out) {
   const int b = row / a.rps, i = row - b * a.rps;
   const int n = a.rows ? a.rows[b] : count_rows(a.tok + (long)b * a.tok_sb, a.rps, a.V, a.len[b], a.max_len, nullptr);
   if (i >= n) return;
+  __shared__ int s_cnt[kMaxBatch];
+  const int cbase = a.shi ? attn_compact_base(a, b, s_cnt) : 0;
   const int G = a.nq / a.nkv, kvh = h / G, qi = i * G + (h - kvh * G);
   const int Tn = a.len[b] + (a.shared ? 0 : n);
   const int chunk = attn_chunk(Tn, a.nsplit);
@@ -797,7 +827,7 @@ __global__ __launch_bounds__(kWG) void k_attn_combine(AttnArgs a, float* out) {
       Ot += so[q][d];
       Lt += sL[q];
     }
-    out[((long)row * a.nq + h) * HD + d] = Ot / Lt;
+    attn_store(a, out, ((long)row * a.nq + h) * HD + d, (long)(cbase + i) * a.nq * HD + h * HD + d, Ot / Lt);
   }
 }
 

@@ -37,6 +37,9 @@ struct AttnArgs {
   const int* rows;   // NULL, or the valid rows of sequence b at rows[b]
   float* out;        // set by run_attention: one split of a bf16 cache writes the output rows here
   int shared;        // 1: the rows read a cache they do not append to (keys 0 .. len[b] - 1 only)
+  uint16_t *shi, *slo;  // NULL, or where the output rows also go split into bf16 hi + lo, at their
+                        // compact row (valid rows of all sequences in order) x nq * hd: the
+                        // activations of o_proj on the MFMA path
 };
 
 // Arguments of the lm_head finalisation kernel.

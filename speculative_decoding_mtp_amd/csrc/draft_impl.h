@@ -923,6 +923,14 @@ hipError_t run_step_t(const StepArgs& s) {
   for (int l = 0; l < c.n_layers; ++l) {
     const mtp_layer_weights& lw = layers[l];
     if ((e = step_gemm<W>(pqkv, (const PQKV<W>*)nullptr, mb, s.stream, prepped)) != hipSuccess) return e;
+    PResidual<W> po;  // o_proj + residual
+    fill_base<W>(po, s);
+    po.K = nq * hd;
+    po.N = H;
+    po.nact = R;
+    po.w = (const T*)lw.wo;
+    po.ain = s.ws.attn_out;
+    po.xres = s.ws.x;
     {  // attention
       AttnArgs a;
       a.q = s.ws.q;
@@ -942,7 +950,13 @@ hipError_t run_step_t(const StepArgs& s) {
       a.part = s.ws.attn_part;
       a.rows = step_rows(s);
       a.shared = s.shared;
+      a.shi = a.slo = nullptr;
+      if (mb && use_mfma<W>(po, mb)) {  // o_proj's split activations straight from the attention
+        a.shi = mb->xhi;
+        a.slo = mb->xlo;
+      }
       if ((e = run_attention(a, hd, c.wdtype, s.ws.attn_out, s.stream)) != hipSuccess) return e;
+      if (a.shi) prepped = Prepped::kPrimary;
     }
     PGateUp<W> pgu;  // gate/up + SwiGLU
     fill_base<W>(pgu, s);
@@ -956,17 +970,7 @@ hipError_t run_step_t(const StepArgs& s) {
     pgu.H = H;
     pgu.F = F;
     pgu.aout = s.ws.act;
-    {  // o_proj + residual
-      PResidual<W> p;
-      fill_base<W>(p, s);
-      p.K = nq * hd;
-      p.N = H;
-      p.nact = R;
-      p.w = (const T*)lw.wo;
-      p.ain = s.ws.attn_out;
-      p.xres = s.ws.x;
-      if ((e = step_gemm<W>(p, &pgu, mb, s.stream, prepped)) != hipSuccess) return e;
-    }
+    if ((e = step_gemm<W>(po, &pgu, mb, s.stream, prepped)) != hipSuccess) return e;
     PResidual<W> pdn;  // down + residual
     fill_base<W>(pdn, s);
     pdn.K = F;
