@@ -689,12 +689,14 @@ hipError_t launch_gemv(P& p, hipStream_t st, int* grid_used = nullptr, const Mfm
         hipLaunchKernelGGL((k_prep<W, P, 4>), dim3(p.nact), dim3(kWG), 0, st, p, *mb);
       }
       if constexpr (!P::kArgmax) {
-        // hundreds of rows (a prefill): 128 x 128 output tiles, when there are enough of them
-        // (by the activation count, an upper bound of the valid rows) to fill the GPU
+        // hundreds of rows (a prefill, by the activation count, an upper bound of the valid
+        // rows): 128 x 128 output tiles, even when they do not fill the GPU -- the streaming
+        // kernel would read the weights once per 64 rows (2048 rows of a 3072 x 2048 QKV: 1.2 ms
+        // against ~0.1 ms)
         static int cap = 0;
         const long items = (long)((p.nact + kTileM - 1) / kTileM) * ((p.N + kTileN - 1) / kTileN);
-        if (p.nact >= kTileRows && items >= resident_cap(k_gemm_tile<P>, &cap)) {
-          const int grid = resident_cap(k_gemm_tile<P>, &cap);
+        if (p.nact >= kTileRows) {
+          const int grid = (int)std::min<long>(items, resident_cap(k_gemm_tile<P>, &cap));
           if (grid_used) *grid_used = grid;
           tm.begin(st, "k_gemm_tile");
           hipLaunchKernelGGL((k_gemm_tile<P>), dim3(grid), dim3(kWG), 0, st, p, *mb);
