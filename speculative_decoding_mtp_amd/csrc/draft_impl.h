@@ -694,13 +694,39 @@ hipError_t launch_gemv(P& p, hipStream_t st, int* grid_used = nullptr, const Mfm
         // kernel would read the weights once per 64 rows (2048 rows of a 3072 x 2048 QKV: 1.2 ms
         // against ~0.1 ms)
         static int cap = 0;
-        const long items = (long)((p.nact + kTileM - 1) / kTileM) * ((p.N + kTileN - 1) / kTileN);
+        const long tiles = (long)((p.nact + kTileM - 1) / kTileM) * ((p.N + kTileN - 1) / kTileN);
         if (p.nact >= kTileRows) {
-          const int grid = (int)std::min<long>(items, resident_cap(k_gemm_tile<P>, &cap));
+          const int slots = resident_cap(k_gemm_tile<P>, &cap);
+          // K ranges side by side while the tiles leave resident slots empty (two per compute
+          // unit; 2048 rows of down_proj, 2048 x 6144: 192 -> 150 us at two ranges; QKV 3072 x
+          // 2048: 136 -> 96 + 26 us of reduction), each range at least kTileMinPairs pairs of
+          // chunks, the partials within the buffer
+          const int npairs = p.K / (2 * kTileK);
+          int ks = 1;
+          while (mb->part && tiles * ks < slots && npairs >= kTileMinPairs * (ks + 1) &&
+                 (long)(ks + 1) * mb->cap * p.N <= mb->part_cap)
+            ++ks;
+          MfmaBufs m = *mb;
+          m.ksplit = ks;
+          if (ks <= 1) m.part = nullptr;
+          if (!rc.split) m.shi = m.slo = nullptr;
+          const int grid = (int)std::min<long>(tiles * ks, slots);
           if (grid_used) *grid_used = grid;
           tm.begin(st, "k_gemm_tile");
-          hipLaunchKernelGGL((k_gemm_tile<P>), dim3(grid), dim3(kWG), 0, st, p, *mb);
+          hipLaunchKernelGGL((k_gemm_tile<P>), dim3(grid), dim3(kWG), 0, st, p, m);
           tm.end(st);
+          if (m.part && rc.hook) {
+            const hipError_t e = (*rc.hook)(m);
+            if (rc.used) *rc.used = e == hipSuccess;
+            return e;
+          }
+          if (m.part) {
+            const long items = (long)m.cap * (p.N / (P::kPair ? 2 : 1));
+            const int rgrid = (int)std::min<long>((items + kWG - 1) / kWG, 4096);
+            hipLaunchKernelGGL((k_splitk_reduce<P>), dim3(rgrid), dim3(kWG), 0, st, p, m);
+          }
+          // the split activations of a kSplitOut policy: by the tile epilogue or the reduction
+          if (rc.split && rc.used) *rc.used = true;
           return hipGetLastError();
         }
       }

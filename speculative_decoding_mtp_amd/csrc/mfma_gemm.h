@@ -275,23 +275,35 @@ __global__ __launch_bounds__(kWG) void k_reduce_prep(P p, Pn pn, MfmaBufs mb) {
 // ---------------------------------------------------------------------------------------------
 // Large tiles for calls with hundreds of activation rows (a prefill).  The streaming kernel
 // (stream_gemm.h) reads the whole weight matrix once per 64-row pass; here each workgroup owns a 128
-// (compact activation rows) x 128 (weight rows) output tile and walks K in 32-column chunks
-// with both operands staged in LDS (double-buffered, one barrier per chunk, two chunks in
-// flight from memory), so the weights of
-// a column group are read once per 128 rows and every staged element feeds four MFMA tiles.
-// The four waves split the tile 2 x 2 (64 x 64 each: 4 x 4 MFMA tiles, hi and lo activation
-// products into the same accumulators).  Global loads are row-contiguous (four threads x 16 B
-// = one row's 64-byte chunk slice), issued two chunks ahead of the one multiplied, every
-// one unconditional: rows past the count or the matrix re-read the last valid row, and their
-// outputs are never stored.  LDS rows are padded to 40 bf16 (20 dwords): the sixteen rows a
-// quarter-wave reads for one operand fall on distinct banks.  K must be a multiple of 64.
-constexpr int kTileM = 128, kTileN = 128, kTileK = 32, kTileLd = kTileK + 8;
-constexpr int kTileRows = 256;  // activation rows from which the large tiles are used
+// (compact activation rows) x 128 (weight rows) output tile -- or one of `ksplit` K ranges of it,
+// when the tiles alone would leave resident workgroup slots empty -- and walks K in 32-column
+// chunks with both operands staged in LDS, so the weights of a column group are read once per 128
+// rows and every staged element feeds four MFMA tiles.  The four waves split the tile 2 x 2 (64 x
+// 64 each: 4 x 4 MFMA tiles, hi and lo activation products into the same accumulators).
+// Global loads take whole 128-byte lines: a line of a row holds two consecutive chunks, and a
+// load of its 64-byte halves one chunk apart fetched most lines twice (measured: the loads alone
+// took 300 us of the 336 us of a 2048 x 12288 x 2048 product; whole lines, 191 us).  So each
+// thread loads 16 bytes of four rows of each operand per pair of chunks; the pair is stored at
+// the start of every odd chunk into the two of three LDS buffers not being read (24 KB each:
+// hi, lo and weights, 128 rows x 64 bytes; two workgroups per compute unit) and the next pair's
+// loads are issued right after, two chunks ahead of their use.  Rows are unpadded, the four
+// 16-byte slots of row r XOR-swizzled by ((r >> 1) ^ (r >> 3)) & 3 so that the sixteen rows a
+// quarter-wave reads for one operand fall on distinct banks.  Every load is unconditional: rows
+// past the count or the matrix re-read the last valid row (their outputs are never stored) and
+// pairs past the range re-read its last pair.  The chunks are multiplied in the same order as
+// in one pass over K, so a single range gives the same sums whatever the staging.
+// K must be a multiple of 64; each K range holds at least one pair.
+constexpr int kTileM = 128, kTileN = 128, kTileK = 32;
+constexpr int kTileOp = kTileM * kTileK;  // bf16 per operand per LDS buffer
+constexpr int kTileRows = 256;            // activation rows from which the large tiles are used
+constexpr int kTileMinPairs = 16;         // K pairs (64 columns) per range at least when split
+
+__device__ __forceinline__ int tile_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
 template <class P>
 __global__ __launch_bounds__(kWG, 2) void k_gemm_tile(P p, MfmaBufs mb) {
-  __shared__ __align__(16) uint16_t sA[2][2][kTileM * kTileLd];  // [buffer][hi/lo][row][k]
-  __shared__ __align__(16) uint16_t sB[2][kTileN * kTileLd];     // [buffer][weight row][k]
+  static_assert(kTileM == 128 && kTileN == 128 && kTileK == 32 && kWG == 256, "the staging map below");
+  __shared__ __align__(16) uint16_t sm[3 * 3 * kTileOp];  // [buffer][hi, lo, weights][row][32]
   __shared__ int s_n[kMaxBatch];
   __shared__ int s_len[kMaxBatch];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -300,42 +312,46 @@ __global__ __launch_bounds__(kWG, 2) void k_gemm_tile(P p, MfmaBufs mb) {
   p.setup(s_n, s_len);
   const int count = *mb.count;
   __syncthreads();
+  const int ks = mb.part ? mb.ksplit : 1;
   const int nrt = (count + kTileM - 1) / kTileM;
   const int nct = (p.N + kTileN - 1) / kTileN;
-  const int nk = p.K / kTileK;
-  // staging map: thread t moves 16 bytes of row (t / 4) + 64 h at column 8 (t % 4) of a chunk
-  const int lr = tid >> 2, lc = 8 * (tid & 3);
-  for (int it = blockIdx.x; it < nrt * nct; it += gridDim.x) {
-    const int i = it % nrt, j = it / nrt;  // consecutive items share the weight column group
-    const uint16_t* arow_hi[2];
-    const uint16_t* arow_lo[2];
-    const uint16_t* brow[2];
+  const int npall = p.K / (2 * kTileK), pp = (npall + ks - 1) / ks;
+  // staging map: thread t moves 16 bytes (slot t % 8 of the 128-byte line) of rows t / 8 + 32 h
+  const int pr = tid >> 3, pc = tid & 7;
+  const int fj = tile_swz(jl);  // the swizzle of rows 16 k + jl is fj ^ (2 k & 3)
+  for (int it = blockIdx.x; it < nrt * nct * ks; it += gridDim.x) {
+    const int s = it % ks, t = it / ks;   // the K ranges of a tile run side by side
+    const int i = t % nrt, j = t / nrt;   // consecutive tiles share the weight column group
+    const int p0 = s * pp, np = min(npall, p0 + pp) - p0, nk = 2 * np;
+    long ao[4];
+    const uint16_t* brow[4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int cr = min(i * kTileM + lr + 64 * h, count - 1);
-      arow_hi[h] = mb.xhi + (long)cr * p.K + lc;
-      arow_lo[h] = mb.xlo + (long)cr * p.K + lc;
-      brow[h] = reinterpret_cast<const uint16_t*>(p.wrow(min(j * kTileN + lr + 64 * h, p.N - 1))) + lc;
+    for (int h = 0; h < 4; ++h) {
+      const int r = pr + 32 * h;
+      ao[h] = (long)min(i * kTileM + r, count - 1) * p.K + 64 * p0 + 8 * pc;
+      brow[h] = reinterpret_cast<const uint16_t*>(p.wrow(min(j * kTileN + r, p.N - 1))) + 64 * p0 + 8 * pc;
     }
-    // two chunks in flight: register slot S holds chunk kc while kc is staged, then receives
-    // kc + 2 (the K loop is unrolled by two so that slots are compile-time; K / 32 is even)
-    uint4 ga[2][2][2], gb[2][2];  // [slot][hi/lo][half], [slot][half]
-    auto gload = [&](int kc, uint4 (&a)[2][2], uint4 (&b)[2]) {
-      const int k0 = kc * kTileK;
+    uint4 g[3][4];  // [hi, lo, weights][row group] of one pair of chunks
+    auto gload = [&](int pair) {
+      const int k0 = 64 * pair;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        b[h] = ld_stream(brow[h] + k0);
-        a[0][h] = ld16(arow_hi[h] + k0);
-        a[1][h] = ld16(arow_lo[h] + k0);
+      for (int h = 0; h < 4; ++h) {
+        g[0][h] = ld16(mb.xhi + ao[h] + k0);
+        g[1][h] = ld16(mb.xlo + ao[h] + k0);
+        g[2][h] = ld_stream(brow[h] + k0);
       }
     };
-    auto sstore = [&](int buf, const uint4 (&a)[2][2], const uint4 (&b)[2]) {
+    // chunks c (held by the lanes with pc < 4) and c + 1 (pc >= 4) into their buffers
+    auto sstore = [&](int c) {
+      const int b0 = c % 3, b1 = b0 == 2 ? 0 : b0 + 1;
+      const int base = ((pc >> 2) ? b1 : b0) * 3 * kTileOp;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int r = lr + 64 * h;
-        *reinterpret_cast<uint4*>(&sB[buf][r * kTileLd + lc]) = b[h];
-        *reinterpret_cast<uint4*>(&sA[buf][0][r * kTileLd + lc]) = a[0][h];
-        *reinterpret_cast<uint4*>(&sA[buf][1][r * kTileLd + lc]) = a[1][h];
+      for (int h = 0; h < 4; ++h) {
+        const int r = pr + 32 * h;
+        const int off = base + r * kTileK + 8 * ((pc & 3) ^ tile_swz(r));
+        *reinterpret_cast<uint4*>(&sm[off]) = g[0][h];
+        *reinterpret_cast<uint4*>(&sm[off + kTileOp]) = g[1][h];
+        *reinterpret_cast<uint4*>(&sm[off + 2 * kTileOp]) = g[2][h];
       }
     };
     f32x4_t acc[4][4];
@@ -343,6 +359,26 @@ __global__ __launch_bounds__(kWG, 2) void k_gemm_tile(P p, MfmaBufs mb) {
     for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int n = 0; n < 4; ++n) acc[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](int c) {
+      const uint16_t* sb = sm + (c % 3) * 3 * kTileOp;
+      bf16x8_t bw[4];
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const int R = wn * 64 + n * 16 + jl;
+        bw[n] = *reinterpret_cast<const bf16x8_t*>(sb + 2 * kTileOp + R * kTileK + 8 * (hq ^ fj ^ ((2 * n) & 3)));
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int o = (wm * 64 + m * 16 + jl) * kTileK + 8 * (hq ^ fj ^ ((2 * m) & 3));
+        const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(sb + o);
+        const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(sb + kTileOp + o);
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bw[n], acc[m][n], 0, 0, 0);
+          acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bw[n], acc[m][n], 0, 0, 0);
+        }
+      }
+    };
     // the padded row and activation index of this lane's 16 output rows, fetched up front (the
     // epilogue would otherwise wait for each pair of loads in turn)
     int orow[4][4], oact[4][4];
@@ -354,43 +390,22 @@ __global__ __launch_bounds__(kWG, 2) void k_gemm_tile(P p, MfmaBufs mb) {
         orow[m][r] = mb.rowmap[cr];
         oact[m][r] = mb.amap[cr];
       }
-    __syncthreads();  // the previous item's readers are done with both buffers
-    gload(0, ga[0], gb[0]);
-    gload(1, ga[1], gb[1]);
-    sstore(0, ga[0], gb[0]);
+    __syncthreads();  // the previous item's readers are done with every buffer
+    gload(0);
+    sstore(0);
+    gload(min(1, np - 1));
     __syncthreads();
-    auto chunk = [&](auto slot, int kc) {
-      constexpr int S = decltype(slot)::value;  // == kc & 1, also the LDS buffer of chunk kc
-      // chunk kc + 2 into the slot chunk kc came in (the last chunk again near the end: every
-      // load unconditional, so the compiler waits for one chunk's loads, not all)
-      gload(min(kc + 2, nk - 1), ga[S], gb[S]);
-#pragma unroll
-      for (int s = 0; s < kTileK / 32; ++s) {
-        const int kk = 32 * s + 8 * hq;
-        bf16x8_t bw[4];
-#pragma unroll
-        for (int n = 0; n < 4; ++n)
-          bw[n] = *reinterpret_cast<const bf16x8_t*>(&sB[S][(wn * 64 + n * 16 + jl) * kTileLd + kk]);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int ra = (wm * 64 + m * 16 + jl) * kTileLd + kk;
-          const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(&sA[S][0][ra]);
-          const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(&sA[S][1][ra]);
-#pragma unroll
-          for (int n = 0; n < 4; ++n) {
-            acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bw[n], acc[m][n], 0, 0, 0);
-            acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bw[n], acc[m][n], 0, 0, 0);
-          }
-        }
+    for (int c = 0; c < nk; c += 2) {
+      compute(c);
+      __syncthreads();  // chunk c - 1's buffer and chunk c's are free
+      if (c + 2 < nk) {
+        sstore(c + 2);
+        gload(min(c / 2 + 2, np - 1));
       }
-      // chunk kc + 1 (requested an iteration ago) into the other buffer, last read before the
-      // previous barrier
-      if (kc + 1 < nk) sstore(S ^ 1, ga[S ^ 1], gb[S ^ 1]);
+      // the loads stay ahead of the chunk's MFMAs (the compiler would sink them to its end)
+      __builtin_amdgcn_sched_barrier(0);
+      compute(c + 1);
       __syncthreads();
-    };
-    for (int kc = 0; kc < nk; kc += 2) {
-      chunk(std::integral_constant<int, 0>{}, kc);
-      chunk(std::integral_constant<int, 1>{}, kc + 1);
     }
     // epilogue: lane holds compact rows 4 hq + r of each 16-row tile, column jl of each weight tile
 #pragma unroll
@@ -404,8 +419,19 @@ __global__ __launch_bounds__(kWG, 2) void k_gemm_tile(P p, MfmaBufs mb) {
           const float v = acc[m][n][r];
           const float partner = __shfl_xor(v, 1, kWave);
           if (cr < count && col < p.N) {
-            if constexpr (P::kPair) {
-              if ((jl & 1) == 0) p.store_pair(col, oact[m][r], orow[m][r], v, partner);
+            if (ks > 1) {
+              mb.part[((long)s * mb.cap + cr) * p.N + col] = v;
+            } else if constexpr (P::kPair) {
+              if ((jl & 1) == 0) {
+                if constexpr (P::kSplitOut) {
+                  if (mb.shi)
+                    p.store_pair_split(col, oact[m][r], orow[m][r], cr, v, partner, mb.shi, mb.slo);
+                  else
+                    p.store_pair(col, oact[m][r], orow[m][r], v, partner);
+                } else {
+                  p.store_pair(col, oact[m][r], orow[m][r], v, partner);
+                }
+              }
             } else {
               p.store(col, oact[m][r], orow[m][r], v);
             }

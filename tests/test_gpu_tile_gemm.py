@@ -1,8 +1,11 @@
 """GPU parity of the large-tile MFMA GEMM (128 x 128 output tiles, both operands staged in LDS),
-which a head call takes for a matrix when it has 256+ activation rows and enough tiles to fill the
-GPU: here the gate/up projection of a head with a 4096-wide FFN (8192 interleaved output rows) over
-a 1152-row prefill (9 x 64 tiles) and over a ragged batch of two sequences (640 and 517 valid rows
-of 640: 1157 compact rows, the last tile partly empty, padding rows excluded from the compaction).
+which a head call takes for every matrix once it has 256+ activation rows: the matrices of a head
+with a 4096-wide FFN (8192 interleaved gate/up rows) over a 1152-row prefill (9 x 64 gate/up
+tiles) and over a ragged batch of two sequences (640 and 517 valid rows of 640: 1157 compact
+rows, the last tile partly empty, padding rows excluded from the compaction); gate/up's epilogue
+writes down_proj's split activations, and down_proj (K 4096, 18 tiles) runs in four K ranges
+whose partials the reduction sums.  The third case (hidden 2048, FFN 1024) runs eh_proj (K 4096,
+144 tiles) in four K ranges whose reduction also prepares QKV's activations.
 
 Compared with the oracle's draft_step ([HB14] "14. MTP: speculative decoding with the built-in
 draft head", section "The draft head"): every valid row's post-norm hidden and appended K/V, the
@@ -21,11 +24,13 @@ M = pytest.importorskip("speculative_decoding_mtp_amd")
 from tests.gpu_util import MARGIN, config, f32, i32, max_rel, upload_weights  # noqa: E402
 
 
-@pytest.mark.parametrize("B, rows, valid", [(1, 1152, [1152]), (2, 640, [640, 517])], ids=["1152rows", "ragged"])
-def test_large_tile_gemm_rows_match_oracle(B, rows, valid):
-    cfg = CONFIGS["tiny"].replace(index=91 + B, wdtype="bf16", n_layers=1, n_heads=4, n_kv_heads=2, head_dim=128,
-                                  hidden=256, ffn=4096, vocab=2000, embed_std=1.0, batch=B, D=1, ctx=0,
-                                  prefill_rows=0)
+@pytest.mark.parametrize("B, rows, valid, hidden, ffn", [(1, 1152, [1152], 256, 4096), (2, 640, [640, 517], 256, 4096),
+                                                    (1, 1152, [1152], 2048, 1024)],
+                         ids=["1152rows", "ragged", "splitk"])
+def test_large_tile_gemm_rows_match_oracle(B, rows, valid, hidden, ffn):
+    cfg = CONFIGS["tiny"].replace(index=91 + B + hidden // 1024, wdtype="bf16", n_layers=1, n_heads=4, n_kv_heads=2,
+                                  head_dim=128, hidden=hidden, ffn=ffn, vocab=2000, embed_std=1.0, batch=B, D=1,
+                                  ctx=0, prefill_rows=0)
     H, V = cfg.hidden, cfg.vocab
     w = make_weights(cfg)
     model = O.OracleModel(cfg, w)
