@@ -463,12 +463,12 @@ hipError_t launch_finalize(LmFinal f, hipStream_t st) {
 // ---------------------------------------------------------------------------------------------
 // Workgroups that can be resident at once for a kernel (occupancy x compute units), cached.
 template <class K>
-int resident_cap(K kernel, int* cache) {
+int resident_cap(K kernel, int* cache, int threads = kWG) {
   if (*cache == 0) {
     int dev = 0, cus = 0, nb = 0;
     (void)hipGetDevice(&dev);
     (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(kernel), kWG, 0);
+    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(kernel), threads, 0);
     *cache = (nb < 1 ? 1 : nb) * (cus < 1 ? 1 : cus);
   }
   return *cache;
@@ -690,20 +690,20 @@ hipError_t launch_gemv(P& p, hipStream_t st, int* grid_used = nullptr, const Mfm
       }
       if constexpr (!P::kArgmax) {
         // hundreds of rows (a prefill, by the activation count, an upper bound of the valid
-        // rows): 128 x 128 output tiles, even when they do not fill the GPU -- the streaming
+        // rows): 128 x 256 output tiles, even when they do not fill the GPU -- the streaming
         // kernel would read the weights once per 64 rows (2048 rows of a 3072 x 2048 QKV: 1.2 ms
         // against ~0.1 ms)
         static int cap = 0;
         const long tiles = (long)((p.nact + kTileM - 1) / kTileM) * ((p.N + kTileN - 1) / kTileN);
         if (p.nact >= kTileRows) {
-          const int slots = resident_cap(k_gemm_tile<P>, &cap);
-          // K ranges side by side while the tiles leave resident slots empty (two per compute
-          // unit; 2048 rows of down_proj, 2048 x 6144: 192 -> 150 us at two ranges; QKV 3072 x
-          // 2048: 136 -> 96 + 26 us of reduction), each range at least kTileMinPairs pairs of
-          // chunks, the partials within the buffer
+          const int slots = resident_cap(k_gemm_tile<P>, &cap, kTileThreads);
+          // K ranges side by side while they all fit the resident slots (one workgroup per
+          // compute unit; 2048 rows of down_proj, 2048 x 6144: 211 -> 125 us at two ranges; QKV's
+          // 192 tiles stay whole: two ranges would take 1.5 rounds), each range at least
+          // kTileMinPairs pairs of chunks, the partials within the buffer
           const int npairs = p.K / (2 * kTileK);
           int ks = 1;
-          while (mb->part && tiles * ks < slots && npairs >= kTileMinPairs * (ks + 1) &&
+          while (mb->part && tiles * (ks + 1) <= slots && npairs >= kTileMinPairs * (ks + 1) &&
                  (long)(ks + 1) * mb->cap * p.N <= mb->part_cap)
             ++ks;
           MfmaBufs m = *mb;
@@ -713,7 +713,7 @@ hipError_t launch_gemv(P& p, hipStream_t st, int* grid_used = nullptr, const Mfm
           const int grid = (int)std::min<long>(tiles * ks, slots);
           if (grid_used) *grid_used = grid;
           tm.begin(st, "k_gemm_tile");
-          hipLaunchKernelGGL((k_gemm_tile<P>), dim3(grid), dim3(kWG), 0, st, p, m);
+          hipLaunchKernelGGL((k_gemm_tile<P>), dim3(grid), dim3(kTileThreads), 0, st, p, m);
           tm.end(st);
           if (m.part && rc.hook) {
             const hipError_t e = (*rc.hook)(m);

@@ -8,7 +8,7 @@
 //   each compact row's padded row and activation index; `count` the number of compact rows.
 //   Those compact rows feed the weight-streaming GEMM (stream_gemm.h) and, for calls with
 //   hundreds of rows, k_gemm_tile below.
-// * k_gemm_tile: 128 x 128 output tiles with both operands staged in LDS (a prefill).
+// * k_gemm_tile: 128 x 256 output tiles with both operands staged in LDS (a prefill).
 // * k_splitk_reduce: sums split-K partials in range order and applies the policy's store.
 // Operand layout of v_mfma_f32_16x16x32_bf16 (checked on the device): lane l supplies
 // A[l % 16][8 (l / 16) + e] and B[8 (l / 16) + e][l % 16], e < 8; result r of lane l is
@@ -274,84 +274,94 @@ __global__ __launch_bounds__(kWG) void k_reduce_prep(P p, Pn pn, MfmaBufs mb) {
 
 // ---------------------------------------------------------------------------------------------
 // Large tiles for calls with hundreds of activation rows (a prefill).  The streaming kernel
-// (stream_gemm.h) reads the whole weight matrix once per 64-row pass; here each workgroup owns a 128
-// (compact activation rows) x 128 (weight rows) output tile -- or one of `ksplit` K ranges of it,
-// when the tiles alone would leave resident workgroup slots empty -- and walks K in 32-column
-// chunks with both operands staged in LDS, so the weights of a column group are read once per 128
-// rows and every staged element feeds four MFMA tiles.  The four waves split the tile 2 x 2 (64 x
-// 64 each: 4 x 4 MFMA tiles, hi and lo activation products into the same accumulators).
+// (stream_gemm.h) reads the whole weight matrix once per 64-row pass; here each workgroup of
+// eight waves owns a 128 (compact activation rows) x 256 (weight rows) output tile -- or one of
+// `ksplit` K ranges of it, when the tiles alone would leave compute units idle -- and walks K in
+// 32-column chunks with both operands staged in LDS.  The waves split the tile 2 x 4 (64 x 64
+// each: 4 x 4 MFMA tiles, hi and lo activation products into the same accumulators).  What
+// limits this GEMM is the operand traffic from L2 (hi + lo activations at 4 bytes per element,
+// weights at 2): per output it falls as 4 / 256 + 2 / 128 bytes per K column here, against
+// 4 / 128 + 2 / 128 for a 128 x 128 tile (2048 x 12288 x 2048: 328 -> 259 us).
 // Global loads take whole 128-byte lines: a line of a row holds two consecutive chunks, and a
-// load of its 64-byte halves one chunk apart fetched most lines twice (measured: the loads alone
-// took 300 us of the 336 us of a 2048 x 12288 x 2048 product; whole lines, 191 us).  So each
-// thread loads 16 bytes of four rows of each operand per pair of chunks; the pair is stored at
-// the start of every odd chunk into the two of three LDS buffers not being read (24 KB each:
-// hi, lo and weights, 128 rows x 64 bytes; two workgroups per compute unit) and the next pair's
-// loads are issued right after, two chunks ahead of their use.  Rows are unpadded, the four
-// 16-byte slots of row r XOR-swizzled by ((r >> 1) ^ (r >> 3)) & 3 so that the sixteen rows a
-// quarter-wave reads for one operand fall on distinct banks.  Every load is unconditional: rows
-// past the count or the matrix re-read the last valid row (their outputs are never stored) and
-// pairs past the range re-read its last pair.  The chunks are multiplied in the same order as
-// in one pass over K, so a single range gives the same sums whatever the staging.
-// K must be a multiple of 64; each K range holds at least one pair.
-constexpr int kTileM = 128, kTileN = 128, kTileK = 32;
-constexpr int kTileOp = kTileM * kTileK;  // bf16 per operand per LDS buffer
-constexpr int kTileRows = 256;            // activation rows from which the large tiles are used
-constexpr int kTileMinPairs = 16;         // K pairs (64 columns) per range at least when split
+// load of its 64-byte halves one chunk apart fetched most lines twice.  So each thread loads 16
+// bytes of rows of each operand per pair of chunks; the pair is stored at the start of every odd
+// chunk into the two of three LDS buffers not being read (32 KB each: hi, lo and weights; one
+// workgroup per compute unit) and the next pair's loads are issued right after, two chunks ahead
+// of their use.  Rows are unpadded, the four 16-byte slots of row r XOR-swizzled by
+// ((r >> 1) ^ (r >> 3)) & 3 so that the sixteen rows a quarter-wave reads for one operand fall on
+// distinct banks.  Work items are taken in contiguous ranges per XCD (workgroup b runs on XCD
+// b % 8), so the tiles sharing a column group, or a row group, share that XCD's L2.  Every load
+// is unconditional: rows past the count or the matrix re-read the last valid row (their outputs
+// are never stored) and pairs past the range re-read its last pair.  The chunks are multiplied in
+// the same order as in one pass over K, so a single range gives the same sums whatever the
+// staging.  K must be a multiple of 64; the host keeps every K range non-empty.
+constexpr int kTileM = 128, kTileN = 256, kTileK = 32, kTileThreads = 512;
+constexpr int kTileOpA = kTileM * kTileK, kTileOpB = kTileN * kTileK;  // bf16 per operand and buffer
+constexpr int kTileBuf = 2 * kTileOpA + kTileOpB;                       // hi, lo, weights
+constexpr int kTileRows = 256;     // activation rows from which the large tiles are used
+constexpr int kTileMinPairs = 16;  // K pairs (64 columns) per range at least when split
 
 __device__ __forceinline__ int tile_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
 template <class P>
-__global__ __launch_bounds__(kWG, 2) void k_gemm_tile(P p, MfmaBufs mb) {
-  static_assert(kTileM == 128 && kTileN == 128 && kTileK == 32 && kWG == 256, "the staging map below");
-  __shared__ __align__(16) uint16_t sm[3 * 3 * kTileOp];  // [buffer][hi, lo, weights][row][32]
+__global__ __launch_bounds__(kTileThreads, 1) void k_gemm_tile(P p, MfmaBufs mb) {
+  static_assert(kTileM == 128 && kTileN == 256 && kTileK == 32 && kTileThreads == 512, "the staging map below");
+  __shared__ __align__(16) uint16_t sm[3 * kTileBuf];  // [buffer][hi, lo, weights][row][32]
   __shared__ int s_n[kMaxBatch];
   __shared__ int s_len[kMaxBatch];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int jl = lane & 15, hq = lane >> 4;
-  const int wm = wid & 1, wn = wid >> 1;  // this wave's 64 x 64 quarter of the tile
-  p.setup(s_n, s_len);
+  const int wm = wid & 1, wn = wid >> 1;  // this wave's 64 x 64 part of the tile
+  p.setup(s_n, s_len);                    // threads past the batch (kMaxBatch) take no sequence
   const int count = *mb.count;
   __syncthreads();
   const int ks = mb.part ? mb.ksplit : 1;
   const int nrt = (count + kTileM - 1) / kTileM;
   const int nct = (p.N + kTileN - 1) / kTileN;
   const int npall = p.K / (2 * kTileK), pp = (npall + ks - 1) / ks;
-  // staging map: thread t moves 16 bytes (slot t % 8 of the 128-byte line) of rows t / 8 + 32 h
+  const int total = nrt * nct * ks, per = (total + 7) / 8;
+  // staging map: thread t moves 16 bytes (slot t % 8 of the 128-byte line) of rows t / 8 + 64 h
   const int pr = tid >> 3, pc = tid & 7;
   const int fj = tile_swz(jl);  // the swizzle of rows 16 k + jl is fj ^ (2 k & 3)
-  for (int it = blockIdx.x; it < nrt * nct * ks; it += gridDim.x) {
+  for (int u = blockIdx.x; u < 8 * per; u += gridDim.x) {
+    const int it = (u & 7) * per + (u >> 3);  // XCD u % 8 takes items [x per, (x + 1) per)
+    if (it >= total) continue;
     const int s = it % ks, t = it / ks;   // the K ranges of a tile run side by side
     const int i = t % nrt, j = t / nrt;   // consecutive tiles share the weight column group
     const int p0 = s * pp, np = min(npall, p0 + pp) - p0, nk = 2 * np;
-    long ao[4];
+    long ao[2];
     const uint16_t* brow[4];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const int r = pr + 32 * h;
-      ao[h] = (long)min(i * kTileM + r, count - 1) * p.K + 64 * p0 + 8 * pc;
-      brow[h] = reinterpret_cast<const uint16_t*>(p.wrow(min(j * kTileN + r, p.N - 1))) + 64 * p0 + 8 * pc;
-    }
-    uint4 g[3][4];  // [hi, lo, weights][row group] of one pair of chunks
+    for (int h = 0; h < 2; ++h) ao[h] = (long)min(i * kTileM + pr + 64 * h, count - 1) * p.K + 64 * p0 + 8 * pc;
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+      brow[h] = reinterpret_cast<const uint16_t*>(p.wrow(min(j * kTileN + pr + 64 * h, p.N - 1))) + 64 * p0 + 8 * pc;
+    uint4 ga[2][2], gb[4];  // one pair of chunks: [hi, lo][row group], [row group]
     auto gload = [&](int pair) {
       const int k0 = 64 * pair;
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        g[0][h] = ld16(mb.xhi + ao[h] + k0);
-        g[1][h] = ld16(mb.xlo + ao[h] + k0);
-        g[2][h] = ld_stream(brow[h] + k0);
+      for (int h = 0; h < 2; ++h) {
+        ga[0][h] = ld16(mb.xhi + ao[h] + k0);
+        ga[1][h] = ld16(mb.xlo + ao[h] + k0);
       }
+#pragma unroll
+      for (int h = 0; h < 4; ++h) gb[h] = ld_stream(brow[h] + k0);
     };
     // chunks c (held by the lanes with pc < 4) and c + 1 (pc >= 4) into their buffers
     auto sstore = [&](int c) {
       const int b0 = c % 3, b1 = b0 == 2 ? 0 : b0 + 1;
-      const int base = ((pc >> 2) ? b1 : b0) * 3 * kTileOp;
+      const int base = ((pc >> 2) ? b1 : b0) * kTileBuf;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = pr + 64 * h;
+        const int off = base + r * kTileK + 8 * ((pc & 3) ^ tile_swz(r));
+        *reinterpret_cast<uint4*>(&sm[off]) = ga[0][h];
+        *reinterpret_cast<uint4*>(&sm[off + kTileOpA]) = ga[1][h];
+      }
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
-        const int r = pr + 32 * h;
-        const int off = base + r * kTileK + 8 * ((pc & 3) ^ tile_swz(r));
-        *reinterpret_cast<uint4*>(&sm[off]) = g[0][h];
-        *reinterpret_cast<uint4*>(&sm[off + kTileOp]) = g[1][h];
-        *reinterpret_cast<uint4*>(&sm[off + 2 * kTileOp]) = g[2][h];
+        const int r = pr + 64 * h;
+        *reinterpret_cast<uint4*>(&sm[base + 2 * kTileOpA + r * kTileK + 8 * ((pc & 3) ^ tile_swz(r))]) = gb[h];
       }
     };
     f32x4_t acc[4][4];
@@ -360,18 +370,18 @@ __global__ __launch_bounds__(kWG, 2) void k_gemm_tile(P p, MfmaBufs mb) {
 #pragma unroll
       for (int n = 0; n < 4; ++n) acc[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     auto compute = [&](int c) {
-      const uint16_t* sb = sm + (c % 3) * 3 * kTileOp;
+      const uint16_t* sb = sm + (c % 3) * kTileBuf;
       bf16x8_t bw[4];
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
         const int R = wn * 64 + n * 16 + jl;
-        bw[n] = *reinterpret_cast<const bf16x8_t*>(sb + 2 * kTileOp + R * kTileK + 8 * (hq ^ fj ^ ((2 * n) & 3)));
+        bw[n] = *reinterpret_cast<const bf16x8_t*>(sb + 2 * kTileOpA + R * kTileK + 8 * (hq ^ fj ^ ((2 * n) & 3)));
       }
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const int o = (wm * 64 + m * 16 + jl) * kTileK + 8 * (hq ^ fj ^ ((2 * m) & 3));
         const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(sb + o);
-        const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(sb + kTileOp + o);
+        const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(sb + kTileOpA + o);
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
           acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bw[n], acc[m][n], 0, 0, 0);

@@ -1,11 +1,13 @@
-"""GPU parity of the large-tile MFMA GEMM (128 x 128 output tiles, both operands staged in LDS),
+"""GPU parity of the large-tile MFMA GEMM (128 x 256 output tiles, both operands staged in LDS),
 which a head call takes for every matrix once it has 256+ activation rows: the matrices of a head
-with a 4096-wide FFN (8192 interleaved gate/up rows) over a 1152-row prefill (9 x 64 gate/up
+with a 4096-wide FFN (8192 interleaved gate/up rows) over a 1152-row prefill (9 x 32 gate/up
 tiles) and over a ragged batch of two sequences (640 and 517 valid rows of 640: 1157 compact
 rows, the last tile partly empty, padding rows excluded from the compaction); gate/up's epilogue
-writes down_proj's split activations, and down_proj (K 4096, 18 tiles) runs in four K ranges
+writes down_proj's split activations, and down_proj (K 4096, 9 tiles) runs in four K ranges
 whose partials the reduction sums.  The third case (hidden 2048, FFN 1024) runs eh_proj (K 4096,
-144 tiles) in four K ranges whose reduction also prepares QKV's activations.
+72 tiles) in three K ranges whose reduction also prepares QKV's activations, QKV (K 2048, 36 tiles)
+in two ranges whose reduction applies RoPE and the cache append, and gate/up (K 2048, 72 tiles) in
+two ranges whose reduction writes down_proj's split activations.
 
 Compared with the oracle's draft_step ([HB14] "14. MTP: speculative decoding with the built-in
 draft head", section "The draft head"): every valid row's post-norm hidden and appended K/V, the
