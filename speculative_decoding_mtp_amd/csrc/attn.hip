@@ -471,6 +471,242 @@ __global__ __launch_bounds__(kWG) void k_attn_mfma(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// bf16 heads, many queries per kv head (a prefill; one split): the MFMA attention above with the
+// queries spread over the waves instead of the positions.  Workgroup (query block, kv head,
+// sequence) takes 64 queries -- 16 per wave, each wave with its own online softmax over every
+// position its queries may attend, so no merge across waves -- and walks the positions in
+// 64-position tiles staged once in LDS for all four waves: keys [position][channel] and values
+// transposed [channel][position] (as the cache holds them), each thread moving 16-byte pieces
+// of whole rows; the next tile's loads are in flight while the current one is multiplied (one
+// barrier per tile).  Per 32-position slice of a tile the products are those of k_attn_mfma:
+// S^T = K Q^T with Q (split bf16 hi + lo) held in registers for the whole walk and O^T += V^T P^T.
+// The softmax runs once per tile over the lane's sixteen positions (one max, sum and rescale of
+// the output per 64 positions), in base 2: scores times log2(e) / sqrt(hd), probabilities by
+// v_exp_f32, split into bf16 hi + lo by the hardware conversion (round to nearest even); tiles
+// inside every query's causal reach skip the masks.  The softmax is VALU work, not MFMA: per
+// slice it had cost 13 VALU instructions per MFMA.  LDS rows are XOR-swizzled in 16-byte slots so that
+// the sixteen rows a quarter-wave reads fall on distinct banks: key row r slot s at
+// s ^ ((r & 3) | (r >> 3 & 3) << 2), value row d slot s at s ^ ((d ^ d >> 3) & 7).  Value
+// positions past the range are stored as zeros (the cache may hold anything there); key rows
+// past it re-read the last one and their scores are masked.
+constexpr int kPfQ = 64;   // queries per workgroup
+constexpr int kPfT = 64;   // positions per LDS tile
+
+__device__ __forceinline__ int pf_kswz(int r) { return (r & 3) | ((r >> 3) & 3) << 2; }
+
+// Max and sum over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lanes of a query column), by the
+// in-register half swaps: with both operands x, a swap returns x[l] and its partner in the two
+// results of every lane, so one max (or add, commutative) per swap leaves every lane with the
+// same value.
+__device__ __forceinline__ float col_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+__device__ __forceinline__ float col_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+__device__ __forceinline__ int pf_vswz(int d) { return (d ^ (d >> 3)) & 7; }
+
+__global__ __launch_bounds__(kWG, 2) void k_attn_prefill(AttnArgs a) {
+  constexpr int HD = 128, NS = HD / 32, ND = HD / 16;
+  __shared__ __align__(16) uint16_t sK[2][kPfT * HD];
+  __shared__ __align__(16) uint16_t sV[2][HD * kPfT];
+  __shared__ int s_n;
+  __shared__ int s_cnt[kMaxBatch];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, j = lane & 15, hq = lane >> 4;
+  // the first half of the grid takes the query blocks longest first, the second half shortest
+  // first: workgroups i and i + half, which tend to share a compute unit, get complementary walks
+  const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int half = gridDim.x * gridDim.y * gridDim.z / 2;
+  const int qblk = lin < half ? gridDim.x - 1 - blockIdx.x : blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int G = a.nq / a.nkv;
+  const int L0 = a.len[b];
+  if (tid == 0) s_n = a.rows ? a.rows[b] : count_rows(a.tok + (long)b * a.tok_sb, a.rps, a.V, L0, a.max_len, nullptr);
+  const int cbase = a.shi ? attn_compact_base(a, b, s_cnt) : 0;  // contains a barrier
+  __syncthreads();
+  const int n = s_n;
+  const int NQ = n * G, q0 = qblk * kPfQ;
+  if (n == 0 || q0 >= NQ) return;
+  const int Tn = L0 + (a.shared ? 0 : n);
+  // positions past the last query row of the block are masked for every query: not visited
+  const int p_end = min(Tn, L0 + (min(NQ, q0 + kPfQ) - 1) / G + 1);
+  const int ntile = (p_end + kPfT - 1) / kPfT;
+  const uint16_t* Kb = reinterpret_cast<const uint16_t*>(a.kc) + ((long)b * a.nkv + kvh) * a.max_len * HD;
+  const uint16_t* Vt = reinterpret_cast<const uint16_t*>(a.vc) + ((long)b * a.nkv + kvh) * a.max_len * HD;
+
+  // this wave's 16 queries as the B operand of the scores, split bf16 hi + lo (zero if absent)
+  const int qi = q0 + 16 * wid + j;
+  const int qrow = qi / G, qg = qi - qrow * G;
+  bf16x8_t qh[NS], ql[NS];
+#pragma unroll
+  for (int st = 0; st < NS; ++st) {
+    float f[8];
+    if (qi < NQ) {
+      const float* qp = a.q + (((long)b * a.rps + qrow) * a.nq + kvh * G + qg) * HD + 32 * st + 8 * hq;
+      const float4 x0 = *reinterpret_cast<const float4*>(qp);
+      const float4 x1 = *reinterpret_cast<const float4*>(qp + 4);
+      f[0] = x0.x; f[1] = x0.y; f[2] = x0.z; f[3] = x0.w;
+      f[4] = x1.x; f[5] = x1.y; f[6] = x1.z; f[7] = x1.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = 0.f;
+    }
+    split_bf16x8(f, qh[st], ql[st]);
+  }
+  const int lim = qi < NQ ? L0 + qrow : -1;  // last position query column j may attend
+
+  // staging: thread t moves key slots z = t + 256 k (row z / 16, slot z % 16) and value slots
+  // (channel z / 8, slot z % 8) of a tile
+  uint4 gk[4], gv[4];
+  auto gload = [&](int p0) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int z = tid + kWG * k;
+      const int pr = min(p0 + (z >> 4), p_end - 1);
+      gk[k] = ld16(Kb + (long)pr * HD + 8 * (z & 15));
+      const int pv = min(p0 + 8 * (z & 7), (p_end - 1) & ~7);
+      gv[k] = ld16(Vt + (long)(z >> 3) * a.max_len + pv);
+    }
+  };
+  auto sstore = [&](int buf, int p0) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int z = tid + kWG * k;
+      const int r = z >> 4, d = z >> 3, sv = z & 7;
+      *reinterpret_cast<uint4*>(&sK[buf][r * HD + 8 * ((z & 15) ^ pf_kswz(r))]) = gk[k];
+      // value positions p0 + 8 sv + e past the range are zeroed
+      const int keep = p_end - (p0 + 8 * sv);
+      uint4 v = gv[k];
+      if (keep < 8) {
+        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          w[q] = (2 * q < keep ? w[q] & 0x0000ffffu : 0u) | (2 * q + 1 < keep ? w[q] & 0xffff0000u : 0u);
+        v = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+      *reinterpret_cast<uint4*>(&sV[buf][d * kPfT + 8 * (sv ^ pf_vswz(d))]) = v;
+    }
+  };
+
+  // running max and sum in base-2 units: scores are taken times log2(e) / sqrt(hd), so that one
+  // v_exp_f32 gives each probability
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4_t acc[ND];
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int krow = 8 * (j >> 2) + (j & 3);  // this lane's key row in sub-tile 0 of a slice (+4 in 1)
+  const float c2 = 1.4426950408889634f / sqrtf(float(HD));
+  // the first query of the wave attends the fewest positions; a tile that ends within its reach
+  // (and within the range) needs no mask when all sixteen queries are present
+  const int q_first = q0 + 16 * wid;
+  const int lim_all = q_first + 15 < NQ ? L0 + q_first / G : -1;
+
+  gload(0);
+  sstore(0, 0);
+  __syncthreads();
+  for (int t = 0; t < ntile; ++t) {
+    const int p0 = t * kPfT, buf = t & 1;
+    if (t + 1 < ntile) gload(p0 + kPfT);
+    __builtin_amdgcn_sched_barrier(0);  // the next tile's loads are issued before this one's use
+    // scores of the tile: lane (j, hq) holds positions p0 + 32 sl + 8 hq + e of query column j
+    float pe[2][8];
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      f32x4_t sc[2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        sc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const int r = 32 * sl + krow + 4 * tt;
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+          const bf16x8_t kop =
+              *reinterpret_cast<const bf16x8_t*>(&sK[buf][r * HD + 8 * ((4 * st + hq) ^ pf_kswz(r))]);
+          sc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qh[st], sc[tt], 0, 0, 0);
+          sc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, ql[st], sc[tt], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pe[sl][e] = sc[e >> 2][e & 3] * c2;
+    }
+    if (!(p0 + kPfT - 1 <= lim_all && p0 + kPfT <= p_end)) {
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int p = p0 + 32 * sl + 8 * hq + e;
+          if (!(p < p_end && p <= lim)) pe[sl][e] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, pe[sl][e]);
+    mx = col_max(mx);
+    const float m_new = fmaxf(m_run, mx);
+    float alpha = 1.f, rs = 0.f;
+    if (m_new != -INFINITY) {
+      alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 while m_run is -inf
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pe[sl][e] = __builtin_amdgcn_exp2f(pe[sl][e] - m_new);  // masked: exp2(-inf) = 0
+          rs += pe[sl][e];
+        }
+    } else {
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pe[sl][e] = 0.f;
+    }
+    rs = col_sum(rs);
+    l_run = l_run * alpha + rs;
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) acc[dt] *= alpha;
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      // probabilities as bf16 hi + lo (hardware round to nearest even)
+      bf16x8_t ph, pl;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        ph[e] = (__bf16)pe[sl][e];
+        pl[e] = (__bf16)(pe[sl][e] - (float)ph[e]);
+      }
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) {
+        const int d = 16 * dt + j;
+        const bf16x8_t vop =
+            *reinterpret_cast<const bf16x8_t*>(&sV[buf][d * kPfT + 8 * ((4 * sl + hq) ^ pf_vswz(d))]);
+        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, ph, acc[dt], 0, 0, 0);
+        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pl, acc[dt], 0, 0, 0);
+      }
+    }
+    if (t + 1 < ntile) sstore(buf ^ 1, p0 + kPfT);  // that buffer's readers passed the last barrier
+    __syncthreads();
+  }
+  // lane (j, hq) holds channels 16 dt + 4 hq + r of query column j
+  if (qi < NQ && l_run > 0.f) {
+    const float inv = 1.0f / l_run;
+    const long o = (((long)b * a.rps + qrow) * a.nq + kvh * G + qg) * HD;
+    const long c = (long)(cbase + qrow) * a.nq * HD + (kvh * G + qg) * HD;
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int d = 16 * dt + 4 * hq + r;
+        attn_store(a, a.out, o + d, c + d, acc[dt][r] * inv);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // bf16 heads with a batch of sequences (B x kv heads fill the GPU): the same MFMA attention with
 // the keys and values staged through LDS.  Reading K and V^T straight in the operand layout
 // fetches 64 bytes of each of 16 rows per load instruction, a pattern that streams well below
@@ -861,6 +1097,15 @@ void launch_attention(AttnArgs a, int wdtype, float* out, hipStream_t st) {
         else
           hipLaunchKernelGGL((k_attn_lds<1, 4, 64, 1, false>), grid, dim3(kWG), 0, st, a);
         if (!a.out) hipLaunchKernelGGL((k_attn_combine<HD>), dim3(a.B * a.rps * a.nq), dim3(kWG), 0, st, a, out);
+        return;
+      }
+    }
+    if constexpr (HD == 128) {
+      // many queries per kv head in one split (a prefill): query blocks over the grid, K/V tiles
+      // through LDS once per 64 queries
+      if (a.nsplit == 1 && a.qstride >= 256) {
+        dim3 grid((a.qstride + kPfQ - 1) / kPfQ, a.nkv, a.B);
+        hipLaunchKernelGGL(k_attn_prefill, grid, dim3(kWG), 0, st, a);
         return;
       }
     }
