@@ -34,6 +34,8 @@ struct PBase {
   static constexpr bool kArgmax = false;
   static constexpr bool kVocab = false;  // output rows are a vocabulary (MFMA: 128 rows per workgroup)
   static constexpr bool kSplitOut = false;  // can also write its outputs split for the next GEMM
+  // the pair store is long (RoPE): a tile epilogue calls it from a loop, not unrolled per output
+  static constexpr bool kRolledStore = false;
   const int32_t* tok;
   int tok_sb;
   int B, rps;
@@ -126,6 +128,25 @@ struct PEhProj : PBase<W> {
   }
 };
 
+// sin r and cos r for |r| <= pi/4 by their Taylor series through r^11 / 11! and r^12 / 12!: the
+// first omitted terms are below 1e-11 there, far under float rounding.  Horner in float.
+__device__ __forceinline__ void sincos_quarter(float r, float& s, float& c) {
+  const float r2 = r * r;
+  s = fmaf(r * r2,
+           fmaf(r2, fmaf(r2, fmaf(r2, fmaf(r2, -2.5052108385441720e-8f, 2.7557319223985893e-6f),
+                                 -1.9841269841269841e-4f),
+                       8.3333333333333333e-3f),
+                -1.6666666666666667e-1f),
+           r);
+  c = fmaf(r2,
+           fmaf(r2, fmaf(r2, fmaf(r2, fmaf(r2, fmaf(r2, 2.0876756987868099e-9f, -2.7557319223985891e-7f),
+                                         2.4801587301587302e-5f),
+                                 -1.3888888888888889e-3f),
+                       4.1666666666666667e-2f),
+                -0.5f),
+           1.0f);
+}
+
 // Q/K/V projection of rms(x) with RoPE on q and k and the K/V append.  Logical rows are
 // ordered per head as (0, hd/2, 1, hd/2+1, ...) so a rotation pair is one (even, odd) pair.
 template <class W>
@@ -155,6 +176,7 @@ struct PQKV : PBase<W> {
 
   __device__ void load_x(int row, int k, float (&f)[W::VE]) const { load_f32_vec<W::VE>(xin + (long)row * H + k, f); }
   __device__ uint4 gain_raw(int k) const { return ld16(g + k); }
+  static constexpr bool kRolledStore = true;
   __device__ const T* wrow(int m) const {
     const int head = m / hd, mm = m - head * hd;
     const int dim = (mm >> 1) + (mm & 1) * (hd >> 1);
@@ -167,13 +189,18 @@ struct PQKV : PBase<W> {
     const int b = row / this->rps, i = row - b * this->rps;
     const int pos = this->lds_len[b] + i + pos_off;
     if (head < nq + nkv) {
-      // rotate q and k by pos * theta^(-2u/hd): the angle in double, reduced to [-pi, pi] in
-      // double (two-part 2 pi), then sine and cosine of the reduced angle in float
+      // rotate q and k by pos * theta^(-2u/hd): the angle in double, reduced to [-pi/4, pi/4]
+      // in double (quadrant k, two-part pi/2), sine and cosine of the remainder in float by their
+      // Taylor series (a library sincosf, inlined at every store, made these kernels up to ten
+      // times larger), then placed by the quadrant: sin(r + k pi/2), cos(r + k pi/2)
       const double ang = double(pos) * inv_freq[u];
-      const double k2pi = rint(ang * 0.15915494309189535);  // 1 / (2 pi)
-      const double red = fma(-k2pi, 2.4492935982947064e-16, fma(-k2pi, 6.283185307179586, ang));
-      float sf, cf;
-      sincosf(float(red), &sf, &cf);
+      const double kq = rint(ang * 0.6366197723675814);  // 2 / pi
+      const double red = fma(-kq, 6.123233995736766e-17, fma(-kq, 1.5707963267948966, ang));
+      float sq, cq;
+      sincos_quarter(float(red), sq, cq);
+      const int q = int(kq) & 3;  // ang >= 0
+      const float sf = q == 0 ? sq : q == 1 ? cq : q == 2 ? -sq : -cq;
+      const float cf = q == 0 ? cq : q == 1 ? -sq : q == 2 ? -cq : sq;
       const float a0 = v0 * cf - v1 * sf, a1 = v1 * cf + v0 * sf;
       v0 = a0;
       v1 = a1;

@@ -417,6 +417,37 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_gemm_tile(P p, MfmaBufs mb)
       compute(c + 1);
       __syncthreads();
     }
+    if constexpr (P::kPair && P::kRolledStore) {
+      if (ks == 1) {
+        // a long pair store (RoPE and the cache append): unrolled over the lane's 64 outputs it
+        // made the kernel ten times larger than the others (and slower, on instruction fetch).
+        // Each half of this wave's 64 x 64 outputs goes through its own 8 KB of the free LDS as
+        // fp32 [row][column]; lane l then stores column pair l % 32 of rows l / 32, + 2, ...
+        float* sE = reinterpret_cast<float*>(sm) + wid * 32 * 64;
+        const int c0 = j * kTileN + wn * 64;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+          for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int n = 0; n < 4; ++n)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) sE[(m * 16 + 4 * hq + r) * 64 + n * 16 + jl] = acc[2 * hf + m][n][r];
+          __builtin_amdgcn_wave_barrier();
+#pragma unroll 1
+          for (int e = lane; e < 32 * 32; e += 64) {
+            const int rr = e >> 5, cp = 2 * (e & 31);
+            const int cr = i * kTileM + wm * 64 + 32 * hf + rr;
+            if (cr < count && c0 + cp < p.N) {
+              const float2 v = *reinterpret_cast<const float2*>(&sE[rr * 64 + cp]);
+              p.store_pair(c0 + cp, mb.amap[cr], mb.rowmap[cr], v.x, v.y);
+            }
+          }
+          __builtin_amdgcn_wave_barrier();  // the second half reuses the region
+        }
+        continue;  // the next item's first barrier waits for these reads
+      }
+    }
     // epilogue: lane holds compact rows 4 hq + r of each 16-row tile, column jl of each weight tile
 #pragma unroll
     for (int m = 0; m < 4; ++m)
@@ -431,6 +462,8 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_gemm_tile(P p, MfmaBufs mb)
           if (cr < count && col < p.N) {
             if (ks > 1) {
               mb.part[((long)s * mb.cap + cr) * p.N + col] = v;
+            } else if constexpr (P::kPair && P::kRolledStore) {
+              // stored by the rolled epilogue above
             } else if constexpr (P::kPair) {
               if ((jl & 1) == 0) {
                 if constexpr (P::kSplitOut) {
