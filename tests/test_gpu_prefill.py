@@ -149,3 +149,45 @@ def test_many_row_call_reports_errors(case):
         M.mtp_check(ws)
     assert e.value.code == code
     assert kv.len.cpu().tolist() == want
+
+
+def test_prefill_one_split_attention_ragged_with_prefix():
+    """Calls with more than 4096 query rows per kv head take one split and the prefill attention
+    (query blocks over the waves, K/V tiles in LDS): 8 query heads on one kv head at 640 rows per
+    sequence, two sequences with 640 and 517 valid rows, after a 40-row call that left 37 and 20
+    positions in the caches (so the causal windows start past position 0 and differ per
+    sequence, and the last tiles are partial).  Every valid row's hidden and K/V, the logits and
+    the drafts against the oracle's two draft_step calls."""
+    cfg = CONFIGS["tiny"].replace(index=43, wdtype="bf16", n_heads=8, n_kv_heads=1, head_dim=128, hidden=256,
+                                  ffn=512, vocab=3000, embed_std=1.0, batch=2, prefill_rows=0)
+    w = make_weights(cfg)
+    model = O.OracleModel(cfg, w)
+    c, gw = config(cfg), upload_weights(cfg, w)
+    rng = np.random.default_rng(cfg.index)
+    B, H = 2, cfg.hidden
+    max_len = M.round_max_len(640 + 40 + 8)
+    kv = M.KVCache(c, B, max_len)
+    cache = O.KVCache(cfg, B, max_len)
+    ws = M.new_workspace(M.mtp_draft_workspace_size(c, B, 640, 1, max_len))
+    ulp = 2.0 ** -7
+    for rows, valid in ((40, [37, 20]), (640, [640, 517])):
+        toks = rng.integers(0, cfg.vocab, size=(B, rows)).astype(np.int32)
+        for b, n in enumerate(valid):
+            toks[b, n:] = -1
+        hid = rng.standard_normal((B, rows, H)).astype(np.float32)
+        hout, draft, logits = _prefill(c, gw, kv, toks, hid, ws)
+        h_o, d_o, l_o, m_o = O.draft_step(model, cache, toks, hid)
+        assert kv.len.cpu().tolist() == cache.len.tolist()
+        hg, lg = hout.cpu().numpy(), logits.cpu().numpy()
+        for b, n in enumerate(valid):
+            for i in range(n):
+                assert max_rel(hg[b, i], h_o[b, i]) < 2e-2, (rows, b, i)
+            assert max_rel(lg[b], l_o[b]) < 2e-2, (rows, b)
+            if m_o[b] >= MARGIN:
+                assert int(draft[b]) == d_o[b], (rows, b)
+    L = cache.len.tolist()
+    kg = kv.k.float().cpu().numpy()
+    vg = kv.v.transpose(-1, -2).float().cpu().numpy()
+    for b in range(B):
+        assert max_rel(kg[:, b, :, :L[b]], cache.K[:, b, :, :L[b]]) < ulp, b
+        assert max_rel(vg[:, b, :, :L[b]], cache.V[:, b, :, :L[b]]) < ulp, b
