@@ -1087,15 +1087,22 @@ void launch_attention(AttnArgs a, int wdtype, float* out, hipStream_t st) {
     const double kv_bytes = 4.0 * a.B * a.nkv * (double)a.max_len * HD;
     if constexpr (HD == 128) {
       // a batch whose (sequence, kv head) pairs fill the GPU on their own, over a long cache:
-      // the LDS-staged kernel (one wave per SIMD, registers free for the prefetch);
-      // (up to 16 queries per kv head, one tile held in registers: a catch-up of several rows
-      // per sequence measured no faster here than k_attn_mfma's two-tile kernel)
-      if (a.B * a.nkv >= 128 && a.max_len >= 1024 && a.qstride <= 16) {
-        dim3 grid(a.nsplit, a.nkv * attn_qgroups(a, 16), a.B);
-        if (a.max_len % 64 == 0)
-          hipLaunchKernelGGL((k_attn_lds<1, 4, 64, 1, true>), grid, dim3(kWG), 0, st, a);
-        else
-          hipLaunchKernelGGL((k_attn_lds<1, 4, 64, 1, false>), grid, dim3(kWG), 0, st, a);
+      // the LDS-staged kernel (one wave per SIMD, registers free for the prefetch), for up to
+      // two query tiles per kv head
+      if (a.B * a.nkv >= 128 && a.max_len >= 1024 && a.qstride <= 32) {
+        if (a.qstride <= 16) {
+          dim3 grid(a.nsplit, a.nkv * attn_qgroups(a, 16), a.B);
+          if (a.max_len % 64 == 0)
+            hipLaunchKernelGGL((k_attn_lds<1, 4, 64, 1, true>), grid, dim3(kWG), 0, st, a);
+          else
+            hipLaunchKernelGGL((k_attn_lds<1, 4, 64, 1, false>), grid, dim3(kWG), 0, st, a);
+        } else {
+          // two query tiles (a catch-up of a few rows per sequence): 32-position superslices keep
+          // the operands and the prefetch in registers (64 spill); their value rows are 64-byte
+          // half lines, so the loads stay cached
+          dim3 grid(a.nsplit, a.nkv * attn_qgroups(a, 32), a.B);
+          hipLaunchKernelGGL((k_attn_lds<2, 4, 32, 1, false>), grid, dim3(kWG), 0, st, a);
+        }
         if (!a.out) hipLaunchKernelGGL((k_attn_combine<HD>), dim3(a.B * a.rps * a.nq), dim3(kWG), 0, st, a, out);
         return;
       }
