@@ -261,12 +261,12 @@ struct PGateUp : PBase<W> {
   __device__ void store_pair(int m, int, int row, float gt, float up) {
     aout[(long)row * F + (m >> 1)] = gt / (1.0f + expf(-gt)) * up;
   }
-  // the same, and the value split into bf16 hi + lo at compact row cr of down_proj's activations
-  // (the split k_prep would make of it: the down projection takes it without a preparation)
+  // the same value, split into bf16 hi + lo at compact row cr of down_proj's activations instead
+  // (the split k_prep would make of it): the down projection then takes it without a
+  // preparation, so the fp32 row (read only by that preparation) is not written
   static constexpr bool kSplitOut = true;
-  __device__ void store_pair_split(int m, int, int row, int cr, float gt, float up, uint16_t* shi, uint16_t* slo) {
+  __device__ void store_pair_split(int m, int, int, int cr, float gt, float up, uint16_t* shi, uint16_t* slo) {
     const float y = gt / (1.0f + expf(-gt)) * up;
-    aout[(long)row * F + (m >> 1)] = y;
     const uint32_t h = bf16_rne(y);
     shi[(long)cr * F + (m >> 1)] = (uint16_t)h;
     slo[(long)cr * F + (m >> 1)] = (uint16_t)bf16_rne(y - __uint_as_float(h << 16));
