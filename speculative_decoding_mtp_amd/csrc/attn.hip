@@ -765,7 +765,8 @@ __global__ __launch_bounds__(64 * NWV) void k_attn_lds(AttnArgs a) {
   const int cbase = a.shi ? attn_compact_base(a, b, s_cnt) : 0;
   const uint16_t* Kb = reinterpret_cast<const uint16_t*>(a.kc) + ((long)b * a.nkv + kvh) * a.max_len * HD;
   const uint16_t* Vt = reinterpret_cast<const uint16_t*>(a.vc) + ((long)b * a.nkv + kvh) * a.max_len * HD;
-  const float scale = 1.0f / sqrtf(float(HD));
+  // scores and running maxima in base 2 (times log2(e) / sqrt(hd)): one v_exp_f32 per probability
+  const float c2 = 1.4426950408889634f / sqrtf(float(HD));
   const int krow = 8 * (j >> 2) + (j & 3);  // this lane's K row in sub-tile 0 (+4 in sub-tile 1)
   char* tK = sKV[wid];
   char* tV = sKV[wid] + KT;
@@ -889,31 +890,33 @@ __global__ __launch_bounds__(64 * NWV) void k_attn_lds(AttnArgs a) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int p = ph + 8 * hq + e;
-            const float v = (p < p_end && p <= lim[qt]) ? sc[e >> 2][e & 3] * scale : -INFINITY;
+            const float v = (p < p_end && p <= lim[qt]) ? sc[e >> 2][e & 3] * c2 : -INFINITY;
             pe[e] = v;
             mx = fmaxf(mx, v);
           }
-          mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-          mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+          mx = col_max(mx);
           const float m_new = fmaxf(m_run[qt], mx);
           float alpha = 1.f, rs = 0.f;
           if (m_new != -INFINITY) {
-            alpha = m_run[qt] == -INFINITY ? 0.f : expf(m_run[qt] - m_new);
+            alpha = __builtin_amdgcn_exp2f(m_run[qt] - m_new);  // 0 while m_run is -inf
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              pe[e] = pe[e] == -INFINITY ? 0.f : expf(pe[e] - m_new);
+              pe[e] = __builtin_amdgcn_exp2f(pe[e] - m_new);  // masked: exp2(-inf) = 0
               rs += pe[e];
             }
           } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) pe[e] = 0.f;
           }
-          rs += __shfl_xor(rs, 16, kWave);
-          rs += __shfl_xor(rs, 32, kWave);
+          rs = col_sum(rs);
           l_run[qt] = l_run[qt] * alpha + rs;
           m_run[qt] = m_new;
-          bf16x8_t pH, pL;
-          split_bf16x8(pe, pH, pL);
+          bf16x8_t pH, pL;  // probabilities as bf16 hi + lo (hardware round to nearest even)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            pH[e] = (__bf16)pe[e];
+            pL[e] = (__bf16)(pe[e] - (float)pH[e]);
+          }
 #pragma unroll
           for (int dt = 0; dt < ND; ++dt) {
             acc[dt][qt] *= alpha;
@@ -940,7 +943,7 @@ __global__ __launch_bounds__(64 * NWV) void k_attn_lds(AttnArgs a) {
         if (c == 0 || pc < p_stop) compute(pc);
       }
     }
-    // merge the waves: o = sum_w o_w e^{m_w - M}, l = sum_w l_w e^{m_w - M}
+    // merge the waves: o = sum_w o_w 2^{m_w - M}, l = sum_w l_w 2^{m_w - M} (base-2 maxima)
     if (hq == 0) {
 #pragma unroll
       for (int qt = 0; qt < NQT; ++qt) {
@@ -959,7 +962,7 @@ __global__ __launch_bounds__(64 * NWV) void k_attn_lds(AttnArgs a) {
 #pragma unroll
     for (int qt = 0; qt < NQT; ++qt) {
       const float M = row_max(16 * qt + j);
-      cw[qt] = m_run[qt] == -INFINITY ? 0.f : expf(m_run[qt] - M);
+      cw[qt] = m_run[qt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[qt] - M);
     }
     for (int w = 0; w < NWV; ++w) {
       if (wid == w) {
@@ -982,7 +985,7 @@ __global__ __launch_bounds__(64 * NWV) void k_attn_lds(AttnArgs a) {
     auto row_sum = [&](int q, float M) {
       float L = 0.f;
       for (int w = 0; w < NWV; ++w)
-        if (sm[w][q] != -INFINITY) L += sl[w][q] * expf(sm[w][q] - M);
+        if (sm[w][q] != -INFINITY) L += sl[w][q] * __builtin_amdgcn_exp2f(sm[w][q] - M);
       return L;
     };
     if (a.out) {  // the only split: normalise here and write the output rows (no combine pass)
@@ -1005,7 +1008,7 @@ __global__ __launch_bounds__(64 * NWV) void k_attn_lds(AttnArgs a) {
       for (int q = tid; q < QB; q += NT) {
         if (q0 + q < NQ) {
           const float M = row_max(q);
-          P[(long)(q0 + q) * (HD + 2) + HD] = M;
+          P[(long)(q0 + q) * (HD + 2) + HD] = M * 0.6931471805599453f;  // the combine's natural units
           P[(long)(q0 + q) * (HD + 2) + HD + 1] = row_sum(q, M);
         }
       }

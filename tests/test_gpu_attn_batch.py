@@ -3,8 +3,9 @@ caches of 1000+ positions, which takes the LDS-staged decode attention -- agains
 
 Ragged per-sequence cache lengths (not multiples of the 64-position superslice), catch-up calls
 of one to four rows per sequence (some sequences without rows), query groups of 2 and 8 per kv
-head (the LDS-staged kernel takes up to 16 queries per kv head, the catch-up of 4 rows x 8 the
-two-tile MFMA kernel), and capacities of 1280 and 1288 positions (value rows on whole 128-byte
+head (the LDS-staged kernel with one query tile up to 16 queries per kv head, with two tiles the
+catch-up of 4 rows x 8; 32 sequences x 4 kv heads take two splits and the combine), and capacities
+of 1280 and 1288 positions (value rows on whole 128-byte
 lines, read nontemporally, or straddling lines, read through the cache).  Every sequence's hiddens, logits and draft of
 each step and the appended K/V are compared.  Bar: 2e-3 max relative error on hiddens and logits
 (bf16 weights and K/V on both sides, fp32 against float64 arithmetic), K/V within one bf16 ulp,
