@@ -32,6 +32,23 @@ __device__ __forceinline__ void attn_store(const AttnArgs& a, float* out, long o
   }
 }
 
+// Max and sum over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lanes of a query column), by the
+// in-register half swaps: with both operands x, a swap returns x[l] and its partner in the two
+// results of every lane, so one max (or add, commutative) per swap leaves every lane with the
+// same value.
+__device__ __forceinline__ float col_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+__device__ __forceinline__ float col_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
 // ---------------------------------------------------------------------------------------------
 // decode attention, split over the cached positions (fp32 caches: VALU kernel)
 // ---------------------------------------------------------------------------------------------
@@ -235,7 +252,8 @@ __global__ __launch_bounds__(kWG) void k_attn(AttnArgs a) {
 //   8 (m / 4) + 4 t + m % 4 of the slice, so that result element r of lane (h = l / 16, j = l % 16)
 //   in sub-tile t is position 8 h + 4 t + r: each lane ends up with 8 consecutive positions of
 //   query column j;
-// * softmax over those 8 scores, reduced over the four lanes of the column;
+// * softmax over those 8 scores, reduced over the four lanes of the column (in base 2: one
+//   v_exp_f32 per probability; the maxima handed to the combine in natural units);
 // * O^T[d][q] += sum_p V^T[d][p] P[q][p] with V^T (the cache holds values transposed) as A and
 //   the lane's 8 probabilities (split hi + lo) as B: the K index 8 h + e of a lane is exactly its
 //   position 8 h + e.
@@ -272,7 +290,8 @@ __global__ __launch_bounds__(kWG) void k_attn_mfma(AttnArgs a) {
   const int cbase = a.shi ? attn_compact_base(a, b, s_cnt) : 0;
   const uint16_t* Kb = reinterpret_cast<const uint16_t*>(a.kc) + ((long)b * a.nkv + kvh) * a.max_len * HD;
   const uint16_t* Vt = reinterpret_cast<const uint16_t*>(a.vc) + ((long)b * a.nkv + kvh) * a.max_len * HD;
-  const float scale = 1.0f / sqrtf(float(HD));
+  // scores and running maxima in base 2 (times log2(e) / sqrt(hd)): one v_exp_f32 per probability
+  const float c2 = 1.4426950408889634f / sqrtf(float(HD));
   const int krow = 8 * (j >> 2) + (j & 3);  // this lane's K row in sub-tile 0 (+4 in sub-tile 1)
 
   for (int q0 = qgrp * QB; q0 < NQ; q0 += QB * nqgrp) {
@@ -356,31 +375,33 @@ __global__ __launch_bounds__(kWG) void k_attn_mfma(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int p = pw + 8 * hq + e;
-          const float v = (p < p_end && p <= lim[qt]) ? sc[e >> 2][e & 3] * scale : -INFINITY;
+          const float v = (p < p_end && p <= lim[qt]) ? sc[e >> 2][e & 3] * c2 : -INFINITY;
           pe[e] = v;
           mx = fmaxf(mx, v);
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+        mx = col_max(mx);
         const float m_new = fmaxf(m_run[qt], mx);
         float alpha = 1.f, rs = 0.f;
         if (m_new != -INFINITY) {
-          alpha = m_run[qt] == -INFINITY ? 0.f : expf(m_run[qt] - m_new);
+          alpha = __builtin_amdgcn_exp2f(m_run[qt] - m_new);  // 0 while m_run is -inf
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            pe[e] = pe[e] == -INFINITY ? 0.f : expf(pe[e] - m_new);
+            pe[e] = __builtin_amdgcn_exp2f(pe[e] - m_new);  // masked: exp2(-inf) = 0
             rs += pe[e];
           }
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) pe[e] = 0.f;
         }
-        rs += __shfl_xor(rs, 16, kWave);
-        rs += __shfl_xor(rs, 32, kWave);
+        rs = col_sum(rs);
         l_run[qt] = l_run[qt] * alpha + rs;
         m_run[qt] = m_new;
-        bf16x8_t ph, pl;
-        split_bf16x8(pe, ph, pl);
+        bf16x8_t ph, pl;  // probabilities as bf16 hi + lo (hardware round to nearest even)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          ph[e] = (__bf16)pe[e];
+          pl[e] = (__bf16)(pe[e] - (float)ph[e]);
+        }
         // value positions of this lane past the range are zeroed (they may hold anything)
         const int keep = p_end - (pw + 8 * hq);
         uint32_t vm[4];
@@ -398,7 +419,7 @@ __global__ __launch_bounds__(kWG) void k_attn_mfma(AttnArgs a) {
         }
       }
     }
-    // merge the four waves: o = sum_w o_w e^{m_w - M}, l = sum_w l_w e^{m_w - M}
+    // merge the four waves: o = sum_w o_w 2^{m_w - M}, l = sum_w l_w 2^{m_w - M} (base-2 maxima)
     if (hq == 0) {
 #pragma unroll
       for (int qt = 0; qt < NQT; ++qt) {
@@ -412,7 +433,7 @@ __global__ __launch_bounds__(kWG) void k_attn_mfma(AttnArgs a) {
     for (int qt = 0; qt < NQT; ++qt) {
       const int q = 16 * qt + j;
       const float M = fmaxf(fmaxf(sm[0][q], sm[1][q]), fmaxf(sm[2][q], sm[3][q]));
-      cw[qt] = m_run[qt] == -INFINITY ? 0.f : expf(m_run[qt] - M);
+      cw[qt] = m_run[qt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[qt] - M);
     }
     for (int w = 0; w < 4; ++w) {
       if (wid == w) {
@@ -437,7 +458,7 @@ __global__ __launch_bounds__(kWG) void k_attn_mfma(AttnArgs a) {
         const float M = fmaxf(fmaxf(sm[0][q], sm[1][q]), fmaxf(sm[2][q], sm[3][q]));
         float L = 0.f;
         for (int w = 0; w < 4; ++w)
-          if (sm[w][q] != -INFINITY) L += sl[w][q] * expf(sm[w][q] - M);
+          if (sm[w][q] != -INFINITY) L += sl[w][q] * __builtin_amdgcn_exp2f(sm[w][q] - M);
         sl[0][q] = L;
       }
       __syncthreads();
@@ -460,8 +481,8 @@ __global__ __launch_bounds__(kWG) void k_attn_mfma(AttnArgs a) {
           const float M = fmaxf(fmaxf(sm[0][q], sm[1][q]), fmaxf(sm[2][q], sm[3][q]));
           float L = 0.f;
           for (int w = 0; w < 4; ++w)
-            if (sm[w][q] != -INFINITY) L += sl[w][q] * expf(sm[w][q] - M);
-          P[(long)(q0 + q) * (HD + 2) + HD] = M;
+            if (sm[w][q] != -INFINITY) L += sl[w][q] * __builtin_amdgcn_exp2f(sm[w][q] - M);
+          P[(long)(q0 + q) * (HD + 2) + HD] = M * 0.6931471805599453f;  // the combine's natural units
           P[(long)(q0 + q) * (HD + 2) + HD + 1] = L;
         }
       }
@@ -494,22 +515,6 @@ constexpr int kPfT = 64;   // positions per LDS tile
 
 __device__ __forceinline__ int pf_kswz(int r) { return (r & 3) | ((r >> 3) & 3) << 2; }
 
-// Max and sum over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lanes of a query column), by the
-// in-register half swaps: with both operands x, a swap returns x[l] and its partner in the two
-// results of every lane, so one max (or add, commutative) per swap leaves every lane with the
-// same value.
-__device__ __forceinline__ float col_max(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
-}
-__device__ __forceinline__ float col_sum(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
-}
 __device__ __forceinline__ int pf_vswz(int d) { return (d ^ (d >> 3)) & 7; }
 
 __global__ __launch_bounds__(kWG, 2) void k_attn_prefill(AttnArgs a) {
