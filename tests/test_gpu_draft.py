@@ -2,7 +2,8 @@
 
 Bar: draft tokens and verify outputs bit-exact except where the oracle's top-2 logit gap is
 below 1e-4 (then the oracle's token is fed to both sides); hiddens and logits within max
-relative error 1e-4 for fp32 weights and 2e-2 for bf16 weights."""
+relative error 1e-4 for fp32 weights and 2e-3 for bf16 weights (fp32 against float64 arithmetic on
+identical bf16 operands)."""
 import numpy as np
 import pytest
 import torch
@@ -18,7 +19,7 @@ from tests.gpu_util import MARGIN, config, f32, i32, kv_from_numpy, max_rel, upl
 
 
 def _tol(cfg):
-    return 1e-4 if cfg.wdtype == "f32" else 2e-2
+    return 1e-4 if cfg.wdtype == "f32" else 2e-3
 
 
 def _setup(cfg, max_extra=64):

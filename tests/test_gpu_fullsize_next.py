@@ -7,7 +7,7 @@ sampled outputs the oracle computes one by one:
   vocab 129280, B 32, D 3, 8192-position caches), three sampled sequences.
 
 Bar: drafts exact except where the oracle's top-2 gap is below 1e-4 (later steps of that sequence
-are then not compared), hiddens and logits within max relative error 2e-2, lengths exact."""
+are then not compared), hiddens and logits within max relative error 2e-3, lengths exact."""
 import numpy as np
 import pytest
 import torch
@@ -20,7 +20,7 @@ pytestmark = [pytest.mark.gpu]
 M = pytest.importorskip("speculative_decoding_mtp_amd")
 from tests.gpu_util import MARGIN, config, f32, i32, kv_from_numpy, max_rel, to_dev, upload_weights  # noqa: E402
 
-TOL = 2e-2
+TOL = 2e-3
 
 
 def _compare(dg, hg, lg, d_o, h_o, l_o, m_o):

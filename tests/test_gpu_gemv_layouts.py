@@ -5,7 +5,7 @@ so does its down projection with a 4096-wide FFN), plus a ragged batch.
 
 Compared with the oracle's draft_step ([HB14] "14. MTP: speculative decoding with the built-in
 draft head", section "The draft head"): every valid row's post-norm hidden and the appended K/V
-within max relative error 1e-4 (fp32) or 2e-2 (bf16), the last row's logits likewise, the draft
+within max relative error 1e-4 (fp32) or 2e-3 (bf16), the last row's logits likewise, the draft
 bit-exact where the oracle's top-2 gap is at least 1e-4, cache lengths exact."""
 import numpy as np
 import pytest
@@ -54,7 +54,7 @@ def test_split_k_layouts_match_oracle(shape, B, rows, valid):
     M.mtp_draft_step(c, gw, kv, rows, i32(toks), f32(hid), hout, draft, logits, ws)
     M.mtp_check(ws)
     h_o, d_o, l_o, m_o = O.draft_step(model, cache, toks, hid)
-    tol = 1e-4 if cfg.wdtype == "f32" else 2e-2
+    tol = 1e-4 if cfg.wdtype == "f32" else 2e-3
     assert kv.len.cpu().tolist() == [cfg.ctx + n for n in valid]
     hg, lg = hout.cpu().numpy(), logits.cpu().numpy()
     kg = kv.k.float().cpu().numpy()

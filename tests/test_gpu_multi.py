@@ -4,7 +4,7 @@ verification and a crop of every module's cache, compared with the oracle round 
 
 Bar as for the single-module loop: drafts bit-exact while the oracle's top-2 gap is at least
 1e-4 (later steps of that round are then not compared); hiddens and logits within 1e-4 (fp32) or
-2e-2 (bf16) max relative error; cache lengths exact.  Both verifiers judge the oracle's drafts."""
+2e-3 (bf16) max relative error; cache lengths exact.  Both verifiers judge the oracle's drafts."""
 import numpy as np
 import pytest
 import torch
@@ -49,7 +49,7 @@ def _rounds(cfg, M, rounds):
     n_acc = torch.zeros(B, dtype=torch.int32, device="cuda")
     out = torch.zeros(B, D + 1, dtype=torch.int32, device="cuda")
     crop = torch.zeros(B, dtype=torch.int32, device="cuda")
-    tol = 1e-4 if cfg.wdtype == "f32" else 2e-2
+    tol = 1e-4 if cfg.wdtype == "f32" else 2e-3
     compared = 0
     for r in range(rounds):
         rps = toks.shape[1]

@@ -6,7 +6,10 @@ attention.
 * parity with the oracle on a small bf16 head at 2048 rows: every row's K/V (up to rare one-ulp
   flips of bf16 rounding), the hiddens of sampled rows and the last row's logits and draft;
 * at the 2048-hidden head's full size: one 2048-row call equals two 1024-row calls (the same
-  cache, hiddens and draft), a property that holds at any size."""
+  cache, hiddens and draft), a property that holds at any size.
+
+bf16 bar: max relative error 1e-3 on hiddens and logits (bf16 weights on both sides, fp32 against
+float64 arithmetic; measured at most 9e-6, printed by each case)."""
 import numpy as np
 import pytest
 import torch
@@ -18,6 +21,8 @@ pytestmark = pytest.mark.gpu
 
 M = pytest.importorskip("speculative_decoding_mtp_amd")
 from tests.gpu_util import MARGIN, config, f32, i32, max_rel, upload_weights  # noqa: E402
+
+TOL = 1e-3  # bf16 weights on both sides, fp32 against float64 arithmetic (measured <= 9e-6)
 
 
 def _prefill(c, gw, kv, toks, hid, ws):
@@ -51,9 +56,10 @@ def test_prefill_2048_rows_matches_oracle():
     assert max_rel(kv.v[..., :R].transpose(-1, -2).float().cpu().numpy(), cache.V[..., :R, :]) < ulp
     rows = list(range(0, R, 61)) + list(range(R - 8, R))
     hg = hout.cpu().numpy()
-    for i in rows:
-        assert max_rel(hg[0, i], h_o[0, i]) < 2e-2, i
-    assert max_rel(logits.cpu().numpy(), l_o) < 2e-2
+    eh = max(max_rel(hg[0, i], h_o[0, i]) for i in rows)
+    el = max_rel(logits.cpu().numpy(), l_o)
+    print("prefill 2048 rows: hidden", eh, "logits", el, flush=True)
+    assert eh < TOL and el < TOL, (eh, el)
     if m_o[0] >= MARGIN:
         assert int(draft[0]) == d_o[0]
 
@@ -114,14 +120,15 @@ def test_ragged_batched_prefill_matches_oracle(wdtype):
     hout, draft, logits = _prefill(c, gw, kv, toks, hid, ws)
     h_o, d_o, l_o, m_o = O.draft_step(model, cache, toks, hid)
     assert kv.len.cpu().tolist() == list(cache.len) == [s + k for s, k in zip(start, n)]
-    tol, ktol = (1e-4, 1e-5) if wdtype == "f32" else (2e-2, 2.0 ** -7)
+    tol, ktol = (1e-4, 1e-5) if wdtype == "f32" else (TOL, 2.0 ** -7)
     hg, lg, dg = hout.cpu().numpy(), logits.cpu().numpy(), draft.cpu().numpy()
     for b in range(3):
         T = start[b] + n[b]
         assert max_rel(kv.k[:, b, :, :T].float().cpu().numpy(), cache.K[:, b, :, :T]) < ktol, b
         assert max_rel(kv.v[:, b, ..., :T].transpose(-1, -2).float().cpu().numpy(), cache.V[:, b, :, :T]) < ktol, b
-        assert max_rel(hg[b, :n[b]], h_o[b, :n[b]]) < tol, b
-        assert max_rel(lg[b], l_o[b]) < tol, b
+        eh, el = max_rel(hg[b, :n[b]], h_o[b, :n[b]]), max_rel(lg[b], l_o[b])
+        print("ragged prefill", wdtype, b, "hidden", eh, "logits", el, flush=True)
+        assert eh < tol and el < tol, (b, eh, el)
         if m_o[b] >= MARGIN:
             assert dg[b] == d_o[b], b
 
@@ -180,9 +187,10 @@ def test_prefill_one_split_attention_ragged_with_prefix():
         assert kv.len.cpu().tolist() == cache.len.tolist()
         hg, lg = hout.cpu().numpy(), logits.cpu().numpy()
         for b, n in enumerate(valid):
-            for i in range(n):
-                assert max_rel(hg[b, i], h_o[b, i]) < 2e-2, (rows, b, i)
-            assert max_rel(lg[b], l_o[b]) < 2e-2, (rows, b)
+            eh = max(max_rel(hg[b, i], h_o[b, i]) for i in range(n))
+            el = max_rel(lg[b], l_o[b])
+            print("one-split prefill", rows, b, "hidden", eh, "logits", el, flush=True)
+            assert eh < TOL and el < TOL, (rows, b, eh, el)
             if m_o[b] >= MARGIN:
                 assert int(draft[b]) == d_o[b], (rows, b)
     L = cache.len.tolist()

@@ -3,7 +3,7 @@ values ([DLM "MTP speculative decoding"] item 1), through mtp_draft_loop_shared_
 
 Bar as for the own-cache head: drafts bit-exact while the oracle's top-2 gap is at least 1e-4
 (after a smaller gap the later steps may follow another token and are not compared); hiddens and
-logits within max relative error 1e-4 (fp32) or 2e-2 (bf16).  The main model's cache and lengths
+logits within max relative error 1e-4 (fp32) or 2e-3 (bf16).  The main model's cache and lengths
 must come back bit-identical."""
 import numpy as np
 import pytest
@@ -54,7 +54,7 @@ def _run(cfg, T, kv_layer, lens, toks, D, drop_kv_weights=False):
     d_o, h_o, l_o, m_o = O.draft_loop_shared(model, ref, kv_layer, toks, hid, D)
     assert torch.equal(kv.k, k0) and torch.equal(kv.v, v0)
     assert kv.len.cpu().tolist() == list(lens)
-    tol = 1e-4 if cfg.wdtype == "f32" else 2e-2
+    tol = 1e-4 if cfg.wdtype == "f32" else 2e-3
     dg, hg, lgg = drafts.cpu().numpy(), hs.cpu().numpy(), lg.cpu().numpy()
     compared = 0
     for b in range(B):

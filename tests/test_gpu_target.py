@@ -4,7 +4,7 @@ GPU -- target prefill, head prefill, draft loop, target verify pass, greedy veri
 giving exactly the target's plain greedy output (the greedy identity of [HB14 "Acceptance rate
 and speed-up"], [DLM] item 3).
 
-Bar: logits and hiddens within max relative error 1e-4 (fp32) / 2e-2 (bf16); K/V within 1e-5
+Bar: logits and hiddens within max relative error 1e-4 (fp32) / 2e-3 (bf16); K/V within 1e-5
 (fp32) or one bf16 ulp (rare rounding flips of values computed in fp32 vs float64);
 emitted tokens identical up to the first plain-greedy decision whose top-2 logit gap is below
 1e-4 (none occur for these seeds)."""
@@ -37,7 +37,7 @@ def test_target_forward_matches_oracle(kind):
     else:
         cfg = CONFIGS["tiny"].replace(index=32, wdtype="bf16", n_heads=4, n_kv_heads=2, head_dim=128, hidden=512,
                                       ffn=1024, vocab=5000, embed_std=1.0)
-        B, rows, tol = (2, 4, 2e-2) if kind == "bf16" else (5, 4, 2e-2)   # 20 rows: the MFMA path
+        B, rows, tol = (2, 4, 2e-3) if kind == "bf16" else (5, 4, 2e-3)   # 20 rows: the MFMA path
     _, tcfg, tw = _target(cfg, 2, std=0.05)
     tm = O.TargetModel(tcfg, tw)
     c, gw = config(tcfg), upload_target_weights(tcfg, tw)

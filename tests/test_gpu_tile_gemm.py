@@ -12,7 +12,9 @@ two ranges whose reduction writes down_proj's split activations.
 Compared with the oracle's draft_step ([HB14] "14. MTP: speculative decoding with the built-in
 draft head", section "The draft head"): every valid row's post-norm hidden and appended K/V, the
 last row's logits and the draft (where the oracle's top-2 gap is at least 1e-4); cache lengths
-exact.  bf16 weights: max relative error 2e-2 per row; the bf16 K/V within one bf16 ulp."""
+exact.  bf16 weights on both sides, fp32 against float64 arithmetic: max relative error 1e-3 per
+row (measured at most 6e-5 on hiddens and 4e-6 on logits; printed by each case), twenty times
+tighter than the 2e-2 the comparison was first held to; the bf16 K/V within one bf16 ulp."""
 import numpy as np
 import pytest
 import torch
@@ -24,6 +26,8 @@ pytestmark = pytest.mark.gpu
 
 M = pytest.importorskip("speculative_decoding_mtp_amd")
 from tests.gpu_util import MARGIN, config, f32, i32, max_rel, upload_weights  # noqa: E402
+
+TOL = 1e-3  # bf16 weights on both sides, fp32 against float64 arithmetic (measured <= 6e-5)
 
 
 @pytest.mark.parametrize("B, rows, valid, hidden, ffn", [(1, 1152, [1152], 256, 4096), (2, 640, [640, 517], 256, 4096),
@@ -57,11 +61,18 @@ def test_large_tile_gemm_rows_match_oracle(B, rows, valid, hidden, ffn):
     kg = kv.k.float().cpu().numpy()
     vg = kv.v.transpose(-1, -2).float().cpu().numpy()
     ulp = 2.0 ** -7
+    err = dict(hidden=0.0, logits=0.0, kv=0.0)  # the largest errors reached, printed below
     for b, n in enumerate(valid):
         for i in range(n):
-            assert max_rel(hg[b, i], h_o[b, i]) < 2e-2, (b, i)
-        assert max_rel(kg[:, b, :, :n], cache.K[:, b, :, :n]) < ulp, b
-        assert max_rel(vg[:, b, :, :n], cache.V[:, b, :, :n]) < ulp, b
-        assert max_rel(lg[b], l_o[b]) < 2e-2, b
+            e = max_rel(hg[b, i], h_o[b, i])
+            err["hidden"] = max(err["hidden"], e)
+            assert e < TOL, (b, i, e)
+        ek, ev = max_rel(kg[:, b, :, :n], cache.K[:, b, :, :n]), max_rel(vg[:, b, :, :n], cache.V[:, b, :, :n])
+        err["kv"] = max(err["kv"], ek, ev)
+        assert ek < ulp and ev < ulp, (b, ek, ev)
+        e = max_rel(lg[b], l_o[b])
+        err["logits"] = max(err["logits"], e)
+        assert e < TOL, (b, e)
         if m_o[b] >= MARGIN:
             assert int(draft[b]) == d_o[b], b
+    print("tile gemm", rows, valid, hidden, ffn, err, flush=True)
