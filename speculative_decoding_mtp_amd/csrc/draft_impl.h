@@ -714,11 +714,17 @@ hipError_t launch_gemv(P& p, hipStream_t st, int* grid_used = nullptr, const Mfm
                        const KTimer& tm = KTimer(), const ReduceCtx& rc = ReduceCtx(), bool prepped = false) {
   if constexpr (std::is_same<W, BF16>::value) {
     if (use_mfma<W>(p, mb)) {
+      // the whole row in registers, with no more chunks per thread than the row has (fewer
+      // registers: more rows resident; the chunks and sums are the same for every choice)
       if (prepped) {
-      } else if (p.K > 4 * kWG * W::VE) {  // rows wider than 8192: the whole row in registers
+      } else if (p.K > 4 * kWG * W::VE) {  // rows wider than 8192
         hipLaunchKernelGGL((k_prep<W, P, 12>), dim3(p.nact), dim3(kWG), 0, st, p, *mb);
-      } else {
+      } else if (p.K > 2 * kWG * W::VE) {
         hipLaunchKernelGGL((k_prep<W, P, 4>), dim3(p.nact), dim3(kWG), 0, st, p, *mb);
+      } else if (p.K > kWG * W::VE) {
+        hipLaunchKernelGGL((k_prep<W, P, 2>), dim3(p.nact), dim3(kWG), 0, st, p, *mb);
+      } else {
+        hipLaunchKernelGGL((k_prep<W, P, 1>), dim3(p.nact), dim3(kWG), 0, st, p, *mb);
       }
       if constexpr (!P::kArgmax) {
         // hundreds of rows (a prefill, by the activation count, an upper bound of the valid
@@ -839,7 +845,13 @@ struct CanFuse<PResidual<W>, PLmHead<W>> : std::true_type {};
 
 template <class W, class P, class Pn>
 hipError_t launch_reduce_prep(const P& p, const Pn& pn, const MfmaBufs& m, hipStream_t st) {
-  if (p.N <= 4 * kWG * 8)
+  // as many chunks per thread as the row needs (the 2048-wide rows of a prefill: one chunk, 38
+  // registers instead of 146, so more rows resident at once)
+  if (p.N <= kWG * 8)
+    hipLaunchKernelGGL((k_reduce_prep<W, P, Pn, 1>), dim3(p.nact), dim3(kWG), 0, st, p, pn, m);
+  else if (p.N <= 2 * kWG * 8)
+    hipLaunchKernelGGL((k_reduce_prep<W, P, Pn, 2>), dim3(p.nact), dim3(kWG), 0, st, p, pn, m);
+  else if (p.N <= 4 * kWG * 8)
     hipLaunchKernelGGL((k_reduce_prep<W, P, Pn, 4>), dim3(p.nact), dim3(kWG), 0, st, p, pn, m);
   else
     hipLaunchKernelGGL((k_reduce_prep<W, P, Pn, 12>), dim3(p.nact), dim3(kWG), 0, st, p, pn, m);

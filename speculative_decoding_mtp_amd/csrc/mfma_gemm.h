@@ -37,7 +37,8 @@ struct MfmaBufs {
 
 // One workgroup per activation index a (grid = nact).  The first KEEP chunks of each thread
 // stay in registers, with their gains, across the norm reduction (KEEP = 12 holds rows of up to
-// 24576 columns, chosen for rows wider than 8192; 4 otherwise); their loads are issued
+// 24576 columns, chosen for rows wider than 8192; otherwise 4, 2 or 1, no more than the row
+// needs, so that fewer registers let more rows run at once); their loads are issued
 // unconditionally from clamped columns -- before the row counts are in LDS when the row is
 // known without them -- so the row arrives in one memory round trip.  The hi / lo rows are
 // written 16 bytes at a time.
