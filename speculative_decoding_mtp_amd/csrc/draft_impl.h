@@ -635,7 +635,7 @@ hipError_t launch_stream_t(P& p, hipStream_t st, int* grid_used, const MfmaBufs&
     return e;
   }
   if (m.part) {
-    const long items = (long)m.cap * (p.N / (P::kPair ? 2 : 1));
+    const long items = (long)m.cap * (p.N / 4);
     const int rgrid = (int)std::min<long>((items + kWG - 1) / kWG, 4096);
     hipLaunchKernelGGL((k_splitk_reduce<P>), dim3(rgrid), dim3(kWG), 0, st, p, m);
   }
@@ -759,7 +759,7 @@ hipError_t launch_gemv(P& p, hipStream_t st, int* grid_used = nullptr, const Mfm
             return e;
           }
           if (m.part) {
-            const long items = (long)m.cap * (p.N / (P::kPair ? 2 : 1));
+            const long items = (long)m.cap * (p.N / 4);
             const int rgrid = (int)std::min<long>((items + kWG - 1) / kWG, 4096);
             hipLaunchKernelGGL((k_splitk_reduce<P>), dim3(rgrid), dim3(kWG), 0, st, p, m);
           }

@@ -487,7 +487,8 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_gemm_tile(P p, MfmaBufs mb)
 }
 
 // Sum the split-K partials of each (compact row, column) in split order and store them through
-// the policy (pairs for pair policies).  One thread per output (or output pair).
+// the policy (pairs for pair policies).  One thread per four consecutive outputs (16-byte partial
+// loads; N % 4 == 0, as every matrix of the MFMA path has), each summed in split order as before.
 template <class P>
 __global__ __launch_bounds__(kWG) void k_splitk_reduce(P p, MfmaBufs mb) {
   __shared__ int s_n[kMaxBatch];
@@ -495,29 +496,35 @@ __global__ __launch_bounds__(kWG) void k_splitk_reduce(P p, MfmaBufs mb) {
   p.setup(s_n, s_len);
   __syncthreads();
   const int count = *mb.count;
-  const int step = P::kPair ? 2 : 1;
-  const long items = (long)count * (p.N / step);
+  const int nq = p.N / 4;
+  const long items = (long)count * nq;
   for (long it = (long)blockIdx.x * kWG + threadIdx.x; it < items; it += (long)gridDim.x * kWG) {
-    const int cr = (int)(it / (p.N / step));
-    const int col = (int)(it - (long)cr * (p.N / step)) * step;
-    float v0 = 0.f, v1 = 0.f;
+    const int cr = (int)(it / nq);
+    const int col = (int)(it - (long)cr * nq) * 4;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
     for (int k = 0; k < mb.ksplit; ++k) {
-      const float* pp = mb.part + ((long)k * mb.cap + cr) * p.N + col;
-      v0 += pp[0];
-      if (P::kPair) v1 += pp[1];
+      const float4 q = *reinterpret_cast<const float4*>(mb.part + ((long)k * mb.cap + cr) * p.N + col);
+      v[0] += q.x;
+      v[1] += q.y;
+      v[2] += q.z;
+      v[3] += q.w;
     }
     const int row = mb.rowmap[cr], a = mb.amap[cr];
     if constexpr (P::kPair) {
-      if constexpr (P::kSplitOut) {
-        if (mb.shi)
-          p.store_pair_split(col, a, row, cr, v0, v1, mb.shi, mb.slo);
-        else
-          p.store_pair(col, a, row, v0, v1);
-      } else {
-        p.store_pair(col, a, row, v0, v1);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if constexpr (P::kSplitOut) {
+          if (mb.shi)
+            p.store_pair_split(col + 2 * h, a, row, cr, v[2 * h], v[2 * h + 1], mb.shi, mb.slo);
+          else
+            p.store_pair(col + 2 * h, a, row, v[2 * h], v[2 * h + 1]);
+        } else {
+          p.store_pair(col + 2 * h, a, row, v[2 * h], v[2 * h + 1]);
+        }
       }
     } else {
-      p.store(col, a, row, v0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p.store(col + e, a, row, v[e]);
     }
   }
 }
